@@ -1,0 +1,243 @@
+"""fp64 CPU oracle for the fused KV-cache quantizer -- test infrastructure only.
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product library never does, and this package never
+imports the product library: the two share no code.  The arithmetic lives in
+``kvq_oracle.c`` (plain C, binary64, single-threaded); this module only
+marshals numpy arrays into it.
+
+Every function takes and returns numpy arrays; binary16 data travels as its
+raw ``uint16`` bit patterns so that the oracle sees exactly the bytes a GPU
+kernel saw.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_LIB = os.path.join(_HERE, "libkvq_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/libkvq_oracle.so``."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=False)
+    _lib = bind(_LIB)
+    return _lib
+
+
+def bind(path: str):
+    """Load a compiled oracle library from `path` and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I64, I32 = ctypes.c_int64, ctypes.c_int
+    sig = {
+        "kvqo_f16_decode": (None, [I64, P, P]),
+        "kvqo_f16_encode": (None, [I64, P, P]),
+        "kvqo_hadamard_entry": (I32, [I32, I32]),
+        "kvqo_rotate_rows": (I32, [I64, I32, P, P, P, P]),
+        "kvqo_unrotate_rows": (I32, [I64, I32, P, P, P, P, P]),
+        "kvqo_pack_nibbles": (None, [I64, P, P]),
+        "kvqo_unpack_nibbles": (None, [I64, P, P]),
+        "kvqo_codes_given_scales": (I32, [I64, I32, I32, P, P, P]),
+        "kvqo_quantize_rows": (I64, [I64, I32, I32, P, P, P, P, P, P]),
+        "kvqo_dequantize_rows": (I32, [I64, I32, I32, P, P, P, P, P, P]),
+        "kvqo_vq_encode_rows": (I32, [I64, I32, I32, I32, P, P, P, P, P, P, P]),
+        "kvqo_vq_distances": (I32, [I64, I32, I32, I32, P, P, P, P, P]),
+        "kvqo_vq_decode_rows": (I32, [I64, I32, I32, I32, P, P, P, P, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _out(shape, dtype):
+    a = np.empty(shape, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rows(x, D):
+    x = np.asarray(x)
+    return int(x.size // D)
+
+
+# --------------------------------------------------------------------- fp16
+def f16_to_f64(bits):
+    bits, pb = _c(bits, np.uint16)
+    out, po = _out(bits.shape, np.float64)
+    _load().kvqo_f16_decode(bits.size, pb, po)
+    return out
+
+
+def f64_to_f16(v):
+    v, pv = _c(v, np.float64)
+    out, po = _out(v.shape, np.uint16)
+    _load().kvqo_f16_encode(v.size, pv, po)
+    return out
+
+
+def hadamard_entry(i: int, j: int) -> int:
+    return int(_load().kvqo_hadamard_entry(int(i), int(j)))
+
+
+# ----------------------------------------------------------------- rotation
+def rotate(x_bits, lam, signs):
+    """y = D^-1/2 H diag(s) diag(lambda) x for every row; x as fp16 bits [n, D]."""
+    x, px = _c(x_bits, np.uint16)
+    D = x.shape[-1]
+    lam, pl = _c(np.broadcast_to(lam, x.shape), np.float32)
+    s, ps = _c(signs, np.int8)
+    y, py = _out(x.shape, np.float64)
+    rc = _load().kvqo_rotate_rows(_rows(x, D), D, px, pl, ps, py)
+    if rc:
+        raise ValueError("oracle rotate rejected D=%d" % D)
+    return y
+
+
+def unrotate(yhat, lam, signs):
+    """(x64, x16bits) = unscale(inverse rotation of yhat) for every row."""
+    yh, py = _c(yhat, np.float64)
+    D = yh.shape[-1]
+    lam, pl = _c(np.broadcast_to(lam, yh.shape), np.float32)
+    s, ps = _c(signs, np.int8)
+    x64, p64 = _out(yh.shape, np.float64)
+    x16, p16 = _out(yh.shape, np.uint16)
+    rc = _load().kvqo_unrotate_rows(_rows(yh, D), D, py, pl, ps, p64, p16)
+    if rc:
+        raise ValueError("oracle unrotate rejected D=%d" % D)
+    return x64, x16
+
+
+# ---------------------------------------------------------------- nibbles
+def pack_nibbles(q):
+    q, pq = _c(q, np.int8)
+    out, po = _out(q.shape[:-1] + (q.shape[-1] // 2,), np.uint8)
+    _load().kvqo_pack_nibbles(q.size, pq, po)
+    return out
+
+
+def unpack_nibbles(b):
+    b, pb = _c(b, np.uint8)
+    out, po = _out(b.shape[:-1] + (b.shape[-1] * 2,), np.int8)
+    _load().kvqo_unpack_nibbles(b.size, pb, po)
+    return out
+
+
+# --------------------------------------------------------------- quantizer
+def codes_given_scales(y, scales_bits, G):
+    """Unpacked int8 codes of rotated rows y [n, D] under given fp16 scales."""
+    y, py = _c(y, np.float64)
+    D = y.shape[-1]
+    sc, ps = _c(scales_bits, np.uint16)
+    q, pq = _out(y.shape, np.int8)
+    rc = _load().kvqo_codes_given_scales(_rows(y, D), D, int(G), py, ps, pq)
+    if rc:
+        raise ValueError("bad group size")
+    return q
+
+
+def quantize(x_bits, lam, signs, G):
+    """Returns (codes u8 [.., D/2], scales fp16-bits [.., D/G], y fp64 [.., D], n_bad)."""
+    x, px = _c(x_bits, np.uint16)
+    D = x.shape[-1]
+    lam, pl = _c(np.broadcast_to(lam, x.shape), np.float32)
+    s, ps = _c(signs, np.int8)
+    codes, pc = _out(x.shape[:-1] + (D // 2,), np.uint8)
+    scales, psc = _out(x.shape[:-1] + (D // G,), np.uint16)
+    y, py = _out(x.shape, np.float64)
+    bad = _load().kvqo_quantize_rows(_rows(x, D), D, int(G), px, pl, ps, pc, psc, py)
+    if bad < 0:
+        raise ValueError("oracle quantize rejected D=%d G=%d" % (D, G))
+    return codes, scales, y, int(bad)
+
+
+def dequantize(codes, scales_bits, lam, signs, G):
+    """Returns (x64 fp64 [.., D], x16 fp16-bits [.., D])."""
+    c, pc = _c(codes, np.uint8)
+    D = c.shape[-1] * 2
+    sc, psc = _c(scales_bits, np.uint16)
+    shape = c.shape[:-1] + (D,)
+    lam, pl = _c(np.broadcast_to(lam, shape), np.float32)
+    s, ps = _c(signs, np.int8)
+    x64, p64 = _out(shape, np.float64)
+    x16, p16 = _out(shape, np.uint16)
+    rc = _load().kvqo_dequantize_rows(_rows(x64, D), D, int(G), pc, psc, pl, ps, p64, p16)
+    if rc:
+        raise ValueError("oracle dequantize rejected D=%d G=%d" % (D, G))
+    return x64, x16
+
+
+# ---------------------------------------------------------------------- VQ
+def vq_encode(x_bits, lam, signs, codebooks_bits, book, sub):
+    """Returns (idx u16 [n, D/sub], y fp64 [n, D]).  codebooks [B, K, sub] fp16 bits."""
+    x, px = _c(x_bits, np.uint16)
+    n, D = x.shape
+    cb, pcb = _c(codebooks_bits, np.uint16)
+    K = cb.shape[-2]
+    bk, pbk = _c(np.broadcast_to(book, (n,)), np.int32)
+    lam, pl = _c(np.broadcast_to(lam, x.shape), np.float32)
+    s, ps = _c(signs, np.int8)
+    idx, pi = _out((n, D // sub), np.uint16)
+    y, py = _out(x.shape, np.float64)
+    rc = _load().kvqo_vq_encode_rows(n, D, int(sub), K, px, pl, ps, pcb, pbk, pi, py)
+    if rc:
+        raise ValueError("oracle vq_encode rejected")
+    return idx, y
+
+
+def vq_distances(y, codebooks_bits, book, idx, sub):
+    y, py = _c(y, np.float64)
+    n, D = y.shape
+    cb, pcb = _c(codebooks_bits, np.uint16)
+    K = cb.shape[-2]
+    bk, pbk = _c(np.broadcast_to(book, (n,)), np.int32)
+    ix, pix = _c(idx, np.uint16)
+    d, pd = _out((n, D // sub), np.float64)
+    rc = _load().kvqo_vq_distances(n, D, int(sub), K, py, pcb, pbk, pix, pd)
+    if rc:
+        raise ValueError("oracle vq_distances rejected (index out of range?)")
+    return d
+
+
+def vq_decode(idx, codebooks_bits, book, lam, signs, sub):
+    ix, pix = _c(idx, np.uint16)
+    n = ix.shape[0]
+    D = ix.shape[1] * sub
+    cb, pcb = _c(codebooks_bits, np.uint16)
+    K = cb.shape[-2]
+    bk, pbk = _c(np.broadcast_to(book, (n,)), np.int32)
+    lam, pl = _c(np.broadcast_to(lam, (n, D)), np.float32)
+    s, ps = _c(signs, np.int8)
+    x64, p64 = _out((n, D), np.float64)
+    x16, p16 = _out((n, D), np.uint16)
+    rc = _load().kvqo_vq_decode_rows(n, D, int(sub), K, pix, pcb, pbk, pl, ps, p64, p16)
+    if rc:
+        raise ValueError("oracle vq_decode rejected (index out of range?)")
+    return x64, x16

@@ -1,0 +1,395 @@
+/*
+ * kvq_oracle.c -- plain, slow, single-threaded fp64 CPU oracle for the fused
+ * per-vector KV-cache quantizer (sign-randomized Walsh-Hadamard rotation with a
+ * per-(head, channel) smooth scale, per-group abs-max int4 with nibble packing,
+ * its inverse, and the product-VQ encode/decode variant).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library's product path includes,
+ * links or calls this file.  It is used by the test-suite, by the smoke check
+ * and by the CPU-baseline leg of the benchmark, and it shares no code, header,
+ * table or constant with the HIP kernels.
+ *
+ * Every value is computed in IEEE binary64.  The Hadamard product is the dense
+ * O(D^2) definition, not a butterfly; the binary16 codec is written from the
+ * IEEE 754 binary16 format definition; rounding to integers uses nearbyint()
+ * under the default round-to-nearest-even mode.  Built with
+ * -ffp-contract=off so that no multiply-add is fused behind our back.
+ *
+ * Sources (cited by page title and section):
+ *  [VQ-blog]  "The Kernel That Finally Did Something -- And Didn't Quite Agree
+ *             With Itself" (VeloxQuant-MLX blog, tag vecinfer), sections
+ *             "What VecInfer does" and "The numbers".
+ *  [README]   VeloxQuant-MLX 0.52.0 package description, section
+ *             "Metal kernels" (quantize_vq: nearest centroid, argmin kept in
+ *             registers).
+ *  [ABSTRACT] "When Quantization Is Free: An int4 KV Cache That Outruns fp16
+ *             on Apple Silicon" (arXiv 2605.05699), abstract.
+ *  [GIST]     gist.science explanation of arXiv 2605.05699, "Technische
+ *             Samenvatting" -> "Methodologie" sections 1 (sign-randomized
+ *             transform), 2 (fused kernel step list), 3 (per-channel plus
+ *             per-group scaling).
+ *
+ * Readings of points the pages leave open (each one is listed, with its
+ * reasoning, in the design notes of the repository):
+ *  - lambda multiplies x before the rotation, and divides after the inverse
+ *    rotation ("smooth scale ... then rotation"; "unscale" last) [VQ-blog].
+ *  - Hadamard in Sylvester (natural) order, H[i][j] = (-1)^popcount(i & j),
+ *    normalised by D^-1/2 in both directions (the transform is described as
+ *    unitary) [GIST s.1].
+ *  - groups are contiguous runs of G rotated coordinates [GIST s.2, s.3].
+ *  - symmetric int4: scale = amax / 7 stored as binary16 (round to nearest
+ *    even), codes = clamp(round_half_even(y / stored_scale), -7, 7); an
+ *    all-zero group gets scale 0 and codes 0 [ABSTRACT; GIST s.2].
+ *  - nibble format: two's complement 4-bit, element 2k in the low nibble of
+ *    byte k [GIST s.2 "two int4 values in one byte"].
+ *  - VQ: contiguous sub-vectors, squared Euclidean distance on the unrounded
+ *    rotated key, lowest index on ties [README "Metal kernels"; VQ-blog].
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16 codec, from the format definition:                       */
+/*   1 sign bit, 5 exponent bits (bias 15), 10 fraction bits;                 */
+/*   exponent 0 = subnormal (fraction * 2^-24), exponent 31 = inf / NaN.      */
+/* ------------------------------------------------------------------------ */
+
+double kvqo_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);
+    } else if (e == 31) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp(1.0 + (double)f / 1024.0, e - 15);
+    }
+    return sign ? -v : v;
+}
+
+/* Round a binary64 value to the nearest binary16, ties to even. */
+uint16_t kvqo_f64_to_f16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v)) return (uint16_t)(sign | 0x7e00);
+    /* 65504 is the largest finite value; half-way to 2^16 is 65520, and the
+       tie goes to the even neighbour 2^16, which overflows to infinity. */
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7c00);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: integer multiple of 2^-24 (a carry to 1024 lands
+           exactly on the smallest normal encoding 0x0400) */
+        double n = nearbyint(ldexp(a, 24));
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int k;
+    double m = frexp(a, &k);      /* a = m * 2^k, m in [0.5, 1) */
+    int E = k - 1;                /* a = (2m) * 2^E, 2m in [1, 2) */
+    double n = nearbyint((2.0 * m - 1.0) * 1024.0);
+    if (n == 1024.0) { n = 0.0; E += 1; }
+    if (E + 15 >= 31) return (uint16_t)(sign | 0x7c00);
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)n);
+}
+
+void kvqo_f16_decode(int64_t n, const uint16_t* h, double* out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = kvqo_f16_to_f64(h[i]);
+}
+
+void kvqo_f16_encode(int64_t n, const double* v, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = kvqo_f64_to_f16(v[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Walsh-Hadamard matrix, Sylvester order                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Entry (i, j) of the unnormalised D x D Sylvester Hadamard matrix. */
+int kvqo_hadamard_entry(int i, int j)
+{
+    return (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1;
+}
+
+static int is_pow2(int d) { return d > 0 && (d & (d - 1)) == 0; }
+
+/* Rotation of one vector [GIST s.1; VQ-blog "What VecInfer does"]:
+     y_i = D^-1/2 * sum_j H[i][j] * s_j * lambda_j * x_j
+   x is binary16 (decoded exactly), lambda binary32, s in {-1, +1}. */
+static void rotate_one(int D, const uint16_t* x, const float* lam,
+                       const int8_t* s, double* v, double* y)
+{
+    for (int j = 0; j < D; j++)
+        v[j] = (double)s[j] * (double)lam[j] * kvqo_f16_to_f64(x[j]);
+    double norm = 1.0 / sqrt((double)D);
+    for (int i = 0; i < D; i++) {
+        double acc = 0.0;
+        for (int j = 0; j < D; j++) acc += kvqo_hadamard_entry(i, j) * v[j];
+        y[i] = acc * norm;
+    }
+}
+
+/* Inverse rotation [VQ-blog "The kernel toggle": inverse transform, then
+   unscale]:  xhat_j = (s_j / lambda_j) * D^-1/2 * sum_i H[i][j] * yhat_i.
+   H is symmetric and H*H = D*I, so this inverts rotate_one exactly. */
+static void unrotate_one(int D, const double* yhat, const float* lam,
+                         const int8_t* s, double* xhat)
+{
+    double norm = 1.0 / sqrt((double)D);
+    for (int j = 0; j < D; j++) {
+        double acc = 0.0;
+        for (int i = 0; i < D; i++) acc += kvqo_hadamard_entry(i, j) * yhat[i];
+        xhat[j] = ((double)s[j] / (double)lam[j]) * (acc * norm);
+    }
+}
+
+/* n vectors of length D; x [n, D] binary16 bits; lam [n, D] (the lambda row
+   that belongs to each vector's layer and head); s [D]; y [n, D]. */
+int kvqo_rotate_rows(int64_t n, int D, const uint16_t* x, const float* lam,
+                     const int8_t* s, double* y)
+{
+    if (!is_pow2(D)) return -1;
+    double* v = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!v) return -2;
+    for (int64_t r = 0; r < n; r++)
+        rotate_one(D, x + r * D, lam + r * D, s, v, y + r * D);
+    free(v);
+    return 0;
+}
+
+/* yhat [n, D] fp64 rotated-domain values -> xhat64 [n, D], and optionally the
+   binary16 rounding of it (xhat16 may be NULL). */
+int kvqo_unrotate_rows(int64_t n, int D, const double* yhat, const float* lam,
+                       const int8_t* s, double* xhat64, uint16_t* xhat16)
+{
+    if (!is_pow2(D)) return -1;
+    for (int64_t r = 0; r < n; r++) {
+        unrotate_one(D, yhat + r * D, lam + r * D, s, xhat64 + r * D);
+        if (xhat16)
+            for (int j = 0; j < D; j++)
+                xhat16[r * D + j] = kvqo_f64_to_f16(xhat64[r * D + j]);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Group quantizer and nibble format [ABSTRACT; GIST s.2, s.3]                 */
+/* ------------------------------------------------------------------------ */
+
+/* Code of one rotated value given the stored (binary16-decoded) scale of its
+   group: 0 for a zero scale, else round-half-even of y/scale clamped to
+   [-7, 7]. */
+static int code_of(double y, double scale)
+{
+    if (scale == 0.0) return 0;
+    double r = nearbyint(y / scale);
+    if (r > 7.0) r = 7.0;
+    if (r < -7.0) r = -7.0;
+    return (int)r;
+}
+
+/* Byte k holds element 2k in bits 0..3 and element 2k+1 in bits 4..7, each
+   as 4-bit two's complement. */
+void kvqo_pack_nibbles(int64_t n_codes, const int8_t* q, uint8_t* bytes)
+{
+    for (int64_t k = 0; k < n_codes / 2; k++)
+        bytes[k] = (uint8_t)(((unsigned)q[2 * k] & 0xfu) |
+                             (((unsigned)q[2 * k + 1] & 0xfu) << 4));
+}
+
+void kvqo_unpack_nibbles(int64_t n_bytes, const uint8_t* bytes, int8_t* q)
+{
+    for (int64_t k = 0; k < n_bytes; k++) {
+        int lo = bytes[k] & 0xf, hi = (bytes[k] >> 4) & 0xf;
+        q[2 * k] = (int8_t)(lo >= 8 ? lo - 16 : lo);
+        q[2 * k + 1] = (int8_t)(hi >= 8 ? hi - 16 : hi);
+    }
+}
+
+/* Codes of rotated vectors y [n, D] under given binary16 scales [n, D/G]
+   (unpacked, one int8 per coordinate). Used both by the quantizer and to
+   condition a comparison on another implementation's stored scale. */
+int kvqo_codes_given_scales(int64_t n, int D, int G, const double* y,
+                            const uint16_t* scales, int8_t* q)
+{
+    if (G <= 0 || D % G) return -1;
+    int ng = D / G;
+    for (int64_t r = 0; r < n; r++)
+        for (int i = 0; i < D; i++)
+            q[r * D + i] = (int8_t)code_of(y[r * D + i],
+                                           kvqo_f16_to_f64(scales[r * ng + i / G]));
+    return 0;
+}
+
+/* Quantize n vectors.  x [n, D] binary16, lam [n, D], s [D];
+   codes [n, D/2] packed bytes, scales [n, D/G] binary16 bits; y_out [n, D]
+   (may be NULL) receives the fp64 rotated values.
+   Per group g (coordinates gG .. gG+G-1):
+     amax = max |y_i|;  scale = binary16_rne(amax / 7);
+     q_i = clamp(rne(y_i / scale), -7, 7)  (0 when scale == 0).
+   Returns the number of vectors outside the domain (a non-finite input or a
+   scale that overflows binary16); their outputs are set to zero. */
+int64_t kvqo_quantize_rows(int64_t n, int D, int G, const uint16_t* x,
+                           const float* lam, const int8_t* s, uint8_t* codes,
+                           uint16_t* scales, double* y_out)
+{
+    if (!is_pow2(D) || G <= 0 || D % G || (G & 1)) return -1;
+    int ng = D / G;
+    double* v = (double*)malloc(sizeof(double) * (size_t)D);
+    double* y = (double*)malloc(sizeof(double) * (size_t)D);
+    int8_t* q = (int8_t*)malloc((size_t)D);
+    int64_t bad = 0;
+    for (int64_t r = 0; r < n; r++) {
+        int ok = 1;
+        for (int j = 0; j < D; j++)
+            if (!isfinite(kvqo_f16_to_f64(x[r * D + j]))) ok = 0;
+        if (ok) rotate_one(D, x + r * D, lam + r * D, s, v, y);
+        for (int g = 0; ok && g < ng; g++) {
+            double amax = 0.0;
+            for (int i = g * G; i < (g + 1) * G; i++)
+                if (fabs(y[i]) > amax) amax = fabs(y[i]);
+            uint16_t sc = kvqo_f64_to_f16(amax / 7.0);
+            if ((sc & 0x7c00) == 0x7c00) { ok = 0; break; }
+            scales[r * ng + g] = sc;
+            double sbar = kvqo_f16_to_f64(sc);
+            for (int i = g * G; i < (g + 1) * G; i++) q[i] = (int8_t)code_of(y[i], sbar);
+        }
+        if (!ok) {
+            bad++;
+            memset(codes + r * (D / 2), 0, (size_t)(D / 2));
+            memset(scales + r * ng, 0, sizeof(uint16_t) * (size_t)ng);
+            if (y_out) for (int i = 0; i < D; i++) y_out[r * D + i] = NAN;
+            continue;
+        }
+        kvqo_pack_nibbles(D, q, codes + r * (D / 2));
+        if (y_out) memcpy(y_out + r * D, y, sizeof(double) * (size_t)D);
+    }
+    free(v); free(y); free(q);
+    return bad;
+}
+
+/* Dequantize n vectors from packed codes [n, D/2] and binary16 scales
+   [n, D/G] [VQ-blog: dequantize -> inverse transform -> unscale]:
+     yhat_i = q_i * scale_g;  xhat = unrotate(yhat);
+   xhat64 [n, D] receives the exact fp64 result and xhat16 [n, D] (may be
+   NULL) its binary16 rounding. */
+int kvqo_dequantize_rows(int64_t n, int D, int G, const uint8_t* codes,
+                         const uint16_t* scales, const float* lam,
+                         const int8_t* s, double* xhat64, uint16_t* xhat16)
+{
+    if (!is_pow2(D) || G <= 0 || D % G || (G & 1)) return -1;
+    int ng = D / G;
+    int8_t* q = (int8_t*)malloc((size_t)D);
+    double* yh = (double*)malloc(sizeof(double) * (size_t)D);
+    for (int64_t r = 0; r < n; r++) {
+        kvqo_unpack_nibbles(D / 2, codes + r * (D / 2), q);
+        for (int i = 0; i < D; i++)
+            yh[i] = (double)q[i] * kvqo_f16_to_f64(scales[r * ng + i / G]);
+        unrotate_one(D, yh, lam + r * D, s, xhat64 + r * D);
+        if (xhat16)
+            for (int j = 0; j < D; j++)
+                xhat16[r * D + j] = kvqo_f64_to_f16(xhat64[r * D + j]);
+    }
+    free(q); free(yh);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Product VQ [README "Metal kernels"; VQ-blog "What VecInfer does"]           */
+/* ------------------------------------------------------------------------ */
+
+/* Squared distance between sub-vector ysub[0..sub) and centroid k of a
+   [K, sub] binary16 codebook, in fp64 (direct form). */
+static double subdist(int sub, const double* ysub, const uint16_t* cb, int k)
+{
+    double d = 0.0;
+    for (int t = 0; t < sub; t++) {
+        double diff = ysub[t] - kvqo_f16_to_f64(cb[(int64_t)k * sub + t]);
+        d += diff * diff;
+    }
+    return d;
+}
+
+/* Encode n vectors: rotate each (same rotation as the scalar quantizer, no
+   group quantizer), split into D/sub contiguous sub-vectors, and give each the
+   lowest index k attaining the minimum squared distance to centroid k.
+   codebooks [n_books, K, sub] binary16; book [n] picks each vector's codebook
+   (the vector's KV head); idx [n, D/sub]; y_out (may be NULL) [n, D]. */
+int kvqo_vq_encode_rows(int64_t n, int D, int sub, int K, const uint16_t* x,
+                        const float* lam, const int8_t* s,
+                        const uint16_t* codebooks, const int32_t* book,
+                        uint16_t* idx, double* y_out)
+{
+    if (!is_pow2(D) || sub <= 0 || D % sub || K <= 0 || K > 65536) return -1;
+    int nsub = D / sub;
+    double* v = (double*)malloc(sizeof(double) * (size_t)D);
+    double* y = (double*)malloc(sizeof(double) * (size_t)D);
+    for (int64_t r = 0; r < n; r++) {
+        rotate_one(D, x + r * D, lam + r * D, s, v, y);
+        const uint16_t* cb = codebooks + (int64_t)book[r] * K * sub;
+        for (int j = 0; j < nsub; j++) {
+            int best = 0;
+            double bd = subdist(sub, y + j * sub, cb, 0);
+            for (int k = 1; k < K; k++) {
+                double d = subdist(sub, y + j * sub, cb, k);
+                if (d < bd) { bd = d; best = k; }
+            }
+            idx[r * nsub + j] = (uint16_t)best;
+        }
+        if (y_out) memcpy(y_out + r * D, y, sizeof(double) * (size_t)D);
+    }
+    free(v); free(y);
+    return 0;
+}
+
+/* Distances d[r, j] between sub-vector j of y [n, D] and the centroid that
+   idx [n, D/sub] names, in fp64. */
+int kvqo_vq_distances(int64_t n, int D, int sub, int K, const double* y,
+                      const uint16_t* codebooks, const int32_t* book,
+                      const uint16_t* idx, double* d)
+{
+    if (sub <= 0 || D % sub) return -1;
+    int nsub = D / sub;
+    for (int64_t r = 0; r < n; r++) {
+        const uint16_t* cb = codebooks + (int64_t)book[r] * K * sub;
+        for (int j = 0; j < nsub; j++) {
+            int k = idx[r * nsub + j];
+            if (k >= K) return -2;
+            d[r * nsub + j] = subdist(sub, y + r * D + j * sub, cb, k);
+        }
+    }
+    return 0;
+}
+
+/* Decode n vectors: yhat = concatenation of the named centroids, then the
+   inverse rotation and unscale; xhat64 [n, D], xhat16 [n, D] (may be NULL). */
+int kvqo_vq_decode_rows(int64_t n, int D, int sub, int K, const uint16_t* idx,
+                        const uint16_t* codebooks, const int32_t* book,
+                        const float* lam, const int8_t* s, double* xhat64,
+                        uint16_t* xhat16)
+{
+    if (!is_pow2(D) || sub <= 0 || D % sub || K <= 0) return -1;
+    int nsub = D / sub;
+    double* yh = (double*)malloc(sizeof(double) * (size_t)D);
+    for (int64_t r = 0; r < n; r++) {
+        const uint16_t* cb = codebooks + (int64_t)book[r] * K * sub;
+        for (int j = 0; j < nsub; j++) {
+            int k = idx[r * nsub + j];
+            if (k >= K) { free(yh); return -2; }
+            for (int t = 0; t < sub; t++)
+                yh[j * sub + t] = kvqo_f16_to_f64(cb[(int64_t)k * sub + t]);
+        }
+        unrotate_one(D, yh, lam + r * D, s, xhat64 + r * D);
+        if (xhat16)
+            for (int j = 0; j < D; j++)
+                xhat16[r * D + j] = kvqo_f64_to_f16(xhat64[r * D + j]);
+    }
+    free(yh);
+    return 0;
+}

@@ -1,0 +1,421 @@
+"""Pins for the fp64 CPU oracle: each check ties it to something other than
+itself -- numpy's binary16 conversion, scipy's Sylvester Hadamard matrix and
+pairwise distances, closed forms, hand-derived worked examples and invariants
+of the quantizer -- chosen so that a dropped term, a wrong sign, a wrong
+index or a swapped order fails at least one of them."""
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.spatial.distance
+
+import oracle
+
+RNG = np.random.default_rng(20260507)
+
+
+def f16bits(a):
+    return np.asarray(a, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def bits_to_f64(b):
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def rand_x(n, D, scale=1.0):
+    return f16bits(RNG.standard_normal((n, D)) * scale)
+
+
+def rand_signs(D):
+    return (RNG.integers(0, 2, D) * 2 - 1).astype(np.int8)
+
+
+def rand_lambda(n, D):
+    return np.exp(RNG.standard_normal((n, D)) * 0.5).astype(np.float32)
+
+
+# ------------------------------------------------------------------ binary16
+def test_f16_decode_all_patterns_match_numpy():
+    b = np.arange(65536, dtype=np.uint16)
+    got = oracle.f16_to_f64(b)
+    ref = b.view(np.float16).astype(np.float64)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+    # signed zeros keep their sign
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0])
+
+
+def test_f16_encode_matches_numpy_rne():
+    # numpy rounds binary64 -> binary16 directly with round-half-even.
+    v = np.concatenate([
+        RNG.standard_normal(200000),
+        RNG.standard_normal(50000) * 1e-5,          # subnormal range
+        RNG.standard_normal(50000) * 3e4,           # near overflow
+        np.array([65504.0, 65519.99, 65520.0, 65536.0, 1e9, -65520.0,
+                  2.0 ** -24, 2.0 ** -25, 1.5 * 2.0 ** -25, 2.0 ** -26,
+                  2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 0.0, -0.0]),
+    ])
+    got = oracle.f64_to_f16(v)
+    ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_f16_encode_midpoints_go_to_even():
+    # Every finite positive pair of neighbours: the exact midpoint (representable
+    # in binary64) must round to the neighbour with an even fraction.
+    lo = np.arange(0, 0x7bff, dtype=np.uint16)
+    a = bits_to_f64(lo)
+    b = bits_to_f64(lo + 1)
+    mid = (a + b) / 2
+    got = oracle.f64_to_f16(mid)
+    want = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint16)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- Hadamard
+@pytest.mark.parametrize("D", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_hadamard_matches_scipy_sylvester(D):
+    H = np.array([[oracle.hadamard_entry(i, j) for j in range(D)] for i in range(D)])
+    assert np.array_equal(H, scipy.linalg.hadamard(D))
+    assert np.array_equal(H @ H.T, D * np.eye(D, dtype=H.dtype))   # H H^T = D I
+    assert np.array_equal(H, H.T)
+    if D >= 2:  # Sylvester recursion H_2n = [[H_n, H_n], [H_n, -H_n]]
+        h = D // 2
+        Hn = H[:h, :h]
+        assert np.array_equal(H[:h, h:], Hn) and np.array_equal(H[h:, :h], Hn)
+        assert np.array_equal(H[h:, h:], -Hn)
+
+
+# ---------------------------------------------------------------- rotation
+@pytest.mark.parametrize("D", [8, 64, 128, 256])
+def test_rotate_matches_dense_scipy_product(D):
+    n = 64
+    x = rand_x(n, D)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    y = oracle.rotate(x, lam, s)
+    H = scipy.linalg.hadamard(D).astype(np.float64)
+    v = bits_to_f64(x) * lam.astype(np.float64) * s
+    ref = (v @ H.T) / np.sqrt(D)
+    assert np.allclose(y, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("D", [8, 128])
+def test_rotate_basis_vectors_give_hadamard_columns(D):
+    H = scipy.linalg.hadamard(D)
+    ones = np.ones(D, np.float32)
+    for k in (0, 1, D // 2 - 1, D - 1):
+        x = np.zeros((1, D))
+        x[0, k] = 1.0
+        y = oracle.rotate(f16bits(x), ones, np.ones(D, np.int8))[0]
+        assert np.allclose(y, H[:, k] / np.sqrt(D), atol=1e-15)
+
+
+def test_lambda_multiplies_before_rotation():
+    D = 16
+    lam = np.ones(D, np.float32)
+    lam[5] = 2.0
+    x = np.zeros((1, D))
+    x[0, 5] = 3.0
+    y = oracle.rotate(f16bits(x), lam, np.ones(D, np.int8))[0]
+    H = scipy.linalg.hadamard(D)
+    assert np.allclose(y, 6.0 * H[:, 5] / 4.0, atol=1e-15)
+
+
+def test_signs_apply_before_rotation():
+    # s * x = all ones  =>  y = sqrt(D) e_0 exactly.
+    D = 128
+    s = rand_signs(D)
+    y = oracle.rotate(f16bits(s.astype(np.float64)[None]), np.ones(D, np.float32), s)[0]
+    want = np.zeros(D)
+    want[0] = np.sqrt(D)
+    assert np.allclose(y, want, atol=1e-12)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_parseval_and_roundtrip(D):
+    n = 200
+    x = rand_x(n, D, 3.0)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    y = oracle.rotate(x, lam, s)
+    lx = bits_to_f64(x) * lam.astype(np.float64)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(lx, axis=1), rtol=1e-12)
+    x64, _ = oracle.unrotate(y, lam, s)
+    xr = bits_to_f64(x)
+    assert np.abs(x64 - xr).max() <= 1e-12 * np.abs(xr).max()
+
+
+def test_unrotate_closed_form():
+    D = 32
+    lam = rand_lambda(1, D)[0]
+    s = rand_signs(D)
+    H = scipy.linalg.hadamard(D)
+    for k in (0, 7, 31):
+        yh = np.zeros((1, D))
+        yh[0, k] = 1.25
+        x64, x16 = oracle.unrotate(yh, lam, s)
+        want = (s / lam.astype(np.float64)) * 1.25 * H[k, :] / np.sqrt(D)
+        assert np.allclose(x64[0], want, rtol=1e-15, atol=0)
+        assert np.array_equal(x16[0], want.astype(np.float16).view(np.uint16))
+
+
+# ---------------------------------------------------------------- nibbles
+def test_nibbles_roundtrip_all_bytes():
+    b = np.arange(256, dtype=np.uint8)[None]
+    q = oracle.unpack_nibbles(b)
+    assert q.min() == -8 and q.max() == 7
+    assert np.array_equal(oracle.pack_nibbles(q), b)
+
+
+def test_nibbles_golden(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "nibbles.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                a, b, h = line.split()
+                rows.append((int(a), int(b), int(h, 16)))
+    q = np.array([[a, b] for a, b, _ in rows], np.int8).reshape(1, -1)
+    got = oracle.pack_nibbles(q)[0]
+    assert list(got) == [h for _, _, h in rows]
+    assert np.array_equal(oracle.unpack_nibbles(got[None])[0], q[0])
+
+
+# ---------------------------------------------------------------- quantizer
+def load_worked(golden_dir):
+    cases, cur = [], {}
+    with open(os.path.join(golden_dir, "worked_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line:
+                if cur:
+                    cases.append(cur)
+                cur = {}
+                continue
+            if line.startswith("#"):
+                continue
+            k, v = line.split(":", 1)
+            cur[k.strip()] = v.split()
+    if cur:
+        cases.append(cur)
+    return cases
+
+
+def test_worked_examples(golden_dir):
+    cases = load_worked(golden_dir)
+    assert len(cases) == 4
+    for c in cases:
+        D, G = int(c["D"][0]), int(c["G"][0])
+        lam = np.array([float(v) for v in c["lambda"]], np.float32)
+        s = np.array([int(v) for v in c["signs"]], np.int8)
+        x = np.array([int(v, 16) for v in c["x"]], np.uint16)[None]
+        codes, scales, y, bad = oracle.quantize(x, lam, s, G)
+        assert bad == 0
+        assert [int(v) for v in scales[0]] == [int(v, 16) for v in c["scales"]], c["name"]
+        assert [int(v) for v in codes[0]] == [int(v, 16) for v in c["codes"]], c["name"]
+        _, x16 = oracle.dequantize(codes, scales, lam, s, G)
+        assert [int(v) for v in x16[0]] == [int(v, 16) for v in c["xhat"]], c["name"]
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_case_single_spike(D):
+    # x = a e_k, lambda = 1, s = 1: every |y_i| = |a|/sqrt(D); every scale is
+    # fp16(|a|/(7 sqrt D)); every code is +-7 with the sign of a H[i][k].
+    G = 32
+    H = scipy.linalg.hadamard(D)
+    for a, k in ((1.5, 3), (-2.0, D - 1), (0.75, 0)):
+        x = np.zeros((1, D))
+        x[0, k] = a
+        codes, scales, _, bad = oracle.quantize(f16bits(x), np.ones(D, np.float32), np.ones(D, np.int8), G)
+        assert bad == 0
+        want_sc = np.float16(abs(a) / (7 * np.sqrt(D))).view(np.uint16)
+        assert (scales == want_sc).all()
+        q = oracle.unpack_nibbles(codes)[0]
+        assert np.array_equal(q, 7 * np.sign(a) * H[:, k])
+
+
+def test_case_all_ones_energy_in_group0():
+    D, G = 128, 32
+    s = rand_signs(D)
+    x = f16bits(s.astype(np.float64)[None])
+    codes, scales, _, bad = oracle.quantize(x, np.ones(D, np.float32), s, G)
+    q = oracle.unpack_nibbles(codes)[0]
+    assert scales[0, 0] == np.float16(np.sqrt(D) / 7).view(np.uint16)
+    assert (scales[0, 1:] == 0).all()
+    assert q[0] == 7 and (q[1:] == 0).all()
+
+
+def test_group_equal_to_D_is_per_vector_absmax():
+    D = 128
+    x = rand_x(50, D)
+    lam = rand_lambda(50, D)
+    s = rand_signs(D)
+    codes, scales, y, _ = oracle.quantize(x, lam, s, D)
+    want = (np.abs(y).max(axis=1) / 7).astype(np.float16).view(np.uint16)
+    assert np.array_equal(scales[:, 0], want)
+
+
+def test_ties_round_half_to_even():
+    # rotated values placed exactly on k + 1/2 steps of a stored scale
+    sc = np.float16(0.375)
+    sbar = float(sc)
+    halves = np.array([-6.5, -5.5, -4.5, -3.5, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5])
+    y = np.zeros((1, 16))
+    y[0, :14] = halves * sbar
+    y[0, 14] = 7.4 * sbar    # clamps to 7
+    y[0, 15] = -9.0 * sbar   # clamps to -7
+    q = oracle.codes_given_scales(y, np.array([[sc.view(np.uint16)]]), 16)[0]
+    want = list(np.round(halves).astype(int)) + [7, -7]     # numpy rounds half to even
+    assert list(q) == want
+    assert list(q[:14]) == [-6, -6, -4, -4, -2, -2, 0, 0, 2, 2, 4, 4, 6, 6]
+
+
+@pytest.mark.parametrize("D,G", [(128, 32), (64, 8)])
+def test_codes_given_scales_matches_quantizer(D, G):
+    # Conditioning on a stored scale must reproduce the quantizer's own codes
+    # when handed the quantizer's own scales (multi-group, so the group index
+    # of every coordinate matters).
+    x = rand_x(100, D)
+    lam = rand_lambda(100, D)
+    s = rand_signs(D)
+    codes, scales, y, _ = oracle.quantize(x, lam, s, G)
+    q = oracle.codes_given_scales(y, scales, G)
+    assert np.array_equal(q, oracle.unpack_nibbles(codes))
+
+
+def test_zero_scale_gives_zero_codes():
+    y = np.ones((1, 8)) * 1e-30
+    q = oracle.codes_given_scales(y, np.array([[0]], np.uint16), 8)
+    assert (q == 0).all()
+    codes, scales, _, bad = oracle.quantize(np.zeros((3, 64), np.uint16), np.ones(64, np.float32),
+                                            np.ones(64, np.int8), 32)
+    assert bad == 0 and (codes == 0).all() and (scales == 0).all()
+
+
+@pytest.mark.parametrize("D,G", [(64, 16), (128, 32), (128, 8), (256, 64), (128, 128)])
+def test_quantizer_invariants(D, G):
+    n = 400
+    x = rand_x(n, D, 2.0)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    codes, scales, y, bad = oracle.quantize(x, lam, s, G)
+    assert bad == 0
+    q = oracle.unpack_nibbles(codes).astype(np.float64)
+    sb = bits_to_f64(scales)
+    sbe = np.repeat(sb, G, axis=1)
+    assert np.abs(q).max() <= 7
+    # |y - q*scale| <= scale/2 for every element (uses the STORED scale)
+    assert (np.abs(y - q * sbe) <= sbe / 2 * (1 + 1e-12)).all()
+    # scale = fp16(amax/7) per group, and every non-zero group reaches |q| = 7
+    amax = np.abs(y).reshape(n, D // G, G).max(axis=2)
+    assert np.array_equal(scales, (amax / 7).astype(np.float16).view(np.uint16))
+    qa = np.abs(q).reshape(n, D // G, G).max(axis=2)
+    assert (qa[sb > 0] == 7).all()
+
+
+def test_out_of_domain_is_rejected():
+    D = 64
+    x = np.zeros((3, D), np.uint16)
+    x[1, 0] = 0x7c00                     # +inf
+    x[2, :] = np.float16(60000).view(np.uint16)   # amax/7 above 65504 once lambda = 16
+    lam = np.ones(D, np.float32) * 16
+    codes, scales, y, bad = oracle.quantize(x, lam, np.ones(D, np.int8), 32)
+    assert bad == 2
+
+
+# ---------------------------------------------------------------- dequant
+def test_dequant_single_code_closed_form():
+    D, G = 64, 16
+    lam = rand_lambda(1, D)[0]
+    s = rand_signs(D)
+    H = scipy.linalg.hadamard(D)
+    for k, c in ((0, 7), (17, -3), (63, 1)):
+        q = np.zeros((1, D), np.int8)
+        q[0, k] = c
+        scales = np.zeros((1, D // G), np.uint16)
+        scales[0, k // G] = np.float16(0.3125).view(np.uint16)
+        x64, x16 = oracle.dequantize(oracle.pack_nibbles(q), scales, lam, s, G)
+        want = (s / lam.astype(np.float64)) * c * 0.3125 * H[k, :] / np.sqrt(D)
+        assert np.allclose(x64[0], want, rtol=1e-14, atol=0)
+        assert np.array_equal(x16[0], want.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("D,G", [(128, 32), (256, 64), (64, 16)])
+def test_roundtrip_error_bound(D, G):
+    # ||lambda*(xhat - x)|| = ||yhat - y|| <= 1/2 sqrt(G * sum scale^2)
+    n = 300
+    x = rand_x(n, D)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    codes, scales, y, _ = oracle.quantize(x, lam, s, G)
+    x64, x16 = oracle.dequantize(codes, scales, lam, s, G)
+    err = np.linalg.norm(lam * (x64 - bits_to_f64(x)), axis=1)
+    bound = 0.5 * np.sqrt(G * (bits_to_f64(scales) ** 2).sum(axis=1))
+    assert (err <= bound * (1 + 1e-9)).all()
+    assert np.array_equal(x16, x64.astype(np.float16).view(np.uint16))
+
+
+def test_byte_accounting_3_56x():
+    # D=128, G=32: 64 code bytes + 4 fp16 scales = 72 B against 256 B of fp16,
+    # the top of the 3.0-3.56x compression range the paper reports.
+    D, G = 128, 32
+    codes, scales, _, _ = oracle.quantize(rand_x(1, D), np.ones(D, np.float32), np.ones(D, np.int8), G)
+    nbytes = codes.nbytes + scales.nbytes
+    assert nbytes == 72 and abs(2 * D / nbytes - 3.56) < 0.005
+
+
+# ---------------------------------------------------------------------- VQ
+@pytest.mark.parametrize("sub", [1, 2, 4, 8])
+@pytest.mark.parametrize("K", [1, 3, 16])
+def test_vq_encode_bruteforce(sub, K):
+    D, n = 16, 40
+    x = rand_x(n, D)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    cb = f16bits(RNG.standard_normal((2, K, sub)))
+    book = RNG.integers(0, 2, n).astype(np.int32)
+    idx, y = oracle.vq_encode(x, lam, s, cb, book, sub)
+    assert np.allclose(y, oracle.rotate(x, lam, s))
+    for r in range(n):
+        C = bits_to_f64(cb[book[r]])
+        d = scipy.spatial.distance.cdist(y[r].reshape(-1, sub), C, "sqeuclidean")
+        assert np.array_equal(idx[r], d.argmin(axis=1))      # first minimum = lowest index
+        got = oracle.vq_distances(y[r:r + 1], cb, book[r:r + 1], idx[r:r + 1], sub)[0]
+        assert np.allclose(got, d.min(axis=1), rtol=1e-13, atol=1e-15)
+
+
+def test_vq_duplicate_centroids_lowest_index_and_exact_hits():
+    # x = c * H[:, k]  =>  y = c * sqrt(D) * e_k exactly (D = 16, sqrt D = 4).
+    D, sub = 16, 4
+    H = scipy.linalg.hadamard(D)
+    x = (0.5 * H[:, 6])[None]            # y = 2 e_6 : sub-vector 1 = (0, 0, 2, 0)
+    cb = np.full((1, 8, sub), 3.0)
+    cb[0, 0] = [1, 1, 1, 1]
+    cb[0, 2] = [0, 0, 2, 0]               # exact hit for sub-vector 1
+    cb[0, 5] = [0, 0, 2, 0]               # duplicate, higher index
+    cb[0, 3] = [0, 0, 0, 0]               # exact hit for sub-vectors 0, 2, 3
+    cb[0, 6] = [0, 0, 0, 0]
+    cbb = f16bits(cb)
+    idx, y = oracle.vq_encode(f16bits(x), np.ones(D, np.float32), np.ones(D, np.int8), cbb,
+                              np.zeros(1, np.int32), sub)
+    assert list(idx[0]) == [3, 2, 3, 3]
+    d = oracle.vq_distances(y, cbb, np.zeros(1, np.int32), idx, sub)
+    assert (d == 0).all()
+
+
+def test_vq_decode_closed_form_and_roundtrip():
+    D, sub, K = 32, 8, 5
+    lam = rand_lambda(1, D)[0]
+    s = rand_signs(D)
+    cb = f16bits(RNG.standard_normal((1, K, sub)))
+    idx = np.array([[4, 0, 2, 2]], np.uint16)
+    x64, x16 = oracle.vq_decode(idx, cb, np.zeros(1, np.int32), lam, s, sub)
+    yh = bits_to_f64(cb[0][idx[0]]).reshape(-1)
+    H = scipy.linalg.hadamard(D)
+    want = (s / lam.astype(np.float64)) * (H @ yh) / np.sqrt(D)
+    assert np.allclose(x64[0], want, rtol=1e-13, atol=1e-15)
+    # encoding the decoded vector's exact rotation recovers the same indices
+    y = oracle.rotate(x16, lam, s)
+    idx2 = oracle.vq_encode(x16, lam, s, cb, np.zeros(1, np.int32), sub)[0]
+    assert np.array_equal(idx2, idx)

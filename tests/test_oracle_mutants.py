@@ -1,0 +1,120 @@
+"""Planted-mistake check of the oracle's pins (CPU only).
+
+Each mutant below copies the oracle's C source, plants one plausible mistake
+(a dropped term, a wrong sign or index, a swapped order, a different rounding
+rule), compiles it to a temporary library and runs the pin battery of
+test_oracle.py against it.  Every mutant must make at least one pin fail;
+the unmodified source must pass them all."""
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import tests.test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "kvq_oracle.c")
+
+MUTANTS = {
+    "lambda_divides_on_quantize": ("(double)s[j] * (double)lam[j] * kvqo_f16_to_f64(x[j])",
+                                   "(double)s[j] / (double)lam[j] * kvqo_f16_to_f64(x[j])"),
+    "signs_dropped": ("(double)s[j] * (double)lam[j] * kvqo_f16_to_f64(x[j])",
+                      "(double)lam[j] * kvqo_f16_to_f64(x[j])"),
+    "no_normalisation": ("y[i] = acc * norm;", "y[i] = acc;"),
+    "hadamard_sign_flipped": ("& 1) ? -1 : 1;", "& 1) ? 1 : -1;"),
+    "hadamard_or_index": ("popcount((unsigned)(i & j))", "popcount((unsigned)(i | j))"),
+    "unstored_scale": ("double sbar = kvqo_f16_to_f64(sc);", "double sbar = amax / 7.0;"),
+    "amax_over_8": ("kvqo_f64_to_f16(amax / 7.0)", "kvqo_f64_to_f16(amax / 8.0)"),
+    "round_half_away": ("double r = nearbyint(y / scale);", "double r = round(y / scale);"),
+    "truncate_codes": ("double r = nearbyint(y / scale);", "double r = trunc(y / scale);"),
+    "nibble_order_swapped": ("bytes[k] = (uint8_t)(((unsigned)q[2 * k] & 0xfu) |\n"
+                             "                             (((unsigned)q[2 * k + 1] & 0xfu) << 4));",
+                             "bytes[k] = (uint8_t)(((unsigned)q[2 * k + 1] & 0xfu) |\n"
+                             "                             (((unsigned)q[2 * k] & 0xfu) << 4));"),
+    "group_index_interleaved": ("kvqo_f16_to_f64(scales[r * ng + i / G]));",
+                                "kvqo_f16_to_f64(scales[r * ng + i % ng]));"),
+    "dequant_group_interleaved": ("(double)q[i] * kvqo_f16_to_f64(scales[r * ng + i / G]);",
+                                  "(double)q[i] * kvqo_f16_to_f64(scales[r * ng + i % ng]);"),
+    "unscale_multiplies": ("((double)s[j] / (double)lam[j]) * (acc * norm)",
+                           "((double)s[j] * (double)lam[j]) * (acc * norm)"),
+    "vq_ties_to_highest": ("if (d < bd) { bd = d; best = k; }", "if (d <= bd) { bd = d; best = k; }"),
+    "vq_abs_distance": ("d += diff * diff;", "d += fabs(diff);"),
+    "f16_truncates": ("double n = nearbyint((2.0 * m - 1.0) * 1024.0);",
+                      "double n = floor((2.0 * m - 1.0) * 1024.0);"),
+    "f16_subnormal_truncates": ("double n = nearbyint(ldexp(a, 24));", "double n = floor(ldexp(a, 24));"),
+}
+
+# every pin of test_oracle.py that takes no fixture other than golden_dir
+BATTERY = [
+    ("test_f16_encode_matches_numpy_rne", {}),
+    ("test_f16_encode_midpoints_go_to_even", {}),
+    ("test_hadamard_matches_scipy_sylvester", {"D": 16}),
+    ("test_rotate_matches_dense_scipy_product", {"D": 128}),
+    ("test_lambda_multiplies_before_rotation", {}),
+    ("test_signs_apply_before_rotation", {}),
+    ("test_parseval_and_roundtrip", {"D": 128}),
+    ("test_unrotate_closed_form", {}),
+    ("test_nibbles_golden", {"golden_dir": None}),
+    ("test_worked_examples", {"golden_dir": None}),
+    ("test_case_single_spike", {"D": 128}),
+    ("test_case_all_ones_energy_in_group0", {}),
+    ("test_ties_round_half_to_even", {}),
+    ("test_codes_given_scales_matches_quantizer", {"D": 128, "G": 32}),
+    ("test_quantizer_invariants", {"D": 128, "G": 32}),
+    ("test_dequant_single_code_closed_form", {}),
+    ("test_roundtrip_error_bound", {"D": 128, "G": 32}),
+    ("test_vq_encode_bruteforce", {"sub": 4, "K": 16}),
+    ("test_vq_duplicate_centroids_lowest_index_and_exact_hits", {}),
+    ("test_vq_decode_closed_form_and_roundtrip", {}),
+]
+
+
+def run_battery(lib, golden_dir):
+    """Run the battery with `lib` bound into the oracle module; return the
+    names of the pins that failed."""
+    failed = []
+    saved = oracle._lib
+    oracle._lib = lib
+    try:
+        for name, kw in BATTERY:
+            kw = {k: (golden_dir if k == "golden_dir" else v) for k, v in kw.items()}
+            try:
+                getattr(pins, name)(**kw)
+            except (AssertionError, ValueError):
+                failed.append(name)
+    finally:
+        oracle._lib = saved
+    return failed
+
+
+def compile_variant(src_text, tmpdir, tag):
+    c = os.path.join(tmpdir, tag + ".c")
+    so = os.path.join(tmpdir, tag + ".so")
+    with open(c, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-o", so, c, "-lm"], check=True)
+    return oracle.bind(so)
+
+
+@pytest.fixture(scope="module")
+def src():
+    with open(SRC) as f:
+        return f.read()
+
+
+def test_unmodified_source_passes_battery(src, golden_dir, tmp_path):
+    lib = compile_variant(src, str(tmp_path), "orig")
+    assert run_battery(lib, golden_dir) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, src, golden_dir, tmp_path):
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, "mutation site not found uniquely: %s" % name
+    lib = compile_variant(src.replace(old, new), str(tmp_path), name)
+    np.random.seed(0)
+    failed = run_battery(lib, golden_dir)
+    assert failed, "planted mistake %r passed every pin" % name
