@@ -1,0 +1,170 @@
+/*
+ * kvq.h -- C ABI of libkvq.so, a fused per-vector KV-cache quantizer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages (cited by title and section):
+ *  - "When Quantization Is Free: An int4 KV Cache That Outruns fp16 on Apple
+ *    Silicon" (arXiv 2605.05699), abstract: one fused kernel doing a
+ *    sign-randomized transform, a per-channel smooth scale lambda, per-group
+ *    abs-max and int4 nibble packing of the KV cache;
+ *  - gist.science explanation of the same paper, "Methodologie" s.1 (the
+ *    transform is diag(sign) then a unitary transform), s.2 (the fused
+ *    kernel's step list: signs in registers, transform, lambda, group
+ *    abs-max, signed int4 rounding, two codes per byte), s.3 (per-channel
+ *    plus per-group scaling);
+ *  - "The Kernel That Finally Did Something -- And Didn't Quite Agree With
+ *    Itself" (VeloxQuant-MLX blog, VecInfer): "What VecInfer does" (smooth
+ *    scale and Walsh-Hadamard rotation of keys, encoding against a trained
+ *    codebook, immediate dequantization), "The kernel toggle" (one fused
+ *    dispatch: smooth scale, Hadamard, quantize, dequantize, inverse
+ *    transform, unscale);
+ *  - VeloxQuant-MLX 0.52.0 package description, "Metal kernels"
+ *    (quantize_vq: nearest centroid search with the argmin kept in registers,
+ *    no [N, n_centroids, sub_dim] difference tensor).
+ *
+ * Definitions (the readings the library implements):
+ *   D = head_dim in {64, 128, 256}; Hd = the Sylvester-order Walsh-Hadamard
+ *   matrix, Hd[i][j] = (-1)^popcount(i & j); s = sign vector in {-1,+1}^D;
+ *   lambda = smooth scale, one fp32 per (layer, head, channel).
+ *   rotate:    y = D^-1/2 * Hd * diag(s) * diag(lambda[l,h,:]) * x
+ *   int4:      for each group g of G consecutive rotated coordinates,
+ *              scale_g = fp16_rne(max|y_i| / 7),
+ *              q_i = 0 if scale_g == 0 else clamp(rne(y_i / scale_g), -7, 7)
+ *              byte k of a vector = (q_2k & 0xF) | (q_2k+1 & 0xF) << 4
+ *   dequant:   yhat_i = q_i * scale_g;
+ *              xhat = fp16_rne(diag(s / lambda[l,h,:]) * Hd * yhat * D^-1/2)
+ *   VQ encode: y as above, split into D/sub_dim contiguous sub-vectors;
+ *              idx_j = lowest k minimising ||y_j - c_k||^2 over the head's
+ *              codebook c[0..n_centroids) (fp16, sub_dim values each)
+ *   VQ decode: yhat = concatenation of c[idx_j]; xhat as in dequant.
+ * GPU arithmetic is fp32; results agree with an fp64 evaluation of these
+ * definitions up to fp32 rounding (a code may differ by one where the exact
+ * y/scale lies within 1e-4 of a rounding boundary, a scale by one fp16 ulp,
+ * a VQ index where two distances differ by less than 1e-4 relative).
+ *
+ * Tensors.  A KV tensor is [layers, tokens, heads, head_dim] with the last
+ * dimension contiguous; a kvq_view gives its base pointer and its three outer
+ * strides, in ELEMENTS of the view's own type (fp16 = 2 bytes, codes = bytes,
+ * scales = fp16, VQ indices = uint16).  Code rows hold D/2 bytes, scale rows
+ * D/G fp16 values, index rows D/sub_dim uint16 values.  A decode-time append
+ * of token t is a call with tokens = 1 and views whose data point at slot t.
+ *
+ * Memory and ownership.  Every data pointer (x, out, codes, scales, indices,
+ * lambda, signs, codebook) is DEVICE memory owned by the caller; the library
+ * allocates nothing, keeps no state except a thread-local error message, and
+ * never synchronises.  Each call validates its arguments on the host, then
+ * enqueues its kernel on `stream` (a hipStream_t passed as void*; NULL is the
+ * default stream) and returns.  Faults inside a kernel surface at the
+ * caller's next synchronisation.  Calls on different streams may run
+ * concurrently when their outputs do not overlap.
+ *
+ * Errors.  A non-OK status means nothing was enqueued (except KVQ_ERR_HIP,
+ * returned when the launch itself failed).  kvq_last_error() then describes
+ * the failing argument.  Device-side preconditions that are NOT checked:
+ * every sign is +-1; lambda is finite and > 0; inputs are finite and small
+ * enough that max|y|/7 fits fp16 (otherwise the outputs of that vector are
+ * unspecified, but no out-of-bounds access happens); VQ indices passed to
+ * decode are < n_centroids (larger ones are clamped to n_centroids - 1).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_ERR_NULL = 1,         /* a required pointer is NULL */
+    KVQ_ERR_SHAPE = 2,        /* negative or inconsistent sizes */
+    KVQ_ERR_ALIGN = 3,        /* pointer or stride not aligned as required */
+    KVQ_ERR_UNSUPPORTED = 4,  /* valid but not instantiated (head_dim, group, sub_dim) */
+    KVQ_ERR_HIP = 5           /* the HIP launch failed */
+} kvq_status;
+
+/* Logical shape of a KV tensor: [layers, tokens, heads, head_dim].  Any of
+   layers, tokens, heads may be 0: the call then checks only head_dim, group,
+   n_centroids and sub_dim (pointers and strides of an empty tensor are not
+   looked at) and returns KVQ_OK without enqueuing anything.  head_dim must be
+   64, 128 or 256. */
+typedef struct kvq_shape {
+    int64_t layers, tokens, heads, head_dim;
+} kvq_shape;
+
+/* A strided view: element (l, t, h, i) lives at
+   data + l*stride_layer + t*stride_token + h*stride_head + i
+   (pointer arithmetic in elements of the view's type). */
+typedef struct kvq_view {
+    void* data;
+    int64_t stride_layer, stride_token, stride_head;
+} kvq_view;
+
+/* Fused rotate + int4 quantize (sign-randomized Walsh-Hadamard with smooth
+ * scale, per-group abs-max, nibble packing) -- the fused kernel of the
+ * "When Quantization Is Free" abstract with the Walsh-Hadamard transform in
+ * place of the FFT (the paper finds the two indistinguishable for KV quality).
+ *   x_f16      fp16 input view, 16-byte aligned data, strides multiples of 8.
+ *   lambda     fp32 [layers, heads, head_dim] contiguous, for the layers of
+ *              this call (offset it for a single-layer append).
+ *   signs      int8 [head_dim], each +1 or -1.
+ *   group      G, a power of two with 8 <= G <= head_dim.
+ *   codes_u8   output view of D/2-byte rows; 16-byte aligned data and strides.
+ *   scales_f16 output view of D/G-element fp16 rows; 2-byte aligned.
+ */
+kvq_status kvq_quantize(kvq_shape shape, kvq_view x_f16, const float* lambda,
+                        const int8_t* signs, int32_t group, kvq_view codes_u8,
+                        kvq_view scales_f16, void* stream);
+
+/* Mirror of kvq_quantize: unpack codes, multiply by the group scale, inverse
+ * Walsh-Hadamard, divide by lambda and apply the signs, round to fp16
+ * (VecInfer blog, "The kernel toggle": dequantize, inverse transform,
+ * unscale).  Views and alignment as for kvq_quantize; out_f16 is the fp16
+ * output view (16-byte aligned, strides multiples of 8). */
+kvq_status kvq_dequantize(kvq_shape shape, kvq_view codes_u8, kvq_view scales_f16,
+                          const float* lambda, const int8_t* signs, int32_t group,
+                          kvq_view out_f16, void* stream);
+
+/* Product-VQ encode (VecInfer blog, "What VecInfer does"; VeloxQuant-MLX
+ * package description, "Metal kernels"): rotate as kvq_quantize does (no
+ * group quantizer), split into D/sub_dim sub-vectors and store, per
+ * sub-vector, the lowest index of a nearest centroid of that head's codebook.
+ *   codebook_f16            fp16 [heads, n_centroids, sub_dim] per layer;
+ *   codebook_layer_stride   elements between layers' codebooks, 0 = one
+ *                           codebook shared by all layers;
+ *   n_centroids             1 .. 65536;
+ *   sub_dim                 8 (must divide head_dim);
+ *   idx_u16                 output view of D/sub_dim uint16 rows; 4-byte
+ *                           aligned data, even strides.
+ * The codebook must be 16-byte aligned.  Distances use the unrounded fp32
+ * rotated key. */
+kvq_status kvq_vq_encode(kvq_shape shape, kvq_view x_f16, const float* lambda,
+                         const int8_t* signs, const void* codebook_f16,
+                         int64_t codebook_layer_stride, int32_t n_centroids,
+                         int32_t sub_dim, kvq_view idx_u16, void* stream);
+
+/* Product-VQ decode: gather the named centroids, inverse Walsh-Hadamard,
+ * unscale, round to fp16 (VecInfer blog, "The kernel toggle").  Arguments as
+ * for kvq_vq_encode; idx_u16 is the input view, out_f16 the fp16 output view
+ * (16-byte aligned, strides multiples of 8). */
+kvq_status kvq_vq_decode(kvq_shape shape, kvq_view idx_u16, const void* codebook_f16,
+                         int64_t codebook_layer_stride, int32_t n_centroids,
+                         int32_t sub_dim, const float* lambda, const int8_t* signs,
+                         kvq_view out_f16, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* kvq_status_string(kvq_status status);
+
+/* Detail of this thread's most recent non-OK return ("" if none); the
+   pointer stays valid until this thread's next kvq_* call. */
+const char* kvq_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

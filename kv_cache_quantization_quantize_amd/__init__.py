@@ -1,0 +1,219 @@
+"""Python binding of libkvq.so, the MI355X (gfx950) fused KV-cache quantizer.
+
+Argument marshalling only: every step of the quantizer runs in the library's
+HIP kernels.  PyTorch provides device memory and the current HIP stream.  If
+the library has not been built, every call raises -- there is no fallback.
+
+Functions (names as in include/kvq.h):
+    quantize(x, lam, signs, group)            -> (codes u8, scales fp16)
+    dequantize(codes, scales, lam, signs, group) -> fp16
+    vq_encode(x, lam, signs, codebook)        -> indices (int16 storage of uint16)
+    vq_decode(idx, codebook, lam, signs)      -> fp16
+    append_quantize(x_tok, cache_codes, cache_scales, t, lam, signs, group)
+KV tensors are [layers, tokens, heads, head_dim] with the last dimension
+contiguous; lam is fp32 [layers, heads, head_dim]; signs int8 [head_dim].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "KvqError", "lib", "library_path", "quantize", "dequantize", "vq_encode", "vq_decode",
+    "append_quantize", "Shape", "View", "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvq.so")
+_lib = None
+
+STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_NULL", 2: "KVQ_ERR_SHAPE", 3: "KVQ_ERR_ALIGN",
+          4: "KVQ_ERR_UNSUPPORTED", 5: "KVQ_ERR_HIP"}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+        self.message = message
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int64), ("tokens", ctypes.c_int64),
+                ("heads", ctypes.c_int64), ("head_dim", ctypes.c_int64)]
+
+
+class View(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_layer", ctypes.c_int64),
+                ("stride_token", ctypes.c_int64), ("stride_head", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libkvq.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libkvq.so is not built (%s); run "
+                           "`python -m kv_cache_quantization_quantize_amd.build`" % _LIB_PATH)
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.kvq_quantize.restype = ctypes.c_int
+    L.kvq_quantize.argtypes = [Shape, View, P, P, I32, View, View, P]
+    L.kvq_dequantize.restype = ctypes.c_int
+    L.kvq_dequantize.argtypes = [Shape, View, View, P, P, I32, View, P]
+    L.kvq_vq_encode.restype = ctypes.c_int
+    L.kvq_vq_encode.argtypes = [Shape, View, P, P, P, I64, I32, I32, View, P]
+    L.kvq_vq_decode.restype = ctypes.c_int
+    L.kvq_vq_decode.argtypes = [Shape, View, P, I64, I32, I32, P, P, View, P]
+    L.kvq_status_string.restype = ctypes.c_char_p
+    L.kvq_status_string.argtypes = [ctypes.c_int]
+    L.kvq_last_error.restype = ctypes.c_char_p
+    L.kvq_last_error.argtypes = []
+    L.kvq_version.restype = I32
+    L.kvq_version.argtypes = []
+    _lib = L
+    return L
+
+
+def _check(st: int):
+    if st != 0:
+        raise KvqError(st, lib().kvq_last_error().decode())
+
+
+# ----------------------------------------------------------------- helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _view(t) -> View:
+    """View of a 4-D tensor [L, T, H, row] whose last dimension is contiguous."""
+    if t.dim() != 4:
+        raise ValueError("expected a 4-D [layers, tokens, heads, row] tensor, got %s" % (tuple(t.shape),))
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    s = t.stride()
+    return View(ctypes.c_void_p(t.data_ptr()), s[0], s[1], s[2])
+
+
+def _shape(t, D: int) -> Shape:
+    return Shape(t.shape[0], t.shape[1], t.shape[2], D)
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+
+
+def _params(lam, signs, L, H, D):
+    torch = _torch()
+    _need(lam, torch.float32, "lam")
+    _need(signs, torch.int8, "signs")
+    if tuple(lam.shape) != (L, H, D) or not lam.is_contiguous():
+        raise ValueError("lam must be a contiguous fp32 [layers, heads, head_dim] = %s tensor" % ((L, H, D),))
+    if tuple(signs.shape) != (D,) or not signs.is_contiguous():
+        raise ValueError("signs must be a contiguous int8 [head_dim] tensor")
+    return ctypes.c_void_p(lam.data_ptr()), ctypes.c_void_p(signs.data_ptr())
+
+
+# ------------------------------------------------------------------ int4
+def quantize(x, lam, signs, group: int, codes=None, scales=None, stream=None):
+    """Fused rotate + int4 quantize of x [L, T, H, D] fp16 -> (codes [L, T, H, D/2]
+    uint8, scales [L, T, H, D/group] fp16)."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    L, T, H, D = x.shape
+    if codes is None:
+        codes = torch.empty((L, T, H, D // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((L, T, H, max(D // max(group, 1), 1)), dtype=torch.float16, device=x.device)
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.float16, "scales")
+    pl, ps = _params(lam, signs, L, H, D)
+    _check(lib().kvq_quantize(_shape(x, D), _view(x), pl, ps, int(group), _view(codes), _view(scales),
+                              _stream(stream)))
+    return codes, scales
+
+
+def dequantize(codes, scales, lam, signs, group: int, out=None, stream=None):
+    """Mirror of quantize: (codes, scales) -> fp16 [L, T, H, D]."""
+    torch = _torch()
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.float16, "scales")
+    L, T, H, half = codes.shape
+    D = 2 * half
+    if out is None:
+        out = torch.empty((L, T, H, D), dtype=torch.float16, device=codes.device)
+    _need(out, torch.float16, "out")
+    pl, ps = _params(lam, signs, L, H, D)
+    _check(lib().kvq_dequantize(_shape(codes, D), _view(codes), _view(scales), pl, ps, int(group), _view(out),
+                                _stream(stream)))
+    return out
+
+
+def append_quantize(x_tok, cache_codes, cache_scales, t: int, lam, signs, group: int, stream=None):
+    """Decode-time append: quantize x_tok [L, 1, H, D] into token slot t of
+    preallocated caches [L, Tmax, H, D/2] / [L, Tmax, H, D/group] (a tokens=1
+    call on views that start at slot t)."""
+    c = cache_codes[:, t:t + 1]
+    s = cache_scales[:, t:t + 1]
+    quantize(x_tok, lam, signs, group, codes=c, scales=s, stream=stream)
+    return c, s
+
+
+# -------------------------------------------------------------------- VQ
+def vq_encode(x, lam, signs, codebook, sub_dim: int = 8, idx=None, codebook_layer_stride: int = 0,
+              stream=None):
+    """Product-VQ encode of x [L, T, H, D] fp16 against codebook [H, K, sub_dim]
+    fp16 (or [L, H, K, sub_dim] with codebook_layer_stride = H*K*sub_dim) ->
+    indices [L, T, H, D/sub_dim] stored in an int16 tensor (read as uint16)."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(codebook, torch.float16, "codebook")
+    L, T, H, D = x.shape
+    K = codebook.shape[-2]
+    if not codebook.is_contiguous():
+        raise ValueError("codebook must be contiguous")
+    if idx is None:
+        idx = torch.empty((L, T, H, D // sub_dim), dtype=torch.int16, device=x.device)
+    _need(idx, torch.int16, "idx")
+    pl, ps = _params(lam, signs, L, H, D)
+    _check(lib().kvq_vq_encode(_shape(x, D), _view(x), pl, ps, ctypes.c_void_p(codebook.data_ptr()),
+                               int(codebook_layer_stride), int(K), int(sub_dim), _view(idx), _stream(stream)))
+    return idx
+
+
+def vq_decode(idx, codebook, lam, signs, sub_dim: int = 8, out=None, codebook_layer_stride: int = 0,
+              stream=None):
+    """Product-VQ decode: indices [L, T, H, D/sub_dim] -> fp16 [L, T, H, D]."""
+    torch = _torch()
+    _need(idx, torch.int16, "idx")
+    _need(codebook, torch.float16, "codebook")
+    L, T, H, nsub = idx.shape
+    D = nsub * sub_dim
+    K = codebook.shape[-2]
+    if out is None:
+        out = torch.empty((L, T, H, D), dtype=torch.float16, device=idx.device)
+    _need(out, torch.float16, "out")
+    pl, ps = _params(lam, signs, L, H, D)
+    _check(lib().kvq_vq_decode(_shape(idx, D), _view(idx), ctypes.c_void_p(codebook.data_ptr()),
+                               int(codebook_layer_stride), int(K), int(sub_dim), pl, ps, _view(out),
+                               _stream(stream)))
+    return out

@@ -1,0 +1,237 @@
+// kvq_api.cpp -- the C ABI of libkvq.so: host-side validation, work
+// decomposition and kernel dispatch.  Validation makes no HIP call, so every
+// error path can be exercised on a machine without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+kvq_status fail(kvq_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned(const void* p, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+kvq_status check_shape(const kvq_shape& s)
+{
+    if (s.layers < 0 || s.tokens < 0 || s.heads < 0)
+        return fail(KVQ_ERR_SHAPE, "negative size: layers=%lld tokens=%lld heads=%lld",
+                    (long long)s.layers, (long long)s.tokens, (long long)s.heads);
+    if (s.head_dim != 64 && s.head_dim != 128 && s.head_dim != 256)
+        return fail(KVQ_ERR_UNSUPPORTED, "head_dim=%lld; supported: 64, 128, 256", (long long)s.head_dim);
+    if (s.layers > INT32_MAX || s.tokens > INT32_MAX || s.heads > INT32_MAX)
+        return fail(KVQ_ERR_SHAPE, "a dimension exceeds 2^31-1");
+    const int64_t tiles = (s.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile;
+    // items = layers*heads*tiles must stay below 2^31 (with room for one more wave's run)
+    if (s.layers > 0 && s.heads > 0 && tiles > 0 &&
+        (double)s.layers * (double)s.heads * (double)tiles > (double)(INT32_MAX - 1024))
+        return fail(KVQ_ERR_SHAPE, "layers*heads*ceil(tokens/16) exceeds 2^31");
+    return KVQ_OK;
+}
+
+bool empty(const kvq_shape& s) { return s.layers == 0 || s.tokens == 0 || s.heads == 0; }
+
+// A view whose rows are `row_bytes` long and must be `align`-byte aligned.
+kvq_status check_view(const char* name, const kvq_view& v, int elem_bytes, int64_t row_elems,
+                      int align, const kvq_shape& s)
+{
+    if (!v.data) return fail(KVQ_ERR_NULL, "%s.data is NULL", name);
+    if (!aligned(v.data, align))
+        return fail(KVQ_ERR_ALIGN, "%s.data must be %d-byte aligned", name, align);
+    const int64_t st[3] = {v.stride_layer, v.stride_token, v.stride_head};
+    const char* sn[3] = {"stride_layer", "stride_token", "stride_head"};
+    const int64_t ext[3] = {s.layers, s.tokens, s.heads};
+    for (int i = 0; i < 3; i++) {
+        if (st[i] < 0) return fail(KVQ_ERR_SHAPE, "%s.%s is negative", name, sn[i]);
+        if ((st[i] * elem_bytes) % align)
+            return fail(KVQ_ERR_ALIGN, "%s.%s*%d bytes must be a multiple of %d", name, sn[i], elem_bytes, align);
+        if (ext[i] > 1 && st[i] < row_elems && st[i] != 0)
+            return fail(KVQ_ERR_SHAPE, "%s.%s=%lld is smaller than a row (%lld elements)", name, sn[i],
+                        (long long)st[i], (long long)row_elems);
+        if (ext[i] > 1 && st[i] == 0)
+            return fail(KVQ_ERR_SHAPE, "%s.%s is 0 for an extent > 1 (outputs would alias)", name, sn[i]);
+    }
+    return KVQ_OK;
+}
+
+kvq_status check_group(int32_t g, int64_t D)
+{
+    if (g < 8 || g > D || (g & (g - 1)))
+        return fail(KVQ_ERR_UNSUPPORTED, "group=%d; must be a power of two with 8 <= group <= head_dim (%lld)",
+                    g, (long long)D);
+    return KVQ_OK;
+}
+
+kvq_status check_params(const float* lambda, const int8_t* signs)
+{
+    if (!lambda) return fail(KVQ_ERR_NULL, "lambda is NULL");
+    if (!signs) return fail(KVQ_ERR_NULL, "signs is NULL");
+    if (!aligned(lambda, 16)) return fail(KVQ_ERR_ALIGN, "lambda must be 16-byte aligned");
+    if (!aligned(signs, 8)) return fail(KVQ_ERR_ALIGN, "signs must be 8-byte aligned");
+    return KVQ_OK;
+}
+
+kvq::Tensor4 t4(const kvq_view& v) { return kvq::Tensor4{v.data, v.stride_layer, v.stride_token, v.stride_head}; }
+
+// Consecutive items per wavefront: long runs keep lambda in registers; short
+// runs give small workloads enough wavefronts.
+int32_t items_per_wave(int64_t n_items)
+{
+    int64_t ipw = n_items / 16384;
+    if (ipw < 1) ipw = 1;
+    if (ipw > 64) ipw = 64;
+    return (int32_t)ipw;
+}
+
+kvq_status hip_status(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return KVQ_OK;
+}
+
+#define KVQ_TRY(expr)                          \
+    do {                                       \
+        kvq_status _st = (expr);               \
+        if (_st != KVQ_OK) return _st;         \
+    } while (0)
+
+kvq_status int4_common(const kvq_shape& shape, const kvq_view& x, const float* lambda,
+                       const int8_t* signs, int32_t group, const kvq_view& codes,
+                       const kvq_view& scales, kvq::Int4Args& a, bool x_is_output)
+{
+    KVQ_TRY(check_shape(shape));
+    KVQ_TRY(check_group(group, shape.head_dim));
+    if (empty(shape)) return KVQ_OK;
+    KVQ_TRY(check_params(lambda, signs));
+    const int64_t D = shape.head_dim;
+    KVQ_TRY(check_view(x_is_output ? "out_f16" : "x_f16", x, 2, D, 16, shape));
+    KVQ_TRY(check_view("codes_u8", codes, 1, D / 2, 16, shape));
+    KVQ_TRY(check_view("scales_f16", scales, 2, D / group, 2, shape));
+    a.L = (int32_t)shape.layers;
+    a.T = (int32_t)shape.tokens;
+    a.H = (int32_t)shape.heads;
+    a.D = (int32_t)D;
+    a.G = group;
+    a.x = t4(x);
+    a.codes = t4(codes);
+    a.scales = t4(scales);
+    a.lambda = lambda;
+    a.signs = signs;
+    a.tiles_per_lh = (int32_t)((shape.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
+    a.n_items = shape.layers * shape.heads * (int64_t)a.tiles_per_lh;
+    a.items_per_wave = items_per_wave(a.n_items);
+    return KVQ_OK;
+}
+
+kvq_status vq_common(const kvq_shape& shape, const kvq_view& x, const float* lambda, const int8_t* signs,
+                     const void* codebook, int64_t cb_layer_stride, int32_t K, int32_t sub,
+                     const kvq_view& idx, kvq::VqArgs& a, bool x_is_output)
+{
+    KVQ_TRY(check_shape(shape));
+    if (K < 1 || K > 65536) return fail(KVQ_ERR_SHAPE, "n_centroids=%d; must be in 1..65536", K);
+    if (sub <= 0 || shape.head_dim % sub) return fail(KVQ_ERR_SHAPE, "sub_dim=%d must divide head_dim", sub);
+    if (sub != 8) return fail(KVQ_ERR_UNSUPPORTED, "sub_dim=%d; only 8 is instantiated", sub);
+    if (empty(shape)) return KVQ_OK;
+    KVQ_TRY(check_params(lambda, signs));
+    if (!codebook) return fail(KVQ_ERR_NULL, "codebook is NULL");
+    if (!aligned(codebook, 16)) return fail(KVQ_ERR_ALIGN, "codebook must be 16-byte aligned");
+    if (cb_layer_stride < 0) return fail(KVQ_ERR_SHAPE, "codebook_layer_stride is negative");
+    if ((cb_layer_stride * 2) % 16) return fail(KVQ_ERR_ALIGN, "codebook_layer_stride*2 bytes must be a multiple of 16");
+    const int64_t D = shape.head_dim;
+    KVQ_TRY(check_view(x_is_output ? "out_f16" : "x_f16", x, 2, D, 16, shape));
+    KVQ_TRY(check_view("idx_u16", idx, 2, D / sub, 4, shape));
+    a.L = (int32_t)shape.layers;
+    a.T = (int32_t)shape.tokens;
+    a.H = (int32_t)shape.heads;
+    a.D = (int32_t)D;
+    a.sub = sub;
+    a.K = K;
+    a.x = t4(x);
+    a.idx = t4(idx);
+    a.lambda = lambda;
+    a.signs = signs;
+    a.codebook = static_cast<const uint16_t*>(codebook);
+    a.cb_layer_stride = cb_layer_stride;
+    a.tiles_per_lh = (int32_t)((shape.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
+    a.n_items = shape.layers * shape.heads * (int64_t)a.tiles_per_lh;
+    a.items_per_wave = items_per_wave(a.n_items);
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_quantize(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,
+                        int32_t group, kvq_view codes_u8, kvq_view scales_f16, void* stream)
+{
+    g_err[0] = 0;
+    kvq::Int4Args a;
+    KVQ_TRY(int4_common(shape, x_f16, lambda, signs, group, codes_u8, scales_f16, a, false));
+    if (empty(shape)) return KVQ_OK;
+    return hip_status(kvq::launch_quantize(a, static_cast<hipStream_t>(stream)), "kvq_quantize launch");
+}
+
+kvq_status kvq_dequantize(kvq_shape shape, kvq_view codes_u8, kvq_view scales_f16, const float* lambda,
+                          const int8_t* signs, int32_t group, kvq_view out_f16, void* stream)
+{
+    g_err[0] = 0;
+    kvq::Int4Args a;
+    KVQ_TRY(int4_common(shape, out_f16, lambda, signs, group, codes_u8, scales_f16, a, true));
+    if (empty(shape)) return KVQ_OK;
+    return hip_status(kvq::launch_dequantize(a, static_cast<hipStream_t>(stream)), "kvq_dequantize launch");
+}
+
+kvq_status kvq_vq_encode(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,
+                         const void* codebook_f16, int64_t codebook_layer_stride, int32_t n_centroids,
+                         int32_t sub_dim, kvq_view idx_u16, void* stream)
+{
+    g_err[0] = 0;
+    kvq::VqArgs a;
+    KVQ_TRY(vq_common(shape, x_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
+                      idx_u16, a, false));
+    if (empty(shape)) return KVQ_OK;
+    return hip_status(kvq::launch_vq_encode(a, static_cast<hipStream_t>(stream)), "kvq_vq_encode launch");
+}
+
+kvq_status kvq_vq_decode(kvq_shape shape, kvq_view idx_u16, const void* codebook_f16,
+                         int64_t codebook_layer_stride, int32_t n_centroids, int32_t sub_dim,
+                         const float* lambda, const int8_t* signs, kvq_view out_f16, void* stream)
+{
+    g_err[0] = 0;
+    kvq::VqArgs a;
+    KVQ_TRY(vq_common(shape, out_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
+                      idx_u16, a, true));
+    if (empty(shape)) return KVQ_OK;
+    return hip_status(kvq::launch_vq_decode(a, static_cast<hipStream_t>(stream)), "kvq_vq_decode launch");
+}
+
+const char* kvq_status_string(kvq_status st)
+{
+    switch (st) {
+        case KVQ_OK: return "KVQ_OK";
+        case KVQ_ERR_NULL: return "KVQ_ERR_NULL";
+        case KVQ_ERR_SHAPE: return "KVQ_ERR_SHAPE";
+        case KVQ_ERR_ALIGN: return "KVQ_ERR_ALIGN";
+        case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED";
+        case KVQ_ERR_HIP: return "KVQ_ERR_HIP";
+    }
+    return "KVQ_ERR_UNKNOWN";
+}
+
+const char* kvq_last_error(void) { return g_err; }
+
+int32_t kvq_version(void) { return 100; }
+
+}  // extern "C"

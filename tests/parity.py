@@ -1,0 +1,127 @@
+"""Parity comparator between the HIP path and the fp64 oracle.
+
+Contract (tolerances from the target statement; each check explained):
+  scales   |s_gpu - s_ora| <= 1e-3 * s_ora, and s_ora == 0 <=> s_gpu == 0.
+           1e-3 admits one fp16 ulp (2^-10): the GPU's fp32 abs-max and the
+           oracle's fp64 abs-max can fall on either side of an fp16 midpoint.
+  codes    compared with the oracle's codes RECOMPUTED WITH THE GPU'S STORED
+           SCALE (so a legitimate scale flip does not cascade); equal, or off
+           by exactly 1 where the exact pre-round value y/scale lies within
+           1e-4 of a rounding boundary (a half-integer).
+  dequant  the oracle dequantizes the GPU's own codes and scales;
+           |xhat_gpu - xhat64| <= 2e-3 / lambda_c + 2^-11 * |xhat64|
+           (2e-3 absolute in the lambda-normalised unit-variance domain, plus
+           half an fp16 ulp for the final rounding).
+  VQ       indices equal, or d64(idx_gpu) - d64(idx_ora) <=
+           1e-4 * max(d64(idx_ora), 1e-6); exact-tie differences are counted
+           separately (a tie must resolve to the lowest index).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+SCALE_REL = 1e-3
+BOUNDARY = 1e-4
+DEQ_ABS = 2e-3
+DEQ_REL = 2.0 ** -11
+VQ_REL = 1e-4
+
+
+def f16(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+class ParityError(AssertionError):
+    pass
+
+
+def check_scales(sc_gpu, sc_ora):
+    g, o = f16(sc_gpu), f16(sc_ora)
+    zero_mismatch = (o == 0) != (g == 0)
+    rel = np.where(o > 0, np.abs(g - o) / np.where(o > 0, o, 1), 0.0)
+    bad = zero_mismatch | (rel > SCALE_REL) | ~np.isfinite(g)
+    return {"n": int(g.size), "bad": int(bad.sum()), "flips": int((g != o).sum()),
+            "max_rel": float(rel.max()) if rel.size else 0.0, "bad_mask": bad}
+
+
+def check_codes(y64, sc_gpu, q_gpu, G):
+    """y64 [n, D] exact rotated values; sc_gpu [n, D/G] fp16 bits; q_gpu [n, D] int8."""
+    q_cond = oracle.codes_given_scales(y64, sc_gpu, G)
+    s = np.repeat(f16(sc_gpu), G, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(s > 0, y64 / np.where(s > 0, s, 1), 0.0)
+    dist = np.abs(r - (np.floor(r) + 0.5))          # distance to the nearest half-integer
+    near = (dist < BOUNDARY) & (np.abs(r) < 7.5)
+    diff = q_gpu.astype(np.int32) - q_cond.astype(np.int32)
+    ok = (diff == 0) | ((np.abs(diff) == 1) & near)
+    return {"n": int(diff.size), "exact": int((diff == 0).sum()), "boundary": int(((diff != 0) & ok).sum()),
+            "bad": int((~ok).sum()), "bad_mask": ~ok, "q_cond": q_cond}
+
+
+def check_dequant(x_gpu_bits, x64, lam):
+    g = f16(x_gpu_bits)
+    tol = DEQ_ABS / lam.astype(np.float64) + DEQ_REL * np.abs(x64)
+    err = np.abs(g - x64)
+    bad = ~(err <= tol)
+    return {"n": int(g.size), "bad": int(bad.sum()), "max_err_over_tol": float((err / tol).max()),
+            "max_abs_norm": float((err * lam).max()), "bad_mask": bad}
+
+
+def check_vq(y64, codebooks, book, idx_gpu, idx_ora, sub):
+    d_g = oracle.vq_distances(y64, codebooks, book, idx_gpu, sub)
+    d_o = oracle.vq_distances(y64, codebooks, book, idx_ora, sub)
+    same = idx_gpu == idx_ora
+    tie = ~same & (d_g == d_o)
+    close = (d_g - d_o) <= VQ_REL * np.maximum(d_o, 1e-6)
+    bad = ~same & ~close
+    return {"n": int(same.size), "exact": int(same.sum()), "near": int((~same & close & ~tie).sum()),
+            "ties": int(tie.sum()), "bad": int(bad.sum()) + int(tie.sum()), "bad_mask": bad | tie}
+
+
+def _raise(what, rep, extra=""):
+    r = {k: v for k, v in rep.items() if not k.endswith("_mask") and k != "q_cond"}
+    raise ParityError("%s parity failed: %s %s" % (what, r, extra))
+
+
+def int4_parity(x_bits, lam_rows, signs, G, codes_gpu, scales_gpu, out_gpu=None):
+    """Full int4 check of n vectors.  x_bits [n, D] fp16 bits, lam_rows [n, D]
+    fp32, codes_gpu [n, D/2] u8, scales_gpu [n, D/G] fp16 bits, out_gpu
+    (optional) [n, D] fp16 bits of the GPU dequantization of its own codes."""
+    x_bits = np.ascontiguousarray(x_bits, np.uint16)
+    lam_rows = np.ascontiguousarray(lam_rows, np.float32)
+    codes_o, scales_o, y64, nbad = oracle.quantize(x_bits, lam_rows, signs, G)
+    if nbad:
+        raise ParityError("%d input vectors are outside the quantizer's domain" % nbad)
+    rep = {}
+    rs = check_scales(scales_gpu, scales_o)
+    rep["scales"] = rs
+    if rs["bad"]:
+        i = np.argwhere(rs["bad_mask"])[:5]
+        _raise("scale", rs, "first bad [row, group]: %s gpu=%s ora=%s" % (
+            i.tolist(), f16(scales_gpu)[tuple(i.T)], f16(scales_o)[tuple(i.T)]))
+    q_gpu = oracle.unpack_nibbles(np.ascontiguousarray(codes_gpu, np.uint8))
+    rc = check_codes(y64, scales_gpu, q_gpu, G)
+    rep["codes"] = rc
+    if rc["bad"]:
+        i = np.argwhere(rc["bad_mask"])[:5]
+        _raise("code", rc, "first bad [row, coord]: %s gpu=%s ora=%s y/s=%s" % (
+            i.tolist(), q_gpu[tuple(i.T)], rc["q_cond"][tuple(i.T)],
+            (y64 / np.repeat(f16(scales_gpu), G, axis=1))[tuple(i.T)]))
+    if out_gpu is not None:
+        x64, _ = oracle.dequantize(codes_gpu, scales_gpu, lam_rows, signs, G)
+        rd = check_dequant(out_gpu, x64, lam_rows)
+        rep["dequant"] = rd
+        if rd["bad"]:
+            i = np.argwhere(rd["bad_mask"])[:5]
+            _raise("dequant", rd, "first bad [row, coord]: %s gpu=%s ora=%s" % (
+                i.tolist(), f16(out_gpu)[tuple(i.T)], x64[tuple(i.T)]))
+    return rep
+
+
+def summary(rep) -> str:
+    parts = []
+    for k, r in rep.items():
+        parts.append("%s: %s" % (k, {a: b for a, b in r.items() if not a.endswith("_mask") and a != "q_cond"}))
+    return "; ".join(parts)

@@ -1,0 +1,150 @@
+"""C ABI checks that need no GPU: libkvq.so loads, exports every function
+include/kvq.h declares, and host-side validation rejects bad arguments with
+the documented status codes before any HIP call (pointers below are fake,
+aligned addresses that validation never dereferences)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_quantization_quantize_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+OK, NULL, SHAPE, ALIGN, UNSUP = 0, 1, 2, 3, 4
+A = 1 << 20          # a fake, well-aligned address
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvq.library_path()):
+        pytest.skip("libkvq.so not built")
+    return kvq.lib()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "kvq_quantize", "kvq_dequantize", "kvq_vq_encode", "kvq_vq_decode",
+        "kvq_status_string", "kvq_last_error", "kvq_version"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.kvq_version() == 100
+    assert lib.kvq_status_string(3) == b"KVQ_ERR_ALIGN"
+    assert lib.kvq_status_string(99) == b"KVQ_ERR_UNKNOWN"
+
+
+def shape(L=2, T=5, H=3, D=128):
+    return kvq.Shape(L, T, H, D)
+
+
+def view(addr=A, row=128, L=2, T=5, H=3):
+    # contiguous [L, T, H, row]
+    return kvq.View(ctypes.c_void_p(addr), T * H * row, H * row, row)
+
+
+def q(lib, sh=None, x=None, lam=A, sg=A, group=32, codes=None, scales=None, D=128):
+    sh = sh or shape(D=D)
+    x = x or view(row=D, L=sh.layers, T=sh.tokens, H=sh.heads)
+    codes = codes or view(row=D // 2, L=sh.layers, T=sh.tokens, H=sh.heads)
+    scales = scales or view(row=D // max(group, 1), L=sh.layers, T=sh.tokens, H=sh.heads)
+    return lib.kvq_quantize(sh, x, ctypes.c_void_p(lam), ctypes.c_void_p(sg), group, codes, scales, None)
+
+
+def test_empty_shapes_are_noops(lib):
+    for L, T, H in ((0, 5, 3), (2, 0, 3), (2, 5, 0)):
+        assert q(lib, sh=shape(L, T, H)) == OK
+
+
+def test_null_pointers(lib):
+    assert q(lib, x=view(addr=0)) == NULL
+    assert b"x_f16" in lib.kvq_last_error()
+    assert q(lib, lam=0) == NULL
+    assert q(lib, sg=0) == NULL
+    assert q(lib, codes=view(addr=0, row=64)) == NULL
+    assert q(lib, scales=view(addr=0, row=4)) == NULL
+
+
+def test_head_dim_and_group(lib):
+    for D in (32, 96, 512, 0):
+        assert q(lib, sh=shape(D=D), D=128) == UNSUP
+    for G in (0, 4, 6, 12, 48, 256):
+        assert q(lib, group=G) == UNSUP, G
+    for G in (8, 16, 32, 64, 128):
+        assert q(lib, group=G, sh=shape(T=0)) == OK
+
+
+def test_negative_and_oversized_shapes(lib):
+    assert q(lib, sh=shape(L=-1)) == SHAPE
+    assert q(lib, sh=shape(T=1 << 31)) == SHAPE
+
+
+def test_alignment(lib):
+    assert q(lib, x=view(addr=A + 2)) == ALIGN
+    assert q(lib, x=kvq.View(ctypes.c_void_p(A), 5 * 3 * 128, 3 * 128 + 4, 128)) == ALIGN
+    assert q(lib, codes=view(addr=A + 4, row=64)) == ALIGN
+    assert q(lib, scales=view(addr=A + 1, row=4)) == ALIGN
+    assert q(lib, lam=A + 4) == ALIGN
+    assert q(lib, sg=A + 1) == ALIGN
+
+
+def test_strides(lib):
+    # stride smaller than a row, zero stride for an extent > 1, negative stride
+    assert q(lib, x=kvq.View(ctypes.c_void_p(A), 5 * 3 * 128, 3 * 128, 64)) == SHAPE
+    assert q(lib, x=kvq.View(ctypes.c_void_p(A), 5 * 3 * 128, 0, 128)) == SHAPE
+    assert q(lib, x=kvq.View(ctypes.c_void_p(A), -8, 3 * 128, 128)) == SHAPE
+    # an empty tensor's pointers and strides are not looked at
+    assert q(lib, sh=shape(T=0), x=kvq.View(ctypes.c_void_p(0), -1, 0, 3)) == OK
+
+
+def test_dequantize_validation(lib):
+    sh = shape()
+    x = view()
+    c = view(row=64)
+    s = view(row=4)
+    P = ctypes.c_void_p
+    assert lib.kvq_dequantize(sh, c, s, P(A), P(A), 32, view(addr=0), None) == NULL
+    assert b"out_f16" in lib.kvq_last_error()
+    assert lib.kvq_dequantize(sh, c, s, P(A), P(A), 24, x, None) == UNSUP
+    assert lib.kvq_dequantize(shape(T=0), c, s, P(A), P(A), 32, x, None) == OK
+
+
+def test_vq_validation(lib):
+    P = ctypes.c_void_p
+    sh = shape()
+    x = view()
+    idx = view(row=16)
+
+    def enc(cb=A, stride=0, K=4096, sub=8, ix=idx, shp=sh):
+        return lib.kvq_vq_encode(shp, x, P(A), P(A), P(cb), stride, K, sub, ix, None)
+
+    assert enc(shp=shape(T=0), cb=0) == OK
+    assert enc(shp=shape(T=0), sub=3) == SHAPE
+    assert enc(cb=0) == NULL
+    assert enc(cb=A + 2) == ALIGN
+    assert enc(K=0) == SHAPE
+    assert enc(K=65537) == SHAPE
+    assert enc(sub=3) == SHAPE
+    assert enc(sub=16, ix=view(row=8)) == UNSUP
+    assert enc(stride=-8) == SHAPE
+    assert enc(stride=4) == ALIGN
+    assert enc(ix=view(addr=A + 2, row=16)) == ALIGN
+    assert lib.kvq_vq_decode(sh, idx, P(A), 0, 4096, 8, P(A), P(A), view(addr=0), None) == NULL
+    assert lib.kvq_vq_decode(shape(T=0), idx, P(A), 0, 4096, 8, P(A), P(A), x, None) == OK
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+    x = torch.zeros((1, 16, 1, 128), dtype=torch.float16)
+    with pytest.raises((ValueError, RuntimeError)):
+        kvq.quantize(x, torch.ones((1, 1, 128)), torch.ones(128, dtype=torch.int8), 32)

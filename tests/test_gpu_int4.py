@@ -1,0 +1,220 @@
+"""GPU parity of the fused int4 quantize / dequantize kernels against the fp64
+oracle (contract in tests/parity.py), called through the C ABI via the
+binding.  Inputs are the seeded synthetic caches of synth/ (shapes of the
+pages' models), plus edge cases: ragged and empty token counts, zero,
+constant, tiny and large vectors, strided views, decode appends."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_quantization_quantize_amd as kvq
+import synth
+from tests import parity
+from tests.gpu_util import all_idx, bits, device, lam_rows, log, rows
+
+pytestmark = pytest.mark.gpu
+
+
+def run_int4(x, lam, signs, G):
+    codes, scales = kvq.quantize(x, lam, signs, G)
+    out = kvq.dequantize(codes, scales, lam, signs, G)
+    torch.cuda.synchronize()
+    return codes, scales, out
+
+
+def check_rows(x, lam, signs, G, codes, scales, out, idx, what):
+    rep = parity.int4_parity(rows(x, idx), lam_rows(lam, idx), signs.cpu().numpy(), G,
+                             rows(codes, idx), rows(scales, idx), rows(out, idx))
+    log(what, parity.summary(rep))
+    return rep
+
+
+def full_check(x, lam, signs, G, what):
+    L, T, H, D = x.shape
+    codes, scales, out = run_int4(x, lam, signs, G)
+    return check_rows(x, lam, signs, G, codes, scales, out, all_idx(L, T, H), what)
+
+
+# ------------------------------------------------------------- workloads
+def test_tiny_config():
+    dev = device()
+    inp = synth.make_inputs(synth.config("tiny"), dev)
+    full_check(inp["K"], inp["lam_K"], inp["signs"], 32, "tiny K")
+
+
+def test_qwen25_config():
+    dev = device()
+    cfg = synth.config("qwen2.5-1.5b")
+    inp = synth.make_inputs(cfg, dev)
+    for name in ("K", "V"):
+        full_check(inp[name], inp["lam_" + name], inp["signs"], cfg.G, "qwen2.5-1.5b " + name)
+
+
+@pytest.mark.parametrize("T", [256, 1024, 4096])
+def test_gemma_config(T):
+    dev = device()
+    cfg = synth.config("gemma-3-1b", T=T)
+    inp = synth.make_inputs(cfg, dev)
+    for name in ("K", "V"):
+        full_check(inp[name], inp["lam_" + name], inp["signs"], cfg.G, "gemma-3-1b T=%d %s" % (T, name))
+
+
+def test_gemma_decode_append():
+    """Single-token append per layer (K and V) into preallocated caches: the
+    appended slot must equal the bulk quantization of that token and no
+    neighbouring slot may change."""
+    dev = device()
+    cfg = synth.config("gemma-3-1b", T=257)
+    inp = synth.make_inputs(cfg, dev)
+    G, Tmax, t = cfg.G, 300, 256
+    for name in ("K", "V"):
+        x, lam, s = inp[name], inp["lam_" + name], inp["signs"]
+        L, T, H, D = x.shape
+        codes = torch.full((L, Tmax, H, D // 2), 0xA5, dtype=torch.uint8, device=dev)
+        scales = torch.full((L, Tmax, H, D // G), 7.0, dtype=torch.float16, device=dev)
+        kvq.quantize(x[:, :t], lam, s, G, codes=codes[:, :t], scales=scales[:, :t])
+        before_c, before_s = codes.clone(), scales.clone()
+        for l in range(L):   # one call per layer, as a decode step would
+            kvq.append_quantize(x[l:l + 1, t:t + 1], codes[l:l + 1], scales[l:l + 1], t,
+                                lam[l:l + 1], s, G)
+        bulk_c, bulk_s = kvq.quantize(x, lam, s, G)
+        torch.cuda.synchronize()
+        assert torch.equal(codes[:, t], bulk_c[:, t]) and torch.equal(scales[:, t], bulk_s[:, t])
+        mask = torch.ones(Tmax, dtype=torch.bool)
+        mask[t] = False
+        assert torch.equal(codes[:, mask], before_c[:, mask])
+        assert torch.equal(scales[:, mask], before_s[:, mask])
+        out = kvq.dequantize(codes[:, t:t + 1], scales[:, t:t + 1], lam, s, G)
+        torch.cuda.synchronize()
+        idx = all_idx(L, 1, H)
+        check_rows(x[:, t:t + 1], lam, s, G, codes[:, t:t + 1], scales[:, t:t + 1], out, idx,
+                   "gemma append " + name)
+
+
+# ------------------------------------------------------- instantiations
+@pytest.mark.parametrize("D,G", [(D, G) for D in (64, 128, 256) for G in (8, 16, 32, 64, 128, 256) if G <= D])
+def test_every_instantiation(D, G):
+    dev = device()
+    g = torch.Generator(device="cpu").manual_seed(D * 1000 + G)
+    L, T, H = 2, 37, 3                         # 3 token tiles per (l, h), ragged tail
+    x = (torch.randn((L, T, H, D), generator=g) * torch.exp(torch.randn((L, 1, H, D), generator=g))
+         ).to(torch.float16).to(dev)
+    lam = torch.exp(0.5 * torch.randn((L, H, D), generator=g)).to(dev)
+    s = (torch.randint(0, 2, (D,), generator=g, dtype=torch.int8) * 2 - 1).to(torch.int8).to(dev)
+    full_check(x, lam, s, G, "D=%d G=%d" % (D, G))
+
+
+# ------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 33])
+def test_ragged_tokens(T):
+    dev = device()
+    g = torch.Generator(device="cpu").manual_seed(T)
+    L, H, D, G = 3, 2, 128, 32
+    x = torch.randn((L, T, H, D), generator=g).to(torch.float16).to(dev)
+    lam = torch.ones((L, H, D), device=dev)
+    s = (torch.randint(0, 2, (D,), generator=g, dtype=torch.int8) * 2 - 1).to(dev)
+    full_check(x, lam, s, G, "ragged T=%d" % T)
+
+
+def test_empty_inputs_are_noops():
+    dev = device()
+    lam = torch.ones((2, 3, 128), device=dev)
+    s = torch.ones(128, dtype=torch.int8, device=dev)
+    for shape in ((0, 4, 3, 128), (2, 0, 3, 128)):
+        L, T, H, D = shape
+        x = torch.zeros(shape, dtype=torch.float16, device=dev)
+        c, sc = kvq.quantize(x, lam[:L] if L else lam[:0], s, 32)
+        o = kvq.dequantize(c, sc, lam[:L] if L else lam[:0], s, 32)
+        torch.cuda.synchronize()
+        assert c.numel() == 0 and o.numel() == 0
+
+
+def test_degenerate_vectors():
+    """Zero vectors (all-zero groups -> scale 0, codes 0), constant vectors
+    (energy in one coordinate), single spikes, tiny values (subnormal fp16
+    scales) and values near the largest the fp16 scale allows."""
+    dev = device()
+    D, G, H = 128, 32, 1
+    vecs = [np.zeros(D), np.ones(D), -np.ones(D) * 3.0]
+    e = np.zeros(D)
+    e[17] = 5.0
+    vecs.append(e)
+    vecs.append(np.random.default_rng(1).standard_normal(D) * 1e-5)   # subnormal scales
+    vecs.append(np.random.default_rng(2).standard_normal(D) * 2e-7)   # some scales round to 0
+    big = np.random.default_rng(3).standard_normal(D)
+    vecs.append(big / np.abs(big).max() * 60000.0)                  # amax/7 well inside fp16
+    half = np.zeros(D)
+    half[:64] = np.random.default_rng(4).standard_normal(64)
+    vecs.append(half)
+    T = len(vecs)
+    x = torch.tensor(np.stack(vecs)[None, :, None, :], dtype=torch.float16, device=dev)
+    lam = torch.ones((1, H, D), device=dev)
+    s = (torch.randint(0, 2, (D,), generator=torch.Generator().manual_seed(5), dtype=torch.int8) * 2 - 1).to(dev)
+    s[0] = 1
+    rep = full_check(x, lam, s, G, "degenerate")
+    codes, scales, out = run_int4(x, lam, s, G)
+    assert (bits(scales[0, 0]) == 0).all() and (codes[0, 0] == 0).all()
+    assert (out[0, 0] == 0).all()        # signed zeros: (s/lambda) * 0 keeps the sign of s
+
+
+def test_strided_views():
+    """Head-major storage seen through a permuted view, a padded token stride,
+    and outputs written into slices of larger sentinel-filled buffers."""
+    dev = device()
+    g = torch.Generator(device="cpu").manual_seed(11)
+    L, T, H, D, G = 2, 40, 4, 128, 32
+    base = torch.randn((L, H, T, D), generator=g).to(torch.float16).to(dev)
+    x = base.permute(0, 2, 1, 3)                       # [L, T, H, D], token stride D
+    lam = torch.exp(0.3 * torch.randn((L, H, D), generator=g)).to(dev)
+    s = (torch.randint(0, 2, (D,), generator=g, dtype=torch.int8) * 2 - 1).to(dev)
+    cbuf = torch.full((L, T + 3, H, D // 2 + 16), 0x5A, dtype=torch.uint8, device=dev)
+    sbuf = torch.full((L, T + 3, H, D // G + 3), -1.0, dtype=torch.float16, device=dev)
+    codes, scales = cbuf[:, 2:T + 2, :, 16:], sbuf[:, 1:T + 1, :, 3:]
+    kvq.quantize(x, lam, s, G, codes=codes, scales=scales)
+    obuf = torch.full((L, T, H + 1, D + 8), 9.0, dtype=torch.float16, device=dev)
+    out = obuf[:, :, 1:, 8:]
+    kvq.dequantize(codes, scales, lam, s, G, out=out)
+    torch.cuda.synchronize()
+    check_rows(x, lam, s, G, codes, scales, out, all_idx(L, T, H), "strided")
+    # nothing outside the views changed
+    assert (cbuf[:, :2] == 0x5A).all() and (cbuf[:, T + 2:] == 0x5A).all() and (cbuf[..., :16] == 0x5A).all()
+    assert (sbuf[:, :1] == -1).all() and (sbuf[:, T + 1:] == -1).all() and (sbuf[..., :3] == -1).all()
+    assert (obuf[:, :, :1] == 9).all() and (obuf[..., :8] == 9).all()
+    # contiguous copies give the same bytes
+    c2, s2 = kvq.quantize(x.contiguous(), lam, s, G)
+    torch.cuda.synchronize()
+    assert torch.equal(c2, codes) and torch.equal(s2, scales)
+
+
+def test_deterministic_repeats():
+    dev = device()
+    cfg = synth.config("qwen2.5-1.5b", T=512)
+    inp = synth.make_inputs(cfg, dev, want_v=False)
+    a = run_int4(inp["K"], inp["lam_K"], inp["signs"], 32)
+    b = run_int4(inp["K"], inp["lam_K"], inp["signs"], 32)
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.uint8) if u.dtype != torch.uint8 else u,
+                           v.view(torch.uint8) if v.dtype != torch.uint8 else v)
+
+
+# ------------------------------------------------ full-size, sampled
+def test_qwen3_8b_full_size_sampled():
+    """The HBM-roofline workload at its full size ([36, 262144, 8, 128], K and
+    V, 19.3 GB each), in the launch configuration the benchmark times;
+    parity on a seeded sample of 24,576 vectors per tensor."""
+    dev = device()
+    cfg = synth.config("qwen3-8b")
+    for name, purpose, chan in (("K", synth.P_KDATA, 0), ("V", synth.P_VDATA, 100)):
+        dist = cfg.k_dist if name == "K" else cfg.v_dist
+        x = synth.draw(cfg.L, cfg.T, cfg.H, cfg.D, dist, synth.seed(cfg.index, purpose),
+                       synth.seed(cfg.index, synth.P_CHAN) + chan, dev)
+        calib = synth.draw(cfg.L, synth.CALIB_TOKENS, cfg.H, cfg.D, dist,
+                           synth.seed(cfg.index, purpose + 2), synth.seed(cfg.index, synth.P_CHAN) + chan, "cpu")
+        lam = synth.calibrate_lambda(calib).to(dev)
+        s = synth.signs(cfg.D, synth.seed(cfg.index, synth.P_SIGNS), dev)
+        log("qwen3-8b %s drawn" % name)
+        codes, scales, out = run_int4(x, lam, s, cfg.G)
+        idx = synth.sample_rows(cfg.L, cfg.T, cfg.H, 24576, 777 + purpose).numpy()
+        check_rows(x, lam, s, cfg.G, codes, scales, out, idx, "qwen3-8b full-size " + name)
+        del x, codes, scales, out
+        torch.cuda.empty_cache()
