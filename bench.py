@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused rotate + int4 KV-cache quantizer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = quantize K and V, then dequantize K and V, of the Qwen3-8B-shaped
+bulk-prefill cache: [36 layers, 262,144 tokens (8 x 32,768), 8 KV heads, 128]
+fp16 per tensor, group size 32 (151 M head vectors per tensor, 49.5 GB of
+algorithmic traffic per tensor and direction).  Inputs are seeded synthetic
+(N(0,1) x per-(layer, head, channel) LogNormal(0,1) scales) and resident in
+HBM before the timed region.  The product-VQ encode/decode of the VecInfer-
+shaped key cache ([36, 8192, 8, 128], 4096-centroid per-head codebooks) is
+timed in the same run and reported under "vq".
+
+Prints ONE JSON line.  `value` is the algorithmic GB/s of a whole step
+(bytes the definition must move / wall time of the step);
+`roofline` grades the dominant kernel (quantize) with per-launch HIP-event
+timings on the stream it runs on; `cpu_baseline` times the fp64 oracle on a
+bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused rotate+int4 quantize GB/s (% of HBM peak) and ns/vector at D=128"
+HBM_PEAK_GBPS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_quantize_d128_g32_qwen3-8b.json")
+KERNEL_SOURCES = ["kv_cache_quantization_quantize_amd/csrc/kvq_int4.hip",
+                  "kv_cache_quantization_quantize_amd/csrc/kvq_device.h"]
+
+
+def bytes_per_vector(D: int, G: int) -> int:
+    """Algorithmic bytes one quantize or dequantize of a vector must move:
+    fp16 vector + packed codes + fp16 scales (lambda/signs amortise to < 0.1%)."""
+    return 2 * D + D // 2 + 2 * (D // G)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(per_launch_alg_bytes):
+    """HBM bytes per quantize launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(K, V, lamK, lamV, signs, G, n_tokens: int):
+    """Time the fp64 oracle (single thread) on a bounded sample: every layer
+    and head, `n_tokens` consecutive tokens, K and V, quantize + dequantize."""
+    import numpy as np
+    import torch
+    import oracle
+    oracle.build(force=False)
+    L, T, H, D = K.shape
+    t0 = (T // 2) // 16 * 16
+    xs, ls = [], []
+    for x, lam in ((K, lamK), (V, lamV)):
+        blk = x[:, t0:t0 + n_tokens].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        xs.append(blk.reshape(-1, D))
+        lr = lam.cpu().numpy()[:, None, :, :].repeat(n_tokens, axis=1)
+        ls.append(lr.reshape(-1, D))
+    x = np.concatenate(xs)
+    lam = np.ascontiguousarray(np.concatenate(ls), np.float32)
+    s = signs.cpu().numpy()
+    t = time.perf_counter()
+    codes, scales, _, _ = oracle.quantize(x, lam, s, G)
+    oracle.dequantize(codes, scales, lam, s, G)
+    dt = time.perf_counter() - t
+    n = x.shape[0]
+    return {"value": round(2 * n * bytes_per_vector(D, G) / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d vectors (36 layers x 8 heads x %d tokens, K and V) quantize+dequantize, "
+                      "single-threaded fp64, %.1f s" % (n, n_tokens, dt),
+            "ns_per_vector": round(dt / n * 1e9, 1)}
+
+
+def copy_ceiling(torch, nbytes: int, reps: int = 5):
+    """GB/s of a plain device-to-device copy (read + write) of `nbytes`."""
+    a = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=8 * 32768, help="tokens per tensor (default: full size)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-vq", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=192, help="tokens per (layer, head) in the CPU sample")
+    ap.add_argument("--copy-bytes", type=int, default=4 << 30, help="size of the plain-copy reference")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the quantizer has no cross-GPU step, and this build "
+              "runs on a single MI355X (requested --gpus %d, WORLD_SIZE %d)." % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_quantization_quantize_amd as kvq
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    kvq.lib()
+    dev = torch.device("cuda:0")
+
+    cfg = synth.config("qwen3-8b", T=args.tokens)
+    L, T, H, D, G = cfg.L, cfg.T, cfg.H, cfg.D, cfg.G
+    inp = synth.make_inputs(cfg, dev)
+    K, V, lamK, lamV, signs = inp["K"], inp["V"], inp["lam_K"], inp["lam_V"], inp["signs"]
+    codes = {n: torch.empty((L, T, H, D // 2), dtype=torch.uint8, device=dev) for n in "KV"}
+    scales = {n: torch.empty((L, T, H, D // G), dtype=torch.float16, device=dev) for n in "KV"}
+    outs = {n: torch.empty((L, T, H, D), dtype=torch.float16, device=dev) for n in "KV"}
+    src = {"K": (K, lamK), "V": (V, lamV)}
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(timed: bool):
+        for n in "KV":
+            x, lam = src[n]
+            if timed:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            kvq.quantize(x, lam, signs, G, codes=codes[n], scales=scales[n], stream=stream)
+            if timed:
+                b.record(stream)
+                ev.append(("quantize", a, b))
+        for n in "KV":
+            x, lam = src[n]
+            if timed:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            kvq.dequantize(codes[n], scales[n], lam, signs, G, out=outs[n], stream=stream)
+            if timed:
+                b.record(stream)
+                ev.append(("dequantize", a, b))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    nvec = L * T * H
+    bpv = bytes_per_vector(D, G)
+    step_bytes = 4 * nvec * bpv
+    ms_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+
+    kern = {}
+    for name in ("quantize", "dequantize"):
+        ms = [a.elapsed_time(b) for (k, a, b) in ev if k == name]
+        avg = sum(ms) / len(ms)
+        gbps = nvec * bpv / (avg * 1e-3) / 1e9
+        kern[name] = {"launches": len(ms), "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4),
+                      "max_ms": round(max(ms), 4), "GB_per_s": round(gbps, 1),
+                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                      "ns_per_vector": round(avg * 1e6 / nvec, 5),
+                      "vectors_per_s": round(nvec / (avg * 1e-3), 1)}
+
+    q = kern["quantize"]
+    per_launch = nvec * bpv
+    traffic = load_traffic(per_launch)
+    roofline = {"bound": "hbm", "achieved": q["GB_per_s"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": q["frac_of_hbm_peak"], "traffic": traffic,
+                "kernel": "kvq::quantize_kernel<128, 32>",
+                "algorithmic_bytes_per_launch": per_launch,
+                "bytes_per_vector": bpv, "vectors_per_launch": nvec}
+
+    del outs
+    torch.cuda.empty_cache()
+    try:
+        copy_gbps = round(copy_ceiling(torch, args.copy_bytes), 1)
+    except RuntimeError:
+        copy_gbps = None
+
+    vq = None
+    if not args.no_vq:
+        vq = bench_vq(torch, kvq, synth, dev, args)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(K, V, lamK, lamV, signs, G, args.cpu_tokens)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-8b-shaped bulk prefill KV cache, int4 quantize + dequantize of K and V",
+                   "tensor_shape": [L, T, H, D], "head_dim": D, "group": G, "tensors": 2,
+                   "vectors_per_tensor": nvec, "step": "quantize K, V then dequantize K, V",
+                   "algorithmic_bytes_per_step": step_bytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kern,
+        "copy_ceiling_GB_per_s": copy_gbps,
+        "vq": vq,
+        "frac_of_hbm_peak_step": round(value / HBM_PEAK_GBPS, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_vq(torch, kvq, synth, dev, args):
+    """Time VQ encode and decode of the VecInfer-shaped key cache."""
+    cfg = synth.config("vq")
+    try:
+        inp = synth.make_inputs(cfg, dev)
+    except RuntimeError:
+        return None
+    x, lam, s, cb = inp["K"], inp["lam_K"], inp["signs"], inp["codebook"]
+    L, T, H, D = x.shape
+    idx = torch.empty((L, T, H, D // cfg.sub_dim), dtype=torch.int16, device=dev)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    try:
+        kvq.vq_encode(x, lam, s, cb, cfg.sub_dim, idx=idx, stream=stream)
+        kvq.vq_decode(idx, cb, lam, s, cfg.sub_dim, out=out, stream=stream)
+        torch.cuda.synchronize()
+    except kvq.KvqError as e:
+        return {"status": "unavailable", "error": str(e)}
+    res = {}
+    reps = max(3, min(args.steps, 10))
+    for name, fn in (("encode", lambda: kvq.vq_encode(x, lam, s, cb, cfg.sub_dim, idx=idx, stream=stream)),
+                     ("decode", lambda: kvq.vq_decode(idx, cb, lam, s, cfg.sub_dim, out=out, stream=stream))):
+        fn()
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        avg = sum(ms) / len(ms)
+        nkeys = L * T * H
+        r = {"avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "ns_per_key": round(avg * 1e6 / nkeys, 4)}
+        if name == "encode":
+            flop = nkeys * (D // cfg.sub_dim) * cfg.n_centroids * cfg.sub_dim * 2
+            tf = flop / (avg * 1e-3) / 1e12
+            r.update({"algorithmic_TFLOP": round(flop / 1e12, 4), "TFLOP_per_s": round(tf, 2),
+                      "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+                      "executed_mfma_flop_factor": 4.0})
+        else:
+            byt = nkeys * (2 * D + 2 * (D // cfg.sub_dim))
+            r.update({"GB_per_s": round(byt / (avg * 1e-3) / 1e9, 1),
+                      "frac_of_hbm_peak": round(byt / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
+        res[name] = r
+    res["workload"] = "vecinfer-shaped keys [36, 8192, 8, 128], codebook [8, 4096, 8] fp16, sub_dim 8"
+    return res
+
+
+if __name__ == "__main__":
+    main()

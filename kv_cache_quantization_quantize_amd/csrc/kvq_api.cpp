@@ -128,8 +128,18 @@ kvq_status int4_common(const kvq_shape& shape, const kvq_view& x, const float* l
     a.scales = t4(scales);
     a.lambda = lambda;
     a.signs = signs;
-    a.tiles_per_lh = (int32_t)((shape.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
-    a.n_items = shape.layers * shape.heads * (int64_t)a.tiles_per_lh;
+    a.token_major = (kvq::kTokensPerTile % shape.heads) == 0;
+    a.h_shift = 0;
+    while ((int64_t(1) << a.h_shift) < shape.heads) a.h_shift++;
+    if (a.token_major) {
+        a.tok_per_item = (int32_t)(kvq::kTokensPerTile / shape.heads);
+        a.items_per_group = (int32_t)((shape.tokens + a.tok_per_item - 1) / a.tok_per_item);
+        a.n_items = shape.layers * (int64_t)a.items_per_group;
+    } else {
+        a.tok_per_item = kvq::kTokensPerTile;
+        a.items_per_group = (int32_t)((shape.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
+        a.n_items = shape.layers * shape.heads * (int64_t)a.items_per_group;
+    }
     a.items_per_wave = items_per_wave(a.n_items);
     return KVQ_OK;
 }

@@ -58,20 +58,18 @@ __device__ __forceinline__ void bfly_reg(float (&v)[N])
     }
 }
 
-// One v_fmac_f32_dpp per value on 8 consecutive values; the leading s_nop
-// covers the two wait states a DPP read needs after a VALU write.
-#define KVQ_FMAC8(PERM)                                                             \
-    asm("s_nop 1\n\t"                                                               \
-        "v_fmac_f32_dpp %0, %0, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t" \
-        "v_fmac_f32_dpp %1, %1, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t" \
-        "v_fmac_f32_dpp %2, %2, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t" \
-        "v_fmac_f32_dpp %3, %3, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t" \
-        "v_fmac_f32_dpp %4, %4, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t" \
-        "v_fmac_f32_dpp %5, %5, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t" \
-        "v_fmac_f32_dpp %6, %6, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf\n\t" \
-        "v_fmac_f32_dpp %7, %7, %8 quad_perm:" PERM " row_mask:0xf bank_mask:0xf"     \
-        : "+v"(v[i]), "+v"(v[i + 1]), "+v"(v[i + 2]), "+v"(v[i + 3]),               \
-          "+v"(v[i + 4]), "+v"(v[i + 5]), "+v"(v[i + 6]), "+v"(v[i + 7])             \
+// One v_fmac_f32_dpp per value on 16 consecutive values v[i..i+15]; the
+// leading s_nop covers the two wait states a DPP read needs after a VALU
+// write of the same register.
+#define KVQ_F(n, P) "v_fmac_f32_dpp %" #n ", %" #n ", %16 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t"
+#define KVQ_FMAC16(P)                                                                          \
+    asm("s_nop 1\n\t" KVQ_F(0, P) KVQ_F(1, P) KVQ_F(2, P) KVQ_F(3, P) KVQ_F(4, P) KVQ_F(5, P)   \
+        KVQ_F(6, P) KVQ_F(7, P) KVQ_F(8, P) KVQ_F(9, P) KVQ_F(10, P) KVQ_F(11, P) KVQ_F(12, P)  \
+        KVQ_F(13, P) KVQ_F(14, P) KVQ_F(15, P)                                                 \
+        : "+v"(v[i]), "+v"(v[i + 1]), "+v"(v[i + 2]), "+v"(v[i + 3]), "+v"(v[i + 4]),          \
+          "+v"(v[i + 5]), "+v"(v[i + 6]), "+v"(v[i + 7]), "+v"(v[i + 8]), "+v"(v[i + 9]),      \
+          "+v"(v[i + 10]), "+v"(v[i + 11]), "+v"(v[i + 12]), "+v"(v[i + 13]),                  \
+          "+v"(v[i + 14]), "+v"(v[i + 15])                                                     \
         : "v"(c))
 
 // Butterfly on lane bit 0 of the quad (coordinate bit 3).  c = +1 on lanes
@@ -79,9 +77,9 @@ __device__ __forceinline__ void bfly_reg(float (&v)[N])
 template <int N>
 __device__ __forceinline__ void bfly_quad1(float (&v)[N], float c)
 {
-    static_assert(N % 8 == 0, "values per lane must be a multiple of 8");
+    static_assert(N % 16 == 0, "values per lane must be a multiple of 16");
 #pragma unroll
-    for (int i = 0; i < N; i += 8) KVQ_FMAC8("[1,0,3,2]");
+    for (int i = 0; i < N; i += 16) KVQ_FMAC16("[1,0,3,2]");
 }
 
 // Butterfly on lane bit 1 of the quad (coordinate bit 4).  c = +1 on lanes
@@ -89,11 +87,12 @@ __device__ __forceinline__ void bfly_quad1(float (&v)[N], float c)
 template <int N>
 __device__ __forceinline__ void bfly_quad2(float (&v)[N], float c)
 {
-    static_assert(N % 8 == 0, "values per lane must be a multiple of 8");
+    static_assert(N % 16 == 0, "values per lane must be a multiple of 16");
 #pragma unroll
-    for (int i = 0; i < N; i += 8) KVQ_FMAC8("[2,3,0,1]");
+    for (int i = 0; i < N; i += 16) KVQ_FMAC16("[2,3,0,1]");
 }
-#undef KVQ_FMAC8
+#undef KVQ_FMAC16
+#undef KVQ_F
 
 // Full in-register transform of N = 8*NJ values per lane (both lane stages
 // included).  Stage "register bit 0" is expected to have been applied by the
@@ -110,20 +109,52 @@ __device__ __forceinline__ void fwht_rest(float (&v)[N], float c1, float c2)
     bfly_quad2(v, c2);
 }
 
-// max over the quad partner at lane xor 1 (and xor 2) for 1..4 values.
-__device__ __forceinline__ void quad_max_x1(float& a)
+// In-place max with the quad partner at lane xor 1 (X2 = false) or xor 2
+// (X2 = true) of n <= 8 values, one asm block so that one s_nop serves all.
+#define KVQ_M(n, P) "v_max_f32_dpp %" #n ", %" #n ", %" #n " quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t"
+template <bool X2, int N>
+__device__ __forceinline__ void quad_max(float (&a)[N])
 {
-    asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
-        : "+v"(a));
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8, "1, 2, 4 or 8 values");
+    if constexpr (N == 1) {
+        if constexpr (X2) asm("s_nop 1\n\t" KVQ_M(0, "[2,3,0,1]") : "+v"(a[0]));
+        else asm("s_nop 1\n\t" KVQ_M(0, "[1,0,3,2]") : "+v"(a[0]));
+    } else if constexpr (N == 2) {
+        if constexpr (X2) asm("s_nop 1\n\t" KVQ_M(0, "[2,3,0,1]") KVQ_M(1, "[2,3,0,1]") : "+v"(a[0]), "+v"(a[1]));
+        else asm("s_nop 1\n\t" KVQ_M(0, "[1,0,3,2]") KVQ_M(1, "[1,0,3,2]") : "+v"(a[0]), "+v"(a[1]));
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            if constexpr (X2)
+                asm("s_nop 1\n\t" KVQ_M(0, "[2,3,0,1]") KVQ_M(1, "[2,3,0,1]") KVQ_M(2, "[2,3,0,1]")
+                    KVQ_M(3, "[2,3,0,1]") : "+v"(a[i]), "+v"(a[i + 1]), "+v"(a[i + 2]), "+v"(a[i + 3]));
+            else
+                asm("s_nop 1\n\t" KVQ_M(0, "[1,0,3,2]") KVQ_M(1, "[1,0,3,2]") KVQ_M(2, "[1,0,3,2]")
+                    KVQ_M(3, "[1,0,3,2]") : "+v"(a[i]), "+v"(a[i + 1]), "+v"(a[i + 2]), "+v"(a[i + 3]));
+        }
+    }
 }
-__device__ __forceinline__ void quad_max_x2(float& a)
+#undef KVQ_M
+
+// Forces v to be computed here: no instruction producing v may sink below
+// this point, and no load or store may move across it (empty asm with a
+// memory clobber).  Used to place the wait for an item's loads before the
+// next item's loads are issued.
+template <int N>
+__device__ __forceinline__ void pin(float (&v)[N])
 {
-    asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
-        : "+v"(a));
+#pragma unroll
+    for (int i = 0; i < N; i++) asm volatile("" : "+v"(v[i]) : : "memory");
 }
 
 // Wave-uniform value as an SGPR (the compiler cannot prove threadIdx.x >> 6
 // uniform on its own).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 }  // namespace kvq

@@ -15,12 +15,18 @@
 // Dequantize is the mirror ("The kernel toggle": dequantize, inverse
 // transform, unscale).
 //
-// Work decomposition.  An item is 16 consecutive tokens of one (l, h) pair;
-// one wavefront owns a run of consecutive items, so lambda's per-lane
-// multipliers stay in registers while (l, h) is unchanged, and the next
-// item's loads are issued before the current item is computed.  The kernel
+// Work decomposition.  An item is 16 head vectors, one per quad of a
+// wavefront.  When the head count divides 16 the item is 16 consecutive
+// (token, head) vectors of one layer -- a contiguous 4 KB run of a [L, T, H,
+// 128] cache -- and each lane keeps one head for the whole layer; otherwise
+// it is 16 consecutive tokens of one (layer, head).  Either way a wavefront
+// owns a run of consecutive items, lambda's per-lane multipliers stay in
+// registers until the layer (or head) changes, and the next item's loads are
+// issued before the current item is computed.  The kernel
 // is HBM-bound: per vector it moves 2D + D/2 + 2D/G bytes and does about
 // 2.9 VALU operations per coordinate.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -42,19 +48,6 @@ struct SqrtD;
 template <> struct SqrtD<64> { static constexpr float v = 8.0f; };
 template <> struct SqrtD<128> { static constexpr float v = 11.3137084989847604f; };
 template <> struct SqrtD<256> { static constexpr float v = 16.0f; };
-
-// Per-item coordinates shared by both kernels.
-struct ItemPos {
-    int lh, tile;
-};
-
-__device__ __forceinline__ ItemPos item_pos(int item, int tiles_per_lh)
-{
-    ItemPos p;
-    p.lh = item / tiles_per_lh;
-    p.tile = item - p.lh * tiles_per_lh;
-    return p;
-}
 
 // Lane's register multipliers for the forward rotation: s_c * lambda_c / sqrt(D).
 template <int D>
@@ -111,26 +104,172 @@ __device__ __forceinline__ uint32_t gather_low_bytes(uint32_t a0, uint32_t a1, u
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// Work items
+// ---------------------------------------------------------------------------
+namespace {
+
+// Scalar position of an item: layer, head (head-major items only), first
+// token, whether all its vectors exist (then loads and stores need no lane
+// mask), and the key its lambda multipliers depend on (layer for
+// token-major items, (layer, head) for head-major ones).
+struct Item {
+    int l, h, t0, key;
+    bool full;
+};
+
+template <bool TM>
+__device__ __forceinline__ Item decode_item(int item, const Int4Args& a)
+{
+    Item it;
+    const int grp = uniform(item / a.items_per_group);
+    const int k = item - grp * a.items_per_group;
+    it.t0 = uniform(k * a.tok_per_item);
+    it.full = it.t0 + a.tok_per_item <= a.T;
+    it.key = grp;
+    if constexpr (TM) {
+        it.l = grp;
+        it.h = 0;
+    } else {
+        it.l = uniform(grp / a.H);
+        it.h = grp - it.l * a.H;
+    }
+    return it;
+}
+
+// Element offset of the item's first vector in a view (wave-uniform).
+__device__ __forceinline__ int64_t outer_offset(const Tensor4& t, const Item& it)
+{
+    return uniform64((int64_t)it.l * t.sl + (int64_t)it.h * t.sh + (int64_t)it.t0 * t.st);
+}
+
+// Per-lane part of an item: token offset and head of the lane's vector.
+struct LaneMap {
+    int tok, head;
+};
+
+template <bool TM>
+__device__ __forceinline__ LaneMap lane_map(int slot, const Int4Args& a)
+{
+    if constexpr (TM) return LaneMap{slot >> a.h_shift, slot & (a.H - 1)};
+    else return LaneMap{slot, 0};
+}
+
+// lambda row of the lane's vector for the item's key.
+template <bool TM>
+__device__ __forceinline__ int64_t lambda_row(const Item& it, const LaneMap& lm, const Int4Args& a)
+{
+    if constexpr (TM) return ((int64_t)it.l * a.H + lm.head) * a.D;
+    else return (int64_t)it.key * a.D;
+}
+
+// The lane's NG fp16 scales packed four per 64-bit word; returns scale g.
+template <int NG>
+__device__ __forceinline__ uint16_t pick_scale(const uint16_t (&s)[NG], int g)
+{
+    uint64_t w[(NG + 3) / 4] = {};
+#pragma unroll
+    for (int i = 0; i < NG; i++) w[i / 4] |= (uint64_t)s[i] << (16 * (i % 4));
+    uint64_t sel = w[0];
+#pragma unroll
+    for (int i = 1; i < (NG + 3) / 4; i++)
+        if (g / 4 == i) sel = w[i];
+    return (uint16_t)(sel >> (16 * (g % 4)));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // Quantize
 // ---------------------------------------------------------------------------
 template <int D, int G>
+struct QuantShape {
+    static constexpr int NJ = D / 32;            // 16-byte chunks per lane
+    static constexpr int N = NJ * 8;             // coordinates per lane
+    static constexpr int NG = D / G;             // groups per vector
+    // groups one lane's registers touch: all NG when a group spans the quad
+    // (G >= 32), else one per chunk
+    static constexpr int LG = (G >= 32) ? NG : NJ;
+    static constexpr int CH_PER_G = (G >= 32) ? G / 32 : 1;
+};
+
+// Item loop shared by both kernels (see the comment below).  With PREFETCH
+// the next item's loads are issued before the current item is finished,
+// using a second register buffer; without it (head_dim 256, where a second
+// buffer would not fit in registers) each item's loads are issued right
+// before its first stage, and only the stores are deferred.
+template <typename Buf, typename Out, int N, bool PREFETCH, typename Load, typename First, typename Store,
+          typename Finish>
+__device__ __forceinline__ void run_pipeline(int begin, int end, Load&& load, First&& first_stage,
+                                             Store&& store, Finish&& finish)
+{
+    Out prev;
+    int prev_item = -1;
+    if constexpr (PREFETCH) {
+        Buf bufA, bufB;
+        load(begin, bufA);
+        for (int item = begin;;) {
+            {
+                float v[N];
+                first_stage(item, bufA, v);
+                pin(v);
+                if (prev_item >= 0) store(prev_item, prev);
+                if (item + 1 < end) load(item + 1, bufB);
+                __builtin_amdgcn_sched_barrier(0);
+                finish(v, prev);
+                prev_item = item;
+            }
+            if (++item >= end) break;
+            {
+                float v[N];
+                first_stage(item, bufB, v);
+                pin(v);
+                store(prev_item, prev);
+                if (item + 1 < end) load(item + 1, bufA);
+                __builtin_amdgcn_sched_barrier(0);
+                finish(v, prev);
+                prev_item = item;
+            }
+            if (++item >= end) break;
+        }
+    } else {
+        for (int item = begin; item < end; ++item) {
+            Buf buf;
+            load(item, buf);
+            float v[N];
+            first_stage(item, buf, v);
+            pin(v);
+            if (prev_item >= 0) store(prev_item, prev);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(v, prev);
+            prev_item = item;
+        }
+    }
+    store(prev_item, prev);
+}
+
+// Software pipeline shared by both kernels.  gfx9 counts loads and stores on
+// one counter (vmcnt), so consuming a load while any store is outstanding
+// waits for everything issued so far.  Each iteration therefore
+//   1. consumes the current item's loaded registers (the wait covers loads
+//      and stores issued one full item of compute earlier),
+//   2. issues the previous item's stores and the next item's loads,
+//   3. computes the rest of the current item,
+// and a scheduling barrier keeps step 2 between steps 1 and 3.
+template <int D, int G, bool TM>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args a)
 {
-    constexpr int NJ = D / 32;              // 16-byte chunks per lane
-    constexpr int N = NJ * 8;               // coordinates per lane
-    constexpr int NG = D / G;               // groups per vector
-    // Groups that one lane's registers touch: all NG when a group spans the
-    // quad (G >= 32), else one per chunk.
-    constexpr int LG = (G >= 32) ? NG : NJ;
-    constexpr int CH_PER_G = (G >= 32) ? G / 32 : 1;
+    using S = QuantShape<D, G>;
+    constexpr int NJ = S::NJ, N = S::N, NG = S::NG, LG = S::LG, CH_PER_G = S::CH_PER_G;
+    // scale values a lane stores per vector
+    constexpr int NSV = (G >= 32) ? (NG + 3) / 4 : NJ;
 
     const int lane = threadIdx.x & 63;
     const int q = lane & 3;
     const int slot = lane >> 2;
     const int wave = uniform((int)(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)));
-    int item = wave * a.items_per_wave;
-    const int item_end = min((int64_t)item + a.items_per_wave, a.n_items);
-    if (item >= item_end) return;
+    const int begin = wave * a.items_per_wave;
+    const int end = (int)min((int64_t)begin + a.items_per_wave, a.n_items);
+    if (begin >= end) return;
 
     const float c1 = (q & 1) ? -1.0f : 1.0f;
     const float c2 = (q & 2) ? -1.0f : 1.0f;
@@ -139,70 +278,104 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
     const _Float16* __restrict__ xg = static_cast<const _Float16*>(a.x.data);
     uint8_t* __restrict__ cg = static_cast<uint8_t*>(a.codes.data);
     uint16_t* __restrict__ sg = static_cast<uint16_t*>(a.scales.data);
-
-    const int64_t x_lane = (int64_t)slot * a.x.st + q * 8;
-    const int64_t c_lane = (int64_t)slot * a.codes.st + q * 4;
-    const int64_t s_lane = (int64_t)slot * a.scales.st;
+    const LaneMap lm = lane_map<TM>(slot, a);
+    const int64_t x_lane = (int64_t)lm.tok * a.x.st + (int64_t)lm.head * a.x.sh + q * 8;
+    // this lane stores code chunks q, q + 4, ... (16 bytes each) of its vector
+    const int64_t c_lane_chunk = (int64_t)lm.tok * a.codes.st + (int64_t)lm.head * a.codes.sh + q * 16;
+    const int64_t s_lane = (int64_t)lm.tok * a.scales.st + (int64_t)lm.head * a.scales.sh;
 
     float m[N];
-    int cur_lh = -1;
-    const _Float16* xbase = nullptr;
-    uint8_t* cbase = nullptr;
-    uint16_t* sbase = nullptr;
+    int cur_key = -1;
 
-    auto bases = [&](int lh) {
-        const int l = lh / a.H, h = lh - (lh / a.H) * a.H;
-        xbase = xg + (int64_t)l * a.x.sl + (int64_t)h * a.x.sh;
-        cbase = cg + (int64_t)l * a.codes.sl + (int64_t)h * a.codes.sh;
-        sbase = sg + (int64_t)l * a.scales.sl + (int64_t)h * a.scales.sh;
+    struct Out {
+        uint32_t word[NJ];
+        uint16_t sv[NSV];
     };
 
-    auto load_x = [&](int it, uint4 (&raw)[NJ]) {
-        const ItemPos p = item_pos(it, a.tiles_per_lh);
-        const int l = p.lh / a.H, h = p.lh - l * a.H;
-        const int t = p.tile * kTokensPerTile + slot;
-        const _Float16* ptr = xg + (int64_t)l * a.x.sl + (int64_t)h * a.x.sh +
-                              (int64_t)p.tile * kTokensPerTile * a.x.st + x_lane;
-        if (t < a.T) {
+    auto load = [&](int item, uint4(&buf)[NJ]) {
+        const Item it = decode_item<TM>(item, a);
+        const _Float16* p = xg + outer_offset(a.x, it) + x_lane;
+        if (it.full) {
 #pragma unroll
-            for (int j = 0; j < NJ; j++) raw[j] = *reinterpret_cast<const uint4*>(ptr + j * 32);
+            for (int j = 0; j < NJ; j++) buf[j] = *reinterpret_cast<const uint4*>(p + j * 32);
         } else {
 #pragma unroll
-            for (int j = 0; j < NJ; j++) raw[j] = make_uint4(0, 0, 0, 0);
+            for (int j = 0; j < NJ; j++) buf[j] = make_uint4(0, 0, 0, 0);
+            if (it.t0 + lm.tok < a.T) {
+#pragma unroll
+                for (int j = 0; j < NJ; j++) buf[j] = *reinterpret_cast<const uint4*>(p + j * 32);
+            }
         }
     };
 
-    uint4 nxt[NJ];
-    load_x(item, nxt);
+    // Code bytes are transposed within each quad through a wave-private LDS
+    // tile so that every lane stores whole 16-byte chunks: code chunk c of a
+    // vector (bytes 16c..16c+15 = word c of lanes q = 0..3) goes to lane c % 4.
+    // Word j of lane (v, q) sits at v*D/2 + ((j ^ (v >> 2)) % NJ)*16 + q*4,
+    // which spreads a wave's 64 dword writes over distinct banks.
+    __shared__ uint32_t lds_codes[kWavesPerBlock][16 * D / 8];
+    uint32_t* my_codes = lds_codes[threadIdx.x >> 6];
+    constexpr int CPL = (NJ + 3) / 4;     // 16-byte code chunks each lane stores
 
-    for (; item < item_end; ++item) {
-        const ItemPos p = item_pos(item, a.tiles_per_lh);
-        if (p.lh != cur_lh) {
-            cur_lh = p.lh;
-            bases(p.lh);
-            load_fwd_mult<D>(a.lambda + (int64_t)p.lh * D, a.signs, q, m);
-        }
-        uint4 cur[NJ];
+    auto store = [&](int item, const Out& o) {
+        const Item it = decode_item<TM>(item, a);
+        uint8_t* cp = cg + outer_offset(a.codes, it) + c_lane_chunk;
+        uint16_t* sp = sg + outer_offset(a.scales, it) + s_lane;
 #pragma unroll
-        for (int j = 0; j < NJ; j++) cur[j] = nxt[j];
-        if (item + 1 < item_end) load_x(item + 1, nxt);
+        for (int j = 0; j < NJ; j++)
+            my_codes[slot * (D / 8) + ((j ^ (slot >> 2)) % NJ) * 4 + q] = o.word[j];
+        const bool ok = it.full || it.t0 + lm.tok < a.T;
+#pragma unroll
+        for (int k = 0; k < CPL; k++) {
+            // lanes with q + 4k >= NJ (head_dim 64 only) read a valid slot and do not store
+            const int c = q + 4 * k;
+            const uint4 chunk =
+                *reinterpret_cast<const uint4*>(&my_codes[slot * (D / 8) + (((c % NJ) ^ (slot >> 2)) % NJ) * 4]);
+            if (ok && c < NJ) *reinterpret_cast<uint4*>(cp + 64 * k) = chunk;
+        }
+        if (ok) {
+            if constexpr (G >= 32) {
+                // lane q writes groups q, q+4, ...
+#pragma unroll
+                for (int k = 0; k < NSV; k++)
+                    if (4 * k + q < NG) sp[4 * k + q] = o.sv[k];
+            } else if constexpr (G == 16) {
+                // lanes q and q^1 share group 2j + (q >> 1); the even lane writes
+                if ((q & 1) == 0) {
+#pragma unroll
+                    for (int j = 0; j < NJ; j++) sp[2 * j + (q >> 1)] = o.sv[j];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NJ; j++) sp[4 * j + q] = o.sv[j];
+            }
+        }
+    };
 
-        // --- load/scale fused with the butterfly on register bit 0 ---------
-        float v[N];
+    // step 1: lambda/sign scaling fused with the butterfly on register bit 0
+    auto first_stage = [&](int item, const uint4(&buf)[NJ], float(&v)[N]) {
+        const Item it = decode_item<TM>(item, a);
+        if (it.key != cur_key) {
+            cur_key = it.key;
+            load_fwd_mult<D>(a.lambda + lambda_row<TM>(it, lm, a), a.signs, q, m);
+        }
 #pragma unroll
         for (int j = 0; j < NJ; j++) {
-            const uint32_t w[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
+            const uint32_t w[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
 #pragma unroll
             for (int k = 0; k < 4; k++) {
                 const int r = j * 8 + 2 * k;
-                const float b = hi_half(w[k]) * m[r + 1];
+                const float b = fmaf(hi_half(w[k]), m[r + 1], 0.0f);   // one v_fma_mix
                 v[r] = fmaf(lo_half(w[k]), m[r], b);
                 v[r + 1] = fmaf(lo_half(w[k]), m[r], -b);
             }
         }
+    };
+
+    // step 3: rest of the transform, scales, codes, packing
+    auto finish = [&](float(&v)[N], Out& o) {
         fwht_rest(v, c1, c2);
 
-        // --- group abs-max --------------------------------------------------
         float amax[LG];
 #pragma unroll
         for (int u = 0; u < LG; u++) amax[u] = 0.0f;
@@ -211,91 +384,76 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
             const int u = (r / 8) / CH_PER_G;
             amax[u] = fmaxf(amax[u], fabsf(v[r]));
         }
-        if constexpr (G >= 16) {
-#pragma unroll
-            for (int u = 0; u < LG; u++) quad_max_x1(amax[u]);
-        }
-        if constexpr (G >= 32) {
-#pragma unroll
-            for (int u = 0; u < LG; u++) quad_max_x2(amax[u]);
-        }
+        if constexpr (G >= 16) quad_max<false>(amax);
+        if constexpr (G >= 32) quad_max<true>(amax);
 
-        // --- scales ---------------------------------------------------------
         uint16_t s16[LG];
         float inv[LG];
+        bool overflow = false;
 #pragma unroll
         for (int u = 0; u < LG; u++) {
             const _Float16 h = (_Float16)(amax[u] * kInv7);
             const float sc = (float)h;
             s16[u] = __builtin_bit_cast(uint16_t, h);
-            inv[u] = sc > 0.0f ? lane_sign * __builtin_amdgcn_rcpf(sc) : 0.0f;
+            const float r = sc > 0.0f ? __builtin_amdgcn_rcpf(sc) : 0.0f;
+            inv[u] = lane_sign * r;
+            // only a subnormal scale can let |y|/scale reach 7.5 (a code of 8)
+            overflow |= amax[u] * r >= 7.5f;
         }
 
-        // --- codes and nibble packing ----------------------------------------
-        uint32_t word[NJ];
+        // codes: 8 + rne(y/scale) lands in the low byte of t; then nibble pack
+        auto encode = [&](auto clamp) {
 #pragma unroll
-        for (int j = 0; j < NJ; j++) {
-            const int u = j / CH_PER_G;
-            uint32_t t[8];
+            for (int j = 0; j < NJ; j++) {
+                const int u = j / CH_PER_G;
+                uint32_t t[8];
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                float f = fmaf(v[j * 8 + e], inv[u], kMagic8);
-                f = __builtin_amdgcn_fmed3f(f, kMagic8 - 7.0f, kMagic8 + 7.0f);
-                t[e] = __float_as_uint(f);
+                for (int e = 0; e < 8; e++) {
+                    float f = fmaf(v[j * 8 + e], inv[u], kMagic8);
+                    if constexpr (decltype(clamp)::value)
+                        f = __builtin_amdgcn_fmed3f(f, kMagic8 - 7.0f, kMagic8 + 7.0f);
+                    t[e] = __float_as_uint(f);
+                }
+                const uint32_t even = gather_low_bytes(t[0], t[2], t[4], t[6]);
+                const uint32_t odd = gather_low_bytes(t[1], t[3], t[5], t[7]);
+                o.word[j] = ((odd << 4) | even) ^ 0x88888888u;
             }
-            const uint32_t even = gather_low_bytes(t[0], t[2], t[4], t[6]);
-            const uint32_t odd = gather_low_bytes(t[1], t[3], t[5], t[7]);
-            word[j] = ((odd << 4) | even) ^ 0x88888888u;
-        }
+        };
+        if (__builtin_amdgcn_ballot_w64(overflow))
+            encode(std::true_type{});
+        else
+            encode(std::false_type{});
 
-        // --- stores -----------------------------------------------------------
-        const int t = p.tile * kTokensPerTile + slot;
-        if (t < a.T) {
-            const int64_t toff = (int64_t)p.tile * kTokensPerTile;
-            uint8_t* cp = cbase + toff * a.codes.st + c_lane;
+        if constexpr (G >= 32) {
 #pragma unroll
-            for (int j = 0; j < NJ; j++) *reinterpret_cast<uint32_t*>(cp + j * 16) = word[j];
-            uint16_t* sp = sbase + toff * a.scales.st + s_lane;
-            if constexpr (G >= 32) {
-                // every lane holds all NG scales; lane q writes groups q, q+4, ...
+            for (int k = 0; k < NSV; k++) o.sv[k] = pick_scale<NG>(s16, (4 * k + q) % NG);
+        } else {
 #pragma unroll
-                for (int g0 = 0; g0 < NG; g0 += 4) {
-                    uint16_t val = s16[g0];
-#pragma unroll
-                    for (int k = 1; k < 4; k++)
-                        if (g0 + k < NG && q == k) val = s16[g0 + k];
-                    if (g0 + q < NG) sp[g0 + q] = val;
-                }
-            } else if constexpr (G == 16) {
-                // lanes q and q^1 share group 2j + (q >> 1); the even lane writes
-                if ((q & 1) == 0) {
-#pragma unroll
-                    for (int j = 0; j < NJ; j++) sp[2 * j + (q >> 1)] = s16[j];
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < NJ; j++) sp[4 * j + q] = s16[j];
-            }
+            for (int j = 0; j < NJ; j++) o.sv[j] = s16[j];
         }
-    }
+    };
+
+    run_pipeline<uint4[NJ], Out, N, (D <= 128)>(begin, end, load, first_stage, store, finish);
 }
 
 // ---------------------------------------------------------------------------
 // Dequantize
 // ---------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, bool TM>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Args a)
 {
     constexpr int NJ = D / 32;
     constexpr int N = NJ * 8;
+    constexpr int NG = D / G;
+    constexpr int NW = (NG + 1) / 2;
 
     const int lane = threadIdx.x & 63;
     const int q = lane & 3;
     const int slot = lane >> 2;
     const int wave = uniform((int)(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)));
-    int item = wave * a.items_per_wave;
-    const int item_end = min((int64_t)item + a.items_per_wave, a.n_items);
-    if (item >= item_end) return;
+    const int begin = wave * a.items_per_wave;
+    const int end = (int)min((int64_t)begin + a.items_per_wave, a.n_items);
+    if (begin >= end) return;
 
     const float c1 = (q & 1) ? -1.0f : 1.0f;
     const float c2 = (q & 2) ? -1.0f : 1.0f;
@@ -304,64 +462,114 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
     _Float16* __restrict__ og = static_cast<_Float16*>(a.x.data);
     const uint8_t* __restrict__ cg = static_cast<const uint8_t*>(a.codes.data);
     const uint16_t* __restrict__ sg = static_cast<const uint16_t*>(a.scales.data);
-
-    const int64_t o_lane = (int64_t)slot * a.x.st + q * 8;
-    const int64_t c_lane = (int64_t)slot * a.codes.st + q * 4;
-    const int64_t s_lane = (int64_t)slot * a.scales.st;
+    const LaneMap lm = lane_map<TM>(slot, a);
+    const int64_t c_lane = (int64_t)lm.tok * a.codes.st + (int64_t)lm.head * a.codes.sh + q * 4;
+    const int64_t s_lane = (int64_t)lm.tok * a.scales.st + (int64_t)lm.head * a.scales.sh;
 
     float m[N];
-    int cur_lh = -1;
+    int cur_key = -1;
 
+    // Raw inputs of one item: the lane's NJ code words and its vector's whole
+    // scale row as packed 32-bit words.
     struct Raw {
         uint32_t w[NJ];
-        uint16_t s[NJ];
+        uint32_t sw[NW];
     };
-    auto load_in = [&](int it, Raw& raw) {
-        const ItemPos p = item_pos(it, a.tiles_per_lh);
-        const int l = p.lh / a.H, h = p.lh - l * a.H;
-        const int t = p.tile * kTokensPerTile + slot;
-        const int64_t toff = (int64_t)p.tile * kTokensPerTile;
-        const uint8_t* cp = cg + (int64_t)l * a.codes.sl + (int64_t)h * a.codes.sh +
-                            toff * a.codes.st + c_lane;
-        const uint16_t* sp = sg + (int64_t)l * a.scales.sl + (int64_t)h * a.scales.sh +
-                             toff * a.scales.st + s_lane;
-        if (t < a.T) {
+    struct Out {
+        uint4 o[NJ];
+    };
+
+    auto load = [&](int item, Raw& raw) {
+        const Item it = decode_item<TM>(item, a);
+        const uint8_t* cp = cg + outer_offset(a.codes, it) + c_lane;
+        const uint16_t* sp = sg + outer_offset(a.scales, it) + s_lane;
+        auto ld = [&]() {
 #pragma unroll
-            for (int j = 0; j < NJ; j++) {
-                raw.w[j] = *reinterpret_cast<const uint32_t*>(cp + j * 16);
-                raw.s[j] = sp[(j * 32 + q * 8) / G];
+            for (int j = 0; j < NJ; j++) raw.w[j] = *reinterpret_cast<const uint32_t*>(cp + j * 16);
+            if constexpr (NG == 1) {
+                raw.sw[0] = sp[0];
+            } else {
+                // scale rows are only 2-byte aligned; gfx950 serves unaligned
+                // dword loads from global memory
+                typedef uint32_t u32_a2 __attribute__((aligned(2)));
+#pragma unroll
+                for (int i = 0; i < NW; i++) raw.sw[i] = reinterpret_cast<const u32_a2*>(sp)[i];
             }
+        };
+        if (it.full) {
+            ld();
         } else {
 #pragma unroll
-            for (int j = 0; j < NJ; j++) {
-                raw.w[j] = 0x88888888u;   // codes 8 ^ 8 = 0 after unbiasing; decodes to zeros
-                raw.s[j] = 0;
-            }
+            for (int j = 0; j < NJ; j++) raw.w[j] = 0x88888888u;   // offset-binary 8 = code 0
+#pragma unroll
+            for (int i = 0; i < NW; i++) raw.sw[i] = 0;
+            if (it.t0 + lm.tok < a.T) ld();
         }
     };
 
-    Raw nxt;
-    load_in(item, nxt);
-
-    for (; item < item_end; ++item) {
-        const ItemPos p = item_pos(item, a.tiles_per_lh);
-        if (p.lh != cur_lh) {
-            cur_lh = p.lh;
-            load_inv_mult<D>(a.lambda + (int64_t)p.lh * D, a.signs, q, lane_sign, m);
+    // The item's 16 output vectors (16 * 2D bytes) are staged through a
+    // wave-private LDS tile so that each global store instruction writes 1 KB
+    // of consecutive vectors instead of 64-byte pieces at a vector stride.
+    // 16-byte chunk c of vector v sits at chunk slot v*CV + (c ^ ((4v) % CV)),
+    // which keeps both the chunk writes and the row reads bank-conflict free.
+    constexpr int CV = D / 8;                  // 16-byte chunks per vector
+    constexpr int VPK = 1024 / (2 * D);        // vectors per 1 KB store row
+    __shared__ uint4 lds_out[kWavesPerBlock][16 * CV];
+    uint4* my_out = lds_out[threadIdx.x >> 6];
+    // store row k: lane covers vector v = k*VPK + lane / CV, chunk lane % CV
+    const int row_c = lane % CV;
+    auto store = [&](int item, const Out& o) {
+        const Item it = decode_item<TM>(item, a);
+        _Float16* ob = og + outer_offset(a.x, it);
+#pragma unroll
+        for (int j = 0; j < NJ; j++) my_out[slot * CV + ((4 * j + q) ^ ((4 * slot) % CV))] = o.o[j];
+        uint4 row[NJ];
+#pragma unroll
+        for (int k = 0; k < NJ; k++) {
+            const int v = k * VPK + lane / CV;
+            row[k] = my_out[v * CV + (row_c ^ ((4 * v) % CV))];
         }
-        Raw cur = nxt;
-        if (item + 1 < item_end) load_in(item + 1, nxt);
+#pragma unroll
+        for (int k = 0; k < NJ; k++) {
+            const LaneMap vm = lane_map<TM>(k * VPK + lane / CV, a);
+            const int64_t off = (int64_t)vm.tok * a.x.st + (int64_t)vm.head * a.x.sh + row_c * 8;
+            if (it.full || it.t0 + vm.tok < a.T) *reinterpret_cast<uint4*>(ob + off) = row[k];
+        }
+    };
 
-        // --- unpack fused with the butterfly on register bit 0 ---------------
-        // Offset-binary nibbles n = q + 8 of the pair (2k, 2k+1), which share a
-        // scale sc:  yhat_2k + yhat_2k+1 = sc * (n0 + n1 - 16),
-        //            yhat_2k - yhat_2k+1 = sc * (n0 - n1 + 16 - 16).
-        float v[N];
+    // scale of chunk j: group (j*32 + q*8) / G of the row
+    auto chunk_scale = [&](const Raw& raw, int j) -> float {
+        uint32_t h;
+        if constexpr (G >= 32) {
+            const int g = (j * 32) / G;
+            h = raw.sw[g / 2] >> (16 * (g % 2));
+        } else if constexpr (G == 16) {
+            h = raw.sw[j] >> ((q & 2) * 8);                         // group 2j + (q >> 1)
+        } else {
+            // group 4j + q: word 2j + (q >> 1), selected without an indexed
+            // access (which would force the row into scratch memory)
+            const uint32_t lo = raw.sw[2 * j], hi = raw.sw[2 * j + 1];
+            const uint32_t wsel = lo ^ ((lo ^ hi) & (0u - (uint32_t)((q >> 1) & 1)));
+            h = wsel >> ((q & 1) * 16);
+        }
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
+    };
+
+    // step 1: unpack fused with the butterfly on register bit 0.  With
+    // offset-binary nibbles n = q + 8 of the pair (2k, 2k+1), which share the
+    // scale sc:  yhat_2k + yhat_2k+1 = sc * (n0 + n1 - 16) and
+    //            yhat_2k - yhat_2k+1 = sc * ((n0 - n1 + 16) - 16).
+    auto first_stage = [&](int item, const Raw& raw, float(&v)[N]) {
+        const Item it = decode_item<TM>(item, a);
+        if (it.key != cur_key) {
+            cur_key = it.key;
+            load_inv_mult<D>(a.lambda + lambda_row<TM>(it, lm, a), a.signs, q, lane_sign, m);
+        }
 #pragma unroll
         for (int j = 0; j < NJ; j++) {
-            const float sc = (float)__builtin_bit_cast(_Float16, cur.s[j]);
+            const float sc = chunk_scale(raw, j);
             const float off = -16.0f * sc;
-            const uint32_t wb = cur.w[j] ^ 0x88888888u;
+            const uint32_t wb = raw.w[j] ^ 0x88888888u;
             const uint32_t lo = wb & 0x0f0f0f0fu;            // n of elements 0,2,4,6
             const uint32_t hi = (wb >> 4) & 0x0f0f0f0fu;     // n of elements 1,3,5,7
             const uint32_t sum = lo + hi;                    // bytewise, <= 30
@@ -374,25 +582,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
                 v[j * 8 + 2 * k + 1] = fmaf(fd, sc, off);
             }
         }
-        fwht_rest(v, c1, c2);
+    };
 
-        // --- unscale, round to fp16, store -----------------------------------
-        const int t = p.tile * kTokensPerTile + slot;
-        if (t < a.T) {
-            const int l = p.lh / a.H, h = p.lh - l * a.H;
-            _Float16* op = og + (int64_t)l * a.x.sl + (int64_t)h * a.x.sh +
-                           (int64_t)p.tile * kTokensPerTile * a.x.st + o_lane;
+    // step 3: rest of the inverse transform, unscale, round to fp16
+    auto finish = [&](float(&v)[N], Out& o) {
+        fwht_rest(v, c1, c2);
 #pragma unroll
-            for (int j = 0; j < NJ; j++) {
-                uint4 o;
-                o.x = pack_half2(v[j * 8 + 0] * m[j * 8 + 0], v[j * 8 + 1] * m[j * 8 + 1]);
-                o.y = pack_half2(v[j * 8 + 2] * m[j * 8 + 2], v[j * 8 + 3] * m[j * 8 + 3]);
-                o.z = pack_half2(v[j * 8 + 4] * m[j * 8 + 4], v[j * 8 + 5] * m[j * 8 + 5]);
-                o.w = pack_half2(v[j * 8 + 6] * m[j * 8 + 6], v[j * 8 + 7] * m[j * 8 + 7]);
-                *reinterpret_cast<uint4*>(op + j * 32) = o;
-            }
+        for (int j = 0; j < NJ; j++) {
+            o.o[j].x = pack_half2(v[j * 8 + 0] * m[j * 8 + 0], v[j * 8 + 1] * m[j * 8 + 1]);
+            o.o[j].y = pack_half2(v[j * 8 + 2] * m[j * 8 + 2], v[j * 8 + 3] * m[j * 8 + 3]);
+            o.o[j].z = pack_half2(v[j * 8 + 4] * m[j * 8 + 4], v[j * 8 + 5] * m[j * 8 + 5]);
+            o.o[j].w = pack_half2(v[j * 8 + 6] * m[j * 8 + 6], v[j * 8 + 7] * m[j * 8 + 7]);
         }
-    }
+    };
+
+    run_pipeline<Raw, Out, N, (D <= 128)>(begin, end, load, first_stage, store, finish);
 }
 
 // ---------------------------------------------------------------------------
@@ -400,19 +604,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
 // ---------------------------------------------------------------------------
 namespace {
 
-template <template <int, int> class K>
-struct Dummy;
-
 template <int D, int G>
 hipError_t launch_q(const Int4Args& a, hipStream_t s, bool inverse)
 {
     const int64_t waves = (a.n_items + a.items_per_wave - 1) / a.items_per_wave;
     const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
     const dim3 block(64 * kWavesPerBlock);
-    if (inverse)
-        hipLaunchKernelGGL((dequantize_kernel<D, G>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((quantize_kernel<D, G>), grid, block, 0, s, a);
+    if (inverse) {
+        if (a.token_major) hipLaunchKernelGGL((dequantize_kernel<D, G, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((dequantize_kernel<D, G, false>), grid, block, 0, s, a);
+    } else {
+        if (a.token_major) hipLaunchKernelGGL((quantize_kernel<D, G, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((quantize_kernel<D, G, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -25,9 +25,17 @@ struct Int4Args {
     Tensor4 scales;         // fp16, D/G per vector
     const float* lambda;    // [L, H, D]
     const int8_t* signs;    // [D]
-    int32_t tiles_per_lh;   // ceil(T / 16)
-    int32_t items_per_wave; // consecutive (layer, head, token-tile) items per wave
-    int64_t n_items;        // L * H * tiles_per_lh
+    // Work items.  Token-major (H divides 16): an item is 16 consecutive
+    // (token, head) vectors of one layer -- 16/H tokens x all H heads, one
+    // contiguous run in a contiguous cache -- and lane slot s always holds
+    // head s % H.  Head-major (other H): an item is 16 consecutive tokens of
+    // one (layer, head) pair.
+    int32_t token_major;
+    int32_t h_shift;         // log2(H) when token-major (H is then a power of two)
+    int32_t items_per_group; // items per layer (token-major) or per (layer, head)
+    int32_t tok_per_item;    // 16/H (token-major) or 16
+    int32_t items_per_wave;  // consecutive items per wavefront
+    int64_t n_items;
 };
 
 struct VqArgs {

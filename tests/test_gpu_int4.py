@@ -92,16 +92,17 @@ def test_gemma_decode_append():
 
 
 # ------------------------------------------------------- instantiations
+@pytest.mark.parametrize("H", [2, 3])           # token-major (H | 16) and head-major items
 @pytest.mark.parametrize("D,G", [(D, G) for D in (64, 128, 256) for G in (8, 16, 32, 64, 128, 256) if G <= D])
-def test_every_instantiation(D, G):
+def test_every_instantiation(D, G, H):
     dev = device()
-    g = torch.Generator(device="cpu").manual_seed(D * 1000 + G)
-    L, T, H = 2, 37, 3                         # 3 token tiles per (l, h), ragged tail
+    g = torch.Generator(device="cpu").manual_seed(D * 1000 + G + H)
+    L, T = 2, 37                               # several items per group, ragged tail
     x = (torch.randn((L, T, H, D), generator=g) * torch.exp(torch.randn((L, 1, H, D), generator=g))
          ).to(torch.float16).to(dev)
     lam = torch.exp(0.5 * torch.randn((L, H, D), generator=g)).to(dev)
     s = (torch.randint(0, 2, (D,), generator=g, dtype=torch.int8) * 2 - 1).to(torch.int8).to(dev)
-    full_check(x, lam, s, G, "D=%d G=%d" % (D, G))
+    full_check(x, lam, s, G, "D=%d G=%d H=%d" % (D, G, H))
 
 
 # ------------------------------------------------------------ edge cases
