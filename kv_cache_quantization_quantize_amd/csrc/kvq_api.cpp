@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
 
@@ -94,6 +96,42 @@ int32_t items_per_wave(int64_t n_items)
     return (int32_t)ipw;
 }
 
+// Work items of the 4-lanes-per-vector kernels: token-major (16 consecutive
+// (token, head) vectors of a layer) when the head count divides 16, else
+// head-major (16 consecutive tokens of one (layer, head)).
+void set_items(const kvq_shape& s, int32_t& token_major, int32_t& h_shift, int32_t& items_per_group,
+               int32_t& tok_per_item, int32_t& ipw, int64_t& n_items)
+{
+    token_major = (kvq::kTokensPerTile % s.heads) == 0;
+    h_shift = 0;
+    while ((int64_t(1) << h_shift) < s.heads) h_shift++;
+    if (token_major) {
+        tok_per_item = (int32_t)(kvq::kTokensPerTile / s.heads);
+        items_per_group = (int32_t)((s.tokens + tok_per_item - 1) / tok_per_item);
+        n_items = s.layers * (int64_t)items_per_group;
+    } else {
+        tok_per_item = kvq::kTokensPerTile;
+        items_per_group = (int32_t)((s.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
+        n_items = s.layers * s.heads * (int64_t)items_per_group;
+    }
+    ipw = items_per_wave(n_items);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static thread_local int cached_dev = -1, cached_cus = 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return cached_cus;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            cached_cus = cus;
+        cached_dev = dev;
+    }
+    return cached_cus;
+}
+
 kvq_status hip_status(hipError_t e, const char* what)
 {
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -128,19 +166,7 @@ kvq_status int4_common(const kvq_shape& shape, const kvq_view& x, const float* l
     a.scales = t4(scales);
     a.lambda = lambda;
     a.signs = signs;
-    a.token_major = (kvq::kTokensPerTile % shape.heads) == 0;
-    a.h_shift = 0;
-    while ((int64_t(1) << a.h_shift) < shape.heads) a.h_shift++;
-    if (a.token_major) {
-        a.tok_per_item = (int32_t)(kvq::kTokensPerTile / shape.heads);
-        a.items_per_group = (int32_t)((shape.tokens + a.tok_per_item - 1) / a.tok_per_item);
-        a.n_items = shape.layers * (int64_t)a.items_per_group;
-    } else {
-        a.tok_per_item = kvq::kTokensPerTile;
-        a.items_per_group = (int32_t)((shape.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
-        a.n_items = shape.layers * shape.heads * (int64_t)a.items_per_group;
-    }
-    a.items_per_wave = items_per_wave(a.n_items);
+    set_items(shape, a.token_major, a.h_shift, a.items_per_group, a.tok_per_item, a.items_per_wave, a.n_items);
     return KVQ_OK;
 }
 
@@ -173,9 +199,11 @@ kvq_status vq_common(const kvq_shape& shape, const kvq_view& x, const float* lam
     a.signs = signs;
     a.codebook = static_cast<const uint16_t*>(codebook);
     a.cb_layer_stride = cb_layer_stride;
-    a.tiles_per_lh = (int32_t)((shape.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
-    a.n_items = shape.layers * shape.heads * (int64_t)a.tiles_per_lh;
-    a.items_per_wave = items_per_wave(a.n_items);
+    set_items(shape, a.token_major, a.h_shift, a.items_per_group, a.tok_per_item, a.items_per_wave, a.n_items);
+    const int64_t tpu = 16 * kvq::vq_encode_waves((int)D);
+    a.enc_units_per_lh = (int32_t)((shape.tokens + tpu - 1) / tpu);
+    a.enc_n_units = shape.layers * shape.heads * (int64_t)a.enc_units_per_lh;
+    a.enc_units_per_block = 1;
     return KVQ_OK;
 }
 
@@ -212,6 +240,10 @@ kvq_status kvq_vq_encode(kvq_shape shape, kvq_view x_f16, const float* lambda, c
     KVQ_TRY(vq_common(shape, x_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
                       idx_u16, a, false));
     if (empty(shape)) return KVQ_OK;
+    // one block per CU holds the 144 KB of LDS; four blocks' worth of units
+    // per CU balance the tail
+    const int64_t blocks = std::min<int64_t>(a.enc_n_units, 4 * (int64_t)device_cus());
+    a.enc_units_per_block = (int32_t)((a.enc_n_units + blocks - 1) / blocks);
     return hip_status(kvq::launch_vq_encode(a, static_cast<hipStream_t>(stream)), "kvq_vq_encode launch");
 }
 

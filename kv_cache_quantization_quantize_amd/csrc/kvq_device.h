@@ -136,6 +136,63 @@ __device__ __forceinline__ void quad_max(float (&a)[N])
 }
 #undef KVQ_M
 
+// 1/sqrt(D) and sqrt(D) for the supported head dims.
+template <int D>
+struct RsqrtD;
+template <> struct RsqrtD<64> { static constexpr float v = 0.125f; };
+template <> struct RsqrtD<128> { static constexpr float v = 0.0883883476483184405f; };
+template <> struct RsqrtD<256> { static constexpr float v = 0.0625f; };
+template <int D>
+struct SqrtD;
+template <> struct SqrtD<64> { static constexpr float v = 8.0f; };
+template <> struct SqrtD<128> { static constexpr float v = 11.3137084989847604f; };
+template <> struct SqrtD<256> { static constexpr float v = 16.0f; };
+
+// Lane's register multipliers for the forward rotation (lane q of a quad,
+// coordinates j*32 + q*8 + e): s_c * lambda_c / sqrt(D).
+template <int D>
+__device__ __forceinline__ void load_fwd_mult(const float* lam_lh, const int8_t* signs, int q,
+                                              float (&m)[D / 4])
+{
+#pragma unroll
+    for (int j = 0; j < D / 32; j++) {
+        const int c0 = j * 32 + q * 8;
+        const float4 l0 = *reinterpret_cast<const float4*>(lam_lh + c0);
+        const float4 l1 = *reinterpret_cast<const float4*>(lam_lh + c0 + 4);
+        const uint2 sg = *reinterpret_cast<const uint2*>(signs + c0);
+        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const uint32_t word = e < 4 ? sg.x : sg.y;
+            const int sv = (int)(int8_t)((word >> (8 * (e & 3))) & 0xff);
+            m[j * 8 + e] = (sv < 0 ? -lv[e] : lv[e]) * RsqrtD<D>::v;
+        }
+    }
+}
+
+// Inverse multipliers s_c / (lambda_c * sqrt(D)), times the lane's final
+// transform sign.
+template <int D>
+__device__ __forceinline__ void load_inv_mult(const float* lam_lh, const int8_t* signs, int q,
+                                              float lane_sign, float (&m)[D / 4])
+{
+#pragma unroll
+    for (int j = 0; j < D / 32; j++) {
+        const int c0 = j * 32 + q * 8;
+        const float4 l0 = *reinterpret_cast<const float4*>(lam_lh + c0);
+        const float4 l1 = *reinterpret_cast<const float4*>(lam_lh + c0 + 4);
+        const uint2 sg = *reinterpret_cast<const uint2*>(signs + c0);
+        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const uint32_t word = e < 4 ? sg.x : sg.y;
+            const int sv = (int)(int8_t)((word >> (8 * (e & 3))) & 0xff);
+            const float sgn = (sv < 0) ? -lane_sign : lane_sign;
+            m[j * 8 + e] = sgn / (lv[e] * SqrtD<D>::v);
+        }
+    }
+}
+
 // Forces v to be computed here: no instruction producing v may sink below
 // this point, and no load or store may move across it (empty asm with a
 // memory clobber).  Used to place the wait for an item's loads before the

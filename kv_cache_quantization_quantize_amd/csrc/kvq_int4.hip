@@ -38,61 +38,6 @@ constexpr float kMagic8 = 12582920.0f;  // 1.5 * 2^23 + 8: fma(y, 1/scale, kMagi
                                         // leaves 8 + rne(y/scale) in the low bits
 constexpr float kInv7 = 0.142857142857142857f;
 
-template <int D>
-struct RsqrtD;
-template <> struct RsqrtD<64> { static constexpr float v = 0.125f; };
-template <> struct RsqrtD<128> { static constexpr float v = 0.0883883476483184405f; };
-template <> struct RsqrtD<256> { static constexpr float v = 0.0625f; };
-template <int D>
-struct SqrtD;
-template <> struct SqrtD<64> { static constexpr float v = 8.0f; };
-template <> struct SqrtD<128> { static constexpr float v = 11.3137084989847604f; };
-template <> struct SqrtD<256> { static constexpr float v = 16.0f; };
-
-// Lane's register multipliers for the forward rotation: s_c * lambda_c / sqrt(D).
-template <int D>
-__device__ __forceinline__ void load_fwd_mult(const float* lam_lh, const int8_t* signs, int q,
-                                              float (&m)[D / 4])
-{
-#pragma unroll
-    for (int j = 0; j < D / 32; j++) {
-        const int c0 = j * 32 + q * 8;
-        const float4 l0 = *reinterpret_cast<const float4*>(lam_lh + c0);
-        const float4 l1 = *reinterpret_cast<const float4*>(lam_lh + c0 + 4);
-        const uint2 sg = *reinterpret_cast<const uint2*>(signs + c0);
-        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const uint32_t word = e < 4 ? sg.x : sg.y;
-            const int sv = (int)(int8_t)((word >> (8 * (e & 3))) & 0xff);
-            m[j * 8 + e] = (sv < 0 ? -lv[e] : lv[e]) * RsqrtD<D>::v;
-        }
-    }
-}
-
-// Inverse multipliers s_c / (lambda_c * sqrt(D)), times the lane's final
-// transform sign.
-template <int D>
-__device__ __forceinline__ void load_inv_mult(const float* lam_lh, const int8_t* signs, int q,
-                                              float lane_sign, float (&m)[D / 4])
-{
-#pragma unroll
-    for (int j = 0; j < D / 32; j++) {
-        const int c0 = j * 32 + q * 8;
-        const float4 l0 = *reinterpret_cast<const float4*>(lam_lh + c0);
-        const float4 l1 = *reinterpret_cast<const float4*>(lam_lh + c0 + 4);
-        const uint2 sg = *reinterpret_cast<const uint2*>(signs + c0);
-        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const uint32_t word = e < 4 ? sg.x : sg.y;
-            const int sv = (int)(int8_t)((word >> (8 * (e & 3))) & 0xff);
-            const float sgn = (sv < 0) ? -lane_sign : lane_sign;
-            m[j * 8 + e] = sgn / (lv[e] * SqrtD<D>::v);
-        }
-    }
-}
-
 // Byte k of the result = low byte of a_k (k = 0..3).
 __device__ __forceinline__ uint32_t gather_low_bytes(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3)
 {

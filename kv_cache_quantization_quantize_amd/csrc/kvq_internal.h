@@ -46,10 +46,21 @@ struct VqArgs {
     const int8_t* signs;    // [D]
     const uint16_t* codebook;   // fp16 bits, [H, K, sub] per layer
     int64_t cb_layer_stride;    // elements; 0 = shared
-    int32_t tiles_per_lh;
-    int32_t items_per_wave;
+    // decode work items: as Int4Args
+    int32_t token_major, h_shift, items_per_group, tok_per_item, items_per_wave;
     int64_t n_items;
+    // encode units: (layer, head, 16*waves-token chunk), ordered head-major
+    // when one codebook serves all layers so that a block rarely re-stages it
+    int32_t enc_units_per_lh;
+    int32_t enc_units_per_block;
+    int64_t enc_n_units;
 };
+
+// Centroids staged in LDS at a time by the VQ encoder (64 KB of fp16).
+constexpr int kVqChunk = 4096;
+
+// Wavefronts per VQ-encode block for a head dim (each stages 16 keys).
+int vq_encode_waves(int D);
 
 // Launchers: enqueue on `stream`, return the launch status.  Arguments have
 // been validated by the caller.

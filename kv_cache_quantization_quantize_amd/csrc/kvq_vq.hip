@@ -1,6 +1,431 @@
-// kvq_vq.hip -- product-VQ encode/decode (in progress).
+// kvq_vq.hip -- product-VQ encode (MFMA nearest-centroid search) and decode
+// for gfx950 (MI355X).
+//
+// The method (VecInfer blog, "What VecInfer does"; VeloxQuant-MLX package
+// description, "Metal kernels"): keys are smooth-scaled and Walsh-Hadamard
+// rotated, split into sub-vectors of 8, and each sub-vector is replaced by
+// the index of its nearest centroid in the head's codebook; the search keeps
+// its running argmin in registers and never materialises the [sub-vectors,
+// centroids, 8] difference tensor.  Decode gathers the centroids back and
+// undoes the rotation and the smooth scale.
+//
+// Encode.  argmin_k ||y - c_k||^2 = argmax_k (y . c_k - ||c_k||^2 / 2).  The
+// dot products of 32 centroids x 32 sub-vectors are one
+// v_mfma_f32_32x32x16_f16: A rows are centroids [c | c] (k = 0..15), B
+// columns are sub-vectors [y_hi ; y_lo] with y_hi = fp16(y), y_lo =
+// fp16(y - y_hi), so A.B = c.(y_hi + y_lo) = c.y to fp32 accuracy without
+// rounding the key to fp16.  A second MFMA adds -(n_hi + n_lo)/2, the fp16
+// split of ||c||^2, into the same accumulator.  Each lane then holds the
+// scores of 16 centroids for one sub-vector: a max3 tree gives the tile
+// maximum, and only the best tile is tracked (strict >, so the earliest tile
+// wins ties).  After a sweep, the lanes that improved re-score the 16
+// candidates of their best tile on VALU to find the position (first maximum,
+// so the lowest index wins), and the two lanes that share a sub-vector (rows
+// 0-3,8-11,.. and 4-7,12-15,..) merge (value, index) lexicographically.
+//
+// The codebook (<= 4096 centroids at a time, 64 KB) and its norms live in
+// LDS; a block of WAVES wavefronts shares it, each wavefront rotating 16 keys
+// of one (layer, head) and sweeping the codebook for GPR groups of 32
+// sub-vectors per pass.  Contraction work per key: D/8 x K x 8 MACs; the MFMA
+// executes 4x that (hi/lo split and the norm MFMA).
+#include <type_traits>
+
+#include "kvq_device.h"
 #include "kvq_internal.h"
+
 namespace kvq {
-hipError_t launch_vq_encode(const VqArgs&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_vq_decode(const VqArgs&, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int D>
+struct VqCfg {
+    static constexpr int NS = D / 8;               // sub-vectors per key
+    static constexpr int NJ = D / 32;              // 16-byte chunks per lane
+    static constexpr int N = D / 4;                // coordinates per lane
+    static constexpr int NGRP = D / 16;            // groups of 32 sub-vectors per 16 keys
+    static constexpr int GPR = NGRP < 4 ? NGRP : 4;   // groups per codebook sweep
+    static constexpr int ROUNDS = NGRP / GPR;
+    static constexpr int WAVES = (D == 256) ? 4 : 8;  // wavefronts per block (LDS budget)
+};
+
+__device__ __forceinline__ h8_t as_h8(uint4 u) { return __builtin_bit_cast(h8_t, u); }
+
+// Swizzled position of 16-byte sub-vector chunk s of key v in a staging row.
+template <int NS>
+__device__ __forceinline__ int stage_slot(int v, int s) { return v * NS + (s ^ ((4 * v) % NS)); }
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs a)
+{
+    using C = VqCfg<D>;
+    constexpr int NS = C::NS, NJ = C::NJ, N = C::N, GPR = C::GPR, ROUNDS = C::ROUNDS, WAVES = C::WAVES;
+
+    __shared__ uint4 cb_lds[kVqChunk];                 // centroid k: 8 fp16
+    __shared__ uint32_t nrm_lds[kVqChunk + 1];         // packed (n_hi, n_lo); last slot 0
+    __shared__ uint4 stage[WAVES][2][16 * NS];         // [wave][hi/lo][key, sub-vector]
+
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 3;
+    const int slot = lane >> 2;
+    const int wid = uniform(threadIdx.x >> 6);
+    const float c1 = (q & 1) ? -1.0f : 1.0f;
+    const float c2 = (q & 2) ? -1.0f : 1.0f;
+    const float lane_sign = (__builtin_popcount(q) & 1) ? -1.0f : 1.0f;
+    const int col = lane & 31;                         // MFMA column (sub-vector in a group)
+    const int half = lane >> 5;                        // 0: rows 0-3, 8-11, ..; 1: rows 4-7, ..
+
+    if (threadIdx.x == 0) nrm_lds[kVqChunk] = 0;
+    // B2 = [-1/2, -1/2, 0 ...] in the k = 0..7 half, zero in the other
+    const uint32_t mhalf2 = 0xB800B800u;               // two fp16 -0.5
+    const h8_t b2 = as_h8(make_uint4(half == 0 ? mhalf2 : 0u, 0u, 0u, 0u));
+
+    const int nchunks = (a.K + kVqChunk - 1) / kVqChunk;
+    const int64_t ubeg = (int64_t)blockIdx.x * a.enc_units_per_block;
+    const int64_t uend = min(ubeg + a.enc_units_per_block, a.enc_n_units);
+    int cur_cb = -1, cur_lh = -1;
+    float m[N];
+
+    const _Float16* __restrict__ xg = static_cast<const _Float16*>(a.x.data);
+    uint16_t* __restrict__ ig = static_cast<uint16_t*>(a.idx.data);
+
+    for (int64_t u = ubeg; u < uend; ++u) {
+        // ---- unit -> (layer, head, token chunk); codebook-major order ----------
+        const int ui = uniform((int)u);
+        const int c = ui % a.enc_units_per_lh;
+        const int g2 = ui / a.enc_units_per_lh;
+        int l, h;
+        if (a.cb_layer_stride == 0) { h = uniform(g2 / a.L); l = g2 - h * a.L; }
+        else { l = uniform(g2 / a.H); h = g2 - l * a.H; }
+        const int lh = l * a.H + h;
+        const int cbkey = a.cb_layer_stride == 0 ? h : lh;
+        const uint16_t* cbp = a.codebook + (int64_t)l * a.cb_layer_stride + (int64_t)h * a.K * 8;
+        if (lh != cur_lh) {
+            cur_lh = lh;
+            load_fwd_mult<D>(a.lambda + (int64_t)lh * D, a.signs, q, m);
+        }
+
+        // ---- rotate this wavefront's 16 keys (4 lanes per key) ---------------
+        const int t0 = c * 16 * WAVES + wid * 16;
+        const int t = t0 + slot;
+        const bool valid = t < a.T;
+        uint4 raw[NJ];
+        {
+            const _Float16* p = xg + (int64_t)l * a.x.sl + (int64_t)h * a.x.sh + (int64_t)t * a.x.st + q * 8;
+#pragma unroll
+            for (int j = 0; j < NJ; j++) raw[j] = make_uint4(0, 0, 0, 0);
+            if (valid) {
+#pragma unroll
+                for (int j = 0; j < NJ; j++) raw[j] = *reinterpret_cast<const uint4*>(p + j * 32);
+            }
+        }
+        float v[N];
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const int r = j * 8 + 2 * k;
+                const float b = fmaf(hi_half(w[k]), m[r + 1], 0.0f);
+                v[r] = fmaf(lo_half(w[k]), m[r], b);
+                v[r + 1] = fmaf(lo_half(w[k]), m[r], -b);
+            }
+        }
+        fwht_rest(v, c1, c2);
+
+        // ---- split y = y_hi + y_lo (fp16 each) and stage by sub-vector -------
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const float y0 = v[j * 8 + 2 * k] * lane_sign, y1 = v[j * 8 + 2 * k + 1] * lane_sign;
+                const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
+                const _Float16 r0 = (_Float16)(y0 - (float)h0), r1 = (_Float16)(y1 - (float)h1);
+                hw[k] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
+                lw[k] = __builtin_bit_cast(uint32_t, half2_t{r0, r1});
+            }
+            const int sl = stage_slot<NS>(slot, 4 * j + q);
+            stage[wid][0][sl] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            stage[wid][1][sl] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+
+        for (int rd = 0; rd < ROUNDS; rd++) {
+            // B operands: group g covers sub-vectors 32g .. 32g+31 of the 16 keys
+            h8_t bop[GPR];
+#pragma unroll
+            for (int gg = 0; gg < GPR; gg++) {
+                const int sv = 32 * (rd * GPR + gg) + col;
+                bop[gg] = as_h8(stage[wid][half][stage_slot<NS>(sv / NS, sv % NS)]);
+            }
+            float best_val[GPR];
+            int best_idx[GPR];
+#pragma unroll
+            for (int gg = 0; gg < GPR; gg++) {
+                best_val[gg] = -__builtin_inff();
+                best_idx[gg] = 0;
+            }
+
+            for (int ch = 0; ch < nchunks; ch++) {
+                const int kbase = ch * kVqChunk;
+                const int kc = min(kVqChunk, a.K - kbase);
+                if (nchunks > 1 || cbkey != cur_cb) {
+                    // ---- stage codebook chunk + split norms (whole block) ----------
+                    __syncthreads();
+                    for (int k = threadIdx.x; k < kVqChunk; k += 64 * WAVES) {
+                        uint4 cv = make_uint4(0, 0, 0, 0);
+                        uint32_t nw = 0x00007C00u;       // n_hi = +inf: padding never wins
+                        if (k < kc) {
+                            cv = *reinterpret_cast<const uint4*>(cbp + (int64_t)(kbase + k) * 8);
+                            const uint32_t w[4] = {cv.x, cv.y, cv.z, cv.w};
+                            float n = 0.0f;
+#pragma unroll
+                            for (int e = 0; e < 4; e++) {
+                                n = fmaf(lo_half(w[e]), lo_half(w[e]), n);
+                                n = fmaf(hi_half(w[e]), hi_half(w[e]), n);
+                            }
+                            const _Float16 nh = (_Float16)n;
+                            const _Float16 nl = (_Float16)(n - (float)nh);
+                            nw = __builtin_bit_cast(uint32_t, half2_t{nh, nl});
+                        }
+                        cb_lds[k] = cv;
+                        nrm_lds[k] = nw;
+                    }
+                    __syncthreads();
+                    cur_cb = nchunks > 1 ? -1 : cbkey;
+                }
+
+                // ---- sweep the chunk: 32 centroids per MFMA tile -------------------
+                const int ntiles = (kc + 31) / 32;
+                int best_tile[GPR];
+#pragma unroll
+                for (int gg = 0; gg < GPR; gg++) best_tile[gg] = -1;
+                for (int tl = 0; tl < ntiles; tl++) {
+                    const h8_t aop = as_h8(cb_lds[tl * 32 + col]);
+                    const h8_t a2 = as_h8(make_uint4(nrm_lds[half == 0 ? tl * 32 + col : kVqChunk], 0u, 0u, 0u));
+#pragma unroll
+                    for (int gg = 0; gg < GPR; gg++) {
+                        f32x16_t acc = {};
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop[gg], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2, b2, acc, 0, 0, 0);
+                        float mx = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+#pragma unroll
+                        for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
+                        mx = fmaxf(mx, acc[15]);
+                        if (mx > best_val[gg]) {
+                            best_val[gg] = mx;
+                            best_tile[gg] = tl;
+                        }
+                    }
+                }
+
+                // ---- lanes whose best moved into this chunk find its position -------
+#pragma unroll
+                for (int gg = 0; gg < GPR; gg++) {
+                    if (best_tile[gg] >= 0) {
+                        const int sv = 32 * (rd * GPR + gg) + col;
+                        const int ss = stage_slot<NS>(sv / NS, sv % NS);
+                        const uint4 yh = stage[wid][0][ss], yl = stage[wid][1][ss];
+                        const uint32_t hwv[4] = {yh.x, yh.y, yh.z, yh.w}, lwv[4] = {yl.x, yl.y, yl.z, yl.w};
+                        float y[8];
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            y[2 * e] = lo_half(hwv[e]) + lo_half(lwv[e]);
+                            y[2 * e + 1] = hi_half(hwv[e]) + hi_half(lwv[e]);
+                        }
+                        float bs = -__builtin_inff();
+                        int bk = 0;
+#pragma unroll
+                        for (int r = 0; r < 16; r++) {
+                            const int row = 8 * (r / 4) + 4 * half + (r % 4);
+                            const int k = best_tile[gg] * 32 + row;
+                            const uint4 cv = cb_lds[k];
+                            const uint32_t nw = nrm_lds[k];
+                            const uint32_t w[4] = {cv.x, cv.y, cv.z, cv.w};
+                            float sc = -0.5f * (lo_half(nw) + hi_half(nw));
+#pragma unroll
+                            for (int e = 0; e < 4; e++) {
+                                sc = fmaf(lo_half(w[e]), y[2 * e], sc);
+                                sc = fmaf(hi_half(w[e]), y[2 * e + 1], sc);
+                            }
+                            if (sc > bs) {
+                                bs = sc;
+                                bk = k;
+                            }
+                        }
+                        best_idx[gg] = kbase + bk;
+                    }
+                }
+            }
+
+            // ---- merge the two row halves of each sub-vector, store indices --------
+#pragma unroll
+            for (int gg = 0; gg < GPR; gg++) {
+                const float ov = __shfl_xor(best_val[gg], 32);
+                const int oi = __shfl_xor(best_idx[gg], 32);
+                int idx = best_idx[gg];
+                if (ov > best_val[gg] || (ov == best_val[gg] && oi < idx)) idx = oi;
+                const int sv = 32 * (rd * GPR + gg) + col;
+                const int key = sv / NS, s = sv % NS;
+                const int tk = t0 + key;
+                if (half == 0 && tk < a.T)
+                    ig[(int64_t)l * a.idx.sl + (int64_t)h * a.idx.sh + (int64_t)tk * a.idx.st + s] = (uint16_t)idx;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: indices -> centroids -> inverse transform -> unscale -> fp16
+// ---------------------------------------------------------------------------
+template <int D, bool TM>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void vq_decode_kernel(VqArgs a)
+{
+    constexpr int NJ = D / 32;
+    constexpr int N = NJ * 8;
+    constexpr int CV = D / 8;
+    constexpr int VPK = 1024 / (2 * D);
+
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 3;
+    const int slot = lane >> 2;
+    const int wave = uniform((int)(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)));
+    const int begin = wave * a.items_per_wave;
+    const int end = (int)min((int64_t)begin + a.items_per_wave, a.n_items);
+    if (begin >= end) return;
+
+    const float c1 = (q & 1) ? -1.0f : 1.0f;
+    const float c2 = (q & 2) ? -1.0f : 1.0f;
+    const float lane_sign = (__builtin_popcount(q) & 1) ? -1.0f : 1.0f;
+
+    _Float16* __restrict__ og = static_cast<_Float16*>(a.x.data);
+    const uint16_t* __restrict__ ig = static_cast<const uint16_t*>(a.idx.data);
+
+    // lane's vector within an item: token offset and head (token-major items
+    // hold 16/H tokens x H heads, head-major items 16 tokens of one head)
+    const int ltok = TM ? (slot >> a.h_shift) : slot;
+    const int lhead = TM ? (slot & (a.H - 1)) : 0;
+
+    __shared__ uint4 lds_out[kWavesPerBlock][16 * CV];
+    uint4* my_out = lds_out[threadIdx.x >> 6];
+    const int row_c = lane % CV;
+
+    float m[N];
+    int cur_key = -1;
+
+    for (int item = begin; item < end; ++item) {
+        const int grp = uniform(item / a.items_per_group);
+        const int kk = item - grp * a.items_per_group;
+        const int t0 = uniform(kk * a.tok_per_item);
+        int l, hbase;
+        if constexpr (TM) { l = grp; hbase = 0; }
+        else { l = uniform(grp / a.H); hbase = grp - l * a.H; }
+        const int h = hbase + lhead;
+        const bool valid = t0 + ltok < a.T;
+        const int key = TM ? l : grp;
+        if (key != cur_key) {
+            cur_key = key;
+            load_inv_mult<D>(a.lambda + ((int64_t)l * a.H + h) * D, a.signs, q, lane_sign, m);
+        }
+        // indices of sub-vectors 4j + q, then the centroids (8 fp16 = chunk j)
+        const uint16_t* ip = ig + (int64_t)l * a.idx.sl + (int64_t)h * a.idx.sh + (int64_t)(t0 + ltok) * a.idx.st + q;
+        const uint16_t* cbp = a.codebook + (int64_t)l * a.cb_layer_stride + (int64_t)h * a.K * 8;
+        uint4 cv[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; j++) cv[j] = make_uint4(0, 0, 0, 0);
+        if (valid) {
+            uint32_t ix[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; j++) ix[j] = min((uint32_t)ip[4 * j], (uint32_t)(a.K - 1));
+#pragma unroll
+            for (int j = 0; j < NJ; j++) cv[j] = *reinterpret_cast<const uint4*>(cbp + (int64_t)ix[j] * 8);
+        }
+        // first butterfly stage straight from the fp16 centroid values
+        float v[N];
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const uint32_t w[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const float x0 = lo_half(w[k]), x1 = hi_half(w[k]);
+                v[j * 8 + 2 * k] = x0 + x1;
+                v[j * 8 + 2 * k + 1] = x0 - x1;
+            }
+        }
+        fwht_rest(v, c1, c2);
+        uint4 o[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            o[j].x = pack_half2(v[j * 8 + 0] * m[j * 8 + 0], v[j * 8 + 1] * m[j * 8 + 1]);
+            o[j].y = pack_half2(v[j * 8 + 2] * m[j * 8 + 2], v[j * 8 + 3] * m[j * 8 + 3]);
+            o[j].z = pack_half2(v[j * 8 + 4] * m[j * 8 + 4], v[j * 8 + 5] * m[j * 8 + 5]);
+            o[j].w = pack_half2(v[j * 8 + 6] * m[j * 8 + 6], v[j * 8 + 7] * m[j * 8 + 7]);
+        }
+        // stage through LDS so each store instruction writes 1 KB of consecutive vectors
+#pragma unroll
+        for (int j = 0; j < NJ; j++) my_out[slot * CV + ((4 * j + q) ^ ((4 * slot) % CV))] = o[j];
+        _Float16* ob = og + (int64_t)l * a.x.sl + (int64_t)hbase * a.x.sh + (int64_t)t0 * a.x.st;
+#pragma unroll
+        for (int k = 0; k < NJ; k++) {
+            const int vv = k * VPK + lane / CV;
+            const uint4 rowv = my_out[vv * CV + (row_c ^ ((4 * vv) % CV))];
+            const int vt = TM ? (vv >> a.h_shift) : vv;
+            const int vh = TM ? (vv & (a.H - 1)) : 0;
+            const int64_t off = (int64_t)vt * a.x.st + (int64_t)vh * a.x.sh + row_c * 8;
+            if (t0 + vt < a.T) *reinterpret_cast<uint4*>(ob + off) = rowv;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int D>
+hipError_t launch_enc(const VqArgs& a, hipStream_t s)
+{
+    const dim3 grid((unsigned)((a.enc_n_units + a.enc_units_per_block - 1) / a.enc_units_per_block));
+    hipLaunchKernelGGL((vq_encode_kernel<D>), grid, dim3(64 * VqCfg<D>::WAVES), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dec(const VqArgs& a, hipStream_t s)
+{
+    const int64_t waves = (a.n_items + a.items_per_wave - 1) / a.items_per_wave;
+    const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+    if (a.token_major) hipLaunchKernelGGL((vq_decode_kernel<D, true>), grid, dim3(64 * kWavesPerBlock), 0, s, a);
+    else hipLaunchKernelGGL((vq_decode_kernel<D, false>), grid, dim3(64 * kWavesPerBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int vq_encode_waves(int D) { return D == 256 ? VqCfg<256>::WAVES : VqCfg<128>::WAVES; }
+
+hipError_t launch_vq_encode(const VqArgs& a, hipStream_t s)
+{
+    switch (a.D) {
+        case 64: return launch_enc<64>(a, s);
+        case 128: return launch_enc<128>(a, s);
+        case 256: return launch_enc<256>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_vq_decode(const VqArgs& a, hipStream_t s)
+{
+    switch (a.D) {
+        case 64: return launch_dec<64>(a, s);
+        case 128: return launch_dec<128>(a, s);
+        case 256: return launch_dec<256>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace kvq

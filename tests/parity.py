@@ -125,3 +125,31 @@ def summary(rep) -> str:
     for k, r in rep.items():
         parts.append("%s: %s" % (k, {a: b for a, b in r.items() if not a.endswith("_mask") and a != "q_cond"}))
     return "; ".join(parts)
+
+
+def vq_parity(x_bits, lam_rows, signs, codebooks_bits, book, sub, idx_gpu, out_gpu=None):
+    """Product-VQ check of n keys: indices against the oracle's (exact, or a
+    distance within 1e-4 relative; an index that differs at an exactly equal
+    distance breaks the lowest-index rule and fails), and, when given, the GPU
+    decode of its own indices against the oracle's decode of the same ones."""
+    x_bits = np.ascontiguousarray(x_bits, np.uint16)
+    lam_rows = np.ascontiguousarray(lam_rows, np.float32)
+    idx_gpu = np.ascontiguousarray(idx_gpu, np.uint16)
+    idx_o, y64 = oracle.vq_encode(x_bits, lam_rows, signs, codebooks_bits, book, sub)
+    K = codebooks_bits.shape[-2]
+    if (idx_gpu >= K).any():
+        raise ParityError("GPU index out of range: max %d >= %d" % (idx_gpu.max(), K))
+    rep = {"vq": check_vq(y64, codebooks_bits, book, idx_gpu, idx_o, sub)}
+    if rep["vq"]["bad"]:
+        i = np.argwhere(rep["vq"]["bad_mask"])[:5]
+        _raise("vq index", rep["vq"], "first bad [key, sub]: %s gpu=%s ora=%s" % (
+            i.tolist(), idx_gpu[tuple(i.T)], idx_o[tuple(i.T)]))
+    if out_gpu is not None:
+        x64, _ = oracle.vq_decode(idx_gpu, codebooks_bits, book, lam_rows, signs, sub)
+        rd = check_dequant(out_gpu, x64, lam_rows)
+        rep["decode"] = rd
+        if rd["bad"]:
+            i = np.argwhere(rd["bad_mask"])[:5]
+            _raise("vq decode", rd, "first bad [key, coord]: %s gpu=%s ora=%s" % (
+                i.tolist(), f16(out_gpu)[tuple(i.T)], x64[tuple(i.T)]))
+    return rep
