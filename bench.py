@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--no-vq", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=192, help="tokens per (layer, head) in the CPU sample")
     ap.add_argument("--copy-bytes", type=int, default=4 << 30, help="size of the plain-copy reference")
+    ap.add_argument("--parts", default="int4,vq",
+                    help="comma list of what to run: int4 (the timed step), vq, copy (the plain-copy "
+                         "reference of --copy-bytes, used to scale memory counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -141,6 +144,14 @@ def main():
         sys.exit(2)
     kvq.lib()
     dev = torch.device("cuda:0")
+    parts = set(args.parts.split(","))
+    if "int4" not in parts:
+        # profiling helper runs: only the requested kernels, no JSON line
+        if "copy" in parts:
+            print("copy reference: %.1f GB/s over %d bytes" % (copy_ceiling(torch, args.copy_bytes), args.copy_bytes))
+        if "vq" in parts:
+            print(json.dumps({"vq": bench_vq(torch, kvq, synth, dev, args)}))
+        return
 
     cfg = synth.config("qwen3-8b", T=args.tokens)
     L, T, H, D, G = cfg.L, cfg.T, cfg.H, cfg.D, cfg.G
@@ -283,7 +294,11 @@ def bench_vq(torch, kvq, synth, dev, args):
             tf = flop / (avg * 1e-3) / 1e12
             r.update({"algorithmic_TFLOP": round(flop / 1e12, 4), "TFLOP_per_s": round(tf, 2),
                       "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
-                      "executed_mfma_flop_factor": 4.0})
+                      # per 32-centroid tile and 4 groups of 32 sub-vectors: four
+                      # 32x32x16 MFMAs on the fp16 hi/lo split plus one 32x32x8
+                      # norm MFMA, against 4 x 32 x 32 x 8 algorithmic MACs
+                      "executed_mfma_flop_factor": 2.25,
+                      "executed_frac_of_fp16_mfma_peak": round(2.25 * tf / FP16_MFMA_PEAK_TFLOPS, 4)})
         else:
             byt = nkeys * (2 * D + 2 * (D // cfg.sub_dim))
             r.update({"GB_per_s": round(byt / (avg * 1e-3) / 1e9, 1),

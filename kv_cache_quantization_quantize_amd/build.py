@@ -32,10 +32,16 @@ COMMON = [
 ]
 
 
+# Per-file extra flags.  The VQ search takes maxima of MFMA results; without
+# -fno-honor-nans every fmaxf first canonicalises its (possibly signalling-NaN)
+# inputs.  Non-finite inputs are outside the library's documented domain.
+EXTRA = {"kvq_vq.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *lang, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *lang, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         sys.stderr.write(r.stdout + r.stderr)
@@ -63,7 +69,8 @@ def asm(src: str = "kvq_int4.hip", out: str | None = None) -> str:
     """Device assembly of one source (for inspecting register use and ISA)."""
     out = out or os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".s")
     os.makedirs(os.path.dirname(out), exist_ok=True)
-    cmd = [HIPCC, "-x", "hip", *COMMON, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, "-x", "hip", *COMMON, *EXTRA.get(src, []), "--cuda-device-only", "-S", os.path.join(CSRC, src),
+           "-o", out]
     subprocess.run(cmd, check=True)
     return out
 

@@ -14,8 +14,9 @@
 // v_mfma_f32_32x32x16_f16: A rows are centroids [c | c] (k = 0..15), B
 // columns are sub-vectors [y_hi ; y_lo] with y_hi = fp16(y), y_lo =
 // fp16(y - y_hi), so A.B = c.(y_hi + y_lo) = c.y to fp32 accuracy without
-// rounding the key to fp16.  A second MFMA adds -(n_hi + n_lo)/2, the fp16
-// split of ||c||^2, into the same accumulator.  Each lane then holds the
+// rounding the key to fp16.  The accumulator input of those MFMAs is
+// -(n_hi + n_lo)/2, the fp16 split of ||c||^2, computed once per centroid
+// tile by a 32x32x8 MFMA and shared by every group of sub-vectors.  Each lane then holds the
 // scores of 16 centroids for one sub-vector: a max3 tree gives the tile
 // maximum, and only the best tile is tracked (strict >, so the earliest tile
 // wins ties).  After a sweep, the lanes that improved re-score the 16
@@ -26,8 +27,9 @@
 // The codebook (<= 4096 centroids at a time, 64 KB) and its norms live in
 // LDS; a block of WAVES wavefronts shares it, each wavefront rotating 16 keys
 // of one (layer, head) and sweeping the codebook for GPR groups of 32
-// sub-vectors per pass.  Contraction work per key: D/8 x K x 8 MACs; the MFMA
-// executes 4x that (hi/lo split and the norm MFMA).
+// sub-vectors per pass.  Contraction work per key: D/8 x K x 8 MACs; the MFMAs
+// execute 2x that for the hi/lo split plus one half-size norm MFMA per tile
+// and GPR groups (2.25x in all for GPR = 4).
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -38,6 +40,7 @@ namespace kvq {
 namespace {
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <int D>
@@ -52,6 +55,7 @@ struct VqCfg {
 };
 
 __device__ __forceinline__ h8_t as_h8(uint4 u) { return __builtin_bit_cast(h8_t, u); }
+__device__ __forceinline__ h4_t as_h4(uint2 u) { return __builtin_bit_cast(h4_t, u); }
 
 // Swizzled position of 16-byte sub-vector chunk s of key v in a staging row.
 template <int NS>
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
     constexpr int NS = C::NS, NJ = C::NJ, N = C::N, GPR = C::GPR, ROUNDS = C::ROUNDS, WAVES = C::WAVES;
 
     __shared__ uint4 cb_lds[kVqChunk];                 // centroid k: 8 fp16
-    __shared__ uint32_t nrm_lds[kVqChunk + 1];         // packed (n_hi, n_lo); last slot 0
+    __shared__ uint32_t nrm_lds[kVqChunk];             // packed (n_hi, n_lo)
     __shared__ uint4 stage[WAVES][2][16 * NS];         // [wave][hi/lo][key, sub-vector]
 
     const int lane = threadIdx.x & 63;
@@ -79,16 +83,16 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
     const int col = lane & 31;                         // MFMA column (sub-vector in a group)
     const int half = lane >> 5;                        // 0: rows 0-3, 8-11, ..; 1: rows 4-7, ..
 
-    if (threadIdx.x == 0) nrm_lds[kVqChunk] = 0;
-    // B2 = [-1/2, -1/2, 0 ...] in the k = 0..7 half, zero in the other
+    // Norm tile: a 32x32x8 MFMA with A2 rows [n_hi, n_lo, 0, 0] (k = 0..3,
+    // and the same words again in k = 4..7) and B2 columns [-1/2, -1/2, 0, 0]
+    // in k = 0..3, zero in k = 4..7.
     const uint32_t mhalf2 = 0xB800B800u;               // two fp16 -0.5
-    const h8_t b2 = as_h8(make_uint4(half == 0 ? mhalf2 : 0u, 0u, 0u, 0u));
+    const h4_t b2 = as_h4(make_uint2(half == 0 ? mhalf2 : 0u, 0u));
 
     const int nchunks = (a.K + kVqChunk - 1) / kVqChunk;
     const int64_t ubeg = (int64_t)blockIdx.x * a.enc_units_per_block;
     const int64_t uend = min(ubeg + a.enc_units_per_block, a.enc_n_units);
-    int cur_cb = -1, cur_lh = -1;
-    float m[N];
+    int cur_cb = -1;
 
     const _Float16* __restrict__ xg = static_cast<const _Float16*>(a.x.data);
     uint16_t* __restrict__ ig = static_cast<uint16_t*>(a.idx.data);
@@ -104,10 +108,8 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
         const int lh = l * a.H + h;
         const int cbkey = a.cb_layer_stride == 0 ? h : lh;
         const uint16_t* cbp = a.codebook + (int64_t)l * a.cb_layer_stride + (int64_t)h * a.K * 8;
-        if (lh != cur_lh) {
-            cur_lh = lh;
-            load_fwd_mult<D>(a.lambda + (int64_t)lh * D, a.signs, q, m);
-        }
+        float m[N];   // reloaded per unit so that it is not live during the sweeps
+        load_fwd_mult<D>(a.lambda + (int64_t)lh * D, a.signs, q, m);
 
         // ---- rotate this wavefront's 16 keys (4 lanes per key) ---------------
         const int t0 = c * 16 * WAVES + wid * 16;
@@ -178,7 +180,10 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
                     __syncthreads();
                     for (int k = threadIdx.x; k < kVqChunk; k += 64 * WAVES) {
                         uint4 cv = make_uint4(0, 0, 0, 0);
-                        uint32_t nw = 0x00007C00u;       // n_hi = +inf: padding never wins
+                        // padding: n_hi = 65504 (largest finite fp16) gives a score of
+                        // -32752, below any in-domain centroid; finite so that the
+                        // zero B2 half never multiplies an infinity
+                        uint32_t nw = 0x00007BFFu;
                         if (k < kc) {
                             cv = *reinterpret_cast<const uint4*>(cbp + (int64_t)(kbase + k) * 8);
                             const uint32_t w[4] = {cv.x, cv.y, cv.z, cv.w};
@@ -200,27 +205,72 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
                 }
 
                 // ---- sweep the chunk: 32 centroids per MFMA tile -------------------
+                // The norm tile -(n_hi + n_lo)/2 is one MFMA per tile, shared by all
+                // groups as their accumulator input.  Software pipeline: tile t+1's
+                // MFMAs are issued (and tile t+2's operands read from LDS) before
+                // tile t's epilogue runs, so the matrix core and the VALU overlap.
                 const int ntiles = (kc + 31) / 32;
                 int best_tile[GPR];
 #pragma unroll
                 for (int gg = 0; gg < GPR; gg++) best_tile[gg] = -1;
-                for (int tl = 0; tl < ntiles; tl++) {
-                    const h8_t aop = as_h8(cb_lds[tl * 32 + col]);
-                    const h8_t a2 = as_h8(make_uint4(nrm_lds[half == 0 ? tl * 32 + col : kVqChunk], 0u, 0u, 0u));
+                const uint4* cb_col = cb_lds + col;
+                const uint32_t* nrm_col = nrm_lds + col;
+                auto read_a = [&](int tl, h8_t& aop, h4_t& a2) {
+                    const int base = tl * 32;
+                    aop = as_h8(cb_col[base]);
+                    a2 = as_h4(make_uint2(nrm_col[base], 0u));
+                };
+                auto issue = [&](const h8_t& aop, const h4_t& a2, f32x16_t (&acc)[GPR]) {
+                    const f32x16_t zero = {};
+                    const f32x16_t nt = __builtin_amdgcn_mfma_f32_32x32x8f16(a2, b2, zero, 0, 0, 0);
+#pragma unroll
+                    for (int gg = 0; gg < GPR; gg++)
+                        acc[gg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop[gg], nt, 0, 0, 0);
+                };
+                auto epilogue = [&](const f32x16_t (&acc)[GPR], int tl) {
 #pragma unroll
                     for (int gg = 0; gg < GPR; gg++) {
-                        f32x16_t acc = {};
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop[gg], acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2, b2, acc, 0, 0, 0);
-                        float mx = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+                        float mx = fmaxf(fmaxf(acc[gg][0], acc[gg][1]), acc[gg][2]);
 #pragma unroll
-                        for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
-                        mx = fmaxf(mx, acc[15]);
+                        for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[gg][r]), acc[gg][r + 1]);
+                        mx = fmaxf(mx, acc[gg][15]);
                         if (mx > best_val[gg]) {
                             best_val[gg] = mx;
                             best_tile[gg] = tl;
                         }
                     }
+                };
+                // Interleave one tile's MFMAs with the previous tile's epilogue (one
+                // group's max tree between consecutive MFMAs; the first gap also
+                // covers the norm MFMA's latency before the dependent mains).
+                auto interleave = [&]() {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // norm MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // operand reads
+                    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+#pragma unroll
+                    for (int gg = 0; gg < GPR; gg++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+                    }
+                };
+                f32x16_t acc0[GPR], acc1[GPR];
+                h8_t a_op;
+                h4_t a_n2;
+                read_a(0, a_op, a_n2);
+                issue(a_op, a_n2, acc0);
+                read_a(min(1, ntiles - 1), a_op, a_n2);
+                for (int tl = 0; tl < ntiles; tl += 2) {
+                    // tile tl+1 may not exist: its MFMAs then run on a repeated tile
+                    // and their result is never read
+                    issue(a_op, a_n2, acc1);
+                    read_a(min(tl + 2, ntiles - 1), a_op, a_n2);
+                    epilogue(acc0, tl);
+                    interleave();
+                    if (tl + 1 >= ntiles) break;
+                    issue(a_op, a_n2, acc0);
+                    read_a(min(tl + 3, ntiles - 1), a_op, a_n2);
+                    epilogue(acc1, tl + 1);
+                    interleave();
                 }
 
                 // ---- lanes whose best moved into this chunk find its position -------
