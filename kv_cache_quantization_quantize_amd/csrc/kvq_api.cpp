@@ -200,6 +200,8 @@ kvq_status vq_common(const kvq_shape& shape, const kvq_view& x, const float* lam
     a.codebook = static_cast<const uint16_t*>(codebook);
     a.cb_layer_stride = cb_layer_stride;
     set_items(shape, a.token_major, a.h_shift, a.items_per_group, a.tok_per_item, a.items_per_wave, a.n_items);
+    a.dec_waves_per_group = (a.items_per_group + a.items_per_wave - 1) / a.items_per_wave;
+    a.dec_n_waves = (a.n_items / a.items_per_group) * a.dec_waves_per_group;
     const int64_t tpu = 16 * kvq::vq_encode_waves((int)D);
     a.enc_units_per_lh = (int32_t)((shape.tokens + tpu - 1) / tpu);
     a.enc_n_units = shape.layers * shape.heads * (int64_t)a.enc_units_per_lh;
@@ -256,6 +258,17 @@ kvq_status kvq_vq_decode(kvq_shape shape, kvq_view idx_u16, const void* codebook
     KVQ_TRY(vq_common(shape, out_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
                       idx_u16, a, true));
     if (empty(shape)) return KVQ_OK;
+    a.dec_items_per_block = 0;
+    if (n_centroids <= kvq::kVqChunk) {
+        // codebook in LDS: head-major 16-token items of one (layer, head);
+        // one block per CU, each a contiguous range of items
+        a.token_major = 0;
+        a.tok_per_item = kvq::kTokensPerTile;
+        a.items_per_group = (int32_t)((shape.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
+        a.n_items = shape.layers * shape.heads * (int64_t)a.items_per_group;
+        const int64_t blocks = device_cus();
+        a.dec_items_per_block = (a.n_items + blocks - 1) / blocks;
+    }
     return hip_status(kvq::launch_vq_decode(a, static_cast<hipStream_t>(stream)), "kvq_vq_decode launch");
 }
 

@@ -49,6 +49,13 @@ struct VqArgs {
     // decode work items: as Int4Args
     int32_t token_major, h_shift, items_per_group, tok_per_item, items_per_wave;
     int64_t n_items;
+    // decode: each wavefront takes up to items_per_wave items of one group
+    // ((layer) or (layer, head)), so it loads one set of multipliers
+    int32_t dec_waves_per_group;
+    int64_t dec_n_waves;
+    // decode with the codebook in LDS (K <= kVqChunk): head-major 16-token
+    // items, each block a contiguous range of this many; 0 selects the other path
+    int64_t dec_items_per_block;
     // encode units: (layer, head, 16*waves-token chunk), ordered head-major
     // when one codebook serves all layers so that a block rarely re-stages it
     int32_t enc_units_per_lh;

@@ -54,8 +54,16 @@ struct VqCfg {
     static constexpr int WAVES = (D == 256) ? 4 : 8;  // wavefronts per block (LDS budget)
 };
 
+// Wavefronts per block of the LDS-codebook decoder (one block per CU:
+// 64 KB of codebook plus 16 vectors of output staging per wavefront).
+template <int D>
+struct VqDecLds {
+    static constexpr int WAVES = (D == 256) ? 4 : 16;
+};
+
 __device__ __forceinline__ h8_t as_h8(uint4 u) { return __builtin_bit_cast(h8_t, u); }
 __device__ __forceinline__ h4_t as_h4(uint2 u) { return __builtin_bit_cast(h4_t, u); }
+
 
 // Swizzled position of 16-byte sub-vector chunk s of key v in a staging row.
 template <int NS>
@@ -335,22 +343,31 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
 template <int D, bool TM>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void vq_decode_kernel(VqArgs a)
 {
-    constexpr int NJ = D / 32;
+    constexpr int NJ = D / 32;          // 16-byte chunks (= sub-vectors) per lane
     constexpr int N = NJ * 8;
-    constexpr int CV = D / 8;
-    constexpr int VPK = 1024 / (2 * D);
+    constexpr int CV = D / 8;           // 16-byte chunks per vector
+    constexpr int VPK = 1024 / (2 * D); // vectors per 1 KB store row
+    constexpr int NIW = D / 64;         // 16-byte words of indices per key
 
     const int lane = threadIdx.x & 63;
     const int q = lane & 3;
     const int slot = lane >> 2;
     const int wave = uniform((int)(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)));
-    const int begin = wave * a.items_per_wave;
-    const int end = (int)min((int64_t)begin + a.items_per_wave, a.n_items);
-    if (begin >= end) return;
+    if (wave >= a.dec_n_waves) return;
+    // the wave's items [begin, end) all lie in group grp
+    const int grp = uniform(wave / a.dec_waves_per_group);
+    const int begin = (wave - grp * a.dec_waves_per_group) * a.items_per_wave;
+    const int end = min(begin + a.items_per_wave, a.items_per_group);
+    int l, hbase;
+    if constexpr (TM) { l = grp; hbase = 0; }
+    else { l = uniform(grp / a.H); hbase = grp - l * a.H; }
 
     const float c1 = (q & 1) ? -1.0f : 1.0f;
     const float c2 = (q & 2) ? -1.0f : 1.0f;
     const float lane_sign = (__builtin_popcount(q) & 1) ? -1.0f : 1.0f;
+    const bool hi_pair = (q & 2) != 0;
+    const uint32_t half_shift = (q & 1) * 16;
+    const uint32_t kmax = (uint32_t)(a.K - 1);
 
     _Float16* __restrict__ og = static_cast<_Float16*>(a.x.data);
     const uint16_t* __restrict__ ig = static_cast<const uint16_t*>(a.idx.data);
@@ -364,69 +381,235 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void vq_decode_kernel(VqArgs a
     uint4* my_out = lds_out[threadIdx.x >> 6];
     const int row_c = lane % CV;
 
-    float m[N];
-    int cur_key = -1;
+    // The quad's key index block (D/8 u16); tokens past the end read the last
+    // token's block so that every load is in bounds and unconditional.
+    typedef uint4 uint4_a4 __attribute__((aligned(4)));
+    const uint16_t* ig_lh = ig + (int64_t)l * a.idx.sl + (int64_t)(hbase + lhead) * a.idx.sh;
+    auto load_idx = [&](int item, uint4 (&W)[NIW]) {
+        const int t = min(item * a.tok_per_item + ltok, a.T - 1);
+        const uint16_t* ip = ig_lh + (int64_t)t * a.idx.st;
+#pragma unroll
+        for (int i = 0; i < NIW; i++) W[i] = *reinterpret_cast<const uint4_a4*>(ip + 8 * i);
+    };
+    // Lane q holds sub-vectors 4j + q; gather their centroids (clamped index).
+    const uint16_t* cbp = a.codebook + (int64_t)l * a.cb_layer_stride + (int64_t)(hbase + lhead) * a.K * 8;
+    auto gather = [&](const uint4 (&W)[NIW], uint4 (&cv)[NJ]) {
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const uint4 wd = W[j / 2];
+            const uint32_t d = (j & 1) ? (hi_pair ? wd.w : wd.z) : (hi_pair ? wd.y : wd.x);
+            const uint32_t ix = min(__builtin_amdgcn_ubfe(d, half_shift, 16), kmax);
+            cv[j] = *reinterpret_cast<const uint4*>(cbp + (int64_t)ix * 8);
+        }
+    };
 
-    for (int item = begin; item < end; ++item) {
-        const int grp = uniform(item / a.items_per_group);
-        const int kk = item - grp * a.items_per_group;
-        const int t0 = uniform(kk * a.tok_per_item);
-        int l, hbase;
-        if constexpr (TM) { l = grp; hbase = 0; }
-        else { l = uniform(grp / a.H); hbase = grp - l * a.H; }
-        const int h = hbase + lhead;
-        const bool valid = t0 + ltok < a.T;
-        const int key = TM ? l : grp;
-        if (key != cur_key) {
-            cur_key = key;
-            load_inv_mult<D>(a.lambda + ((int64_t)l * a.H + h) * D, a.signs, q, lane_sign, m);
-        }
-        // indices of sub-vectors 4j + q, then the centroids (8 fp16 = chunk j)
-        const uint16_t* ip = ig + (int64_t)l * a.idx.sl + (int64_t)h * a.idx.sh + (int64_t)(t0 + ltok) * a.idx.st + q;
-        const uint16_t* cbp = a.codebook + (int64_t)l * a.cb_layer_stride + (int64_t)h * a.K * 8;
-        uint4 cv[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; j++) cv[j] = make_uint4(0, 0, 0, 0);
-        if (valid) {
-            uint32_t ix[NJ];
-#pragma unroll
-            for (int j = 0; j < NJ; j++) ix[j] = min((uint32_t)ip[4 * j], (uint32_t)(a.K - 1));
-#pragma unroll
-            for (int j = 0; j < NJ; j++) cv[j] = *reinterpret_cast<const uint4*>(cbp + (int64_t)ix[j] * 8);
-        }
+    float m[N];
+    load_inv_mult<D>(a.lambda + ((int64_t)l * a.H + hbase + lhead) * D, a.signs, q, lane_sign, m);
+    _Float16* og_l = og + (int64_t)l * a.x.sl + (int64_t)hbase * a.x.sh;
+    auto compute_store = [&](int item, const uint4 (&cv)[NJ]) {
+        const int t0 = item * a.tok_per_item;
         // first butterfly stage straight from the fp16 centroid values
         float v[N];
 #pragma unroll
         for (int j = 0; j < NJ; j++) {
-            const uint32_t w[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
+            const uint32_t wd[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
 #pragma unroll
             for (int k = 0; k < 4; k++) {
-                const float x0 = lo_half(w[k]), x1 = hi_half(w[k]);
+                const float x0 = lo_half(wd[k]), x1 = hi_half(wd[k]);
                 v[j * 8 + 2 * k] = x0 + x1;
                 v[j * 8 + 2 * k + 1] = x0 - x1;
             }
         }
         fwht_rest(v, c1, c2);
-        uint4 o[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; j++) {
-            o[j].x = pack_half2(v[j * 8 + 0] * m[j * 8 + 0], v[j * 8 + 1] * m[j * 8 + 1]);
-            o[j].y = pack_half2(v[j * 8 + 2] * m[j * 8 + 2], v[j * 8 + 3] * m[j * 8 + 3]);
-            o[j].z = pack_half2(v[j * 8 + 4] * m[j * 8 + 4], v[j * 8 + 5] * m[j * 8 + 5]);
-            o[j].w = pack_half2(v[j * 8 + 6] * m[j * 8 + 6], v[j * 8 + 7] * m[j * 8 + 7]);
-        }
         // stage through LDS so each store instruction writes 1 KB of consecutive vectors
 #pragma unroll
-        for (int j = 0; j < NJ; j++) my_out[slot * CV + ((4 * j + q) ^ ((4 * slot) % CV))] = o[j];
-        _Float16* ob = og + (int64_t)l * a.x.sl + (int64_t)hbase * a.x.sh + (int64_t)t0 * a.x.st;
+        for (int j = 0; j < NJ; j++) {
+            uint4 o;
+            o.x = pack_half2(v[j * 8 + 0] * m[j * 8 + 0], v[j * 8 + 1] * m[j * 8 + 1]);
+            o.y = pack_half2(v[j * 8 + 2] * m[j * 8 + 2], v[j * 8 + 3] * m[j * 8 + 3]);
+            o.z = pack_half2(v[j * 8 + 4] * m[j * 8 + 4], v[j * 8 + 5] * m[j * 8 + 5]);
+            o.w = pack_half2(v[j * 8 + 6] * m[j * 8 + 6], v[j * 8 + 7] * m[j * 8 + 7]);
+            my_out[slot * CV + ((4 * j + q) ^ ((4 * slot) % CV))] = o;
+        }
+        // A vector past the last token was decoded from the last token's
+        // indices (the loads are clamped), so its row is stored over that
+        // token's row with identical bytes: every store is unconditional.
+        _Float16* ob = og_l + (int64_t)t0 * a.x.st;
+        const int last = a.T - 1 - t0;
 #pragma unroll
         for (int k = 0; k < NJ; k++) {
             const int vv = k * VPK + lane / CV;
             const uint4 rowv = my_out[vv * CV + (row_c ^ ((4 * vv) % CV))];
-            const int vt = TM ? (vv >> a.h_shift) : vv;
+            const int vt = min(TM ? (vv >> a.h_shift) : vv, last);
             const int vh = TM ? (vv & (a.H - 1)) : 0;
             const int64_t off = (int64_t)vt * a.x.st + (int64_t)vh * a.x.sh + row_c * 8;
-            if (t0 + vt < a.T) *reinterpret_cast<uint4*>(ob + off) = rowv;
+            *reinterpret_cast<uint4*>(ob + off) = rowv;
+        }
+    };
+
+    // Pipeline: while item i is computed, the centroids of item i + 1 and
+    // the indices of item i + 2 are in flight.  All loads are unconditional
+    // (items past the wave's range are clamped to its last item) so that the
+    // wait before each use is a fixed count; the two centroid buffers
+    // alternate by unrolling, never by copying registers that may still be
+    // waiting on a load.
+    uint4 W[NIW];
+    uint4 cvA[NJ], cvB[NJ];
+    load_idx(begin, W);
+    gather(W, cvA);
+    load_idx(min(begin + 1, end - 1), W);
+    auto step = [&](int item, const uint4 (&cur)[NJ], uint4 (&nxt)[NJ]) {
+        gather(W, nxt);
+        load_idx(min(item + 2, end - 1), W);
+        __builtin_amdgcn_sched_barrier(0);   // issue the loads before the compute
+        compute_store(item, cur);
+    };
+    // The first step is peeled so that the loop is entered with the same
+    // loads and stores in flight as on its back edge.
+    step(begin, cvA, cvB);
+    for (int item = begin + 1; item < end;) {
+        step(item, cvB, cvA);
+        if (++item >= end) break;
+        step(item, cvA, cvB);
+        ++item;
+    }
+}
+
+// Decode with the head's codebook staged in LDS (n_centroids <= kVqChunk).
+// Work items are head-major runs of 16 tokens of one (layer, head); a block
+// takes a contiguous range of them (one block per CU, so a range spans one
+// or two (layer, head) segments), stages the codebook once per segment, and
+// its wavefronts split each segment into contiguous runs.  The centroid
+// gathers are then LDS reads rather than 16-byte pieces of L2 lines.  Each
+// wavefront keeps the indices of its next three items in flight.
+template <int D>
+__global__ __launch_bounds__(64 * VqDecLds<D>::WAVES) void vq_decode_lds_kernel(VqArgs a)
+{
+    constexpr int WAVES = VqDecLds<D>::WAVES;
+    constexpr int NJ = D / 32;
+    constexpr int N = NJ * 8;
+    constexpr int CV = D / 8;
+    constexpr int VPK = 1024 / (2 * D);
+    constexpr int NIW = D / 64;
+
+    __shared__ uint4 cb_lds[kVqChunk];
+    __shared__ uint4 lds_out[WAVES][16 * CV];
+
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 3;
+    const int slot = lane >> 2;
+    const int wid = uniform(threadIdx.x >> 6);
+
+    const float c1 = (q & 1) ? -1.0f : 1.0f;
+    const float c2 = (q & 2) ? -1.0f : 1.0f;
+    const float lane_sign = (__builtin_popcount(q) & 1) ? -1.0f : 1.0f;
+    const bool hi_pair = (q & 2) != 0;
+    const uint32_t half_shift = (q & 1) * 16;
+    const uint32_t kmax = (uint32_t)(a.K - 1);
+
+    _Float16* __restrict__ og = static_cast<_Float16*>(a.x.data);
+    const uint16_t* __restrict__ ig = static_cast<const uint16_t*>(a.idx.data);
+    uint4* my_out = lds_out[wid];
+    const int row_c = lane % CV;
+    typedef uint4 uint4_a4 __attribute__((aligned(4)));
+
+    const int64_t g_end = min((int64_t)(blockIdx.x + 1) * a.dec_items_per_block, a.n_items);
+    for (int64_t g = (int64_t)blockIdx.x * a.dec_items_per_block; g < g_end;) {
+        const int lh = uniform((int)(g / a.items_per_group));
+        const int l = uniform(lh / a.H);
+        const int h = lh - l * a.H;
+        const int64_t seg0 = (int64_t)lh * a.items_per_group;
+        const int i0 = (int)(g - seg0);
+        const int i1 = (int)(min(g_end, seg0 + a.items_per_group) - seg0);
+        g = seg0 + i1;
+
+        // stage the codebook of (l, h): K centroids of 16 bytes
+        __syncthreads();   // the previous segment's gathers are done
+        const uint4* cbg = reinterpret_cast<const uint4*>(a.codebook + (int64_t)l * a.cb_layer_stride +
+                                                          (int64_t)h * a.K * 8);
+        for (int k = threadIdx.x; k < a.K; k += 64 * WAVES) cb_lds[k] = cbg[k];
+        __syncthreads();
+
+        const int per_wave = (i1 - i0 + WAVES - 1) / WAVES;
+        const int begin = i0 + wid * per_wave;
+        const int end = min(begin + per_wave, i1);
+        if (begin >= end) continue;
+
+        const uint16_t* ig_lh = ig + (int64_t)l * a.idx.sl + (int64_t)h * a.idx.sh;
+        // the quad's index block; tokens past the end read the last token's
+        auto load_idx = [&](int item, uint4 (&W)[NIW]) {
+            const int t = min(item * kTokensPerTile + slot, a.T - 1);
+            const uint16_t* ip = ig_lh + (int64_t)t * a.idx.st;
+#pragma unroll
+            for (int i = 0; i < NIW; i++) W[i] = *reinterpret_cast<const uint4_a4*>(ip + 8 * i);
+        };
+
+        float m[N];
+        load_inv_mult<D>(a.lambda + ((int64_t)l * a.H + h) * D, a.signs, q, lane_sign, m);
+        _Float16* og_lh = og + (int64_t)l * a.x.sl + (int64_t)h * a.x.sh;
+
+        // One item: centroids from LDS, then the indices of item + 3 into the
+        // same buffer, then the inverse transform and the stores.
+        auto step = [&](int item, uint4 (&W)[NIW]) {
+            item = min(item, end - 1);
+            // lane q holds sub-vectors 4j + q
+            uint4 cv[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; j++) {
+                const uint4 wd = W[j / 2];
+                const uint32_t d = (j & 1) ? (hi_pair ? wd.w : wd.z) : (hi_pair ? wd.y : wd.x);
+                cv[j] = cb_lds[min(__builtin_amdgcn_ubfe(d, half_shift, 16), kmax)];
+            }
+            load_idx(min(item + 3, end - 1), W);
+            __builtin_amdgcn_sched_barrier(0);   // issue the indices before the compute
+            float v[N];
+#pragma unroll
+            for (int j = 0; j < NJ; j++) {
+                const uint32_t wd[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const float x0 = lo_half(wd[k]), x1 = hi_half(wd[k]);
+                    v[j * 8 + 2 * k] = x0 + x1;
+                    v[j * 8 + 2 * k + 1] = x0 - x1;
+                }
+            }
+            fwht_rest(v, c1, c2);
+#pragma unroll
+            for (int j = 0; j < NJ; j++) {
+                uint4 o;
+                o.x = pack_half2(v[j * 8 + 0] * m[j * 8 + 0], v[j * 8 + 1] * m[j * 8 + 1]);
+                o.y = pack_half2(v[j * 8 + 2] * m[j * 8 + 2], v[j * 8 + 3] * m[j * 8 + 3]);
+                o.z = pack_half2(v[j * 8 + 4] * m[j * 8 + 4], v[j * 8 + 5] * m[j * 8 + 5]);
+                o.w = pack_half2(v[j * 8 + 6] * m[j * 8 + 6], v[j * 8 + 7] * m[j * 8 + 7]);
+                my_out[slot * CV + ((4 * j + q) ^ ((4 * slot) % CV))] = o;
+            }
+            // rows of tokens past the end repeat the last token's row (same bytes)
+            const int t0 = item * kTokensPerTile;
+            _Float16* ob = og_lh + (int64_t)t0 * a.x.st;
+            const int last = a.T - 1 - t0;
+#pragma unroll
+            for (int k = 0; k < NJ; k++) {
+                const int vv = k * VPK + lane / CV;
+                const uint4 rowv = my_out[vv * CV + (row_c ^ ((4 * vv) % CV))];
+                *reinterpret_cast<uint4*>(ob + (int64_t)min(vv, last) * a.x.st + row_c * 8) = rowv;
+            }
+        };
+
+        // Three index buffers in rotation.  Steps past the run repeat its
+        // last item (same bytes to the same places), so every step is
+        // unconditional and the first three, peeled, leave the same loads
+        // and stores in flight as the loop's back edge.
+        uint4 WA[NIW], WB[NIW], WC[NIW];
+        load_idx(begin, WA);
+        load_idx(min(begin + 1, end - 1), WB);
+        load_idx(min(begin + 2, end - 1), WC);
+        step(begin, WA);
+        step(begin + 1, WB);
+        step(begin + 2, WC);
+        for (int item = begin + 3; item < end; item += 3) {
+            step(item, WA);
+            step(item + 1, WB);
+            step(item + 2, WC);
         }
     }
 }
@@ -447,8 +630,12 @@ hipError_t launch_enc(const VqArgs& a, hipStream_t s)
 template <int D>
 hipError_t launch_dec(const VqArgs& a, hipStream_t s)
 {
-    const int64_t waves = (a.n_items + a.items_per_wave - 1) / a.items_per_wave;
-    const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+    if (a.dec_items_per_block > 0) {
+        const dim3 grid((unsigned)((a.n_items + a.dec_items_per_block - 1) / a.dec_items_per_block));
+        hipLaunchKernelGGL((vq_decode_lds_kernel<D>), grid, dim3(64 * VqDecLds<D>::WAVES), 0, s, a);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((a.dec_n_waves + kWavesPerBlock - 1) / kWavesPerBlock));
     if (a.token_major) hipLaunchKernelGGL((vq_decode_kernel<D, true>), grid, dim3(64 * kWavesPerBlock), 0, s, a);
     else hipLaunchKernelGGL((vq_decode_kernel<D, false>), grid, dim3(64 * kWavesPerBlock), 0, s, a);
     return hipGetLastError();

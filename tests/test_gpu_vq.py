@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import kv_cache_quantization_quantize_amd as kvq
+import oracle
 import synth
 from tests import parity
 from tests.gpu_util import all_idx, bits, device, lam_rows, log, rows
@@ -121,6 +122,31 @@ def test_decode_clamps_out_of_range_indices():
     out = kvq.vq_decode(idx2, cb, lam, s, 8)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("K,L,T,H,D", [
+    (4096, 3, 1000, 3, 128),    # codebook staged in LDS; block ranges span (layer, head) segments
+    (257, 2, 77, 8, 64),
+    (4096, 1, 45, 1, 256),
+    (5000, 2, 333, 2, 128),     # codebook above one LDS chunk: gathers from global memory, token-major
+    (5000, 2, 50, 3, 256),      # ... head-major
+])
+def test_decode_random_indices(K, L, T, H, D):
+    """Decode of indices drawn uniformly (not produced by the encoder), so
+    every centroid position and both decode paths are exercised; each GPU
+    output is compared with the oracle's decode of the same indices."""
+    x, lam, s, cb = rand_case(L, T, H, D, K, seed=K + T)
+    g = torch.Generator(device="cpu").manual_seed(K * 7 + T)
+    idx = torch.randint(0, K, (L, T, H, D // 8), generator=g, dtype=torch.int32).to(torch.int16).to(x.device)
+    out = kvq.vq_decode(idx, cb, lam, s, 8)
+    torch.cuda.synchronize()
+    sel = all_idx(L, T, H)
+    cbb = bits(cb).reshape(H, K, 8)
+    x64, _ = oracle.vq_decode(rows(idx, sel), cbb, sel[:, 2].astype(np.int32), lam_rows(lam, sel),
+                              s.cpu().numpy(), 8)
+    rep = parity.check_dequant(rows(out, sel), x64, lam_rows(lam, sel))
+    log("decode K=%d [%d,%d,%d,%d]" % (K, L, T, H, D), {k: v for k, v in rep.items() if k != "bad_mask"})
+    assert rep["bad"] == 0
 
 
 def test_vecinfer_full_size_sampled():
