@@ -65,6 +65,8 @@ def bind(path: str):
         "kvqo_vq_encode_rows": (I32, [I64, I32, I32, I32, P, P, P, P, P, P, P]),
         "kvqo_vq_distances": (I32, [I64, I32, I32, I32, P, P, P, P, P]),
         "kvqo_vq_decode_rows": (I32, [I64, I32, I32, I32, P, P, P, P, P, P, P]),
+        "kvqo_attend_decode": (I32, [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P,
+                                     ctypes.c_double, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -241,3 +243,33 @@ def vq_decode(idx, codebooks_bits, book, lam, signs, sub):
     if rc:
         raise ValueError("oracle vq_decode rejected (index out of range?)")
     return x64, x16
+
+
+def attend_decode(q_bits, k_codes, k_scales, v_codes, v_scales, lam_k, lam_v, signs, G, scale,
+                  lengths=None):
+    """Decode attention in fp64 over an int4 cache.  q_bits [L, H*R, D]
+    binary16 bits; k/v codes [L, T, H, D/2] u8; k/v scales [L, T, H, D/G]
+    binary16 bits; lam_k/lam_v [L, H, D]; lengths [L] or None (all T).
+    Returns out64 [L, H*R, D]."""
+    kc, pkc = _c(k_codes, np.uint8)
+    L, T, H, half = kc.shape
+    D = 2 * half
+    qb, pq = _c(q_bits, np.uint16)
+    R = qb.shape[1] // H
+    if qb.shape != (L, H * R, D):
+        raise ValueError("q shape %s does not match [L, H*R, D]" % (qb.shape,))
+    ks, pks = _c(k_scales, np.uint16)
+    vc, pvc = _c(v_codes, np.uint8)
+    vs, pvs = _c(v_scales, np.uint16)
+    lk, plk = _c(lam_k, np.float32)
+    lv, plv = _c(lam_v, np.float32)
+    s, ps = _c(signs, np.int8)
+    pl = None
+    if lengths is not None:
+        ln, pl = _c(lengths, np.int32)
+    out, po = _out((L, H * R, D), np.float64)
+    rc = _load().kvqo_attend_decode(L, T, H, R, D, int(G), pq, pkc, pks, pvc, pvs, plk, plv, ps, pl,
+                                    float(scale), po)
+    if rc:
+        raise ValueError("oracle attend_decode rejected its arguments (%d)" % rc)
+    return out

@@ -28,6 +28,10 @@
  *             Samenvatting" -> "Methodologie" sections 1 (sign-randomized
  *             transform), 2 (fused kernel step list), 3 (per-channel plus
  *             per-group scaling).
+ *  [SCALAR-ATTEND] VeloxQuant-MLX 0.52.0 package description, section
+ *             "Fused group-affine (KIVI-style) attention": single-query decode
+ *             attention straight from group-quantized codes, online softmax
+ *             accumulated in fp32, no dequantized cache in memory.
  *
  * Readings of points the pages leave open (each one is listed, with its
  * reasoning, in the design notes of the repository):
@@ -391,5 +395,67 @@ int kvqo_vq_decode_rows(int64_t n, int D, int sub, int K, const uint16_t* idx,
                 xhat16[r * D + j] = kvqo_f64_to_f16(xhat64[r * D + j]);
     }
     free(yh);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over the int4 cache [SCALAR-ATTEND]                       */
+/* ------------------------------------------------------------------------ */
+
+/* One decode step of softmax attention for R query heads per KV head (query
+   head j reads KV head j / R), over the first len[l] tokens of each outer
+   index l (len == NULL: all T tokens):
+     khat_t = dequantize(K codes_t, K scales_t)   (exact fp64, never rounded)
+     vhat_t = dequantize(V codes_t, V scales_t)
+     a_t = scale * (q_j . khat_t),  p = softmax over t of a,  out_j = sum p_t vhat_t
+   The softmax subtracts the largest a_t before exponentiating.  Layouts,
+   all contiguous: q [L, H*R, D] binary16; codes [L, T, H, D/2]; scales
+   [L, T, H, D/G] binary16; lamK, lamV [L, H, D]; out64 [L, H*R, D].  An
+   outer index with len 0 gets zeros. */
+int kvqo_attend_decode(int L, int T, int H, int R, int D, int G, const uint16_t* q,
+                       const uint8_t* kc, const uint16_t* ks, const uint8_t* vc,
+                       const uint16_t* vs, const float* lamK, const float* lamV,
+                       const int8_t* s, const int32_t* len, double scale, double* out64)
+{
+    if (!is_pow2(D) || G <= 0 || D % G || (G & 1) || L < 0 || T < 0 || H <= 0 || R <= 0) return -1;
+    int ng = D / G;
+    double* kh = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * D);
+    double* vh = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * D);
+    double* a = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    for (int l = 0; l < L; l++) {
+        int n = len ? len[l] : T;
+        if (n < 0 || n > T) { free(kh); free(vh); free(a); return -2; }
+        for (int h = 0; h < H; h++) {
+            const float* lk = lamK + ((int64_t)l * H + h) * D;
+            const float* lv = lamV + ((int64_t)l * H + h) * D;
+            for (int t = 0; t < n; t++) {
+                int64_t row = ((int64_t)l * T + t) * H + h;
+                kvqo_dequantize_rows(1, D, G, kc + row * (D / 2), ks + row * ng, lk, s, kh + (int64_t)t * D, NULL);
+                kvqo_dequantize_rows(1, D, G, vc + row * (D / 2), vs + row * ng, lv, s, vh + (int64_t)t * D, NULL);
+            }
+            for (int r = 0; r < R; r++) {
+                int j = h * R + r;
+                const uint16_t* qj = q + ((int64_t)l * H * R + j) * D;
+                double* o = out64 + ((int64_t)l * H * R + j) * D;
+                for (int c = 0; c < D; c++) o[c] = 0.0;
+                if (n == 0) continue;
+                double amax = -INFINITY;
+                for (int t = 0; t < n; t++) {
+                    double dot = 0.0;
+                    for (int c = 0; c < D; c++) dot += kvqo_f16_to_f64(qj[c]) * kh[(int64_t)t * D + c];
+                    a[t] = scale * dot;
+                    if (a[t] > amax) amax = a[t];
+                }
+                double z = 0.0;
+                for (int t = 0; t < n; t++) {
+                    double w = exp(a[t] - amax);
+                    z += w;
+                    for (int c = 0; c < D; c++) o[c] += w * vh[(int64_t)t * D + c];
+                }
+                for (int c = 0; c < D; c++) o[c] /= z;
+            }
+        }
+    }
+    free(kh); free(vh); free(a);
     return 0;
 }

@@ -419,3 +419,88 @@ def test_vq_decode_closed_form_and_roundtrip():
     y = oracle.rotate(x16, lam, s)
     idx2 = oracle.vq_encode(x16, lam, s, cb, np.zeros(1, np.int32), sub)[0]
     assert np.array_equal(idx2, idx)
+
+
+# ------------------------------------------------------- decode attention
+def attn_case(L, T, H, R, D, G, seed, qscale=1.0):
+    """Random int4 K/V caches produced by the oracle's own (pinned) quantizer,
+    plus queries; returns everything attend_decode takes and the exact fp64
+    dequantized K/V ([L, T, H, D]) for the library comparisons."""
+    rng = np.random.default_rng(seed)
+    s = (rng.integers(0, 2, D) * 2 - 1).astype(np.int8)
+    out = {"s": s}
+    for name in "kv":
+        x = f16bits(rng.standard_normal((L, T, H, D)) * np.exp(0.5 * rng.standard_normal((L, 1, H, D))))
+        lam = np.exp(0.3 * rng.standard_normal((L, H, D))).astype(np.float32)
+        lam_rows = np.broadcast_to(lam[:, None], (L, T, H, D)).reshape(-1, D)
+        codes, scales, _, _ = oracle.quantize(x.reshape(-1, D), lam_rows, s, G)
+        x64, _ = oracle.dequantize(codes, scales, lam_rows, s, G)
+        out[name] = (codes.reshape(L, T, H, D // 2), scales.reshape(L, T, H, D // G), lam,
+                     x64.reshape(L, T, H, D))
+    out["q"] = f16bits(rng.standard_normal((L, H * R, D)) * qscale)
+    return out
+
+
+def attend(c, G, scale, lengths=None):
+    kc, ks, lk, _ = c["k"]
+    vc, vs, lv, _ = c["v"]
+    return oracle.attend_decode(c["q"], kc, ks, vc, vs, lk, lv, c["s"], G, scale, lengths)
+
+
+def test_attend_single_token_returns_its_value():
+    # softmax over one token is exactly 1, so the output is that token's vhat
+    c = attn_case(2, 5, 3, 2, 64, 16, seed=1)
+    out = attend(c, 16, 0.125, lengths=np.array([1, 1], np.int32))
+    vhat = c["v"][3]
+    for l in range(2):
+        for j in range(6):
+            assert np.array_equal(out[l, j], vhat[l, 0, j // 2])
+
+
+def test_attend_zero_query_is_mean_of_values():
+    c = attn_case(1, 37, 2, 3, 128, 32, seed=2)
+    c["q"][:] = 0
+    out = attend(c, 32, 0.1)
+    want = c["v"][3].mean(axis=1)                       # [L, H, D]
+    for j in range(6):
+        assert np.allclose(out[0, j], want[0, j // 3], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("R", [1, 2, 4])
+def test_attend_matches_torch_sdpa(R):
+    # the attention step against torch's scaled_dot_product_attention in
+    # float64 on the (separately pinned) dequantized cache; GQA maps query
+    # head j to KV head j // R; ragged lengths attend to a prefix
+    import torch
+    L, T, H, D, G = 3, 50, 3, 128, 32
+    c = attn_case(L, T, H, R, D, G, seed=10 + R)
+    lengths = np.array([50, 17, 1], np.int32)
+    scale = 0.0883
+    out = attend(c, G, scale, lengths)
+    kh, vh = torch.from_numpy(c["k"][3]), torch.from_numpy(c["v"][3])
+    q = torch.from_numpy(bits_to_f64(c["q"]))
+    for l in range(L):
+        n = int(lengths[l])
+        k = kh[l, :n].permute(1, 0, 2).repeat_interleave(R, dim=0)     # [H*R, n, D]
+        v = vh[l, :n].permute(1, 0, 2).repeat_interleave(R, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q[l][:, None, :], k, v, scale=scale)[:, 0]
+        assert np.allclose(out[l], ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attend_large_scores_stay_finite():
+    # scores in the thousands: exp without the max shift would overflow
+    import torch
+    c = attn_case(1, 20, 1, 1, 64, 16, seed=4, qscale=30.0)
+    out = attend(c, 16, 1.0)
+    assert np.isfinite(out).all()
+    k = torch.from_numpy(c["k"][3][0, :, 0])[None]
+    v = torch.from_numpy(c["v"][3][0, :, 0])[None]
+    q = torch.from_numpy(bits_to_f64(c["q"][0]))[:, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=1.0)[:, 0]
+    assert np.allclose(out[0], ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attend_empty_context_gives_zeros():
+    c = attn_case(2, 4, 1, 2, 64, 32, seed=5)
+    out = attend(c, 32, 0.125, lengths=np.array([0, 4], np.int32))
+    assert (out[0] == 0).all() and np.abs(out[1]).sum() > 0

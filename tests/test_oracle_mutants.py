@@ -44,6 +44,12 @@ MUTANTS = {
     "f16_truncates": ("double n = nearbyint((2.0 * m - 1.0) * 1024.0);",
                       "double n = floor((2.0 * m - 1.0) * 1024.0);"),
     "f16_subnormal_truncates": ("double n = nearbyint(ldexp(a, 24));", "double n = floor(ldexp(a, 24));"),
+    "attend_no_max_shift": ("double w = exp(a[t] - amax);", "double w = exp(a[t]);"),
+    "attend_scale_dropped": ("a[t] = scale * dot;", "a[t] = dot;"),
+    "attend_values_from_keys": ("o[c] += w * vh[(int64_t)t * D + c];", "o[c] += w * kh[(int64_t)t * D + c];"),
+    "attend_query_head_interleaved": ("int j = h * R + r;", "int j = r * H + h;"),
+    "attend_one_token_short": ("for (int t = 0; t < n; t++) {\n                    double w",
+                               "for (int t = 0; t + 1 < n; t++) {\n                    double w"),
 }
 
 # every pin of test_oracle.py that takes no fixture other than golden_dir
@@ -68,6 +74,11 @@ BATTERY = [
     ("test_vq_encode_bruteforce", {"sub": 4, "K": 16}),
     ("test_vq_duplicate_centroids_lowest_index_and_exact_hits", {}),
     ("test_vq_decode_closed_form_and_roundtrip", {}),
+    ("test_attend_single_token_returns_its_value", {}),
+    ("test_attend_zero_query_is_mean_of_values", {}),
+    ("test_attend_matches_torch_sdpa", {"R": 4}),
+    ("test_attend_large_scores_stay_finite", {}),
+    ("test_attend_empty_context_gives_zeros", {}),
 ]
 
 
