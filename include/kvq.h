@@ -153,6 +153,53 @@ kvq_status kvq_vq_decode(kvq_shape shape, kvq_view idx_u16, const void* codebook
                          int32_t sub_dim, const float* lambda, const int8_t* signs,
                          kvq_view out_f16, void* stream);
 
+/* Decode attention straight from the int4 cache (VeloxQuant-MLX package
+ * description, "Fused group-affine (KIVI-style) attention": one query per
+ * head, online softmax accumulated in fp32, codes turned into values in
+ * registers, no dequantized cache written).  For every outer index l, KV
+ * head h and query head j = h * q_per_kv + r (0 <= r < q_per_kv), over the
+ * first n_l tokens (n_l = lengths[l] clamped to [0, tokens], or all tokens
+ * when lengths is NULL):
+ *   khat_t, vhat_t = the kvq_dequantize values of token t's K and V codes,
+ *                    unrounded,
+ *   a_t = softmax_scale * (q_j . khat_t),  p = softmax_t(a),
+ *   out_j = sum_t p_t vhat_t, rounded to fp16; an outer index with n_l = 0
+ *   gets zeros.
+ * It runs in the rotated domain: each query is rotated once (by the key
+ * cache's lambda and signs), keys are never inverse-transformed, and the
+ * weighted value sum is inverse-transformed once per query.
+ *   shape        layers = outer index (layers, or sequences sharing one
+ *                layer), tokens = context capacity T, heads = KV heads,
+ *                head_dim = D.
+ *   q_per_kv     query heads per KV head, 1 .. 1024.
+ *   q_f16        fp16 [layers, heads * q_per_kv, head_dim], contiguous,
+ *                16-byte aligned; out_f16 likewise.
+ *   k_codes_u8, k_scales_f16, v_codes_u8, v_scales_f16
+ *                views as written by kvq_quantize (same alignment rules).
+ *   lambda_k, lambda_v
+ *                fp32 [layers, heads, head_dim], the lambdas the caches
+ *                were quantized with; signs the shared sign vector.
+ *   group        the caches' group size.
+ *   lengths      device int32 [layers], or NULL.
+ *   softmax_scale  finite; usually 1/sqrt(head_dim).
+ *   workspace    device memory of at least kvq_attend_decode_workspace()
+ *                bytes, 16-byte aligned, owned by the caller; its contents
+ *                on entry do not matter and are overwritten.  Calls that
+ *                share a workspace must not overlap.
+ * Errors: as for kvq_quantize, plus KVQ_ERR_SHAPE when workspace_bytes is
+ * smaller than needed.  layers == 0 or heads == 0 is a no-op. */
+kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f16,
+                             kvq_view k_codes_u8, kvq_view k_scales_f16,
+                             kvq_view v_codes_u8, kvq_view v_scales_f16,
+                             const float* lambda_k, const float* lambda_v,
+                             const int8_t* signs, int32_t group, const int32_t* lengths,
+                             float softmax_scale, void* out_f16, void* workspace,
+                             int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes kvq_attend_decode needs for this shape and q_per_kv on the
+ * current device (written to *bytes; 0 for an empty shape). */
+kvq_status kvq_attend_decode_workspace(kvq_shape shape, int32_t q_per_kv, int64_t* bytes);
+
 /* Static, human-readable name of a status code. */
 const char* kvq_status_string(kvq_status status);
 

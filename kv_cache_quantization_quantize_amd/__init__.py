@@ -70,6 +70,11 @@ def lib():
     L.kvq_vq_encode.argtypes = [Shape, View, P, P, P, I64, I32, I32, View, P]
     L.kvq_vq_decode.restype = ctypes.c_int
     L.kvq_vq_decode.argtypes = [Shape, View, P, I64, I32, I32, P, P, View, P]
+    L.kvq_attend_decode.restype = ctypes.c_int
+    L.kvq_attend_decode.argtypes = [Shape, I32, P, View, View, View, View, P, P, P, I32, P, ctypes.c_float, P, P,
+                                    I64, P]
+    L.kvq_attend_decode_workspace.restype = ctypes.c_int
+    L.kvq_attend_decode_workspace.argtypes = [Shape, I32, ctypes.POINTER(I64)]
     L.kvq_status_string.restype = ctypes.c_char_p
     L.kvq_status_string.argtypes = [ctypes.c_int]
     L.kvq_last_error.restype = ctypes.c_char_p
@@ -216,4 +221,56 @@ def vq_decode(idx, codebook, lam, signs, sub_dim: int = 8, out=None, codebook_la
     _check(lib().kvq_vq_decode(_shape(idx, D), _view(idx), ctypes.c_void_p(codebook.data_ptr()),
                                int(codebook_layer_stride), int(K), int(sub_dim), pl, ps, _view(out),
                                _stream(stream)))
+    return out
+
+
+# -------------------------------------------------------- decode attention
+def attend_decode_workspace_bytes(L: int, T: int, H: int, D: int, q_per_kv: int) -> int:
+    """Workspace bytes attend_decode needs for this shape on the current device."""
+    b = ctypes.c_int64(0)
+    _check(lib().kvq_attend_decode_workspace(Shape(L, T, H, D), int(q_per_kv), ctypes.byref(b)))
+    return int(b.value)
+
+
+def attend_decode(q, k_codes, k_scales, v_codes, v_scales, lam_k, lam_v, signs, group: int,
+                  softmax_scale=None, lengths=None, out=None, workspace=None, stream=None):
+    """One decode step of attention over int4 caches.  q [L, H*R, D] fp16
+    (R query heads per KV head), caches [L, T, H, D/2] u8 and [L, T, H, D/G]
+    fp16 as written by quantize, lam_k / lam_v [L, H, D] fp32, lengths [L]
+    int32 or None -> fp16 [L, H*R, D].  The workspace (a uint8 tensor) is
+    allocated here when not given."""
+    torch = _torch()
+    for t, dt, name in ((q, torch.float16, "q"), (k_codes, torch.uint8, "k_codes"),
+                        (k_scales, torch.float16, "k_scales"), (v_codes, torch.uint8, "v_codes"),
+                        (v_scales, torch.float16, "v_scales")):
+        _need(t, dt, name)
+    L, T, H, half = k_codes.shape
+    D = 2 * half
+    if q.dim() != 3 or q.shape[0] != L or q.shape[2] != D or q.shape[1] % H or not q.is_contiguous():
+        raise ValueError("q must be a contiguous fp16 [layers, heads*q_per_kv, head_dim] tensor")
+    R = q.shape[1] // H
+    if tuple(v_codes.shape) != (L, T, H, half):
+        raise ValueError("v_codes must match k_codes in shape")
+    pk, ps = _params(lam_k, signs, L, H, D)
+    pv, _ = _params(lam_v, signs, L, H, D)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.float16, "out")
+    if tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    pl = None
+    if lengths is not None:
+        _need(lengths, torch.int32, "lengths")
+        if tuple(lengths.shape) != (L,) or not lengths.is_contiguous():
+            raise ValueError("lengths must be a contiguous int32 [layers] tensor")
+        pl = ctypes.c_void_p(lengths.data_ptr())
+    need = attend_decode_workspace_bytes(L, T, H, D, R)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, torch.uint8, "workspace")
+    scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
+    _check(lib().kvq_attend_decode(Shape(L, T, H, D), int(R), ctypes.c_void_p(q.data_ptr()), _view(k_codes),
+                                   _view(k_scales), _view(v_codes), _view(v_scales), pk, pv, ps, int(group), pl,
+                                   scale, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+                                   int(workspace.numel()), _stream(stream)))
     return out

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
@@ -209,6 +210,49 @@ kvq_status vq_common(const kvq_shape& shape, const kvq_view& x, const float* lam
     return KVQ_OK;
 }
 
+// Split plan of the decode-attention kernels: query heads per pass, token
+// splits per (outer index, KV head), tokens per split (a multiple of the
+// block's token slots) and partial states per (outer index, query head).
+// A deterministic function of the shape and the current device, so that the
+// workspace query and the call agree.
+struct AttnPlan {
+    int32_t rp, S, chunk, parts;
+};
+
+AttnPlan attn_plan(const kvq_shape& s, int32_t R)
+{
+    AttnPlan p;
+    const int64_t ts = 1024 / s.head_dim;                  // token slots per wavefront
+    const int64_t step = kvq::kAttnWaves * ts;             // tokens per block step
+    p.rp = R == 1 ? 1 : (R == 2 ? 2 : 4);
+    const int64_t passes = (R + p.rp - 1) / p.rp;
+    const int64_t base = std::max<int64_t>(1, s.layers * s.heads * passes);
+    const int64_t target = 4LL * device_cus();             // blocks wanted in flight
+    int64_t S = (target + base - 1) / base;
+    S = std::min<int64_t>(S, std::max<int64_t>(1, (s.tokens + 4 * step - 1) / (4 * step)));
+    int64_t chunk = std::max<int64_t>(1, (s.tokens + S - 1) / S);
+    chunk = (chunk + step - 1) / step * step;
+    S = std::max<int64_t>(1, (s.tokens + chunk - 1) / chunk);
+    p.S = (int32_t)S;
+    p.chunk = (int32_t)chunk;
+    p.parts = (int32_t)(S * kvq::kAttnWaves * ts);
+    return p;
+}
+
+int64_t attn_workspace_bytes(const kvq_shape& s, int32_t R, const AttnPlan& p)
+{
+    return s.layers * s.heads * (int64_t)R * p.parts * (s.head_dim + 4) * (int64_t)sizeof(float);
+}
+
+kvq_status attn_check(const kvq_shape& shape, int32_t R)
+{
+    KVQ_TRY(check_shape(shape));
+    if (R < 1 || R > 1024) return fail(KVQ_ERR_SHAPE, "q_per_kv=%d; must be in 1..1024", R);
+    if ((double)shape.layers * shape.heads * R > (double)(INT32_MAX / 2))
+        return fail(KVQ_ERR_SHAPE, "layers*heads*q_per_kv exceeds 2^30");
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -270,6 +314,73 @@ kvq_status kvq_vq_decode(kvq_shape shape, kvq_view idx_u16, const void* codebook
         a.dec_items_per_block = (a.n_items + blocks - 1) / blocks;
     }
     return hip_status(kvq::launch_vq_decode(a, static_cast<hipStream_t>(stream)), "kvq_vq_decode launch");
+}
+
+kvq_status kvq_attend_decode_workspace(kvq_shape shape, int32_t q_per_kv, int64_t* bytes)
+{
+    g_err[0] = 0;
+    if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
+    *bytes = 0;
+    KVQ_TRY(attn_check(shape, q_per_kv));
+    if (shape.layers == 0 || shape.heads == 0) return KVQ_OK;
+    *bytes = attn_workspace_bytes(shape, q_per_kv, attn_plan(shape, q_per_kv));
+    return KVQ_OK;
+}
+
+kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f16, kvq_view k_codes_u8,
+                             kvq_view k_scales_f16, kvq_view v_codes_u8, kvq_view v_scales_f16,
+                             const float* lambda_k, const float* lambda_v, const int8_t* signs, int32_t group,
+                             const int32_t* lengths, float softmax_scale, void* out_f16, void* workspace,
+                             int64_t workspace_bytes, void* stream)
+{
+    g_err[0] = 0;
+    KVQ_TRY(attn_check(shape, q_per_kv));
+    KVQ_TRY(check_group(group, shape.head_dim));
+    if (shape.layers == 0 || shape.heads == 0) return KVQ_OK;
+    if (!q_f16) return fail(KVQ_ERR_NULL, "q_f16 is NULL");
+    if (!out_f16) return fail(KVQ_ERR_NULL, "out_f16 is NULL");
+    if (!aligned(q_f16, 16) || !aligned(out_f16, 16)) return fail(KVQ_ERR_ALIGN, "q_f16 and out_f16 must be 16-byte aligned");
+    KVQ_TRY(check_params(lambda_k, signs));
+    KVQ_TRY(check_params(lambda_v, signs));
+    if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_SHAPE, "softmax_scale is not finite");
+    const int64_t D = shape.head_dim;
+    if (shape.tokens > 0) {
+        KVQ_TRY(check_view("k_codes_u8", k_codes_u8, 1, D / 2, 16, shape));
+        KVQ_TRY(check_view("k_scales_f16", k_scales_f16, 2, D / group, 2, shape));
+        KVQ_TRY(check_view("v_codes_u8", v_codes_u8, 1, D / 2, 16, shape));
+        KVQ_TRY(check_view("v_scales_f16", v_scales_f16, 2, D / group, 2, shape));
+    }
+    const AttnPlan p = attn_plan(shape, q_per_kv);
+    const int64_t need = attn_workspace_bytes(shape, q_per_kv, p);
+    if (!workspace) return fail(KVQ_ERR_NULL, "workspace is NULL (%lld bytes needed)", (long long)need);
+    if (!aligned(workspace, 16)) return fail(KVQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(KVQ_ERR_SHAPE, "workspace_bytes=%lld; %lld needed", (long long)workspace_bytes, (long long)need);
+    kvq::AttnArgs a;
+    a.L = (int32_t)shape.layers;
+    a.T = (int32_t)shape.tokens;
+    a.H = (int32_t)shape.heads;
+    a.D = (int32_t)D;
+    a.R = q_per_kv;
+    a.g_shift = 0;
+    while ((1 << a.g_shift) < group) a.g_shift++;
+    a.rp = p.rp;
+    a.S = p.S;
+    a.chunk = p.chunk;
+    a.parts = p.parts;
+    a.q = static_cast<const _Float16*>(q_f16);
+    a.out = static_cast<_Float16*>(out_f16);
+    a.kc = t4(k_codes_u8);
+    a.ks = t4(k_scales_f16);
+    a.vc = t4(v_codes_u8);
+    a.vs = t4(v_scales_f16);
+    a.lam_k = lambda_k;
+    a.lam_v = lambda_v;
+    a.signs = signs;
+    a.lengths = lengths;
+    a.qscale = softmax_scale * 1.4426950408889634f;
+    a.ws = static_cast<float*>(workspace);
+    return hip_status(kvq::launch_attend_decode(a, static_cast<hipStream_t>(stream)), "kvq_attend_decode launch");
 }
 
 const char* kvq_status_string(kvq_status st)

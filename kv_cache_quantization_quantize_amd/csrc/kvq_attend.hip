@@ -1,0 +1,382 @@
+// kvq_attend.hip -- single-query decode attention straight from the int4
+// cache, for gfx950 (MI355X).
+//
+// The operation (VeloxQuant-MLX package description, "Fused group-affine
+// (KIVI-style) attention"): one decode step of softmax attention whose keys
+// and values are rebuilt from their codes in registers inside a
+// flash-decoding online softmax accumulated in fp32; no dequantized cache is
+// ever written.  Here the codes are those of the rotated int4 quantizer
+// ("When Quantization Is Free", abstract; gist.science summary,
+// "Methodologie" s.1-2), and the attention runs in the rotated domain: the
+// rotation is orthogonal and the smooth scale and signs are diagonal, so with
+//   qt = H (s * q / lambda_K) / sqrt(D)
+//   q . khat_t = qt . yhat_t,            yhat_t,c = code_t,c * scale_t,g(c)
+//   sum_t p_t vhat_t = s / (lambda_V sqrt(D)) * H (sum_t p_t yhatV_t).
+// Each query is rotated once, keys are never inverse-transformed, and the
+// value sum is inverse-transformed once per query.
+//
+// Partial kernel.  Block = one (outer index, KV head), one token range (a
+// split) and up to RP query heads of that KV head.  Lanes: LPT = D/16 lanes
+// per token hold 16 coordinates each; a wavefront has TS = 64/LPT token
+// slots, and each slot keeps its own online-softmax state over the tokens
+// t = slot, slot + TS, ... of the wavefront's range.  Scores are in the
+// log2 domain (log2 e is folded into the rotated query).  The codes are
+// offset-binary after an xor with 0x88888888; the -8 offset is folded into a
+// per-lane query sum (keys) and a running sum of p * scale (values).  Each
+// slot writes one partial (max, sum of weights, weighted value sum in the
+// rotated domain) to the workspace.
+//
+// Combine kernel.  One quad per (outer index, query head): merges the
+// partials, normalises, applies the inverse rotation and unscale, writes fp16.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+namespace {
+
+// DPP lane exchanges within rows of 16 (hazards are left to the compiler).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
+
+// Sum over the LPT consecutive lanes of a token slot; every lane of the slot
+// receives the total.
+template <int LPT>
+__device__ __forceinline__ float slot_sum(float v)
+{
+    v += dpp_mov<kDppXor1>(v);
+    v += dpp_mov<kDppXor2>(v);
+    if constexpr (LPT >= 8) v += dpp_mov<kDppHalfMirror>(v);
+    if constexpr (LPT >= 16) v += dpp_mov<kDppMirror>(v);
+    return v;
+}
+
+// 16 offset-binary codes (code + 8) of a lane as floats, coordinate order.
+__device__ __forceinline__ void unpack16(uint2 w, float (&u)[16])
+{
+    const uint32_t x[2] = {w.x ^ 0x88888888u, w.y ^ 0x88888888u};
+#pragma unroll
+    for (int d = 0; d < 2; d++) {
+        const uint32_t lo = x[d] & 0x0F0F0F0Fu, hi = (x[d] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            u[8 * d + 2 * k] = (float)((lo >> (8 * k)) & 0xFFu);
+            u[8 * d + 2 * k + 1] = (float)((hi >> (8 * k)) & 0xFFu);
+        }
+    }
+}
+
+}  // namespace
+
+template <int D, int RP>
+__global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArgs a)
+{
+    constexpr int LPT = D / 16;          // lanes per token
+    constexpr int TS = 64 / LPT;         // token slots per wavefront
+    constexpr int NJ = D / 32;
+    constexpr int N = D / 4;
+
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    const int lh = uniform((int)(blockIdx.x / a.S));
+    const int split = (int)blockIdx.x - lh * a.S;
+    const int l = uniform(lh / a.H);
+    const int h = lh - l * a.H;
+    const int r0 = blockIdx.y * RP;
+    const int n = a.lengths ? min(max(a.lengths[l], 0), a.T) : a.T;
+
+    // ---- rotate the pass's queries into LDS (quad r: query r0 + r) ---------
+    __shared__ float qt[RP][D];
+    if (wid == 0) {
+        const int qd = lane >> 2, qq = lane & 3;
+        const int rr = min(qd, RP - 1);
+        const int qi = min(r0 + rr, a.R - 1);
+        const _Float16* qp = a.q + (((int64_t)l * a.H + h) * a.R + qi) * D;
+        const float* lk = a.lam_k + ((int64_t)l * a.H + h) * D;
+        float v[N];
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const int c0 = 32 * j + 8 * qq;
+            const uint4 qw = *reinterpret_cast<const uint4*>(qp + c0);
+            const float4 l0 = *reinterpret_cast<const float4*>(lk + c0);
+            const float4 l1 = *reinterpret_cast<const float4*>(lk + c0 + 4);
+            const uint2 sg = *reinterpret_cast<const uint2*>(a.signs + c0);
+            const uint32_t w[4] = {qw.x, qw.y, qw.z, qw.w};
+            const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const uint32_t word = e < 4 ? sg.x : sg.y;
+                const int sv = (int)(int8_t)((word >> (8 * (e & 3))) & 0xff);
+                const float qv = (e & 1) ? hi_half(w[e / 2]) : lo_half(w[e / 2]);
+                x[e] = (sv < 0 ? -qv : qv) / (lv[e] * SqrtD<D>::v);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                v[8 * j + 2 * k] = x[2 * k] + x[2 * k + 1];
+                v[8 * j + 2 * k + 1] = x[2 * k] - x[2 * k + 1];
+            }
+        }
+        fwht_rest(v, (qq & 1) ? -1.0f : 1.0f, (qq & 2) ? -1.0f : 1.0f);
+        const float f = ((__builtin_popcount(qq) & 1) ? -1.0f : 1.0f) * a.qscale;
+        if (qd < RP) {
+#pragma unroll
+            for (int j = 0; j < NJ; j++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) qt[rr][32 * j + 8 * qq + e] = v[8 * j + e] * f;
+        }
+    }
+    __syncthreads();
+
+    const int slot = lane / LPT;
+    const int ck = lane % LPT;           // this lane's coordinates: 16 ck .. 16 ck + 15
+    float qv[RP][16], qs0[RP], qs1[RP];
+#pragma unroll
+    for (int r = 0; r < RP; r++) {
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+            const float4 t4 = *reinterpret_cast<const float4*>(&qt[r][16 * ck + i]);
+            qv[r][i] = t4.x; qv[r][i + 1] = t4.y; qv[r][i + 2] = t4.z; qv[r][i + 3] = t4.w;
+        }
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) { s0 += qv[r][i]; s1 += qv[r][8 + i]; }
+        qs0[r] = -8.0f * s0;
+        qs1[r] = -8.0f * s1;
+    }
+
+    // ---- this wavefront's token range --------------------------------------
+    const int cb = split * a.chunk;
+    const int ce = min(cb + a.chunk, n);
+    const int per_wave = ((a.chunk + kAttnWaves * TS - 1) / (kAttnWaves * TS)) * TS;
+    const int wb = cb + wid * per_wave;
+    const int we = min(wb + per_wave, ce);
+
+    const uint8_t* kcg = static_cast<const uint8_t*>(a.kc.data) + (int64_t)l * a.kc.sl + (int64_t)h * a.kc.sh + 8 * ck;
+    const uint8_t* vcg = static_cast<const uint8_t*>(a.vc.data) + (int64_t)l * a.vc.sl + (int64_t)h * a.vc.sh + 8 * ck;
+    const uint16_t* ksg = static_cast<const uint16_t*>(a.ks.data) + (int64_t)l * a.ks.sl + (int64_t)h * a.ks.sh;
+    const uint16_t* vsg = static_cast<const uint16_t*>(a.vs.data) + (int64_t)l * a.vs.sl + (int64_t)h * a.vs.sh;
+    const int g0 = (16 * ck) >> a.g_shift, g1 = (16 * ck + 8) >> a.g_shift;
+
+    struct Buf {
+        uint2 kw, vw;
+        uint16_t k0, k1, v0, v1;
+    };
+    // loads of token t0 + slot (a token past the range reads token wb instead)
+    auto load = [&](int t0, Buf& b) {
+        const int t = (t0 + slot < we) ? t0 + slot : wb;
+        b.kw = *reinterpret_cast<const uint2*>(kcg + (int64_t)t * a.kc.st);
+        b.vw = *reinterpret_cast<const uint2*>(vcg + (int64_t)t * a.vc.st);
+        const uint16_t* kp = ksg + (int64_t)t * a.ks.st;
+        const uint16_t* vp = vsg + (int64_t)t * a.vs.st;
+        b.k0 = kp[g0]; b.k1 = kp[g1];
+        b.v0 = vp[g0]; b.v1 = vp[g1];
+    };
+
+    float m[RP], lsum[RP], acc[RP][16], vs0[RP], vs1[RP];
+#pragma unroll
+    for (int r = 0; r < RP; r++) {
+        m[r] = -__builtin_inff();
+        lsum[r] = 0.0f;
+        vs0[r] = 0.0f;
+        vs1[r] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[r][i] = 0.0f;
+    }
+
+    auto compute = [&](int t0, const Buf& b) {
+        const bool valid = t0 + slot < we;
+        float u[16];
+        unpack16(b.kw, u);
+        const float sk0 = (float)__builtin_bit_cast(_Float16, b.k0), sk1 = (float)__builtin_bit_cast(_Float16, b.k1);
+        float s[RP];
+#pragma unroll
+        for (int r = 0; r < RP; r++) {
+            float d0 = qs0[r], d1 = qs1[r];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                d0 = fmaf(qv[r][i], u[i], d0);
+                d1 = fmaf(qv[r][8 + i], u[8 + i], d1);
+            }
+            s[r] = slot_sum<LPT>(fmaf(sk0, d0, sk1 * d1));
+            s[r] = valid ? s[r] : -__builtin_inff();
+        }
+        bool grow = false;
+#pragma unroll
+        for (int r = 0; r < RP; r++) grow |= s[r] > m[r];
+        if (grow) {
+#pragma unroll
+            for (int r = 0; r < RP; r++) {
+                const float c = (s[r] > m[r]) ? exp2f(m[r] - s[r]) : 1.0f;
+                m[r] = fmaxf(m[r], s[r]);
+                lsum[r] *= c;
+                vs0[r] *= c;
+                vs1[r] *= c;
+#pragma unroll
+                for (int i = 0; i < 16; i++) acc[r][i] *= c;
+            }
+        }
+        unpack16(b.vw, u);
+        const float sv0 = (float)__builtin_bit_cast(_Float16, b.v0), sv1 = (float)__builtin_bit_cast(_Float16, b.v1);
+#pragma unroll
+        for (int r = 0; r < RP; r++) {
+            const float p = valid ? exp2f(s[r] - m[r]) : 0.0f;
+            lsum[r] += p;
+            const float p0 = p * sv0, p1 = p * sv1;
+            vs0[r] += p0;
+            vs1[r] += p1;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                acc[r][i] = fmaf(p0, u[i], acc[r][i]);
+                acc[r][8 + i] = fmaf(p1, u[8 + i], acc[r][8 + i]);
+            }
+        }
+    };
+
+    // ---- stream the range, loads one step ahead ----------------------------
+    if (wb < we) {
+        Buf A, B;
+        load(wb, A);
+        for (int t0 = wb;; t0 += 2 * TS) {
+            load(t0 + TS, B);
+            compute(t0, A);
+            if (t0 + TS >= we) break;
+            load(t0 + 2 * TS, A);
+            compute(t0 + TS, B);
+            if (t0 + 2 * TS >= we) break;
+        }
+    }
+
+    // ---- write this slot's partial: [max, weight sum, 2 pad, acc[D]] -------
+    const int part = (split * kAttnWaves + wid) * TS + slot;
+#pragma unroll
+    for (int r = 0; r < RP; r++) {
+        if (r0 + r >= a.R) break;
+        float* P = a.ws + ((((int64_t)lh * a.R + r0 + r) * a.parts) + part) * (D + 4);
+        if (ck == 0) *reinterpret_cast<float2*>(P) = make_float2(m[r], lsum[r]);
+        float o[16];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            o[i] = acc[r][i] - 8.0f * vs0[r];
+            o[8 + i] = acc[r][8 + i] - 8.0f * vs1[r];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i += 4)
+            *reinterpret_cast<float4*>(P + 4 + 16 * ck + i) = make_float4(o[i], o[i + 1], o[i + 2], o[i + 3]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kAttnWaves) void attend_combine_kernel(AttnArgs a)
+{
+    constexpr int NJ = D / 32;
+    constexpr int N = D / 4;
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 3;
+    const int64_t nvec = (int64_t)a.L * a.H * a.R;
+    const int64_t vraw = ((int64_t)blockIdx.x * kAttnWaves + (threadIdx.x >> 6)) * 16 + (lane >> 2);
+    const bool live = vraw < nvec;
+    const int64_t vec = live ? vraw : nvec - 1;
+    const int l = (int)(vec / ((int64_t)a.H * a.R));
+    const int rest = (int)(vec - (int64_t)l * a.H * a.R);
+    const int h = rest / a.R;
+    const int r = rest - h * a.R;
+    const float* P = a.ws + (((int64_t)l * a.H + h) * a.R + r) * a.parts * (D + 4);
+
+    // merge the partials: running max M, weight sum L, value sum y (lane's
+    // coordinates 32 j + 8 q + e)
+    float M = -__builtin_inff(), Ls = 0.0f, y[N];
+#pragma unroll
+    for (int i = 0; i < N; i++) y[i] = 0.0f;
+    for (int p = 0; p < a.parts; p++, P += D + 4) {
+        const float2 ml = *reinterpret_cast<const float2*>(P);
+        if (ml.x == -__builtin_inff()) continue;
+        if (ml.x > M) {
+            const float c = exp2f(M - ml.x);
+            Ls *= c;
+#pragma unroll
+            for (int i = 0; i < N; i++) y[i] *= c;
+            M = ml.x;
+        }
+        const float w = exp2f(ml.x - M);
+        Ls = fmaf(w, ml.y, Ls);
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const float4 a0 = *reinterpret_cast<const float4*>(P + 4 + 32 * j + 8 * q);
+            const float4 a1 = *reinterpret_cast<const float4*>(P + 4 + 32 * j + 8 * q + 4);
+            const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++) y[8 * j + e] = fmaf(w, av[e], y[8 * j + e]);
+        }
+    }
+    const float inv = (Ls > 0.0f) ? 1.0f / Ls : 0.0f;
+
+    // inverse rotation and unscale: x = s / (lambda_V sqrt(D)) * H (y / L)
+    float v[N];
+#pragma unroll
+    for (int k = 0; k < N; k += 2) {
+        v[k] = (y[k] + y[k + 1]) * inv;
+        v[k + 1] = (y[k] - y[k + 1]) * inv;
+    }
+    fwht_rest(v, (q & 1) ? -1.0f : 1.0f, (q & 2) ? -1.0f : 1.0f);
+    float mi[N];
+    load_inv_mult<D>(a.lam_v + ((int64_t)l * a.H + h) * D, a.signs, q,
+                     (__builtin_popcount(q) & 1) ? -1.0f : 1.0f, mi);
+    if (live) {
+        _Float16* o = a.out + vec * D;
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            uint4 w;
+            w.x = pack_half2(v[8 * j + 0] * mi[8 * j + 0], v[8 * j + 1] * mi[8 * j + 1]);
+            w.y = pack_half2(v[8 * j + 2] * mi[8 * j + 2], v[8 * j + 3] * mi[8 * j + 3]);
+            w.z = pack_half2(v[8 * j + 4] * mi[8 * j + 4], v[8 * j + 5] * mi[8 * j + 5]);
+            w.w = pack_half2(v[8 * j + 6] * mi[8 * j + 6], v[8 * j + 7] * mi[8 * j + 7]);
+            *reinterpret_cast<uint4*>(o + 32 * j + 8 * q) = w;
+        }
+    }
+}
+
+namespace {
+
+template <int D, int RP>
+hipError_t launch_part(const AttnArgs& a, hipStream_t s)
+{
+    const dim3 grid((unsigned)((int64_t)a.L * a.H * a.S), (unsigned)((a.R + RP - 1) / RP));
+    hipLaunchKernelGGL((attend_partial_kernel<D, RP>), grid, dim3(64 * kAttnWaves), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t s)
+{
+    hipError_t e;
+    if (a.rp == 1) e = launch_part<D, 1>(a, s);
+    else if (a.rp == 2) e = launch_part<D, 2>(a, s);
+    else e = launch_part<D, 4>(a, s);
+    if (e != hipSuccess) return e;
+    const int64_t nvec = (int64_t)a.L * a.H * a.R;
+    const dim3 grid((unsigned)((nvec + 16 * kAttnWaves - 1) / (16 * kAttnWaves)));
+    hipLaunchKernelGGL((attend_combine_kernel<D>), grid, dim3(64 * kAttnWaves), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attend_decode(const AttnArgs& a, hipStream_t s)
+{
+    switch (a.D) {
+        case 64: return launch_d<64>(a, s);
+        case 128: return launch_d<128>(a, s);
+        case 256: return launch_d<256>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvq

@@ -63,6 +63,26 @@ struct VqArgs {
     int64_t enc_n_units;
 };
 
+// Decode attention over the int4 cache.
+struct AttnArgs {
+    int32_t L, T, H, D, R;          // R query heads per KV head
+    int32_t g_shift;                // log2(group)
+    int32_t rp;                     // query heads per partial-kernel pass (1, 2 or 4)
+    int32_t S;                      // token splits per (outer index, KV head)
+    int32_t chunk;                  // tokens per split
+    int32_t parts;                  // partial states per (outer index, query head)
+    const _Float16* q;              // [L, H*R, D]
+    _Float16* out;                  // [L, H*R, D]
+    Tensor4 kc, ks, vc, vs;         // codes u8 (D/2), scales fp16 (D/G)
+    const float* lam_k;             // [L, H, D]
+    const float* lam_v;
+    const int8_t* signs;            // [D]
+    const int32_t* lengths;         // [L] or null
+    float qscale;                   // softmax scale * log2(e)
+    float* ws;                      // partials: [L*H][R][parts][D + 4] floats
+};
+constexpr int kAttnWaves = 4;       // wavefronts per attention block
+
 // Centroids staged in LDS at a time by the VQ encoder (64 KB of fp16).
 constexpr int kVqChunk = 4096;
 
@@ -75,5 +95,6 @@ hipError_t launch_quantize(const Int4Args& a, hipStream_t stream);
 hipError_t launch_dequantize(const Int4Args& a, hipStream_t stream);
 hipError_t launch_vq_encode(const VqArgs& a, hipStream_t stream);
 hipError_t launch_vq_decode(const VqArgs& a, hipStream_t stream);
+hipError_t launch_attend_decode(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace kvq

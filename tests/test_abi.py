@@ -33,6 +33,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "kvq_quantize", "kvq_dequantize", "kvq_vq_encode", "kvq_vq_decode",
+        "kvq_attend_decode", "kvq_attend_decode_workspace",
         "kvq_status_string", "kvq_last_error", "kvq_version"])
 
 
@@ -148,3 +149,52 @@ def test_binding_raises_without_gpu_tensors():
     x = torch.zeros((1, 16, 1, 128), dtype=torch.float16)
     with pytest.raises((ValueError, RuntimeError)):
         kvq.quantize(x, torch.ones((1, 1, 128)), torch.ones(128, dtype=torch.int8), 32)
+
+
+# ------------------------------------------------------- decode attention
+def ws_bytes(lib, sh, R):
+    b = ctypes.c_int64(-1)
+    st = lib.kvq_attend_decode_workspace(sh, R, ctypes.byref(b))
+    return st, b.value
+
+
+def att(lib, sh=None, R=4, qp=A, out=A, kc=None, ks=None, vc=None, vs=None, lk=A, lv=A, sg=A, group=32,
+        lengths=None, scale=0.088, ws=A, ws_bytes_=1 << 40):
+    sh = sh or shape()
+    D = sh.head_dim
+    kc = kc or view(row=D // 2, L=sh.layers, T=sh.tokens, H=sh.heads)
+    vc = vc or view(row=D // 2, L=sh.layers, T=sh.tokens, H=sh.heads)
+    ks = ks or view(row=D // group, L=sh.layers, T=sh.tokens, H=sh.heads)
+    vs = vs or view(row=D // group, L=sh.layers, T=sh.tokens, H=sh.heads)
+    return lib.kvq_attend_decode(sh, R, ctypes.c_void_p(qp), kc, ks, vc, vs, ctypes.c_void_p(lk),
+                                 ctypes.c_void_p(lv), ctypes.c_void_p(sg), group, lengths, ctypes.c_float(scale),
+                                 ctypes.c_void_p(out), ctypes.c_void_p(ws), ws_bytes_, None)
+
+
+def test_attend_workspace_query(lib):
+    st, b = ws_bytes(lib, shape(2, 1000, 3, 128), 4)
+    assert st == OK and b > 0 and b % 16 == 0
+    # at least one partial per (outer, query head): [max, sum, pad, pad, D values]
+    assert b >= 2 * 3 * 4 * (128 + 4) * 4
+    assert ws_bytes(lib, shape(0, 1000, 3, 128), 4) == (OK, 0)
+    assert ws_bytes(lib, shape(2, 1000, 3, 128), 0)[0] == SHAPE
+    assert ws_bytes(lib, shape(2, 1000, 3, 96), 4)[0] == UNSUP
+    assert lib.kvq_attend_decode_workspace(shape(), 4, None) == NULL
+
+
+def test_attend_validation(lib):
+    assert att(lib, sh=shape(0, 5, 3)) == OK                 # empty: no-op
+    assert att(lib, R=0) == SHAPE
+    assert att(lib, qp=0) == NULL
+    assert att(lib, out=0) == NULL
+    assert att(lib, qp=A + 8) == ALIGN
+    assert att(lib, lk=0) == NULL and att(lib, lv=0) == NULL
+    assert att(lib, group=24) == UNSUP
+    assert att(lib, scale=float("inf")) == SHAPE
+    assert att(lib, kc=view(addr=0, row=64)) == NULL
+    assert att(lib, vs=view(addr=A + 1, row=4)) == ALIGN
+    assert att(lib, ws=0) == NULL
+    assert b"needed" in lib.kvq_last_error()
+    assert att(lib, ws=A + 4) == ALIGN
+    st, need = ws_bytes(lib, shape(), 4)
+    assert att(lib, ws_bytes_=need - 1) == SHAPE
