@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=8 * 32768, help="tokens per tensor (default: full size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-vq", action="store_true")
+    ap.add_argument("--no-attend", action="store_true")
+    ap.add_argument("--attend-seqs", type=int, default=8,
+                    help="sequences the int4 cache's token axis is split into for the decode-attention leg")
     ap.add_argument("--cpu-tokens", type=int, default=192, help="tokens per (layer, head) in the CPU sample")
     ap.add_argument("--copy-bytes", type=int, default=4 << 30, help="size of the plain-copy reference")
     ap.add_argument("--parts", default="int4,vq",
@@ -223,6 +226,11 @@ def main():
 
     del outs
     torch.cuda.empty_cache()
+
+    attend = None
+    if not args.no_attend:
+        attend = bench_attend(torch, kvq, codes, scales, lamK, lamV, signs, (L, T, H, D, G), args)
+
     try:
         copy_gbps = round(copy_ceiling(torch, args.copy_bytes), 1)
     except RuntimeError:
@@ -250,9 +258,58 @@ def main():
         "kernels": kern,
         "copy_ceiling_GB_per_s": copy_gbps,
         "vq": vq,
+        "attend": attend,
         "frac_of_hbm_peak_step": round(value / HBM_PEAK_GBPS, 4),
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_attend(torch, kvq, codes, scales, lamK, lamV, signs, dims, args):
+    """Time one decode step of attention over the quantized K/V caches: the
+    [36, 262144, 8, 128] caches read as 36 layers x B sequences of T/B
+    tokens, 4 query heads per KV head (Qwen3-8B: 32 query, 8 KV heads)."""
+    L, T, H, D, G = dims
+    B, R = args.attend_seqs, 4
+    if T % B:
+        return None
+    Lo, Tq = L * B, T // B
+    kc, ks = codes["K"].view(Lo, Tq, H, D // 2), scales["K"].view(Lo, Tq, H, D // G)
+    vc, vs = codes["V"].view(Lo, Tq, H, D // 2), scales["V"].view(Lo, Tq, H, D // G)
+    lk = lamK.repeat_interleave(B, dim=0).contiguous()
+    lv = lamV.repeat_interleave(B, dim=0).contiguous()
+    g = torch.Generator(device="cpu").manual_seed(4321)
+    q = torch.randn((Lo, H * R, D), generator=g).to(torch.float16).to(kc.device)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(16, kvq.attend_decode_workspace_bytes(Lo, Tq, H, D, R)), dtype=torch.uint8,
+                     device=kc.device)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        kvq.attend_decode(q, kc, ks, vc, vs, lk, lv, signs, G, out=out, workspace=ws, stream=stream)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(max(3, min(args.steps, 20))):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        ms.append((a, b))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ms]
+    avg = sum(ms) / len(ms)
+    cache_bytes = 2 * Lo * Tq * H * (D // 2 + 2 * (D // G))        # K and V codes + scales
+    qo_bytes = 2 * Lo * H * R * D * 2                               # queries in, outputs out
+    byt = cache_bytes + qo_bytes
+    gbps = byt / (avg * 1e-3) / 1e9
+    return {"workload": "qwen3-8b-shaped decode step: %d layers x %d sequences x %d tokens, %d KV heads, "
+                        "%d query heads per KV head, head_dim %d, group %d" % (L, B, Tq, H, R, D, G),
+            "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "GB_per_s": round(gbps, 1),
+            "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_call": byt,
+            "ns_per_token_head": round(avg * 1e6 / (Lo * Tq * H), 5),
+            "workspace_bytes": int(ws.numel())}
 
 
 def bench_vq(torch, kvq, synth, dev, args):
