@@ -58,6 +58,14 @@ __device__ __forceinline__ float slot_sum(float v)
     return v;
 }
 
+// Bytes 0..3 of x as floats (one v_cvt_f32_ubyteN each).
+__device__ __forceinline__ void bytes_to_f32(uint32_t x, float& a, float& b, float& c, float& d)
+{
+    asm("v_cvt_f32_ubyte0 %0, %4\n\tv_cvt_f32_ubyte1 %1, %4\n\tv_cvt_f32_ubyte2 %2, %4\n\tv_cvt_f32_ubyte3 %3, %4"
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=v"(d)
+        : "v"(x));
+}
+
 // 16 offset-binary codes (code + 8) of a lane as floats, coordinate order.
 __device__ __forceinline__ void unpack16(uint2 w, float (&u)[16])
 {
@@ -65,17 +73,14 @@ __device__ __forceinline__ void unpack16(uint2 w, float (&u)[16])
 #pragma unroll
     for (int d = 0; d < 2; d++) {
         const uint32_t lo = x[d] & 0x0F0F0F0Fu, hi = (x[d] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            u[8 * d + 2 * k] = (float)((lo >> (8 * k)) & 0xFFu);
-            u[8 * d + 2 * k + 1] = (float)((hi >> (8 * k)) & 0xFFu);
-        }
+        bytes_to_f32(lo, u[8 * d + 0], u[8 * d + 2], u[8 * d + 4], u[8 * d + 6]);
+        bytes_to_f32(hi, u[8 * d + 1], u[8 * d + 3], u[8 * d + 5], u[8 * d + 7]);
     }
 }
 
 }  // namespace
 
-template <int D, int RP>
+template <int D, int RP, bool SPLIT>
 __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArgs a)
 {
     constexpr int LPT = D / 16;          // lanes per token
@@ -158,26 +163,51 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
     const int per_wave = ((a.chunk + kAttnWaves * TS - 1) / (kAttnWaves * TS)) * TS;
     const int wb = cb + wid * per_wave;
     const int we = min(wb + per_wave, ce);
+    const int nfull = we > wb ? (we - wb) / TS : 0;       // steps where every slot has a token
+    const int rem = we > wb ? (we - wb) - nfull * TS : 0; // slots with a token in the last step
 
     const uint8_t* kcg = static_cast<const uint8_t*>(a.kc.data) + (int64_t)l * a.kc.sl + (int64_t)h * a.kc.sh + 8 * ck;
     const uint8_t* vcg = static_cast<const uint8_t*>(a.vc.data) + (int64_t)l * a.vc.sl + (int64_t)h * a.vc.sh + 8 * ck;
-    const uint16_t* ksg = static_cast<const uint16_t*>(a.ks.data) + (int64_t)l * a.ks.sl + (int64_t)h * a.ks.sh;
-    const uint16_t* vsg = static_cast<const uint16_t*>(a.vs.data) + (int64_t)l * a.vs.sl + (int64_t)h * a.vs.sh;
-    const int g0 = (16 * ck) >> a.g_shift, g1 = (16 * ck + 8) >> a.g_shift;
+    const int g0 = (16 * ck) >> a.g_shift;
+    const uint16_t* ksg = static_cast<const uint16_t*>(a.ks.data) + (int64_t)l * a.ks.sl + (int64_t)h * a.ks.sh + g0;
+    const uint16_t* vsg = static_cast<const uint16_t*>(a.vs.data) + (int64_t)l * a.vs.sl + (int64_t)h * a.vs.sh + g0;
 
     struct Buf {
         uint2 kw, vw;
         uint16_t k0, k1, v0, v1;
     };
-    // loads of token t0 + slot (a token past the range reads token wb instead)
-    auto load = [&](int t0, Buf& b) {
-        const int t = (t0 + slot < we) ? t0 + slot : wb;
-        b.kw = *reinterpret_cast<const uint2*>(kcg + (int64_t)t * a.kc.st);
-        b.vw = *reinterpret_cast<const uint2*>(vcg + (int64_t)t * a.vc.st);
-        const uint16_t* kp = ksg + (int64_t)t * a.ks.st;
-        const uint16_t* vp = vsg + (int64_t)t * a.vs.st;
-        b.k0 = kp[g0]; b.k1 = kp[g1];
-        b.v0 = vp[g0]; b.v1 = vp[g1];
+    // Pointers of this lane's token; a step advances them by TS tokens.
+    struct Ptr {
+        const uint8_t* k;
+        const uint8_t* v;
+        const uint16_t* ks;
+        const uint16_t* vs;
+    };
+    auto at = [&](int t) {
+        return Ptr{kcg + (int64_t)t * a.kc.st, vcg + (int64_t)t * a.vc.st, ksg + (int64_t)t * a.ks.st,
+                   vsg + (int64_t)t * a.vs.st};
+    };
+    const int64_t dk = (int64_t)TS * a.kc.st, dv = (int64_t)TS * a.vc.st;
+    const int64_t dks = (int64_t)TS * a.ks.st, dvs = (int64_t)TS * a.vs.st;
+    auto load = [&](const Ptr& p, Buf& b) {
+        b.kw = *reinterpret_cast<const uint2*>(p.k);
+        b.vw = *reinterpret_cast<const uint2*>(p.v);
+        b.k0 = p.ks[0];
+        b.v0 = p.vs[0];
+        if constexpr (SPLIT) {     // group 8: the lane's second 8 coordinates have their own scale
+            b.k1 = p.ks[1];
+            b.v1 = p.vs[1];
+        } else {
+            b.k1 = b.k0;
+            b.v1 = b.v0;
+        }
+    };
+    // advance by one step when `more` (a wave-uniform flag), else stay
+    auto advance = [&](Ptr& p, bool more) {
+        p.k += more ? dk : 0;
+        p.v += more ? dv : 0;
+        p.ks += more ? dks : 0;
+        p.vs += more ? dvs : 0;
     };
 
     float m[RP], lsum[RP], acc[RP][16], vs0[RP], vs1[RP];
@@ -191,12 +221,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
         for (int i = 0; i < 16; i++) acc[r][i] = 0.0f;
     }
 
-    auto compute = [&](int t0, const Buf& b) {
-        const bool valid = t0 + slot < we;
+    // scores of one step (log2 domain); -inf for a slot without a token
+    auto scores = [&](const Buf& b, bool valid, float (&s)[RP]) {
         float u[16];
         unpack16(b.kw, u);
         const float sk0 = (float)__builtin_bit_cast(_Float16, b.k0), sk1 = (float)__builtin_bit_cast(_Float16, b.k1);
-        float s[RP];
 #pragma unroll
         for (int r = 0; r < RP; r++) {
             float d0 = qs0[r], d1 = qs1[r];
@@ -208,26 +237,30 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
             s[r] = slot_sum<LPT>(fmaf(sk0, d0, sk1 * d1));
             s[r] = valid ? s[r] : -__builtin_inff();
         }
-        bool grow = false;
+    };
+    // online softmax: a new maximum rescales what the slot has so far
+    auto rescale = [&](const float (&smax)[RP]) {
 #pragma unroll
-        for (int r = 0; r < RP; r++) grow |= s[r] > m[r];
-        if (grow) {
+        for (int r = 0; r < RP; r++) {
+            const float c = (smax[r] > m[r]) ? __builtin_amdgcn_exp2f(m[r] - smax[r]) : 1.0f;
+            m[r] = fmaxf(m[r], smax[r]);
+            lsum[r] *= c;
+            vs0[r] *= c;
+            vs1[r] *= c;
 #pragma unroll
-            for (int r = 0; r < RP; r++) {
-                const float c = (s[r] > m[r]) ? exp2f(m[r] - s[r]) : 1.0f;
-                m[r] = fmaxf(m[r], s[r]);
-                lsum[r] *= c;
-                vs0[r] *= c;
-                vs1[r] *= c;
-#pragma unroll
-                for (int i = 0; i < 16; i++) acc[r][i] *= c;
-            }
+            for (int i = 0; i < 16; i++) acc[r][i] *= c;
         }
+    };
+    // weights and value accumulation of one step (after rescale)
+    auto accumulate = [&](const Buf& b, const float (&s)[RP]) {
+        float u[16];
         unpack16(b.vw, u);
         const float sv0 = (float)__builtin_bit_cast(_Float16, b.v0), sv1 = (float)__builtin_bit_cast(_Float16, b.v1);
 #pragma unroll
         for (int r = 0; r < RP; r++) {
-            const float p = valid ? exp2f(s[r] - m[r]) : 0.0f;
+            // exp2(-inf) = 0 for a slot without a token (m is finite once any
+            // token has been seen; before that every weight is 0 anyway)
+            const float p = (s[r] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(s[r] - m[r]);
             lsum[r] += p;
             const float p0 = p * sv0, p1 = p * sv1;
             vs0[r] += p0;
@@ -239,19 +272,50 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
             }
         }
     };
+    // two steps share one rescale
+    auto pair = [&](const Buf& b0, const Buf& b1, bool valid1) {
+        float s0[RP], s1[RP], sm[RP];
+        scores(b0, true, s0);
+        scores(b1, valid1, s1);
+#pragma unroll
+        for (int r = 0; r < RP; r++) sm[r] = fmaxf(s0[r], s1[r]);
+        rescale(sm);
+        accumulate(b0, s0);
+        accumulate(b1, s1);
+    };
 
-    // ---- stream the range, loads one step ahead ----------------------------
-    if (wb < we) {
-        Buf A, B;
-        load(wb, A);
-        for (int t0 = wb;; t0 += 2 * TS) {
-            load(t0 + TS, B);
-            compute(t0, A);
-            if (t0 + TS >= we) break;
-            load(t0 + 2 * TS, A);
-            compute(t0 + TS, B);
-            if (t0 + 2 * TS >= we) break;
+    // ---- full steps in pairs, the next pair's loads in flight --------------
+    if (nfull > 0) {
+        Ptr p = at(wb + slot);
+        Buf A, B, C, E;
+        load(p, A);
+        advance(p, 1 < nfull);
+        load(p, B);
+        for (int i = 0;; i += 4) {
+            // a step past the last full step reloads the last one (in range)
+            advance(p, i + 2 < nfull);
+            load(p, C);
+            advance(p, i + 3 < nfull);
+            load(p, E);
+            pair(A, B, i + 1 < nfull);
+            if (i + 2 >= nfull) break;
+            advance(p, i + 4 < nfull);
+            load(p, A);
+            advance(p, i + 5 < nfull);
+            load(p, B);
+            pair(C, E, i + 3 < nfull);
+            if (i + 4 >= nfull) break;
         }
+    }
+    // ---- last, partial step: slots past the range read the first token ---
+    if (rem > 0) {
+        const bool valid = slot < rem;
+        Buf b;
+        load(at(valid ? wb + nfull * TS + slot : wb), b);
+        float s1[RP];
+        scores(b, valid, s1);
+        rescale(s1);
+        accumulate(b, s1);
     }
 
     // ---- write this slot's partial: [max, weight sum, 2 pad, acc[D]] -------
@@ -349,7 +413,8 @@ template <int D, int RP>
 hipError_t launch_part(const AttnArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)((int64_t)a.L * a.H * a.S), (unsigned)((a.R + RP - 1) / RP));
-    hipLaunchKernelGGL((attend_partial_kernel<D, RP>), grid, dim3(64 * kAttnWaves), 0, s, a);
+    if (a.g_shift == 3) hipLaunchKernelGGL((attend_partial_kernel<D, RP, true>), grid, dim3(64 * kAttnWaves), 0, s, a);
+    else hipLaunchKernelGGL((attend_partial_kernel<D, RP, false>), grid, dim3(64 * kAttnWaves), 0, s, a);
     return hipGetLastError();
 }
 
