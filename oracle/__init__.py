@@ -65,6 +65,9 @@ def bind(path: str):
         "kvqo_vq_encode_rows": (I32, [I64, I32, I32, I32, P, P, P, P, P, P, P]),
         "kvqo_vq_distances": (I32, [I64, I32, I32, I32, P, P, P, P, P]),
         "kvqo_vq_decode_rows": (I32, [I64, I32, I32, I32, P, P, P, P, P, P, P]),
+        "kvqo_codes8_given_scales": (I32, [I64, I32, I32, P, P, P]),
+        "kvqo_quantize8_rows": (I64, [I64, I32, I32, P, P, P, P, P, P]),
+        "kvqo_dequantize8_rows": (I32, [I64, I32, I32, P, P, P, P, P, P]),
         "kvqo_attend_decode": (I32, [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P,
                                      ctypes.c_double, P]),
     }
@@ -273,3 +276,46 @@ def attend_decode(q_bits, k_codes, k_scales, v_codes, v_scales, lam_k, lam_v, si
     if rc:
         raise ValueError("oracle attend_decode rejected its arguments (%d)" % rc)
     return out
+
+
+# ------------------------------------------------------------------ int8
+def codes8_given_scales(y, scales_bits, G):
+    """int8 codes of rotated values y [n, D] under given binary16 scales."""
+    yy, py = _c(y, np.float64)
+    D = yy.shape[-1]
+    sc, ps = _c(scales_bits, np.uint16)
+    q, pq = _out(yy.shape, np.int8)
+    if _load().kvqo_codes8_given_scales(_rows(yy, D), D, int(G), py, ps, pq):
+        raise ValueError("bad group size")
+    return q
+
+
+def quantize8(x_bits, lam, signs, G):
+    """int8 group quantizer: x [n, D] binary16 bits, lam [n, D] fp32, signs
+    [D] -> (codes int8 [n, D], scales binary16 bits [n, D/G], y fp64 [n, D],
+    number of vectors outside the domain)."""
+    x, px = _c(x_bits, np.uint16)
+    n, D = x.shape
+    lam, pl = _c(np.broadcast_to(lam, (n, D)), np.float32)
+    s, ps = _c(signs, np.int8)
+    codes, pc = _out((n, D), np.int8)
+    scales, psc = _out((n, D // G), np.uint16)
+    y, py = _out((n, D), np.float64)
+    bad = _load().kvqo_quantize8_rows(n, D, int(G), px, pl, ps, pc, psc, py)
+    if bad < 0:
+        raise ValueError("oracle quantize8 rejected its arguments")
+    return codes, scales, y, int(bad)
+
+
+def dequantize8(codes, scales_bits, lam, signs, G):
+    """Inverse of quantize8 -> (xhat fp64 [n, D], xhat binary16 bits [n, D])."""
+    c, pc = _c(codes, np.int8)
+    n, D = c.shape
+    sc, psc = _c(scales_bits, np.uint16)
+    lam, pl = _c(np.broadcast_to(lam, (n, D)), np.float32)
+    s, ps = _c(signs, np.int8)
+    x64, p64 = _out((n, D), np.float64)
+    x16, p16 = _out((n, D), np.uint16)
+    if _load().kvqo_dequantize8_rows(n, D, int(G), pc, psc, pl, ps, p64, p16):
+        raise ValueError("oracle dequantize8 rejected its arguments")
+    return x64, x16

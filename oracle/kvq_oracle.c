@@ -305,6 +305,95 @@ int kvqo_dequantize_rows(int64_t n, int D, int G, const uint8_t* codes,
 }
 
 /* ------------------------------------------------------------------------ */
+/* int8 variant [GIST s.2: the fused kernel rounds to signed int4 or int8]    */
+/* ------------------------------------------------------------------------ */
+
+/* Same rotation and groups as the int4 quantizer, with 127 levels each side:
+     scale = binary16_rne(amax / 127);
+     q_i = clamp(rne(y_i / scale), -127, 127)  (0 when scale == 0),
+   one two's-complement byte per coordinate (element i in byte i). */
+static int code8_of(double y, double scale)
+{
+    if (scale == 0.0) return 0;
+    double r = nearbyint(y / scale);
+    if (r > 127.0) r = 127.0;
+    if (r < -127.0) r = -127.0;
+    return (int)r;
+}
+
+int kvqo_codes8_given_scales(int64_t n, int D, int G, const double* y,
+                             const uint16_t* scales, int8_t* q)
+{
+    if (G <= 0 || D % G) return -1;
+    int ng = D / G;
+    for (int64_t r = 0; r < n; r++)
+        for (int i = 0; i < D; i++)
+            q[r * D + i] = (int8_t)code8_of(y[r * D + i],
+                                            kvqo_f16_to_f64(scales[r * ng + i / G]));
+    return 0;
+}
+
+/* Quantize n vectors to int8 codes [n, D] and binary16 scales [n, D/G];
+   y_out [n, D] (may be NULL) receives the fp64 rotated values.  Returns the
+   number of vectors outside the domain (zeroed), as kvqo_quantize_rows. */
+int64_t kvqo_quantize8_rows(int64_t n, int D, int G, const uint16_t* x,
+                            const float* lam, const int8_t* s, int8_t* codes,
+                            uint16_t* scales, double* y_out)
+{
+    if (!is_pow2(D) || G <= 0 || D % G || (G & 1)) return -1;
+    int ng = D / G;
+    double* v = (double*)malloc(sizeof(double) * (size_t)D);
+    double* y = (double*)malloc(sizeof(double) * (size_t)D);
+    int64_t bad = 0;
+    for (int64_t r = 0; r < n; r++) {
+        int ok = 1;
+        for (int j = 0; j < D; j++)
+            if (!isfinite(kvqo_f16_to_f64(x[r * D + j]))) ok = 0;
+        if (ok) rotate_one(D, x + r * D, lam + r * D, s, v, y);
+        for (int g = 0; ok && g < ng; g++) {
+            double amax = 0.0;
+            for (int i = g * G; i < (g + 1) * G; i++)
+                if (fabs(y[i]) > amax) amax = fabs(y[i]);
+            uint16_t sc = kvqo_f64_to_f16(amax / 127.0);
+            if ((sc & 0x7c00) == 0x7c00) { ok = 0; break; }
+            scales[r * ng + g] = sc;
+            double sbar = kvqo_f16_to_f64(sc);
+            for (int i = g * G; i < (g + 1) * G; i++) codes[r * D + i] = (int8_t)code8_of(y[i], sbar);
+        }
+        if (!ok) {
+            bad++;
+            memset(codes + r * D, 0, (size_t)D);
+            memset(scales + r * ng, 0, sizeof(uint16_t) * (size_t)ng);
+            if (y_out) for (int i = 0; i < D; i++) y_out[r * D + i] = NAN;
+            continue;
+        }
+        if (y_out) memcpy(y_out + r * D, y, sizeof(double) * (size_t)D);
+    }
+    free(v); free(y);
+    return bad;
+}
+
+/* Dequantize n int8 vectors: yhat_i = q_i * scale_g, xhat = unrotate(yhat). */
+int kvqo_dequantize8_rows(int64_t n, int D, int G, const int8_t* codes,
+                          const uint16_t* scales, const float* lam,
+                          const int8_t* s, double* xhat64, uint16_t* xhat16)
+{
+    if (!is_pow2(D) || G <= 0 || D % G || (G & 1)) return -1;
+    int ng = D / G;
+    double* yh = (double*)malloc(sizeof(double) * (size_t)D);
+    for (int64_t r = 0; r < n; r++) {
+        for (int i = 0; i < D; i++)
+            yh[i] = (double)codes[r * D + i] * kvqo_f16_to_f64(scales[r * ng + i / G]);
+        unrotate_one(D, yh, lam + r * D, s, xhat64 + r * D);
+        if (xhat16)
+            for (int j = 0; j < D; j++)
+                xhat16[r * D + j] = kvqo_f64_to_f16(xhat64[r * D + j]);
+    }
+    free(yh);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Product VQ [README "Metal kernels"; VQ-blog "What VecInfer does"]           */
 /* ------------------------------------------------------------------------ */
 

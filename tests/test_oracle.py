@@ -504,3 +504,88 @@ def test_attend_empty_context_gives_zeros():
     c = attn_case(2, 4, 1, 2, 64, 32, seed=5)
     out = attend(c, 32, 0.125, lengths=np.array([0, 4], np.int32))
     assert (out[0] == 0).all() and np.abs(out[1]).sum() > 0
+
+
+# --------------------------------------------------------------------- int8
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_int8_single_spike(D):
+    # x = a e_k, lambda = 1, s = 1: every |y_i| = |a|/sqrt(D); every scale is
+    # fp16(|a|/(127 sqrt D)); every code is +-127 with the sign of a H[i][k]
+    G = 32
+    H = scipy.linalg.hadamard(D)
+    for a, k in ((1.5, 3), (-2.0, D - 1), (0.75, 0)):
+        x = np.zeros((1, D))
+        x[0, k] = a
+        codes, scales, _, bad = oracle.quantize8(f16bits(x), np.ones(D, np.float32), np.ones(D, np.int8), G)
+        assert bad == 0
+        assert (scales == np.float16(abs(a) / (127 * np.sqrt(D))).view(np.uint16)).all()
+        assert np.array_equal(codes[0], 127 * np.sign(a) * H[:, k])
+
+
+def test_int8_ties_round_half_to_even_and_clamp():
+    sc = np.float16(0.0625)
+    sbar = float(sc)
+    halves = np.array([-126.5, -125.5, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 125.5, 126.5])
+    y = np.zeros((1, 16))
+    y[0, :10] = halves * sbar
+    y[0, 10] = 127.4 * sbar      # rounds to 127
+    y[0, 11] = 127.6 * sbar      # would round to 128: clamps to 127
+    y[0, 12] = -300.0 * sbar     # clamps to -127
+    q = oracle.codes8_given_scales(y, np.array([[sc.view(np.uint16)]]), 16)[0]
+    assert list(q[:13]) == [-126, -126, -2, -2, 0, 0, 2, 2, 126, 126, 127, 127, -127]
+
+
+@pytest.mark.parametrize("D,G", [(64, 16), (128, 32), (128, 8), (256, 64), (128, 128)])
+def test_int8_quantizer_invariants(D, G):
+    n = 300
+    x = rand_x(n, D, 2.0)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    codes, scales, y, bad = oracle.quantize8(x, lam, s, G)
+    assert bad == 0
+    # the rotation is the (separately pinned) int4 quantizer's
+    _, _, y4, _ = oracle.quantize(x, lam, s, G)
+    assert np.array_equal(y, y4)
+    q = codes.astype(np.float64)
+    sb = bits_to_f64(scales)
+    sbe = np.repeat(sb, G, axis=1)
+    assert np.abs(q).max() <= 127
+    assert (np.abs(y - q * sbe) <= sbe / 2 * (1 + 1e-12)).all()
+    amax = np.abs(y).reshape(n, D // G, G).max(axis=2)
+    assert np.array_equal(scales, (amax / 127).astype(np.float16).view(np.uint16))
+    qa = np.abs(q).reshape(n, D // G, G).max(axis=2)
+    assert (qa[sb > 0] == 127).all()
+    assert np.array_equal(oracle.codes8_given_scales(y, scales, G), codes)
+
+
+def test_int8_dequant_single_code_closed_form():
+    D, G = 64, 16
+    lam = rand_lambda(1, D)[0]
+    s = rand_signs(D)
+    H = scipy.linalg.hadamard(D)
+    for k, c in ((0, 127), (17, -3), (63, -127)):
+        q = np.zeros((1, D), np.int8)
+        q[0, k] = c
+        scales = np.zeros((1, D // G), np.uint16)
+        scales[0, k // G] = np.float16(0.0078125).view(np.uint16)
+        x64, x16 = oracle.dequantize8(q, scales, lam, s, G)
+        want = (s / lam.astype(np.float64)) * c * 0.0078125 * H[k, :] / np.sqrt(D)
+        assert np.allclose(x64[0], want, rtol=1e-14, atol=0)
+        assert np.array_equal(x16[0], want.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("D,G", [(128, 32), (256, 64)])
+def test_int8_roundtrip_error_bound_and_finer_than_int4(D, G):
+    n = 300
+    x = rand_x(n, D)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    codes, scales, _, _ = oracle.quantize8(x, lam, s, G)
+    x64, _ = oracle.dequantize8(codes, scales, lam, s, G)
+    err8 = np.linalg.norm(lam * (x64 - bits_to_f64(x)), axis=1)
+    assert (err8 <= 0.5 * np.sqrt(G * (bits_to_f64(scales) ** 2).sum(axis=1)) * (1 + 1e-9)).all()
+    c4, s4, _, _ = oracle.quantize(x, lam, s, G)
+    x4, _ = oracle.dequantize(c4, s4, lam, s, G)
+    err4 = np.linalg.norm(lam * (x4 - bits_to_f64(x)), axis=1)
+    # 127 levels against 7: the error shrinks by about 127/7 on average
+    assert err8.mean() * 10 < err4.mean()

@@ -25,16 +25,17 @@ MUTANTS = {
     "no_normalisation": ("y[i] = acc * norm;", "y[i] = acc;"),
     "hadamard_sign_flipped": ("& 1) ? -1 : 1;", "& 1) ? 1 : -1;"),
     "hadamard_or_index": ("popcount((unsigned)(i & j))", "popcount((unsigned)(i | j))"),
-    "unstored_scale": ("double sbar = kvqo_f16_to_f64(sc);", "double sbar = amax / 7.0;"),
+    "unstored_scale": ("double sbar = kvqo_f16_to_f64(sc);\n            for (int i = g * G; i < (g + 1) * G; i++) q[i]",
+                       "double sbar = amax / 7.0;\n            for (int i = g * G; i < (g + 1) * G; i++) q[i]"),
     "amax_over_8": ("kvqo_f64_to_f16(amax / 7.0)", "kvqo_f64_to_f16(amax / 8.0)"),
-    "round_half_away": ("double r = nearbyint(y / scale);", "double r = round(y / scale);"),
-    "truncate_codes": ("double r = nearbyint(y / scale);", "double r = trunc(y / scale);"),
+    "round_half_away": ("double r = nearbyint(y / scale);\n    if (r > 7.0)", "double r = round(y / scale);\n    if (r > 7.0)"),
+    "truncate_codes": ("double r = nearbyint(y / scale);\n    if (r > 7.0)", "double r = trunc(y / scale);\n    if (r > 7.0)"),
     "nibble_order_swapped": ("bytes[k] = (uint8_t)(((unsigned)q[2 * k] & 0xfu) |\n"
                              "                             (((unsigned)q[2 * k + 1] & 0xfu) << 4));",
                              "bytes[k] = (uint8_t)(((unsigned)q[2 * k + 1] & 0xfu) |\n"
                              "                             (((unsigned)q[2 * k] & 0xfu) << 4));"),
-    "group_index_interleaved": ("kvqo_f16_to_f64(scales[r * ng + i / G]));",
-                                "kvqo_f16_to_f64(scales[r * ng + i % ng]));"),
+    "group_index_interleaved": ("code_of(y[r * D + i],\n                                           kvqo_f16_to_f64(scales[r * ng + i / G]));",
+                                "code_of(y[r * D + i],\n                                           kvqo_f16_to_f64(scales[r * ng + i % ng]));"),
     "dequant_group_interleaved": ("(double)q[i] * kvqo_f16_to_f64(scales[r * ng + i / G]);",
                                   "(double)q[i] * kvqo_f16_to_f64(scales[r * ng + i % ng]);"),
     "unscale_multiplies": ("((double)s[j] / (double)lam[j]) * (acc * norm)",
@@ -44,6 +45,9 @@ MUTANTS = {
     "f16_truncates": ("double n = nearbyint((2.0 * m - 1.0) * 1024.0);",
                       "double n = floor((2.0 * m - 1.0) * 1024.0);"),
     "f16_subnormal_truncates": ("double n = nearbyint(ldexp(a, 24));", "double n = floor(ldexp(a, 24));"),
+    "int8_amax_over_128": ("kvqo_f64_to_f16(amax / 127.0)", "kvqo_f64_to_f16(amax / 128.0)"),
+    "int8_clamp_128": ("if (r > 127.0) r = 127.0;", "if (r > 128.0) r = 128.0;"),
+    "int8_truncates": ("double r = nearbyint(y / scale);\n    if (r > 127.0)", "double r = trunc(y / scale);\n    if (r > 127.0)"),
     "attend_no_max_shift": ("double w = exp(a[t] - amax);", "double w = exp(a[t]);"),
     "attend_scale_dropped": ("a[t] = scale * dot;", "a[t] = dot;"),
     "attend_values_from_keys": ("o[c] += w * vh[(int64_t)t * D + c];", "o[c] += w * kh[(int64_t)t * D + c];"),
@@ -74,6 +78,10 @@ BATTERY = [
     ("test_vq_encode_bruteforce", {"sub": 4, "K": 16}),
     ("test_vq_duplicate_centroids_lowest_index_and_exact_hits", {}),
     ("test_vq_decode_closed_form_and_roundtrip", {}),
+    ("test_int8_single_spike", {"D": 128}),
+    ("test_int8_ties_round_half_to_even_and_clamp", {}),
+    ("test_int8_quantizer_invariants", {"D": 128, "G": 32}),
+    ("test_int8_dequant_single_code_closed_form", {}),
     ("test_attend_single_token_returns_its_value", {}),
     ("test_attend_zero_query_is_mean_of_values", {}),
     ("test_attend_matches_torch_sdpa", {"R": 4}),
