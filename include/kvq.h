@@ -126,6 +126,25 @@ kvq_status kvq_dequantize(kvq_shape shape, kvq_view codes_u8, kvq_view scales_f1
                           const float* lambda, const int8_t* signs, int32_t group,
                           kvq_view out_f16, void* stream);
 
+/* int8 variant of kvq_quantize (gist.science summary, "Methodologie" s.2:
+ * the fused kernel rounds to signed int4 or int8): the same rotation and
+ * groups, scale = fp16_rne(amax / 127), q = clamp(rne(y / scale), -127, 127)
+ * with the stored scale, one two's-complement byte per coordinate (element i
+ * in byte i of the row).
+ *   codes_i8   output view of D-byte rows; 16-byte aligned data and strides.
+ * Everything else (shapes, lambda, signs, group, scales, errors) as for
+ * kvq_quantize. */
+kvq_status kvq_quantize_int8(kvq_shape shape, kvq_view x_f16, const float* lambda,
+                             const int8_t* signs, int32_t group, kvq_view codes_i8,
+                             kvq_view scales_f16, void* stream);
+
+/* Mirror of kvq_quantize_int8: code times its group scale, inverse
+ * Walsh-Hadamard, unscale, fp16.  Views as for kvq_dequantize, with D-byte
+ * code rows. */
+kvq_status kvq_dequantize_int8(kvq_shape shape, kvq_view codes_i8, kvq_view scales_f16,
+                               const float* lambda, const int8_t* signs, int32_t group,
+                               kvq_view out_f16, void* stream);
+
 /* Product-VQ encode (VecInfer blog, "What VecInfer does"; VeloxQuant-MLX
  * package description, "Metal kernels"): rotate as kvq_quantize does (no
  * group quantizer), split into D/sub_dim sub-vectors and store, per

@@ -66,6 +66,10 @@ def lib():
     L.kvq_quantize.argtypes = [Shape, View, P, P, I32, View, View, P]
     L.kvq_dequantize.restype = ctypes.c_int
     L.kvq_dequantize.argtypes = [Shape, View, View, P, P, I32, View, P]
+    L.kvq_quantize_int8.restype = ctypes.c_int
+    L.kvq_quantize_int8.argtypes = [Shape, View, P, P, I32, View, View, P]
+    L.kvq_dequantize_int8.restype = ctypes.c_int
+    L.kvq_dequantize_int8.argtypes = [Shape, View, View, P, P, I32, View, P]
     L.kvq_vq_encode.restype = ctypes.c_int
     L.kvq_vq_encode.argtypes = [Shape, View, P, P, P, I64, I32, I32, View, P]
     L.kvq_vq_decode.restype = ctypes.c_int
@@ -181,6 +185,40 @@ def append_quantize(x_tok, cache_codes, cache_scales, t: int, lam, signs, group:
     s = cache_scales[:, t:t + 1]
     quantize(x_tok, lam, signs, group, codes=c, scales=s, stream=stream)
     return c, s
+
+
+# ------------------------------------------------------------------ int8
+def quantize_int8(x, lam, signs, group: int, codes=None, scales=None, stream=None):
+    """int8 variant of quantize: x [L, T, H, D] fp16 -> (codes int8 [L, T, H, D],
+    scales fp16 [L, T, H, D/group])."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    L, T, H, D = x.shape
+    if codes is None:
+        codes = torch.empty((L, T, H, D), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((L, T, H, D // group), dtype=torch.float16, device=x.device)
+    _need(codes, torch.int8, "codes")
+    _need(scales, torch.float16, "scales")
+    pl, ps = _params(lam, signs, L, H, D)
+    _check(lib().kvq_quantize_int8(_shape(x, D), _view(x), pl, ps, int(group), _view(codes), _view(scales),
+                                   _stream(stream)))
+    return codes, scales
+
+
+def dequantize_int8(codes, scales, lam, signs, group: int, out=None, stream=None):
+    """Mirror of quantize_int8: (codes int8, scales) -> fp16 [L, T, H, D]."""
+    torch = _torch()
+    _need(codes, torch.int8, "codes")
+    _need(scales, torch.float16, "scales")
+    L, T, H, D = codes.shape
+    if out is None:
+        out = torch.empty((L, T, H, D), dtype=torch.float16, device=codes.device)
+    _need(out, torch.float16, "out")
+    pl, ps = _params(lam, signs, L, H, D)
+    _check(lib().kvq_dequantize_int8(_shape(codes, D), _view(codes), _view(scales), pl, ps, int(group), _view(out),
+                                     _stream(stream)))
+    return out
 
 
 # -------------------------------------------------------------------- VQ

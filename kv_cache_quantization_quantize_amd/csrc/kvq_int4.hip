@@ -34,9 +34,24 @@ namespace kvq {
 
 namespace {
 
-constexpr float kMagic8 = 12582920.0f;  // 1.5 * 2^23 + 8: fma(y, 1/scale, kMagic8)
-                                        // leaves 8 + rne(y/scale) in the low bits
-constexpr float kInv7 = 0.142857142857142857f;
+// fma(y, 1/scale, kMagic) with kMagic = 1.5 * 2^23 + Z leaves Z + rne(y/scale)
+// in the low bits (Z = 8 for int4 codes, 128 for int8 codes).
+template <int BITS>
+struct CodeFmt;
+template <>
+struct CodeFmt<4> {
+    static constexpr float kMagic = 12582920.0f;     // 1.5 * 2^23 + 8
+    static constexpr float kQmax = 7.0f;
+    static constexpr float kInvQmax = 0.142857142857142857f;
+    static constexpr uint32_t kFlip = 0x88888888u;   // offset binary <-> two's complement
+};
+template <>
+struct CodeFmt<8> {
+    static constexpr float kMagic = 12583040.0f;     // 1.5 * 2^23 + 128
+    static constexpr float kQmax = 127.0f;
+    static constexpr float kInvQmax = 0.00787401574803149606f;
+    static constexpr uint32_t kFlip = 0x80808080u;
+};
 
 // Byte k of the result = low byte of a_k (k = 0..3).
 __device__ __forceinline__ uint32_t gather_low_bytes(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3)
@@ -200,10 +215,12 @@ __device__ __forceinline__ void run_pipeline(int begin, int end, Load&& load, Fi
 //   2. issues the previous item's stores and the next item's loads,
 //   3. computes the rest of the current item,
 // and a scheduling barrier keeps step 2 between steps 1 and 3.
-template <int D, int G, bool TM>
+template <int D, int G, bool TM, int BITS>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args a)
 {
     using S = QuantShape<D, G>;
+    using F = CodeFmt<BITS>;
+    constexpr int WPJ = BITS / 4;        // code dwords per 8-coordinate chunk
     constexpr int NJ = S::NJ, N = S::N, NG = S::NG, LG = S::LG, CH_PER_G = S::CH_PER_G;
     // scale values a lane stores per vector
     constexpr int NSV = (G >= 32) ? (NG + 3) / 4 : NJ;
@@ -233,7 +250,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
     int cur_key = -1;
 
     struct Out {
-        uint32_t word[NJ];
+        uint32_t word[NJ * WPJ];
         uint16_t sv[NSV];
     };
 
@@ -255,28 +272,43 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
 
     // Code bytes are transposed within each quad through a wave-private LDS
     // tile so that every lane stores whole 16-byte chunks: code chunk c of a
-    // vector (bytes 16c..16c+15 = word c of lanes q = 0..3) goes to lane c % 4.
-    // Word j of lane (v, q) sits at v*D/2 + ((j ^ (v >> 2)) % NJ)*16 + q*4,
-    // which spreads a wave's 64 dword writes over distinct banks.
-    __shared__ uint32_t lds_codes[kWavesPerBlock][16 * D / 8];
+    // vector (bytes 16c..16c+15) goes to lane c % 4.  int4: chunk j is word j
+    // of lanes q = 0..3, and word j of lane (v, q) sits at
+    // v*D/8 + ((j ^ (v >> 2)) % NJ)*4 + q, which spreads a wave's 64 dword
+    // writes over distinct banks.  int8: lane q's 8 bytes of chunk position
+    // j are bytes 32j + 8q .. of the vector, i.e. half (q & 1) of 16-byte
+    // chunk 2j + (q >> 1); chunk c of vector v sits at v*CV8 + (c ^ (v % CV8)).
+    constexpr int CV8 = D / 16;                                   // int8 chunks per vector
+    constexpr int ROWW = BITS == 4 ? D / 8 : D / 4;               // code dwords per vector
+    __shared__ uint32_t lds_codes[kWavesPerBlock][16 * ROWW];
     uint32_t* my_codes = lds_codes[threadIdx.x >> 6];
-    constexpr int CPL = (NJ + 3) / 4;     // 16-byte code chunks each lane stores
+    constexpr int NCH = BITS == 4 ? NJ : CV8;                     // 16-byte code chunks per vector
+    constexpr int CPL = (NCH + 3) / 4;                            // chunks each lane stores
+    auto chunk_pos = [&](int v, int c) {                          // dword index of chunk c of vector v
+        if constexpr (BITS == 4) return v * ROWW + ((c ^ (v >> 2)) % NJ) * 4;
+        else return v * ROWW + (c ^ (v % CV8)) * 4;
+    };
 
     auto store = [&](int item, const Out& o) {
         const Item it = decode_item<TM>(item, a);
         uint8_t* cp = cg + outer_offset(a.codes, it) + c_lane_chunk;
         uint16_t* sp = sg + outer_offset(a.scales, it) + s_lane;
+        if constexpr (BITS == 4) {
 #pragma unroll
-        for (int j = 0; j < NJ; j++)
-            my_codes[slot * (D / 8) + ((j ^ (slot >> 2)) % NJ) * 4 + q] = o.word[j];
+            for (int j = 0; j < NJ; j++) my_codes[chunk_pos(slot, j) + q] = o.word[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < NJ; j++)
+                *reinterpret_cast<uint2*>(&my_codes[chunk_pos(slot, 2 * j + (q >> 1)) + 2 * (q & 1)]) =
+                    make_uint2(o.word[2 * j], o.word[2 * j + 1]);
+        }
         const bool ok = it.full || it.t0 + lm.tok < a.T;
 #pragma unroll
         for (int k = 0; k < CPL; k++) {
-            // lanes with q + 4k >= NJ (head_dim 64 only) read a valid slot and do not store
+            // lanes with q + 4k >= NCH (int4, head_dim 64 only) read a valid slot and do not store
             const int c = q + 4 * k;
-            const uint4 chunk =
-                *reinterpret_cast<const uint4*>(&my_codes[slot * (D / 8) + (((c % NJ) ^ (slot >> 2)) % NJ) * 4]);
-            if (ok && c < NJ) *reinterpret_cast<uint4*>(cp + 64 * k) = chunk;
+            const uint4 chunk = *reinterpret_cast<const uint4*>(&my_codes[chunk_pos(slot, c % NCH)]);
+            if (ok && c < NCH) *reinterpret_cast<uint4*>(cp + 64 * k) = chunk;
         }
         if (ok) {
             if constexpr (G >= 32) {
@@ -337,16 +369,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
         bool overflow = false;
 #pragma unroll
         for (int u = 0; u < LG; u++) {
-            const _Float16 h = (_Float16)(amax[u] * kInv7);
+            const _Float16 h = (_Float16)(amax[u] * F::kInvQmax);
             const float sc = (float)h;
             s16[u] = __builtin_bit_cast(uint16_t, h);
             const float r = sc > 0.0f ? __builtin_amdgcn_rcpf(sc) : 0.0f;
             inv[u] = lane_sign * r;
-            // only a subnormal scale can let |y|/scale reach 7.5 (a code of 8)
-            overflow |= amax[u] * r >= 7.5f;
+            // only a subnormal scale can let |y|/scale reach qmax + 1/2
+            overflow |= amax[u] * r >= F::kQmax + 0.5f;
         }
 
-        // codes: 8 + rne(y/scale) lands in the low byte of t; then nibble pack
+        // codes: Z + rne(y/scale) lands in the low byte of t; then nibble
+        // pack (int4) or byte pack (int8), back to two's complement
         auto encode = [&](auto clamp) {
 #pragma unroll
             for (int j = 0; j < NJ; j++) {
@@ -354,14 +387,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
                 uint32_t t[8];
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
-                    float f = fmaf(v[j * 8 + e], inv[u], kMagic8);
+                    float f = fmaf(v[j * 8 + e], inv[u], F::kMagic);
                     if constexpr (decltype(clamp)::value)
-                        f = __builtin_amdgcn_fmed3f(f, kMagic8 - 7.0f, kMagic8 + 7.0f);
+                        f = __builtin_amdgcn_fmed3f(f, F::kMagic - F::kQmax, F::kMagic + F::kQmax);
                     t[e] = __float_as_uint(f);
                 }
-                const uint32_t even = gather_low_bytes(t[0], t[2], t[4], t[6]);
-                const uint32_t odd = gather_low_bytes(t[1], t[3], t[5], t[7]);
-                o.word[j] = ((odd << 4) | even) ^ 0x88888888u;
+                if constexpr (BITS == 4) {
+                    const uint32_t even = gather_low_bytes(t[0], t[2], t[4], t[6]);
+                    const uint32_t odd = gather_low_bytes(t[1], t[3], t[5], t[7]);
+                    o.word[j] = ((odd << 4) | even) ^ F::kFlip;
+                } else {
+                    o.word[2 * j] = gather_low_bytes(t[0], t[1], t[2], t[3]) ^ F::kFlip;
+                    o.word[2 * j + 1] = gather_low_bytes(t[4], t[5], t[6], t[7]) ^ F::kFlip;
+                }
             }
         };
         if (__builtin_amdgcn_ballot_w64(overflow))
@@ -384,9 +422,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
 // ---------------------------------------------------------------------------
 // Dequantize
 // ---------------------------------------------------------------------------
-template <int D, int G, bool TM>
+template <int D, int G, bool TM, int BITS>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Args a)
 {
+    constexpr int WPJ = BITS / 4;        // code dwords per 8-coordinate chunk
     constexpr int NJ = D / 32;
     constexpr int N = NJ * 8;
     constexpr int NG = D / G;
@@ -408,7 +447,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
     const uint8_t* __restrict__ cg = static_cast<const uint8_t*>(a.codes.data);
     const uint16_t* __restrict__ sg = static_cast<const uint16_t*>(a.scales.data);
     const LaneMap lm = lane_map<TM>(slot, a);
-    const int64_t c_lane = (int64_t)lm.tok * a.codes.st + (int64_t)lm.head * a.codes.sh + q * 4;
+    const int64_t c_lane = (int64_t)lm.tok * a.codes.st + (int64_t)lm.head * a.codes.sh + q * 4 * WPJ;
     const int64_t s_lane = (int64_t)lm.tok * a.scales.st + (int64_t)lm.head * a.scales.sh;
 
     float m[N];
@@ -417,7 +456,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
     // Raw inputs of one item: the lane's NJ code words and its vector's whole
     // scale row as packed 32-bit words.
     struct Raw {
-        uint32_t w[NJ];
+        uint32_t w[NJ * WPJ];
         uint32_t sw[NW];
     };
     struct Out {
@@ -429,8 +468,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
         const uint8_t* cp = cg + outer_offset(a.codes, it) + c_lane;
         const uint16_t* sp = sg + outer_offset(a.scales, it) + s_lane;
         auto ld = [&]() {
+            if constexpr (BITS == 4) {
 #pragma unroll
-            for (int j = 0; j < NJ; j++) raw.w[j] = *reinterpret_cast<const uint32_t*>(cp + j * 16);
+                for (int j = 0; j < NJ; j++) raw.w[j] = *reinterpret_cast<const uint32_t*>(cp + j * 16);
+            } else {
+#pragma unroll
+                for (int j = 0; j < NJ; j++) {
+                    const uint2 d = *reinterpret_cast<const uint2*>(cp + j * 32);
+                    raw.w[2 * j] = d.x;
+                    raw.w[2 * j + 1] = d.y;
+                }
+            }
             if constexpr (NG == 1) {
                 raw.sw[0] = sp[0];
             } else {
@@ -445,7 +493,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
             ld();
         } else {
 #pragma unroll
-            for (int j = 0; j < NJ; j++) raw.w[j] = 0x88888888u;   // offset-binary 8 = code 0
+            for (int j = 0; j < NJ * WPJ; j++) raw.w[j] = 0u;      // code 0
 #pragma unroll
             for (int i = 0; i < NW; i++) raw.sw[i] = 0;
             if (it.t0 + lm.tok < a.T) ld();
@@ -513,6 +561,23 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
 #pragma unroll
         for (int j = 0; j < NJ; j++) {
             const float sc = chunk_scale(raw, j);
+            if constexpr (BITS == 8) {
+                // offset-binary bytes u = q + 128 of the pair (2k, 2k+1):
+                // yhat_2k + yhat_2k+1 = sc * (u0 + u1 - 256), difference sc * (u0 - u1)
+                const float off8 = -256.0f * sc;
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const uint32_t wb = raw.w[2 * j + h] ^ 0x80808080u;
+#pragma unroll
+                    for (int k = 0; k < 2; k++) {
+                        const float u0 = (float)((wb >> (16 * k)) & 0xffu);
+                        const float u1 = (float)((wb >> (16 * k + 8)) & 0xffu);
+                        v[j * 8 + 4 * h + 2 * k] = fmaf(u0 + u1, sc, off8);
+                        v[j * 8 + 4 * h + 2 * k + 1] = (u0 - u1) * sc;
+                    }
+                }
+                continue;
+            }
             const float off = -16.0f * sc;
             const uint32_t wb = raw.w[j] ^ 0x88888888u;
             const uint32_t lo = wb & 0x0f0f0f0fu;            // n of elements 0,2,4,6
@@ -549,20 +614,26 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int D, int G>
-hipError_t launch_q(const Int4Args& a, hipStream_t s, bool inverse)
+template <int D, int G, int BITS>
+hipError_t launch_qb(const Int4Args& a, hipStream_t s, bool inverse)
 {
     const int64_t waves = (a.n_items + a.items_per_wave - 1) / a.items_per_wave;
     const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
     const dim3 block(64 * kWavesPerBlock);
     if (inverse) {
-        if (a.token_major) hipLaunchKernelGGL((dequantize_kernel<D, G, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((dequantize_kernel<D, G, false>), grid, block, 0, s, a);
+        if (a.token_major) hipLaunchKernelGGL((dequantize_kernel<D, G, true, BITS>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((dequantize_kernel<D, G, false, BITS>), grid, block, 0, s, a);
     } else {
-        if (a.token_major) hipLaunchKernelGGL((quantize_kernel<D, G, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((quantize_kernel<D, G, false>), grid, block, 0, s, a);
+        if (a.token_major) hipLaunchKernelGGL((quantize_kernel<D, G, true, BITS>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((quantize_kernel<D, G, false, BITS>), grid, block, 0, s, a);
     }
     return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_q(const Int4Args& a, hipStream_t s, bool inverse)
+{
+    return a.bits == 8 ? launch_qb<D, G, 8>(a, s, inverse) : launch_qb<D, G, 4>(a, s, inverse);
 }
 
 template <int D>

@@ -46,14 +46,15 @@ def check_scales(sc_gpu, sc_ora):
             "max_rel": float(rel.max()) if rel.size else 0.0, "bad_mask": bad}
 
 
-def check_codes(y64, sc_gpu, q_gpu, G):
-    """y64 [n, D] exact rotated values; sc_gpu [n, D/G] fp16 bits; q_gpu [n, D] int8."""
-    q_cond = oracle.codes_given_scales(y64, sc_gpu, G)
+def check_codes(y64, sc_gpu, q_gpu, G, qmax=7):
+    """y64 [n, D] exact rotated values; sc_gpu [n, D/G] fp16 bits; q_gpu [n, D]
+    int8 codes of a quantizer with levels -qmax..qmax (7: int4, 127: int8)."""
+    q_cond = (oracle.codes_given_scales if qmax == 7 else oracle.codes8_given_scales)(y64, sc_gpu, G)
     s = np.repeat(f16(sc_gpu), G, axis=1)
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.where(s > 0, y64 / np.where(s > 0, s, 1), 0.0)
     dist = np.abs(r - (np.floor(r) + 0.5))          # distance to the nearest half-integer
-    near = (dist < BOUNDARY) & (np.abs(r) < 7.5)
+    near = (dist < BOUNDARY) & (np.abs(r) < qmax + 0.5)
     diff = q_gpu.astype(np.int32) - q_cond.astype(np.int32)
     ok = (diff == 0) | ((np.abs(diff) == 1) & near)
     return {"n": int(diff.size), "exact": int((diff == 0).sum()), "boundary": int(((diff != 0) & ok).sum()),
@@ -151,5 +152,38 @@ def vq_parity(x_bits, lam_rows, signs, codebooks_bits, book, sub, idx_gpu, out_g
         if rd["bad"]:
             i = np.argwhere(rd["bad_mask"])[:5]
             _raise("vq decode", rd, "first bad [key, coord]: %s gpu=%s ora=%s" % (
+                i.tolist(), f16(out_gpu)[tuple(i.T)], x64[tuple(i.T)]))
+    return rep
+
+
+def int8_parity(x_bits, lam_rows, signs, G, codes_gpu, scales_gpu, out_gpu=None):
+    """int8 variant of int4_parity: codes_gpu [n, D] int8 (one byte per
+    coordinate), same scale / code / dequant contract with 127 levels."""
+    x_bits = np.ascontiguousarray(x_bits, np.uint16)
+    lam_rows = np.ascontiguousarray(lam_rows, np.float32)
+    codes_o, scales_o, y64, nbad = oracle.quantize8(x_bits, lam_rows, signs, G)
+    if nbad:
+        raise ParityError("%d input vectors are outside the quantizer's domain" % nbad)
+    rep = {}
+    rs = check_scales(scales_gpu, scales_o)
+    rep["scales"] = rs
+    if rs["bad"]:
+        i = np.argwhere(rs["bad_mask"])[:5]
+        _raise("int8 scale", rs, "first bad [row, group]: %s gpu=%s ora=%s" % (
+            i.tolist(), f16(scales_gpu)[tuple(i.T)], f16(scales_o)[tuple(i.T)]))
+    q_gpu = np.ascontiguousarray(codes_gpu).view(np.int8)
+    rc = check_codes(y64, scales_gpu, q_gpu, G, qmax=127)
+    rep["codes"] = rc
+    if rc["bad"]:
+        i = np.argwhere(rc["bad_mask"])[:5]
+        _raise("int8 code", rc, "first bad [row, coord]: %s gpu=%s ora=%s" % (
+            i.tolist(), q_gpu[tuple(i.T)], rc["q_cond"][tuple(i.T)]))
+    if out_gpu is not None:
+        x64, _ = oracle.dequantize8(q_gpu, scales_gpu, lam_rows, signs, G)
+        rd = check_dequant(out_gpu, x64, lam_rows)
+        rep["dequant"] = rd
+        if rd["bad"]:
+            i = np.argwhere(rd["bad_mask"])[:5]
+            _raise("int8 dequant", rd, "first bad [row, coord]: %s gpu=%s ora=%s" % (
                 i.tolist(), f16(out_gpu)[tuple(i.T)], x64[tuple(i.T)]))
     return rep

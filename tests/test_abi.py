@@ -33,7 +33,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "kvq_quantize", "kvq_dequantize", "kvq_vq_encode", "kvq_vq_decode",
-        "kvq_attend_decode", "kvq_attend_decode_workspace",
+        "kvq_attend_decode", "kvq_attend_decode_workspace", "kvq_quantize_int8", "kvq_dequantize_int8",
         "kvq_status_string", "kvq_last_error", "kvq_version"])
 
 
@@ -198,3 +198,17 @@ def test_attend_validation(lib):
     assert att(lib, ws=A + 4) == ALIGN
     st, need = ws_bytes(lib, shape(), 4)
     assert att(lib, ws_bytes_=need - 1) == SHAPE
+
+
+def test_int8_validation(lib):
+    sh = shape()
+    x = view(row=128)
+    codes = view(row=128)
+    scales = view(row=4)
+    A_ = ctypes.c_void_p(A)
+    assert lib.kvq_quantize_int8(sh, x, A_, A_, 32, view(addr=0, row=128), scales, None) == NULL
+    assert b"codes_i8" in lib.kvq_last_error()
+    # int8 rows are D bytes: a stride of D/2 is too small
+    assert lib.kvq_quantize_int8(sh, x, A_, A_, 32, view(row=64), scales, None) == SHAPE
+    assert lib.kvq_dequantize_int8(shape(0, 5, 3), codes, scales, A_, A_, 32, x, None) == OK
+    assert lib.kvq_dequantize_int8(sh, codes, scales, A_, A_, 24, x, None) == UNSUP
