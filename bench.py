@@ -122,6 +122,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-vq", action="store_true")
     ap.add_argument("--no-attend", action="store_true")
+    ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--attend-seqs", type=int, default=8,
                     help="sequences the int4 cache's token axis is split into for the decode-attention leg")
     ap.add_argument("--cpu-tokens", type=int, default=192, help="tokens per (layer, head) in the CPU sample")
@@ -227,6 +228,10 @@ def main():
     del outs
     torch.cuda.empty_cache()
 
+    int8 = None
+    if not args.no_int8:
+        int8 = bench_int8(torch, kvq, K, lamK, signs, (L, T, H, D, G), args)
+
     attend = None
     if not args.no_attend:
         attend = bench_attend(torch, kvq, codes, scales, lamK, lamV, signs, (L, T, H, D, G), args)
@@ -259,9 +264,48 @@ def main():
         "copy_ceiling_GB_per_s": copy_gbps,
         "vq": vq,
         "attend": attend,
+        "int8": int8,
         "frac_of_hbm_peak_step": round(value / HBM_PEAK_GBPS, 4),
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_int8(torch, kvq, K, lamK, signs, dims, args):
+    """Time the int8 variant (quantize, then dequantize) on the K cache."""
+    L, T, H, D, G = dims
+    codes = torch.empty((L, T, H, D), dtype=torch.int8, device=K.device)
+    scales = torch.empty((L, T, H, D // G), dtype=torch.float16, device=K.device)
+    out = torch.empty_like(K)
+    stream = torch.cuda.current_stream()
+    kvq.quantize_int8(K, lamK, signs, G, codes=codes, scales=scales, stream=stream)
+    kvq.dequantize_int8(codes, scales, lamK, signs, G, out=out, stream=stream)
+    torch.cuda.synchronize()
+    ev = {"quantize": [], "dequantize": []}
+    for _ in range(max(3, min(args.steps, 10))):
+        for name, fn in (("quantize", lambda: kvq.quantize_int8(K, lamK, signs, G, codes=codes, scales=scales,
+                                                                 stream=stream)),
+                         ("dequantize", lambda: kvq.dequantize_int8(codes, scales, lamK, signs, G, out=out,
+                                                                     stream=stream))):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev[name].append((a, b))
+    torch.cuda.synchronize()
+    nvec = L * T * H
+    bpv = 2 * D + D + 2 * (D // G)
+    res = {"workload": "qwen3-8b-shaped K cache [%d, %d, %d, %d], group %d, int8 codes" % (L, T, H, D, G),
+           "bytes_per_vector": bpv}
+    for name, pairs in ev.items():
+        ms = [a.elapsed_time(b) for a, b in pairs]
+        avg = sum(ms) / len(ms)
+        gbps = nvec * bpv / (avg * 1e-3) / 1e9
+        res[name] = {"avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "GB_per_s": round(gbps, 1),
+                     "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                     "ns_per_vector": round(avg * 1e6 / nvec, 5)}
+    del codes, scales, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_attend(torch, kvq, codes, scales, lamK, lamV, signs, dims, args):

@@ -389,6 +389,7 @@ kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f1
     a.S = p.S;
     a.chunk = p.chunk;
     a.parts = p.parts;
+    a.xcd_map = ((int64_t)a.L * a.S) % 8 == 0;
     a.q = static_cast<const _Float16*>(q_f16);
     a.out = static_cast<_Float16*>(out_f16);
     a.kc = t4(k_codes_u8);

@@ -90,10 +90,28 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
 
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
-    const int lh = uniform((int)(blockIdx.x / a.S));
-    const int split = (int)blockIdx.x - lh * a.S;
-    const int l = uniform(lh / a.H);
-    const int h = lh - l * a.H;
+    // Block -> (outer index l, split, KV head h).  The heads of one (l, split)
+    // read interleaved rows of the same cache lines ([T, H, D/2] codes,
+    // [T, H, D/G] scales), so when the (l, split) count is a multiple of the
+    // 8 XCDs (blocks go to XCDs round-robin by index) they are given
+    // consecutive block indices of one XCD and share its L2.
+    int l, h, split;
+    {
+        const int b = blockIdx.x;
+        int u;
+        if (a.xcd_map) {
+            const int k = b >> 3;
+            u = ((k / a.H) << 3) + (b & 7);
+            h = k - (k / a.H) * a.H;
+        } else {
+            u = b / a.H;
+            h = b - u * a.H;
+        }
+        l = uniform(u / a.S);
+        split = u - l * a.S;
+        h = uniform(h);
+    }
+    const int lh = l * a.H + h;
     const int r0 = blockIdx.y * RP;
     const int n = a.lengths ? min(max(a.lengths[l], 0), a.T) : a.T;
 

@@ -72,6 +72,7 @@ struct AttnArgs {
     int32_t S;                      // token splits per (outer index, KV head)
     int32_t chunk;                  // tokens per split
     int32_t parts;                  // partial states per (outer index, query head)
+    int32_t xcd_map;                // (L*S) % 8 == 0: heads of one (l, split) on one XCD
     const _Float16* q;              // [L, H*R, D]
     _Float16* out;                  // [L, H*R, D]
     Tensor4 kc, ks, vc, vs;         // codes u8 (D/2), scales fp16 (D/G)
