@@ -83,16 +83,39 @@ def cpu_baseline(K, V, lamK, lamV, signs, G, n_tokens: int):
     x = np.concatenate(xs)
     lam = np.ascontiguousarray(np.concatenate(ls), np.float32)
     s = signs.cpu().numpy()
-    t = time.perf_counter()
-    codes, scales, _, _ = oracle.quantize(x, lam, s, G)
-    oracle.dequantize(codes, scales, lam, s, G)
-    dt = time.perf_counter() - t
+    # one core: the oracle is single-threaded; pin it so that the figure is a
+    # one-core rate whatever the host's load
+    try:
+        saved = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(saved)})
+    except (AttributeError, OSError):
+        saved = None
+    try:
+        t = time.perf_counter()
+        codes, scales, _, _ = oracle.quantize(x, lam, s, G)
+        oracle.dequantize(codes, scales, lam, s, G)
+        dt = time.perf_counter() - t
+    finally:
+        if saved is not None:
+            os.sched_setaffinity(0, saved)
     n = x.shape[0]
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(2 * n * bytes_per_vector(D, G) / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": "%d vectors (36 layers x 8 heads x %d tokens, K and V) quantize+dequantize, "
-                      "single-threaded fp64, %.1f s" % (n, n_tokens, dt),
-            "ns_per_vector": round(dt / n * 1e9, 1)}
+                      "single-threaded fp64 pinned to one core, %.1f s" % (n, n_tokens, dt),
+            "ns_per_vector": round(dt / n * 1e9, 1),
+            "vectors_per_s": round(n / dt, 1),
+            "extrapolated_step_s": round(dt / n * 2 * L * T * H, 1),
+            "cpu_model": cpu, "host_cpus": os.cpu_count()}
 
 
 def copy_ceiling(torch, nbytes: int, reps: int = 5):
@@ -123,6 +146,7 @@ def main():
     ap.add_argument("--no-vq", action="store_true")
     ap.add_argument("--no-attend", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
+    ap.add_argument("--no-small", action="store_true", help="skip the Qwen2.5 / Gemma cache timings")
     ap.add_argument("--attend-seqs", type=int, default=8,
                     help="sequences the int4 cache's token axis is split into for the decode-attention leg")
     ap.add_argument("--cpu-tokens", type=int, default=192, help="tokens per (layer, head) in the CPU sample")
@@ -245,6 +269,10 @@ def main():
     if not args.no_vq:
         vq = bench_vq(torch, kvq, synth, dev, args)
 
+    small = None
+    if not args.no_small:
+        small = bench_small(torch, kvq, synth, dev, args)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(K, V, lamK, lamV, signs, G, args.cpu_tokens)
@@ -265,9 +293,77 @@ def main():
         "vq": vq,
         "attend": attend,
         "int8": int8,
+        "small_workloads": small,
         "frac_of_hbm_peak_step": round(value / HBM_PEAK_GBPS, 4),
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_small(torch, kvq, synth, dev, args):
+    """The pages' smaller caches: quantize + dequantize of Qwen2.5-1.5B- and
+    Gemma-3-1B-shaped K/V caches, warm (the tensors fit in the 256 MB
+    Infinity Cache) and after a 1 GB scrub, plus the Gemma decode append (one
+    token per layer, K and V) as a latency."""
+    stream = torch.cuda.current_stream()
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    res = {}
+
+    def timed(fn, reps, do_scrub):
+        ms = []
+        for _ in range(reps):
+            if do_scrub:
+                scrub.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        ms.sort()
+        return ms[len(ms) // 2]
+
+    for name, T in (("qwen2.5-1.5b", None), ("gemma-3-1b", 4096)):
+        cfg = synth.config(name, T=T) if T else synth.config(name)
+        inp = synth.make_inputs(cfg, dev)
+        L, T, H, D, G = cfg.L, cfg.T, cfg.H, cfg.D, cfg.G
+        nvec = L * T * H
+        byt = nvec * bytes_per_vector(D, G)
+        r = {"shape": [L, T, H, D], "group": G}
+        for t in ("K", "V"):
+            x, lam = inp[t], inp["lam_" + t]
+            codes, scales = kvq.quantize(x, lam, inp["signs"], G, stream=stream)
+            out = torch.empty_like(x)
+            for mode in ("warm", "scrubbed"):
+                qms = timed(lambda: kvq.quantize(x, lam, inp["signs"], G, codes=codes, scales=scales, stream=stream),
+                            10, mode == "scrubbed")
+                dms = timed(lambda: kvq.dequantize(codes, scales, lam, inp["signs"], G, out=out, stream=stream),
+                            10, mode == "scrubbed")
+                r["%s_%s" % (t, mode)] = {"quantize_us": round(qms * 1e3, 2), "dequantize_us": round(dms * 1e3, 2),
+                                          "quantize_GB_per_s": round(byt / (qms * 1e-3) / 1e9, 1),
+                                          "dequantize_GB_per_s": round(byt / (dms * 1e-3) / 1e9, 1)}
+        if name == "gemma-3-1b":
+            # decode append: layer by layer, K then V, one token into slot T - 1
+            caches = {t: kvq.quantize(inp[t], inp["lam_" + t], inp["signs"], G, stream=stream) for t in ("K", "V")}
+            tok = {t: inp[t][:, T - 1:T].contiguous() for t in ("K", "V")}
+            lam1 = {t: [inp["lam_" + t][l:l + 1].contiguous() for l in range(L)] for t in ("K", "V")}
+
+            def step():
+                for l in range(L):
+                    for t in ("K", "V"):
+                        c, sc = caches[t]
+                        kvq.quantize(tok[t][l:l + 1], lam1[t][l], inp["signs"], G, codes=c[l:l + 1, T - 1:T],
+                                     scales=sc[l:l + 1, T - 1:T], stream=stream)
+            step()
+            torch.cuda.synchronize()
+            sms = timed(step, 10, False)
+            r["decode_append"] = {"us_per_layer_K_and_V": round(sms * 1e3 / L, 2), "us_per_step": round(sms * 1e3, 1),
+                                  "layers": L, "note": "two launches per layer; launch-bound"}
+        res[name] = r
+        del inp
+        torch.cuda.empty_cache()
+    del scrub
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_int8(torch, kvq, K, lamK, signs, dims, args):
