@@ -68,6 +68,10 @@ def bind(path: str):
         "kvqo_codes8_given_scales": (I32, [I64, I32, I32, P, P, P]),
         "kvqo_quantize8_rows": (I64, [I64, I32, I32, P, P, P, P, P, P]),
         "kvqo_dequantize8_rows": (I32, [I64, I32, I32, P, P, P, P, P, P]),
+        "kvqo_e2m1_value": (ctypes.c_double, [I32]),
+        "kvqo_quantize_mxfp4_rows": (I64, [I64, I32, P, P, P, P, P, P]),
+        "kvqo_mxfp4_codes_given_scales": (I32, [I64, I32, P, P, P]),
+        "kvqo_dequantize_mxfp4_rows": (I32, [I64, I32, P, P, P, P, P, P]),
         "kvqo_attend_decode": (I32, [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P,
                                      ctypes.c_double, P]),
     }
@@ -318,4 +322,50 @@ def dequantize8(codes, scales_bits, lam, signs, G):
     x16, p16 = _out((n, D), np.uint16)
     if _load().kvqo_dequantize8_rows(n, D, int(G), pc, psc, pl, ps, p64, p16):
         raise ValueError("oracle dequantize8 rejected its arguments")
+    return x64, x16
+
+
+# ----------------------------------------------------------------- MXFP4
+def e2m1_value(code: int) -> float:
+    return float(_load().kvqo_e2m1_value(int(code)))
+
+
+def quantize_mxfp4(x_bits, lam, signs):
+    """Block-scaled E2M1: x [n, D] binary16 bits -> (codes u8 [n, D/2] packed
+    nibbles, E8M0 scales u8 [n, D/32], y fp64 [n, D], vectors out of domain)."""
+    x, px = _c(x_bits, np.uint16)
+    n, D = x.shape
+    lam, pl = _c(np.broadcast_to(lam, (n, D)), np.float32)
+    s, ps = _c(signs, np.int8)
+    codes, pc = _out((n, D // 2), np.uint8)
+    scales, psc = _out((n, D // 32), np.uint8)
+    y, py = _out((n, D), np.float64)
+    bad = _load().kvqo_quantize_mxfp4_rows(n, D, px, pl, ps, pc, psc, py)
+    if bad < 0:
+        raise ValueError("oracle quantize_mxfp4 rejected its arguments")
+    return codes, scales, y, int(bad)
+
+
+def mxfp4_codes_given_scales(y, scales):
+    """E2M1 codes (one per byte) of rotated values y [n, D] under E8M0 scales."""
+    yy, py = _c(y, np.float64)
+    n, D = yy.shape
+    sc, ps = _c(scales, np.uint8)
+    q, pq = _out((n, D), np.uint8)
+    if _load().kvqo_mxfp4_codes_given_scales(n, D, py, ps, pq):
+        raise ValueError("head_dim must be a multiple of 32")
+    return q
+
+
+def dequantize_mxfp4(codes, scales, lam, signs):
+    c, pc = _c(codes, np.uint8)
+    n, half = c.shape
+    D = 2 * half
+    sc, psc = _c(scales, np.uint8)
+    lam, pl = _c(np.broadcast_to(lam, (n, D)), np.float32)
+    s, ps = _c(signs, np.int8)
+    x64, p64 = _out((n, D), np.float64)
+    x16, p16 = _out((n, D), np.uint16)
+    if _load().kvqo_dequantize_mxfp4_rows(n, D, pc, psc, pl, ps, p64, p16):
+        raise ValueError("oracle dequantize_mxfp4 rejected its arguments")
     return x64, x16

@@ -28,6 +28,10 @@
  *             Samenvatting" -> "Methodologie" sections 1 (sign-randomized
  *             transform), 2 (fused kernel step list), 3 (per-channel plus
  *             per-group scaling).
+ *  [POLAR]    PolarQuant / block-FP4 abstract (Apple M5 Max): names block-scaled
+ *             E2M1 FP4 as a KV-cache format; the format is taken as the OCP
+ *             Microscaling (MX) v1.0 MXFP4 definition (32-element blocks,
+ *             E8M0 power-of-two scale, E2M1 elements).
  *  [SCALAR-ATTEND] VeloxQuant-MLX 0.52.0 package description, section
  *             "Fused group-affine (KIVI-style) attention": single-query decode
  *             attention straight from group-quantized codes, online softmax
@@ -384,6 +388,128 @@ int kvqo_dequantize8_rows(int64_t n, int D, int G, const int8_t* codes,
     for (int64_t r = 0; r < n; r++) {
         for (int i = 0; i < D; i++)
             yh[i] = (double)codes[r * D + i] * kvqo_f16_to_f64(scales[r * ng + i / G]);
+        unrotate_one(D, yh, lam + r * D, s, xhat64 + r * D);
+        if (xhat16)
+            for (int j = 0; j < D; j++)
+                xhat16[r * D + j] = kvqo_f64_to_f16(xhat64[r * D + j]);
+    }
+    free(yh);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block-scaled E2M1 (MXFP4) variant [POLAR: "block-scaled E2M1 FP4";         */
+/* the format itself as the OCP Microscaling (MX) v1.0 definition]            */
+/* ------------------------------------------------------------------------ */
+
+/* E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; exponent 0
+   is subnormal (mantissa * 0.5).  Magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6. */
+double kvqo_e2m1_value(int code)
+{
+    int e = (code >> 1) & 3, m = code & 1;
+    double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (code & 8) ? -mag : mag;
+}
+
+/* Nearest E2M1 code of v, ties to the even code (mantissa bit 0), magnitudes
+   above 6 saturating to 6; the sign bit is v's sign bit (so -0 -> 0x8). */
+static int e2m1_code(double v)
+{
+    double a = fabs(v);
+    int mag;
+    if (a >= 6.0) {
+        mag = 7;
+    } else {
+        mag = 0;
+        while (mag < 7 && kvqo_e2m1_value(mag + 1) <= a) mag++;
+        double lo = kvqo_e2m1_value(mag), hi = kvqo_e2m1_value(mag + 1);
+        if (a - lo > hi - a || (a - lo == hi - a && (mag & 1))) mag++;
+    }
+    return (signbit(v) ? 8 : 0) | mag;
+}
+
+/* Shared block exponent of a 32-element block with abs-max amax:
+   floor(log2(amax)) - 2 (the largest E2M1 exponent), clamped to
+   [-127, 127]; -127 for an all-zero block.  Stored as E8M0: e + 127. */
+static int mx_exponent(double amax)
+{
+    if (amax == 0.0) return -127;
+    int E;
+    frexp(amax, &E);                 /* amax = f * 2^E, f in [0.5, 1) */
+    int e = (E - 1) - 2;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* Quantize n vectors: same rotation as the int4 quantizer, then blocks of 32
+   rotated coordinates: X = 2^e with e = mx_exponent(amax), code_i =
+   e2m1_code(y_i / X).  codes [n, D/2] packed like the int4 nibbles (element
+   2k in the low nibble of byte k); scales [n, D/32] E8M0 bytes (e + 127).
+   Returns the number of vectors outside the domain (non-finite input),
+   zeroed. */
+int64_t kvqo_quantize_mxfp4_rows(int64_t n, int D, const uint16_t* x, const float* lam,
+                                 const int8_t* s, uint8_t* codes, uint8_t* scales, double* y_out)
+{
+    if (!is_pow2(D) || D < 32) return -1;
+    int nb = D / 32;
+    double* v = (double*)malloc(sizeof(double) * (size_t)D);
+    double* y = (double*)malloc(sizeof(double) * (size_t)D);
+    int8_t* q = (int8_t*)malloc((size_t)D);
+    int64_t bad = 0;
+    for (int64_t r = 0; r < n; r++) {
+        int ok = 1;
+        for (int j = 0; j < D; j++)
+            if (!isfinite(kvqo_f16_to_f64(x[r * D + j]))) ok = 0;
+        if (!ok) {
+            bad++;
+            memset(codes + r * (D / 2), 0, (size_t)(D / 2));
+            memset(scales + r * nb, 0, (size_t)nb);
+            if (y_out) for (int i = 0; i < D; i++) y_out[r * D + i] = NAN;
+            continue;
+        }
+        rotate_one(D, x + r * D, lam + r * D, s, v, y);
+        for (int b = 0; b < nb; b++) {
+            double amax = 0.0;
+            for (int i = 32 * b; i < 32 * (b + 1); i++)
+                if (fabs(y[i]) > amax) amax = fabs(y[i]);
+            int e = mx_exponent(amax);
+            scales[r * nb + b] = (uint8_t)(e + 127);
+            for (int i = 32 * b; i < 32 * (b + 1); i++) q[i] = (int8_t)e2m1_code(ldexp(y[i], -e));
+        }
+        for (int k = 0; k < D / 2; k++)
+            codes[r * (D / 2) + k] = (uint8_t)((q[2 * k] & 0xf) | ((q[2 * k + 1] & 0xf) << 4));
+        if (y_out) memcpy(y_out + r * D, y, sizeof(double) * (size_t)D);
+    }
+    free(v); free(y); free(q);
+    return bad;
+}
+
+/* E2M1 codes [n, D] (one per byte, low nibble) of rotated values y [n, D]
+   under given E8M0 block scales [n, D/32]. */
+int kvqo_mxfp4_codes_given_scales(int64_t n, int D, const double* y, const uint8_t* scales, uint8_t* q)
+{
+    if (D % 32) return -1;
+    int nb = D / 32;
+    for (int64_t r = 0; r < n; r++)
+        for (int i = 0; i < D; i++)
+            q[r * D + i] = (uint8_t)e2m1_code(ldexp(y[r * D + i], -((int)scales[r * nb + i / 32] - 127)));
+    return 0;
+}
+
+/* Dequantize: yhat_i = 2^(scale_b - 127) * value(code_i), then unrotate. */
+int kvqo_dequantize_mxfp4_rows(int64_t n, int D, const uint8_t* codes, const uint8_t* scales,
+                               const float* lam, const int8_t* s, double* xhat64, uint16_t* xhat16)
+{
+    if (!is_pow2(D) || D < 32) return -1;
+    int nb = D / 32;
+    double* yh = (double*)malloc(sizeof(double) * (size_t)D);
+    for (int64_t r = 0; r < n; r++) {
+        for (int i = 0; i < D; i++) {
+            int byte = codes[r * (D / 2) + i / 2];
+            int c = (i & 1) ? (byte >> 4) & 0xf : byte & 0xf;
+            yh[i] = ldexp(kvqo_e2m1_value(c), (int)scales[r * nb + i / 32] - 127);
+        }
         unrotate_one(D, yh, lam + r * D, s, xhat64 + r * D);
         if (xhat16)
             for (int j = 0; j < D; j++)

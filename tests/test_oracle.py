@@ -589,3 +589,108 @@ def test_int8_roundtrip_error_bound_and_finer_than_int4(D, G):
     err4 = np.linalg.norm(lam * (x4 - bits_to_f64(x)), axis=1)
     # 127 levels against 7: the error shrinks by about 127/7 on average
     assert err8.mean() * 10 < err4.mean()
+
+
+# -------------------------------------------------------------------- MXFP4
+def e2m1_golden(golden_dir):
+    out = {}
+    for line in open(os.path.join(golden_dir, "e2m1.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            c, v = line.split()
+            out[int(c, 16)] = float(v)
+    return out
+
+
+def test_e2m1_table_golden(golden_dir):
+    table = e2m1_golden(golden_dir)
+    assert len(table) == 16
+    for c, v in table.items():
+        got = oracle.e2m1_value(c)
+        assert got == v and np.signbit(got) == np.signbit(v), (c, got, v)
+
+
+def test_e2m1_rounding_ties_even_and_saturation(golden_dir):
+    # with scale byte 127 (X = 1) the codes are the E2M1 rounding of y itself
+    table = e2m1_golden(golden_dir)
+    mags = sorted(v for c, v in table.items() if c < 8)
+    cases = []
+    for lo, hi in zip(mags[:-1], mags[1:]):
+        mid = (lo + hi) / 2
+        even = min((c for c in range(8) if table[c] in (lo, hi)), key=lambda c: c & 1)   # mantissa bit 0
+        cases += [(mid, table[even]), (np.nextafter(mid, 0), lo), (np.nextafter(mid, 10), hi), (lo, lo)]
+    cases += [(6.0, 6.0), (6.5, 6.0), (7.0, 6.0), (1e30, 6.0), (0.0, 0.0)]
+    y = np.array([[v for v, _ in cases] + [-v for v, _ in cases]])
+    y = np.pad(y, ((0, 0), (0, (-y.shape[1]) % 32)))
+    q = oracle.mxfp4_codes_given_scales(y, np.full((1, y.shape[1] // 32), 127, np.uint8))[0]
+    got = [table[c] for c in q[:2 * len(cases)]]
+    want = [w for _, w in cases] + [-w for _, w in cases]
+    assert got == want
+    # the sign bit follows the input's, -0 included
+    assert all(np.signbit(g) == np.signbit(yv) for g, yv in zip(got, y[0]))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_mxfp4_block_scale_rule_and_invariants(D, golden_dir):
+    table = e2m1_golden(golden_dir)
+    n = 300
+    x = rand_x(n, D, 2.0)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    codes, scales, y, bad = oracle.quantize_mxfp4(x, lam, s)
+    assert bad == 0
+    _, _, y4, _ = oracle.quantize(x, lam, s, 32)
+    assert np.array_equal(y, y4)                                    # the int4 path's rotation
+    e = scales.astype(np.int64) - 127
+    amax = np.abs(y).reshape(n, D // 32, 32).max(axis=2)
+    r = amax / np.exp2(e)
+    assert ((r >= 4) & (r < 8)).all()                               # largest magnitude lands in [4, 8)
+    q = oracle.unpack_nibbles(codes).astype(np.int64) & 0xF
+    vals = np.vectorize(table.get)(q) * np.repeat(np.exp2(e), 32, axis=1)
+    v = y / np.repeat(np.exp2(e), 32, axis=1)
+    grid = np.array(sorted(set(abs(t) for t in table.values())))
+    # nearest grid point (saturating at 6): |v - q| <= half the local spacing
+    idx = np.clip(np.searchsorted(grid, np.abs(v)), 1, len(grid) - 1)
+    half = (grid[idx] - grid[idx - 1]) / 2
+    err = np.abs(np.abs(v) - np.abs(vals / np.repeat(np.exp2(e), 32, axis=1)))
+    assert ((err <= half + 1e-12) | (np.abs(v) >= 6)).all()
+    assert np.array_equal(np.sign(vals)[vals != 0], np.sign(y)[vals != 0])
+    # conditioning on the quantizer's own scales reproduces its codes
+    assert np.array_equal(oracle.mxfp4_codes_given_scales(y, scales) & 0xF, q)
+
+
+def test_mxfp4_zero_block_and_single_spike(golden_dir):
+    D = 128
+    table = e2m1_golden(golden_dir)
+    codes, scales, _, bad = oracle.quantize_mxfp4(np.zeros((2, D), np.uint16), np.ones(D, np.float32),
+                                                  np.ones(D, np.int8))
+    assert bad == 0 and (codes == 0).all() and (scales == 0).all()     # e = -127 for an all-zero block
+    H = scipy.linalg.hadamard(D)
+    for a, k in ((1.5, 3), (-2.0, D - 1)):
+        x = np.zeros((1, D))
+        x[0, k] = a
+        codes, scales, _, _ = oracle.quantize_mxfp4(f16bits(x), np.ones(D, np.float32), np.ones(D, np.int8))
+        m = abs(a) / np.sqrt(D)
+        e = int(np.floor(np.log2(m))) - 2
+        assert (scales == e + 127).all()
+        v = m / 2.0 ** e                                              # in [4, 8)
+        want_mag = 4.0 if v <= 5.0 else 6.0                           # ties at 5 go to 4 (even)
+        q = oracle.unpack_nibbles(codes)[0].astype(np.int64) & 0xF
+        got = np.array([table[c] for c in q])
+        assert np.array_equal(got, want_mag * np.sign(a) * H[:, k])
+
+
+def test_mxfp4_dequant_single_code_closed_form():
+    D = 64
+    lam = rand_lambda(1, D)[0]
+    s = rand_signs(D)
+    H = scipy.linalg.hadamard(D)
+    for k, c, sb in ((0, 0x7, 120), (17, 0xB, 130), (63, 0x1, 127)):
+        q = np.zeros((1, D), np.int8)
+        q[0, k] = c if c < 8 else c - 16
+        scales = np.full((1, D // 32), 127, np.uint8)
+        scales[0, k // 32] = sb
+        x64, x16 = oracle.dequantize_mxfp4(oracle.pack_nibbles(q), scales, lam, s)
+        val = {0x7: 6.0, 0xB: -1.5, 0x1: 0.5}[c] * 2.0 ** (sb - 127)
+        want = (s / lam.astype(np.float64)) * val * H[k, :] / np.sqrt(D)
+        assert np.allclose(x64[0], want, rtol=1e-14, atol=0)

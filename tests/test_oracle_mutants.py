@@ -48,6 +48,10 @@ MUTANTS = {
     "int8_amax_over_128": ("kvqo_f64_to_f16(amax / 127.0)", "kvqo_f64_to_f16(amax / 128.0)"),
     "int8_clamp_128": ("if (r > 127.0) r = 127.0;", "if (r > 128.0) r = 128.0;"),
     "int8_truncates": ("double r = nearbyint(y / scale);\n    if (r > 127.0)", "double r = trunc(y / scale);\n    if (r > 127.0)"),
+    "mx_ties_to_odd": ("(a - lo == hi - a && (mag & 1))", "(a - lo == hi - a && !(mag & 1))"),
+    "mx_exponent_off_by_one": ("int e = (E - 1) - 2;", "int e = (E - 1) - 1;"),
+    "mx_subnormal_quarter": ("double mag = e == 0 ? 0.5 * m", "double mag = e == 0 ? 0.25 * m"),
+    "mx_scale_multiplies": ("q[i] = (int8_t)e2m1_code(ldexp(y[i], -e));", "q[i] = (int8_t)e2m1_code(ldexp(y[i], e));"),
     "attend_no_max_shift": ("double w = exp(a[t] - amax);", "double w = exp(a[t]);"),
     "attend_scale_dropped": ("a[t] = scale * dot;", "a[t] = dot;"),
     "attend_values_from_keys": ("o[c] += w * vh[(int64_t)t * D + c];", "o[c] += w * kh[(int64_t)t * D + c];"),
@@ -82,6 +86,10 @@ BATTERY = [
     ("test_int8_ties_round_half_to_even_and_clamp", {}),
     ("test_int8_quantizer_invariants", {"D": 128, "G": 32}),
     ("test_int8_dequant_single_code_closed_form", {}),
+    ("test_e2m1_table_golden", {"golden_dir": None}),
+    ("test_e2m1_rounding_ties_even_and_saturation", {"golden_dir": None}),
+    ("test_mxfp4_block_scale_rule_and_invariants", {"D": 128, "golden_dir": None}),
+    ("test_mxfp4_zero_block_and_single_spike", {"golden_dir": None}),
     ("test_attend_single_token_returns_its_value", {}),
     ("test_attend_zero_query_is_mean_of_values", {}),
     ("test_attend_matches_torch_sdpa", {"R": 4}),
