@@ -146,6 +146,7 @@ def main():
     ap.add_argument("--no-vq", action="store_true")
     ap.add_argument("--no-attend", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
+    ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--no-small", action="store_true", help="skip the Qwen2.5 / Gemma cache timings")
     ap.add_argument("--attend-seqs", type=int, default=8,
                     help="sequences the int4 cache's token axis is split into for the decode-attention leg")
@@ -254,7 +255,10 @@ def main():
 
     int8 = None
     if not args.no_int8:
-        int8 = bench_int8(torch, kvq, K, lamK, signs, (L, T, H, D, G), args)
+        int8 = bench_variant(torch, kvq, K, lamK, signs, (L, T, H, D, G), args, "int8")
+    mxfp4 = None
+    if not args.no_mxfp4:
+        mxfp4 = bench_variant(torch, kvq, K, lamK, signs, (L, T, H, D, G), args, "mxfp4")
 
     attend = None
     if not args.no_attend:
@@ -293,6 +297,7 @@ def main():
         "vq": vq,
         "attend": attend,
         "int8": int8,
+        "mxfp4": mxfp4,
         "small_workloads": small,
         "frac_of_hbm_peak_step": round(value / HBM_PEAK_GBPS, 4),
     }
@@ -366,22 +371,33 @@ def bench_small(torch, kvq, synth, dev, args):
     return res
 
 
-def bench_int8(torch, kvq, K, lamK, signs, dims, args):
-    """Time the int8 variant (quantize, then dequantize) on the K cache."""
+def bench_variant(torch, kvq, K, lamK, signs, dims, args, kind):
+    """Time one code variant of the fused quantizer (quantize, then dequantize)
+    on the K cache: "int8" (127 levels, fp16 group scales) or "mxfp4"
+    (E2M1 elements, one E8M0 scale byte per 32 coordinates)."""
     L, T, H, D, G = dims
-    codes = torch.empty((L, T, H, D), dtype=torch.int8, device=K.device)
-    scales = torch.empty((L, T, H, D // G), dtype=torch.float16, device=K.device)
+    if kind == "int8":
+        codes = torch.empty((L, T, H, D), dtype=torch.int8, device=K.device)
+        scales = torch.empty((L, T, H, D // G), dtype=torch.float16, device=K.device)
+        bpv = 2 * D + D + 2 * (D // G)
+        what = "group %d, int8 codes" % G
+        qf = lambda: kvq.quantize_int8(K, lamK, signs, G, codes=codes, scales=scales, stream=stream)
+        df = lambda: kvq.dequantize_int8(codes, scales, lamK, signs, G, out=out, stream=stream)
+    else:
+        codes = torch.empty((L, T, H, D // 2), dtype=torch.uint8, device=K.device)
+        scales = torch.empty((L, T, H, D // 32), dtype=torch.uint8, device=K.device)
+        bpv = 2 * D + D // 2 + D // 32
+        what = "blocks of 32, E2M1 codes, E8M0 scales"
+        qf = lambda: kvq.quantize_mxfp4(K, lamK, signs, codes=codes, scales=scales, stream=stream)
+        df = lambda: kvq.dequantize_mxfp4(codes, scales, lamK, signs, out=out, stream=stream)
     out = torch.empty_like(K)
     stream = torch.cuda.current_stream()
-    kvq.quantize_int8(K, lamK, signs, G, codes=codes, scales=scales, stream=stream)
-    kvq.dequantize_int8(codes, scales, lamK, signs, G, out=out, stream=stream)
+    qf()
+    df()
     torch.cuda.synchronize()
     ev = {"quantize": [], "dequantize": []}
     for _ in range(max(3, min(args.steps, 10))):
-        for name, fn in (("quantize", lambda: kvq.quantize_int8(K, lamK, signs, G, codes=codes, scales=scales,
-                                                                 stream=stream)),
-                         ("dequantize", lambda: kvq.dequantize_int8(codes, scales, lamK, signs, G, out=out,
-                                                                     stream=stream))):
+        for name, fn in (("quantize", qf), ("dequantize", df)):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             fn()
@@ -389,8 +405,7 @@ def bench_int8(torch, kvq, K, lamK, signs, dims, args):
             ev[name].append((a, b))
     torch.cuda.synchronize()
     nvec = L * T * H
-    bpv = 2 * D + D + 2 * (D // G)
-    res = {"workload": "qwen3-8b-shaped K cache [%d, %d, %d, %d], group %d, int8 codes" % (L, T, H, D, G),
+    res = {"workload": "qwen3-8b-shaped K cache [%d, %d, %d, %d], %s" % (L, T, H, D, what),
            "bytes_per_vector": bpv}
     for name, pairs in ev.items():
         ms = [a.elapsed_time(b) for a, b in pairs]

@@ -145,6 +145,29 @@ kvq_status kvq_dequantize_int8(kvq_shape shape, kvq_view codes_i8, kvq_view scal
                                const float* lambda, const int8_t* signs, int32_t group,
                                kvq_view out_f16, void* stream);
 
+/* Block-scaled E2M1 variant of kvq_quantize (the PolarQuant/block-FP4
+ * abstract names block-scaled E2M1 FP4 as a KV-cache format; the format is
+ * the OCP Microscaling MXFP4 one): the same rotation, then blocks of 32
+ * rotated coordinates, each with a power-of-two scale X = 2^e, e =
+ * floor(log2(amax)) - 2 clamped to [-127, 127] (-127 for an all-zero block),
+ * stored as the E8M0 byte e + 127, and E2M1 elements = y / X rounded to
+ * nearest (ties to the even code), saturating at +-6, sign bit kept.
+ *   codes_u8     output view of D/2-byte rows: element 2k in the low nibble
+ *                of byte k; 16-byte aligned data and strides.
+ *   scales_e8m0  output view of D/32-byte rows.
+ * The E2M1 rounding uses the gfx950 v_cvt_scalef32_pk_fp4_f32 conversion on
+ * y * 2^-e.  Other arguments and errors as for kvq_quantize. */
+kvq_status kvq_quantize_mxfp4(kvq_shape shape, kvq_view x_f16, const float* lambda,
+                              const int8_t* signs, kvq_view codes_u8, kvq_view scales_e8m0,
+                              void* stream);
+
+/* Mirror of kvq_quantize_mxfp4: E2M1 value times 2^(scale - 127), inverse
+ * Walsh-Hadamard, unscale, fp16.  Views as for kvq_dequantize, with D/32-byte
+ * E8M0 scale rows. */
+kvq_status kvq_dequantize_mxfp4(kvq_shape shape, kvq_view codes_u8, kvq_view scales_e8m0,
+                                const float* lambda, const int8_t* signs, kvq_view out_f16,
+                                void* stream);
+
 /* Product-VQ encode (VecInfer blog, "What VecInfer does"; VeloxQuant-MLX
  * package description, "Metal kernels"): rotate as kvq_quantize does (no
  * group quantizer), split into D/sub_dim sub-vectors and store, per

@@ -70,6 +70,10 @@ def lib():
     L.kvq_quantize_int8.argtypes = [Shape, View, P, P, I32, View, View, P]
     L.kvq_dequantize_int8.restype = ctypes.c_int
     L.kvq_dequantize_int8.argtypes = [Shape, View, View, P, P, I32, View, P]
+    L.kvq_quantize_mxfp4.restype = ctypes.c_int
+    L.kvq_quantize_mxfp4.argtypes = [Shape, View, P, P, View, View, P]
+    L.kvq_dequantize_mxfp4.restype = ctypes.c_int
+    L.kvq_dequantize_mxfp4.argtypes = [Shape, View, View, P, P, View, P]
     L.kvq_vq_encode.restype = ctypes.c_int
     L.kvq_vq_encode.argtypes = [Shape, View, P, P, P, I64, I32, I32, View, P]
     L.kvq_vq_decode.restype = ctypes.c_int
@@ -218,6 +222,41 @@ def dequantize_int8(codes, scales, lam, signs, group: int, out=None, stream=None
     pl, ps = _params(lam, signs, L, H, D)
     _check(lib().kvq_dequantize_int8(_shape(codes, D), _view(codes), _view(scales), pl, ps, int(group), _view(out),
                                      _stream(stream)))
+    return out
+
+
+# ----------------------------------------------------------------- MXFP4
+def quantize_mxfp4(x, lam, signs, codes=None, scales=None, stream=None):
+    """Block-scaled E2M1 variant of quantize: x [L, T, H, D] fp16 -> (codes
+    uint8 [L, T, H, D/2] packed E2M1 nibbles, scales uint8 [L, T, H, D/32]
+    E8M0 bytes)."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    L, T, H, D = x.shape
+    if codes is None:
+        codes = torch.empty((L, T, H, D // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((L, T, H, D // 32), dtype=torch.uint8, device=x.device)
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    pl, ps = _params(lam, signs, L, H, D)
+    _check(lib().kvq_quantize_mxfp4(_shape(x, D), _view(x), pl, ps, _view(codes), _view(scales), _stream(stream)))
+    return codes, scales
+
+
+def dequantize_mxfp4(codes, scales, lam, signs, out=None, stream=None):
+    """Mirror of quantize_mxfp4 -> fp16 [L, T, H, D]."""
+    torch = _torch()
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    L, T, H, half = codes.shape
+    D = 2 * half
+    if out is None:
+        out = torch.empty((L, T, H, D), dtype=torch.float16, device=codes.device)
+    _need(out, torch.float16, "out")
+    pl, ps = _params(lam, signs, L, H, D)
+    _check(lib().kvq_dequantize_mxfp4(_shape(codes, D), _view(codes), _view(scales), pl, ps, _view(out),
+                                      _stream(stream)))
     return out
 
 

@@ -147,7 +147,8 @@ kvq_status hip_status(hipError_t e, const char* what)
 
 kvq_status int4_common(const kvq_shape& shape, const kvq_view& x, const float* lambda,
                        const int8_t* signs, int32_t group, const kvq_view& codes,
-                       const kvq_view& scales, kvq::Int4Args& a, bool x_is_output, int bits = 4)
+                       const kvq_view& scales, kvq::Int4Args& a, bool x_is_output, int bits = 4,
+                       bool mx = false)
 {
     KVQ_TRY(check_shape(shape));
     KVQ_TRY(check_group(group, shape.head_dim));
@@ -156,13 +157,15 @@ kvq_status int4_common(const kvq_shape& shape, const kvq_view& x, const float* l
     const int64_t D = shape.head_dim;
     KVQ_TRY(check_view(x_is_output ? "out_f16" : "x_f16", x, 2, D, 16, shape));
     KVQ_TRY(check_view(bits == 4 ? "codes_u8" : "codes_i8", codes, 1, bits == 4 ? D / 2 : D, 16, shape));
-    KVQ_TRY(check_view("scales_f16", scales, 2, D / group, 2, shape));
+    if (mx) KVQ_TRY(check_view("scales_e8m0", scales, 1, D / group, 1, shape));
+    else KVQ_TRY(check_view("scales_f16", scales, 2, D / group, 2, shape));
     a.L = (int32_t)shape.layers;
     a.T = (int32_t)shape.tokens;
     a.H = (int32_t)shape.heads;
     a.D = (int32_t)D;
     a.G = group;
     a.bits = bits;
+    a.mx = mx ? 1 : 0;
     a.x = t4(x);
     a.codes = t4(codes);
     a.scales = t4(scales);
@@ -296,6 +299,26 @@ kvq_status kvq_dequantize_int8(kvq_shape shape, kvq_view codes_i8, kvq_view scal
     KVQ_TRY(int4_common(shape, out_f16, lambda, signs, group, codes_i8, scales_f16, a, true, 8));
     if (empty(shape)) return KVQ_OK;
     return hip_status(kvq::launch_dequantize(a, static_cast<hipStream_t>(stream)), "kvq_dequantize_int8 launch");
+}
+
+kvq_status kvq_quantize_mxfp4(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,
+                              kvq_view codes_u8, kvq_view scales_e8m0, void* stream)
+{
+    g_err[0] = 0;
+    kvq::Int4Args a;
+    KVQ_TRY(int4_common(shape, x_f16, lambda, signs, 32, codes_u8, scales_e8m0, a, false, 4, true));
+    if (empty(shape)) return KVQ_OK;
+    return hip_status(kvq::launch_quantize(a, static_cast<hipStream_t>(stream)), "kvq_quantize_mxfp4 launch");
+}
+
+kvq_status kvq_dequantize_mxfp4(kvq_shape shape, kvq_view codes_u8, kvq_view scales_e8m0, const float* lambda,
+                                const int8_t* signs, kvq_view out_f16, void* stream)
+{
+    g_err[0] = 0;
+    kvq::Int4Args a;
+    KVQ_TRY(int4_common(shape, out_f16, lambda, signs, 32, codes_u8, scales_e8m0, a, true, 4, true));
+    if (empty(shape)) return KVQ_OK;
+    return hip_status(kvq::launch_dequantize(a, static_cast<hipStream_t>(stream)), "kvq_dequantize_mxfp4 launch");
 }
 
 kvq_status kvq_vq_encode(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,

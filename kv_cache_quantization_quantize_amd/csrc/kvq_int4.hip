@@ -215,9 +215,10 @@ __device__ __forceinline__ void run_pipeline(int begin, int end, Load&& load, Fi
 //   2. issues the previous item's stores and the next item's loads,
 //   3. computes the rest of the current item,
 // and a scheduling barrier keeps step 2 between steps 1 and 3.
-template <int D, int G, bool TM, int BITS>
+template <int D, int G, bool TM, int BITS, bool MX>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args a)
 {
+    static_assert(!MX || (BITS == 4 && G == 32), "MXFP4: 4-bit codes in blocks of 32");
     using S = QuantShape<D, G>;
     using F = CodeFmt<BITS>;
     constexpr int WPJ = BITS / 4;        // code dwords per 8-coordinate chunk
@@ -240,6 +241,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
     const _Float16* __restrict__ xg = static_cast<const _Float16*>(a.x.data);
     uint8_t* __restrict__ cg = static_cast<uint8_t*>(a.codes.data);
     uint16_t* __restrict__ sg = static_cast<uint16_t*>(a.scales.data);
+    uint8_t* __restrict__ sg8 = static_cast<uint8_t*>(a.scales.data);      // MXFP4: E8M0 bytes
     const LaneMap lm = lane_map<TM>(slot, a);
     const int64_t x_lane = (int64_t)lm.tok * a.x.st + (int64_t)lm.head * a.x.sh + q * 8;
     // this lane stores code chunks q, q + 4, ... (16 bytes each) of its vector
@@ -311,7 +313,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
             if (ok && c < NCH) *reinterpret_cast<uint4*>(cp + 64 * k) = chunk;
         }
         if (ok) {
-            if constexpr (G >= 32) {
+            if constexpr (MX) {
+                uint8_t* sp8 = sg8 + outer_offset(a.scales, it) + s_lane;
+#pragma unroll
+                for (int k = 0; k < NSV; k++)
+                    if (4 * k + q < NG) sp8[4 * k + q] = (uint8_t)o.sv[k];
+            } else if constexpr (G >= 32) {
                 // lane q writes groups q, q+4, ...
 #pragma unroll
                 for (int k = 0; k < NSV; k++)
@@ -363,6 +370,35 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
         }
         if constexpr (G >= 16) quad_max<false>(amax);
         if constexpr (G >= 32) quad_max<true>(amax);
+
+        if constexpr (MX) {
+            // Block exponent e = floor(log2 amax) - 2, clamped at -127, stored
+            // as the E8M0 byte e + 127 = max(biased exponent of amax - 2, 0).
+            // The E2M1 conversion (round to nearest even, saturating at 6,
+            // sign kept) runs on y * 2^-e, an exact power-of-two scaling.
+            uint16_t sb[LG];
+            float inv[LG];
+#pragma unroll
+            for (int u = 0; u < LG; u++) {
+                const uint32_t eb = (__float_as_uint(amax[u]) >> 23) & 0xffu;
+                const uint32_t byte = eb > 2u ? eb - 2u : 0u;
+                sb[u] = (uint16_t)byte;
+                inv[u] = lane_sign * __uint_as_float((254u - byte) << 23);
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; j++) {
+                const float f = inv[j];
+                uint32_t w = 0u;
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j + 0] * f, v[8 * j + 1] * f, 1.0f, 0);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j + 2] * f, v[8 * j + 3] * f, 1.0f, 1);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j + 4] * f, v[8 * j + 5] * f, 1.0f, 2);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j + 6] * f, v[8 * j + 7] * f, 1.0f, 3);
+                o.word[j] = w;
+            }
+#pragma unroll
+            for (int k = 0; k < NSV; k++) o.sv[k] = pick_scale<NG>(sb, (4 * k + q) % NG);
+            return;
+        }
 
         uint16_t s16[LG];
         float inv[LG];
@@ -422,9 +458,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
 // ---------------------------------------------------------------------------
 // Dequantize
 // ---------------------------------------------------------------------------
-template <int D, int G, bool TM, int BITS>
+template <int D, int G, bool TM, int BITS, bool MX>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Args a)
 {
+    static_assert(!MX || (BITS == 4 && G == 32), "MXFP4: 4-bit codes in blocks of 32");
     constexpr int WPJ = BITS / 4;        // code dwords per 8-coordinate chunk
     constexpr int NJ = D / 32;
     constexpr int N = NJ * 8;
@@ -457,7 +494,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
     // scale row as packed 32-bit words.
     struct Raw {
         uint32_t w[NJ * WPJ];
-        uint32_t sw[NW];
+        uint32_t sw[MX ? NG : NW];      // MXFP4: one E8M0 byte per block
     };
     struct Out {
         uint4 o[NJ];
@@ -479,7 +516,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
                     raw.w[2 * j + 1] = d.y;
                 }
             }
-            if constexpr (NG == 1) {
+            if constexpr (MX) {
+                const uint8_t* sp8 = reinterpret_cast<const uint8_t*>(sg) + outer_offset(a.scales, it) + s_lane;
+#pragma unroll
+                for (int g = 0; g < NG; g++) raw.sw[g] = sp8[g];
+            } else if constexpr (NG == 1) {
                 raw.sw[0] = sp[0];
             } else {
                 // scale rows are only 2-byte aligned; gfx950 serves unaligned
@@ -495,7 +536,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
 #pragma unroll
             for (int j = 0; j < NJ * WPJ; j++) raw.w[j] = 0u;      // code 0
 #pragma unroll
-            for (int i = 0; i < NW; i++) raw.sw[i] = 0;
+            for (int i = 0; i < (MX ? NG : NW); i++) raw.sw[i] = 0;
             if (it.t0 + lm.tok < a.T) ld();
         }
     };
@@ -560,6 +601,22 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
         }
 #pragma unroll
         for (int j = 0; j < NJ; j++) {
+            if constexpr (MX) {
+                // E2M1 pairs straight to f32 (exact), times the block's 2^(b - 127)
+                const float X = __builtin_amdgcn_ldexpf(1.0f, (int)raw.sw[j] - 127);
+                typedef float f2_t __attribute__((ext_vector_type(2)));
+                const f2_t p[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(raw.w[j], 1.0f, 0),
+                                   __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(raw.w[j], 1.0f, 1),
+                                   __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(raw.w[j], 1.0f, 2),
+                                   __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(raw.w[j], 1.0f, 3)};
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const float t = p[k].y * X;
+                    v[j * 8 + 2 * k] = fmaf(p[k].x, X, t);
+                    v[j * 8 + 2 * k + 1] = fmaf(p[k].x, X, -t);
+                }
+                continue;
+            }
             const float sc = chunk_scale(raw, j);
             if constexpr (BITS == 8) {
                 // offset-binary bytes u = q + 128 of the pair (2k, 2k+1):
@@ -614,18 +671,18 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int D, int G, int BITS>
+template <int D, int G, int BITS, bool MX = false>
 hipError_t launch_qb(const Int4Args& a, hipStream_t s, bool inverse)
 {
     const int64_t waves = (a.n_items + a.items_per_wave - 1) / a.items_per_wave;
     const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
     const dim3 block(64 * kWavesPerBlock);
     if (inverse) {
-        if (a.token_major) hipLaunchKernelGGL((dequantize_kernel<D, G, true, BITS>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((dequantize_kernel<D, G, false, BITS>), grid, block, 0, s, a);
+        if (a.token_major) hipLaunchKernelGGL((dequantize_kernel<D, G, true, BITS, MX>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((dequantize_kernel<D, G, false, BITS, MX>), grid, block, 0, s, a);
     } else {
-        if (a.token_major) hipLaunchKernelGGL((quantize_kernel<D, G, true, BITS>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((quantize_kernel<D, G, false, BITS>), grid, block, 0, s, a);
+        if (a.token_major) hipLaunchKernelGGL((quantize_kernel<D, G, true, BITS, MX>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((quantize_kernel<D, G, false, BITS, MX>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -633,6 +690,8 @@ hipError_t launch_qb(const Int4Args& a, hipStream_t s, bool inverse)
 template <int D, int G>
 hipError_t launch_q(const Int4Args& a, hipStream_t s, bool inverse)
 {
+    if constexpr (G == 32)
+        if (a.mx) return launch_qb<D, 32, 4, true>(a, s, inverse);
     return a.bits == 8 ? launch_qb<D, G, 8>(a, s, inverse) : launch_qb<D, G, 4>(a, s, inverse);
 }
 

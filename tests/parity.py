@@ -187,3 +187,70 @@ def int8_parity(x_bits, lam_rows, signs, G, codes_gpu, scales_gpu, out_gpu=None)
             _raise("int8 dequant", rd, "first bad [row, coord]: %s gpu=%s ora=%s" % (
                 i.tolist(), f16(out_gpu)[tuple(i.T)], x64[tuple(i.T)]))
     return rep
+
+
+# ------------------------------------------------------------------ MXFP4
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+MX_AMAX_REL = 2.0 ** -20      # fp32 vs fp64 abs-max straddling a power of two
+
+
+def e2m1(codes):
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    v = _E2M1[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def mxfp4_parity(x_bits, lam_rows, signs, codes_gpu, scales_gpu, out_gpu=None):
+    """Block-scaled E2M1 contract.
+    scales  equal E8M0 bytes, or one apart where the block's exact abs-max is
+            within 2^-20 of a power of two (the GPU's fp32 abs-max may land on
+            the other side);
+    codes   compared with the oracle's codes recomputed under the GPU's
+            scales: equal, or adjacent E2M1 values where the exact y / X lies
+            within 1e-4 of the rounding midpoint between them (zero magnitude
+            of either sign counts as equal);
+    dequant the oracle decodes the GPU's own codes and scales, same bound as
+            the int4 dequantizer."""
+    x_bits = np.ascontiguousarray(x_bits, np.uint16)
+    lam_rows = np.ascontiguousarray(lam_rows, np.float32)
+    codes_o, scales_o, y64, nbad = oracle.quantize_mxfp4(x_bits, lam_rows, signs)
+    if nbad:
+        raise ParityError("%d input vectors are outside the quantizer's domain" % nbad)
+    sg = np.ascontiguousarray(scales_gpu, np.uint8)
+    n, D = y64.shape
+    amax = np.abs(y64).reshape(n, D // 32, 32).max(axis=2)
+    with np.errstate(divide="ignore"):
+        l2 = np.log2(np.where(amax > 0, amax, 1.0))
+    near_pow2 = np.abs(np.exp2(np.round(l2)) - amax) <= MX_AMAX_REL * amax
+    ds = sg.astype(np.int64) - scales_o.astype(np.int64)
+    sbad = ~((ds == 0) | ((np.abs(ds) == 1) & near_pow2))
+    rep = {"scales": {"n": int(sg.size), "bad": int(sbad.sum()), "flips": int((ds != 0).sum())}}
+    if sbad.any():
+        i = np.argwhere(sbad)[:5]
+        _raise("mxfp4 scale", rep["scales"], "first bad [row, block]: %s gpu=%s ora=%s" % (
+            i.tolist(), sg[tuple(i.T)], scales_o[tuple(i.T)]))
+    q_gpu = oracle.unpack_nibbles(np.ascontiguousarray(codes_gpu, np.uint8)).astype(np.int64) & 0xF
+    q_cond = oracle.mxfp4_codes_given_scales(y64, sg).astype(np.int64)
+    vg, vo = e2m1(q_gpu), e2m1(q_cond)
+    X = np.repeat(np.exp2(sg.astype(np.float64) - 127), 32, axis=1)
+    v = y64 / X
+    same = (q_gpu == q_cond) | ((vg == 0) & (vo == 0))
+    mid = (vg + vo) / 2
+    adjacent = np.abs(np.searchsorted(_E2M1, np.abs(vg)) - np.searchsorted(_E2M1, np.abs(vo))) == 1
+    boundary = ~same & adjacent & (np.sign(vg) * np.sign(vo) >= 0) & (np.abs(v - mid) <= 1e-4)
+    cbad = ~(same | boundary)
+    rep["codes"] = {"n": int(q_gpu.size), "exact": int(same.sum()), "boundary": int(boundary.sum()),
+                    "bad": int(cbad.sum())}
+    if cbad.any():
+        i = np.argwhere(cbad)[:5]
+        _raise("mxfp4 code", rep["codes"], "first bad [row, coord]: %s gpu=%s ora=%s y/X=%s" % (
+            i.tolist(), q_gpu[tuple(i.T)], q_cond[tuple(i.T)], v[tuple(i.T)]))
+    if out_gpu is not None:
+        x64, _ = oracle.dequantize_mxfp4(np.ascontiguousarray(codes_gpu, np.uint8), sg, lam_rows, signs)
+        rd = check_dequant(out_gpu, x64, lam_rows)
+        rep["dequant"] = rd
+        if rd["bad"]:
+            i = np.argwhere(rd["bad_mask"])[:5]
+            _raise("mxfp4 dequant", rd, "first bad [row, coord]: %s gpu=%s ora=%s" % (
+                i.tolist(), f16(out_gpu)[tuple(i.T)], x64[tuple(i.T)]))
+    return rep

@@ -34,6 +34,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "kvq_quantize", "kvq_dequantize", "kvq_vq_encode", "kvq_vq_decode",
         "kvq_attend_decode", "kvq_attend_decode_workspace", "kvq_quantize_int8", "kvq_dequantize_int8",
+        "kvq_quantize_mxfp4", "kvq_dequantize_mxfp4",
         "kvq_status_string", "kvq_last_error", "kvq_version"])
 
 
@@ -212,3 +213,16 @@ def test_int8_validation(lib):
     assert lib.kvq_quantize_int8(sh, x, A_, A_, 32, view(row=64), scales, None) == SHAPE
     assert lib.kvq_dequantize_int8(shape(0, 5, 3), codes, scales, A_, A_, 32, x, None) == OK
     assert lib.kvq_dequantize_int8(sh, codes, scales, A_, A_, 24, x, None) == UNSUP
+
+
+def test_mxfp4_validation(lib):
+    sh = shape()
+    A_ = ctypes.c_void_p(A)
+    x = view(row=128)
+    codes = view(row=64)
+    assert lib.kvq_quantize_mxfp4(sh, x, A_, A_, codes, view(addr=0, row=4), None) == NULL
+    assert b"scales_e8m0" in lib.kvq_last_error()
+    # E8M0 rows are D/32 bytes; any byte alignment is accepted, a short stride is not
+    assert lib.kvq_quantize_mxfp4(sh, x, A_, A_, codes, view(addr=A + 1, row=2), None) == SHAPE
+    assert lib.kvq_dequantize_mxfp4(shape(2, 0, 3), codes, view(row=4), A_, A_, x, None) == OK
+    assert lib.kvq_dequantize_mxfp4(shape(D=96), codes, view(row=4), A_, A_, x, None) == UNSUP
