@@ -65,6 +65,73 @@ def load_traffic(per_launch_alg_bytes):
     return t.get("traffic_bytes_per_launch")
 
 
+def _counter_means(path, counter):
+    """Per-kernel mean of one rocprofv3 counter (KiB per dispatch) and the
+    per-dispatch values, from a `--pmc <counter> --output-format csv` run."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"].split("(")[0].replace("void ", ""), []).append(
+                    float(r["Counter_Value"]))
+    return vals
+
+
+def ingest_counters(fetch_csv, write_csv, copy_bytes):
+    """Turn the FETCH_SIZE and WRITE_SIZE counter runs of this benchmark into
+    HBM bytes per launch for each timed kernel and write TRAFFIC_FILE.
+
+    Both counters are scaled by what they read for the plain-copy reference
+    that the same runs time (a device-to-device copy of copy_bytes, which
+    must read and write exactly copy_bytes), so that the result is in real
+    bytes."""
+    fe, wr = _counter_means(fetch_csv, "FETCH_SIZE"), _counter_means(write_csv, "WRITE_SIZE")
+    kib = copy_bytes / 1024
+    cw = [v for v in wr.get("__amd_rocclr_copyBuffer", []) if abs(v - kib) < 1]
+    if not cw:
+        raise SystemExit("no %d-byte reference copy in %s" % (copy_bytes, write_csv))
+    cf = sorted(fe["__amd_rocclr_copyBuffer"])[-len(cw):]
+    f_scale, w_scale = kib / (sum(cf) / len(cf)), kib / (sum(cw) / len(cw))
+    L, T, H, D, G = 36, 262144, 8, 128, 32
+    nv = L * T * H
+    B, R = 8, 4
+    att = 2 * L * T * H * (D // 2 + 2 * (D // G)) + 2 * (L * B) * H * R * D * 2
+    nk = 36 * 8192 * 8
+    kernels = {
+        "quantize": ("kvq::quantize_kernel<128, 32, true, 4, false>", nv * bytes_per_vector(D, G)),
+        "dequantize": ("kvq::dequantize_kernel<128, 32, true, 4, false>", nv * bytes_per_vector(D, G)),
+        "quantize_int8": ("kvq::quantize_kernel<128, 32, true, 8, false>", nv * (3 * D + 2 * (D // G))),
+        "dequantize_int8": ("kvq::dequantize_kernel<128, 32, true, 8, false>", nv * (3 * D + 2 * (D // G))),
+        "quantize_mxfp4": ("kvq::quantize_kernel<128, 32, true, 4, true>", nv * (2 * D + D // 2 + D // 32)),
+        "dequantize_mxfp4": ("kvq::dequantize_kernel<128, 32, true, 4, true>", nv * (2 * D + D // 2 + D // 32)),
+        "attend_partial": ("kvq::attend_partial_kernel<128, 4, false>", att),
+        "attend_combine": ("kvq::attend_combine_kernel<128>", None),
+        "vq_encode": ("kvq::vq_encode_kernel<128>", nk * (2 * D + 2 * (D // 8))),
+        "vq_decode": ("kvq::vq_decode_lds_kernel<128>", nk * (2 * D + 2 * (D // 8))),
+    }
+    out = {"workload": "qwen3-8b-shaped cache [36, 262144, 8, 128] fp16, group 32, one tensor per launch; "
+                       "decode attention over it as 288 sequences of 32768 tokens, 4 query heads per KV head; "
+                       "vecinfer-shaped keys [36, 8192, 8, 128] for vq",
+           "source_hash": kernel_source_hash(), "copy_reference_bytes": copy_bytes,
+           "fetch_scale": round(f_scale, 6), "write_scale": round(w_scale, 6)}
+    for key, (name, alg) in kernels.items():
+        if name not in fe or name not in wr:
+            continue
+        f, w = sum(fe[name]) / len(fe[name]), sum(wr[name]) / len(wr[name])
+        tb = int(f * 1024 * f_scale + w * 1024 * w_scale)
+        d = {"kernel": name, "fetch_kib_per_dispatch": round(f, 1), "write_kib_per_dispatch": round(w, 1),
+             "dispatches": len(fe[name]), "traffic_bytes_per_launch": tb}
+        if alg:
+            d["algorithmic_bytes_per_launch"] = alg
+            d["traffic_over_algorithmic"] = round(tb / alg, 5)
+        out[key] = d
+    out["traffic_bytes_per_launch"] = out["quantize"]["traffic_bytes_per_launch"]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def cpu_baseline(K, V, lamK, lamV, signs, G, n_tokens: int):
     """Time the fp64 oracle (single thread) on a bounded sample: every layer
     and head, `n_tokens` consecutive tokens, K and V, quantize + dequantize."""
@@ -155,7 +222,16 @@ def main():
     ap.add_argument("--parts", default="int4,vq",
                     help="comma list of what to run: int4 (the timed step), vq, copy (the plain-copy "
                          "reference of --copy-bytes, used to scale memory counters)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and a "
+                         "WRITE_SIZE rocprofv3 run of this benchmark into the traffic summary under "
+                         "profiles/ and exit")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        t = ingest_counters(args.ingest_counters[0], args.ingest_counters[1], args.copy_bytes)
+        print(json.dumps({k: v.get("traffic_over_algorithmic") for k, v in t.items() if isinstance(v, dict)}))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
