@@ -346,16 +346,21 @@ kvq_status kvq_vq_decode(kvq_shape shape, kvq_view idx_u16, const void* codebook
     KVQ_TRY(vq_common(shape, out_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
                       idx_u16, a, true));
     if (empty(shape)) return KVQ_OK;
-    a.dec_items_per_block = 0;
+    a.dec_rows_per_range = 0;
+    a.dec_range_groups = 0;
     if (n_centroids <= kvq::kVqChunk) {
-        // codebook in LDS: head-major 16-token items of one (layer, head);
-        // one block per CU, each a contiguous range of items
+        // codebook in LDS: one block per CU.  The (layer, 16-token tile) rows
+        // are cut into ranges; each range is decoded by H blocks, one per
+        // head, placed on the same XCD so that the heads' indices of a token,
+        // which share cache lines, are fetched from HBM once.
         a.token_major = 0;
         a.tok_per_item = kvq::kTokensPerTile;
         a.items_per_group = (int32_t)((shape.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
         a.n_items = shape.layers * shape.heads * (int64_t)a.items_per_group;
-        const int64_t blocks = device_cus();
-        a.dec_items_per_block = (a.n_items + blocks - 1) / blocks;
+        const int64_t rows = shape.layers * (int64_t)a.items_per_group;
+        a.dec_range_groups = (int32_t)std::max<int64_t>(1, device_cus() / (8 * shape.heads));
+        const int64_t ranges = 8 * (int64_t)a.dec_range_groups;
+        a.dec_rows_per_range = (rows + ranges - 1) / ranges;
     }
     return hip_status(kvq::launch_vq_decode(a, static_cast<hipStream_t>(stream)), "kvq_vq_decode launch");
 }

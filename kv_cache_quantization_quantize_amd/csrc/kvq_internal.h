@@ -55,9 +55,11 @@ struct VqArgs {
     // ((layer) or (layer, head)), so it loads one set of multipliers
     int32_t dec_waves_per_group;
     int64_t dec_n_waves;
-    // decode with the codebook in LDS (K <= kVqChunk): head-major 16-token
-    // items, each block a contiguous range of this many; 0 selects the other path
-    int64_t dec_items_per_block;
+    // decode with the codebook in LDS (K <= kVqChunk): the (layer, 16-token
+    // tile) rows are cut into 8 * dec_range_groups ranges of this many rows;
+    // the H blocks of one range run on one XCD.  0 selects the other path
+    int64_t dec_rows_per_range;
+    int32_t dec_range_groups;
     // encode units: (layer, head, 16*waves-token chunk), ordered head-major
     // when one codebook serves all layers so that a block rarely re-stages it
     int32_t enc_units_per_lh;

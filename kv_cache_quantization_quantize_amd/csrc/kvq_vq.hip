@@ -476,12 +476,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void vq_decode_kernel(VqArgs a
 }
 
 // Decode with the head's codebook staged in LDS (n_centroids <= kVqChunk).
-// Work items are head-major runs of 16 tokens of one (layer, head); a block
-// takes a contiguous range of them (one block per CU, so a range spans one
-// or two (layer, head) segments), stages the codebook once per segment, and
-// its wavefronts split each segment into contiguous runs.  The centroid
-// gathers are then LDS reads rather than 16-byte pieces of L2 lines.  Each
-// wavefront keeps the indices of its next three items in flight.
+// Work items are runs of 16 tokens of one (layer, head).  A block decodes one
+// head over a contiguous range of (layer, 16-token tile) rows (one block per
+// CU), stages the codebook when it changes, and its wavefronts split each
+// layer's part of the range into contiguous runs.  The centroid gathers are
+// LDS reads rather than 16-byte pieces of L2 lines.  Each wavefront keeps the
+// indices of its next three items in flight.
 template <int D>
 __global__ __launch_bounds__(64 * VqDecLds<D>::WAVES) void vq_decode_lds_kernel(VqArgs a)
 {
@@ -513,22 +513,35 @@ __global__ __launch_bounds__(64 * VqDecLds<D>::WAVES) void vq_decode_lds_kernel(
     const int row_c = lane % CV;
     typedef uint4 uint4_a4 __attribute__((aligned(4)));
 
-    const int64_t g_end = min((int64_t)(blockIdx.x + 1) * a.dec_items_per_block, a.n_items);
-    for (int64_t g = (int64_t)blockIdx.x * a.dec_items_per_block; g < g_end;) {
-        const int lh = uniform((int)(g / a.items_per_group));
-        const int l = uniform(lh / a.H);
-        const int h = lh - l * a.H;
-        const int64_t seg0 = (int64_t)lh * a.items_per_group;
+    // Block b runs on XCD b % 8.  Its head is (b / 8) % H and its row range
+    // is ((b / 8) / H) * 8 + b % 8, so the H blocks of a range share an XCD
+    // (and its L2) and run concurrently.
+    const int xcd = blockIdx.x & 7;
+    const int kx = blockIdx.x >> 3;
+    const int grp = kx / a.H;
+    const int h = kx - grp * a.H;
+    const int64_t rows = (int64_t)a.L * a.items_per_group;
+    const int64_t r0 = ((int64_t)grp * 8 + xcd) * a.dec_rows_per_range;
+    const int64_t g_end = min(r0 + a.dec_rows_per_range, rows);
+    int staged = -1;
+    for (int64_t g = r0; g < g_end;) {
+        const int l = uniform((int)(g / a.items_per_group));
+        const int64_t seg0 = (int64_t)l * a.items_per_group;
         const int i0 = (int)(g - seg0);
         const int i1 = (int)(min(g_end, seg0 + a.items_per_group) - seg0);
         g = seg0 + i1;
 
-        // stage the codebook of (l, h): K centroids of 16 bytes
-        __syncthreads();   // the previous segment's gathers are done
-        const uint4* cbg = reinterpret_cast<const uint4*>(a.codebook + (int64_t)l * a.cb_layer_stride +
-                                                          (int64_t)h * a.K * 8);
-        for (int k = threadIdx.x; k < a.K; k += 64 * WAVES) cb_lds[k] = cbg[k];
-        __syncthreads();
+        // stage the codebook of (l, h), K centroids of 16 bytes, unless the
+        // one in LDS is already it (one codebook for all layers)
+        const int cb_l = a.cb_layer_stride ? l : 0;
+        if (cb_l != staged) {
+            __syncthreads();   // the previous segment's gathers are done
+            const uint4* cbg = reinterpret_cast<const uint4*>(a.codebook + (int64_t)cb_l * a.cb_layer_stride +
+                                                              (int64_t)h * a.K * 8);
+            for (int k = threadIdx.x; k < a.K; k += 64 * WAVES) cb_lds[k] = cbg[k];
+            __syncthreads();
+            staged = cb_l;
+        }
 
         const int per_wave = (i1 - i0 + WAVES - 1) / WAVES;
         const int begin = i0 + wid * per_wave;
@@ -630,8 +643,8 @@ hipError_t launch_enc(const VqArgs& a, hipStream_t s)
 template <int D>
 hipError_t launch_dec(const VqArgs& a, hipStream_t s)
 {
-    if (a.dec_items_per_block > 0) {
-        const dim3 grid((unsigned)((a.n_items + a.dec_items_per_block - 1) / a.dec_items_per_block));
+    if (a.dec_rows_per_range > 0) {
+        const dim3 grid((unsigned)(8 * a.H * a.dec_range_groups));
         hipLaunchKernelGGL((vq_decode_lds_kernel<D>), grid, dim3(64 * VqDecLds<D>::WAVES), 0, s, a);
         return hipGetLastError();
     }
