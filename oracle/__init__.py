@@ -64,6 +64,7 @@ def bind(path: str):
         "kvqo_dequantize_rows": (I32, [I64, I32, I32, P, P, P, P, P, P]),
         "kvqo_vq_encode_rows": (I32, [I64, I32, I32, I32, P, P, P, P, P, P, P]),
         "kvqo_vq_distances": (I32, [I64, I32, I32, I32, P, P, P, P, P]),
+        "kvqo_kmeans_update": (I32, [I64, I32, I32, P, P, P, P, P, P, P]),
         "kvqo_vq_decode_rows": (I32, [I64, I32, I32, I32, P, P, P, P, P, P, P]),
         "kvqo_codes8_given_scales": (I32, [I64, I32, I32, P, P, P]),
         "kvqo_quantize8_rows": (I64, [I64, I32, I32, P, P, P, P, P, P]),
@@ -250,6 +251,37 @@ def vq_decode(idx, codebooks_bits, book, lam, signs, sub):
     if rc:
         raise ValueError("oracle vq_decode rejected (index out of range?)")
     return x64, x16
+
+
+def kmeans_update(ysub, idx, codebook_bits):
+    """Update half of one Lloyd step: ysub fp64 [n, sub] samples, idx [n]
+    their assigned centroids, codebook fp16 bits [K, sub].  Returns
+    (new codebook fp16 bits [K, sub], fp64 means [K, sub], counts u32 [K],
+    mean |y| per centroid and coordinate [K, sub])."""
+    y, py = _c(ysub, np.float64)
+    n, sub = y.shape
+    ix, pix = _c(np.asarray(idx).reshape(n), np.uint16)
+    cb, pcb = _c(codebook_bits, np.uint16)
+    K = cb.shape[0]
+    m64, pm = _out((K, sub), np.float64)
+    new, pn = _out((K, sub), np.uint16)
+    cnt, pc = _out((K,), np.uint32)
+    am, pa = _out((K, sub), np.float64)
+    rc = _load().kvqo_kmeans_update(n, int(sub), K, py, pix, pcb, pm, pn, pc, pa)
+    if rc:
+        raise ValueError("oracle kmeans_update rejected (index out of range?)")
+    return new, m64, cnt, am
+
+
+def kmeans_step(x_bits, lam, signs, codebook_bits, sub):
+    """One Lloyd step on the rotated sub-vectors of x [n, D] (all rows train
+    the one codebook [K, sub]).  Returns (idx [n, D/sub] assignments to the
+    input codebook, new codebook fp16 bits, fp64 means, counts, mean |y|,
+    rotated sub-vectors fp64 [n * D/sub, sub])."""
+    idx, y = vq_encode(x_bits, lam, signs, np.asarray(codebook_bits)[None], 0, sub)
+    ysub = y.reshape(-1, sub)
+    new, m64, cnt, am = kmeans_update(ysub, idx.reshape(-1), codebook_bits)
+    return idx, new, m64, cnt, am, ysub
 
 
 def attend_decode(q_bits, k_codes, k_scales, v_codes, v_scales, lam_k, lam_v, signs, G, scale,

@@ -52,6 +52,11 @@
  *    byte k [GIST s.2 "two int4 values in one byte"].
  *  - VQ: contiguous sub-vectors, squared Euclidean distance on the unrounded
  *    rotated key, lowest index on ties [README "Metal kernels"; VQ-blog].
+ *  - codebook training is Lloyd's k-means on the rotated sub-vectors of
+ *    synthetic samples: assign each to its nearest centroid (the encode
+ *    above), then move each centroid to the mean of its samples; a centroid
+ *    with no samples stays where it was; the result is stored as binary16
+ *    like the codebook it replaces [VQ-blog, calibration caveat].
  */
 #include <math.h>
 #include <stddef.h>
@@ -610,6 +615,54 @@ int kvqo_vq_decode_rows(int64_t n, int D, int sub, int K, const uint16_t* idx,
                 xhat16[r * D + j] = kvqo_f64_to_f16(xhat64[r * D + j]);
     }
     free(yh);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Codebook training: one Lloyd (k-means) step [VQ-blog "What VecInfer does,  */
+/* and the calibration caveat up front"]                                       */
+/* ------------------------------------------------------------------------ */
+
+/* The update half of a Lloyd iteration, given each sample's assignment.
+   ysub [n, sub] are the samples (rotated sub-vectors, fp64) and idx [n] their
+   assigned centroids (the nearest one in cb_old, as kvqo_vq_encode_rows gives
+   them).  For every centroid k of the [K, sub] binary16 codebook cb_old:
+     counts[k]   = number of samples assigned to k;
+     mean64[k]   = their mean, in fp64; a centroid with no samples keeps its
+                   old value;
+     cb_new[k]   = binary16 RNE of mean64[k] (cb_old[k] unchanged if empty);
+     abs_mean[k] = mean of |y| per coordinate over its samples (0 if empty),
+                   a scale for judging a summation in lower precision.
+   Returns -2 if an assignment is out of range. */
+int kvqo_kmeans_update(int64_t n, int sub, int K, const double* ysub, const uint16_t* idx,
+                       const uint16_t* cb_old, double* mean64, uint16_t* cb_new,
+                       uint32_t* counts, double* abs_mean)
+{
+    if (sub <= 0 || K <= 0 || K > 65536) return -1;
+    for (int64_t k = 0; k < (int64_t)K * sub; k++) { mean64[k] = 0.0; abs_mean[k] = 0.0; }
+    for (int k = 0; k < K; k++) counts[k] = 0;
+    for (int64_t i = 0; i < n; i++) {
+        int k = idx[i];
+        if (k >= K) return -2;
+        counts[k]++;
+        for (int t = 0; t < sub; t++) {
+            mean64[(int64_t)k * sub + t] += ysub[i * sub + t];
+            abs_mean[(int64_t)k * sub + t] += fabs(ysub[i * sub + t]);
+        }
+    }
+    for (int k = 0; k < K; k++) {
+        for (int t = 0; t < sub; t++) {
+            int64_t e = (int64_t)k * sub + t;
+            if (counts[k] == 0) {
+                mean64[e] = kvqo_f16_to_f64(cb_old[e]);
+                cb_new[e] = cb_old[e];
+            } else {
+                mean64[e] /= (double)counts[k];
+                abs_mean[e] /= (double)counts[k];
+                cb_new[e] = kvqo_f64_to_f16(mean64[e]);
+            }
+        }
+    }
     return 0;
 }
 

@@ -421,6 +421,92 @@ def test_vq_decode_closed_form_and_roundtrip():
     assert np.array_equal(idx2, idx)
 
 
+# ------------------------------------------------ codebook training (k-means)
+def test_kmeans_step_matches_scipy_lloyd_iteration():
+    """One step on rotated sub-vectors against scipy.cluster.vq.kmeans2 with the
+    same initial codebook and iter=1 (assign with vq, move to the cluster
+    means, keep empty clusters in place); one centroid is placed far away so
+    that it gets no samples."""
+    import warnings
+
+    import scipy.cluster.vq
+    D, sub, n, K = 64, 8, 40, 12
+    x = rand_x(n, D)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    cb = RNG.standard_normal((K, sub))
+    cb[5] = 50.0
+    cbb = f16bits(cb)
+    idx, new, m64, cnt, am, ysub = oracle.kmeans_step(x, lam, s, cbb, sub)
+    assert np.allclose(ysub, oracle.rotate(x, lam, s).reshape(-1, sub))
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        ref_cb, ref_lab = scipy.cluster.vq.kmeans2(ysub, bits_to_f64(cbb), iter=1, minit="matrix",
+                                                   missing="warn")
+    assert np.array_equal(idx.reshape(-1), ref_lab)
+    assert np.allclose(m64, ref_cb, rtol=1e-13, atol=1e-15)
+    assert cnt[5] == 0 and np.array_equal(new[5], cbb[5])
+    assert np.array_equal(cnt, np.bincount(ref_lab, minlength=K))
+    assert np.array_equal(new, f16bits(m64))
+
+
+def test_kmeans_update_closed_form_clusters():
+    """Samples built as mu_k +/- delta_t pairs around K centres: each centre's
+    samples average to it exactly, and every sample is assigned to its own
+    centre when the codebook is the centres themselves."""
+    sub, K = 8, 6
+    mu = np.round(RNG.standard_normal((K, sub)) * 8) / 4        # exact in fp16
+    d = np.eye(sub) * 0.25
+    ys, lab = [], []
+    for k in range(K):
+        for t in range(k + 1):                                  # k+1 pairs: counts 2, 4, ...
+            ys += [mu[k] + d[t % sub], mu[k] - d[t % sub]]
+            lab += [k, k]
+    ys = np.array(ys)
+    lab = np.array(lab)
+    new, m64, cnt, am = oracle.kmeans_update(ys, lab, f16bits(mu))
+    assert np.array_equal(m64, mu)
+    assert np.array_equal(bits_to_f64(new), mu)
+    assert np.array_equal(cnt, 2 * (np.arange(K) + 1))
+    assert np.allclose(am, [np.abs(ys[lab == k]).mean(0) for k in range(K)], rtol=1e-15)
+
+
+def test_kmeans_update_is_the_sse_minimiser_and_lloyd_descends():
+    """For fixed assignments the update gives, per centroid, the point with the
+    least summed squared distance (any perturbation costs more), and repeated
+    steps never raise the within-cluster SSE by more than the fp16 storage
+    rounding of the centroids."""
+    D, sub, n, K = 32, 8, 60, 10
+    x = rand_x(n, D)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    cbb = f16bits(RNG.standard_normal((K, sub)))
+    idx, new, m64, cnt, am, ysub = oracle.kmeans_step(x, lam, s, cbb, sub)
+    lab = idx.reshape(-1)
+    for k in np.flatnonzero(cnt):
+        yk = ysub[lab == k]
+        best = ((yk - m64[k]) ** 2).sum()
+        for _ in range(5):
+            pert = m64[k] + RNG.standard_normal(sub) * 1e-3
+            assert ((yk - pert) ** 2).sum() > best
+    sse_prev, prev_idx = None, None
+    for it in range(200):
+        idx, new, m64, cnt, am, ysub = oracle.kmeans_step(x, lam, s, cbb, sub)
+        C = bits_to_f64(cbb)
+        sse = ((ysub - C[idx.reshape(-1)]) ** 2).sum()
+        if sse_prev is not None:
+            slack = 2.0 ** -10 * np.abs(ysub).sum() * 4
+            assert sse <= sse_prev + slack
+        if prev_idx is not None and np.array_equal(idx, prev_idx):
+            break
+        sse_prev, prev_idx = sse, idx
+        cbb = new
+    else:
+        raise AssertionError("Lloyd steps did not settle")
+    # settled: the same assignments give back the same (stored) centroids
+    assert it > 1 and np.array_equal(new, cbb)
+
+
 # ------------------------------------------------------- decode attention
 def attn_case(L, T, H, R, D, G, seed, qscale=1.0):
     """Random int4 K/V caches produced by the oracle's own (pinned) quantizer,

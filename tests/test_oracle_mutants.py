@@ -52,6 +52,13 @@ MUTANTS = {
     "mx_exponent_off_by_one": ("int e = (E - 1) - 2;", "int e = (E - 1) - 1;"),
     "mx_subnormal_quarter": ("double mag = e == 0 ? 0.5 * m", "double mag = e == 0 ? 0.25 * m"),
     "mx_scale_multiplies": ("q[i] = (int8_t)e2m1_code(ldexp(y[i], -e));", "q[i] = (int8_t)e2m1_code(ldexp(y[i], e));"),
+    "kmeans_divides_by_count_plus_one": ("mean64[e] /= (double)counts[k];", "mean64[e] /= (double)(counts[k] + 1);"),
+    "kmeans_empty_cluster_to_zero": ("mean64[e] = kvqo_f16_to_f64(cb_old[e]);\n                cb_new[e] = cb_old[e];",
+                                     "mean64[e] = 0.0;\n                cb_new[e] = 0;"),
+    "kmeans_drops_first_sample": ("for (int64_t i = 0; i < n; i++) {\n        int k = idx[i];",
+                                  "for (int64_t i = 1; i < n; i++) {\n        int k = idx[i];"),
+    "kmeans_coordinate_shifted": ("mean64[(int64_t)k * sub + t] += ysub[i * sub + t];",
+                                  "mean64[(int64_t)k * sub + t] += ysub[i * sub + (t + 1) % sub];"),
     "attend_no_max_shift": ("double w = exp(a[t] - amax);", "double w = exp(a[t]);"),
     "attend_scale_dropped": ("a[t] = scale * dot;", "a[t] = dot;"),
     "attend_values_from_keys": ("o[c] += w * vh[(int64_t)t * D + c];", "o[c] += w * kh[(int64_t)t * D + c];"),
@@ -90,6 +97,9 @@ BATTERY = [
     ("test_e2m1_rounding_ties_even_and_saturation", {"golden_dir": None}),
     ("test_mxfp4_block_scale_rule_and_invariants", {"D": 128, "golden_dir": None}),
     ("test_mxfp4_zero_block_and_single_spike", {"golden_dir": None}),
+    ("test_kmeans_step_matches_scipy_lloyd_iteration", {}),
+    ("test_kmeans_update_closed_form_clusters", {}),
+    ("test_kmeans_update_is_the_sse_minimiser_and_lloyd_descends", {}),
     ("test_attend_single_token_returns_its_value", {}),
     ("test_attend_zero_query_is_mean_of_values", {}),
     ("test_attend_matches_torch_sdpa", {"R": 4}),
