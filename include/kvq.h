@@ -195,6 +195,21 @@ kvq_status kvq_vq_decode(kvq_shape shape, kvq_view idx_u16, const void* codebook
                          int32_t sub_dim, const float* lambda, const int8_t* signs,
                          kvq_view out_f16, void* stream);
 
+/* Product VQ with one-byte indices, for codebooks of at most 256 centroids
+ * (the 8-bit value codebooks of the VecInfer blog, "The numbers":
+ * value_codebook_bits = 8).  The same computation as kvq_vq_encode /
+ * kvq_vq_decode, including the rotation with the tensor's own lambda;
+ * idx_u8 holds D/sub_dim bytes per vector (4-byte aligned data and strides).
+ * KVQ_ERR_SHAPE if n_centroids > 256. */
+kvq_status kvq_vq_encode_u8(kvq_shape shape, kvq_view x_f16, const float* lambda,
+                            const int8_t* signs, const void* codebook_f16,
+                            int64_t codebook_layer_stride, int32_t n_centroids,
+                            int32_t sub_dim, kvq_view idx_u8, void* stream);
+kvq_status kvq_vq_decode_u8(kvq_shape shape, kvq_view idx_u8, const void* codebook_f16,
+                            int64_t codebook_layer_stride, int32_t n_centroids,
+                            int32_t sub_dim, const float* lambda, const int8_t* signs,
+                            kvq_view out_f16, void* stream);
+
 /* Decode attention straight from the int4 cache (VeloxQuant-MLX package
  * description, "Fused group-affine (KIVI-style) attention": one query per
  * head, online softmax accumulated in fp32, codes turned into values in

@@ -78,6 +78,10 @@ def lib():
     L.kvq_vq_encode.argtypes = [Shape, View, P, P, P, I64, I32, I32, View, P]
     L.kvq_vq_decode.restype = ctypes.c_int
     L.kvq_vq_decode.argtypes = [Shape, View, P, I64, I32, I32, P, P, View, P]
+    L.kvq_vq_encode_u8.restype = ctypes.c_int
+    L.kvq_vq_encode_u8.argtypes = [Shape, View, P, P, P, I64, I32, I32, View, P]
+    L.kvq_vq_decode_u8.restype = ctypes.c_int
+    L.kvq_vq_decode_u8.argtypes = [Shape, View, P, I64, I32, I32, P, P, View, P]
     L.kvq_attend_decode.restype = ctypes.c_int
     L.kvq_attend_decode.argtypes = [Shape, I32, P, View, View, View, View, P, P, P, I32, P, ctypes.c_float, P, P,
                                     I64, P]
@@ -261,11 +265,7 @@ def dequantize_mxfp4(codes, scales, lam, signs, out=None, stream=None):
 
 
 # -------------------------------------------------------------------- VQ
-def vq_encode(x, lam, signs, codebook, sub_dim: int = 8, idx=None, codebook_layer_stride: int = 0,
-              stream=None):
-    """Product-VQ encode of x [L, T, H, D] fp16 against codebook [H, K, sub_dim]
-    fp16 (or [L, H, K, sub_dim] with codebook_layer_stride = H*K*sub_dim) ->
-    indices [L, T, H, D/sub_dim] stored in an int16 tensor (read as uint16)."""
+def _vq_encode(x, lam, signs, codebook, sub_dim, idx, codebook_layer_stride, stream, u8):
     torch = _torch()
     _need(x, torch.float16, "x")
     _need(codebook, torch.float16, "codebook")
@@ -273,20 +273,20 @@ def vq_encode(x, lam, signs, codebook, sub_dim: int = 8, idx=None, codebook_laye
     K = codebook.shape[-2]
     if not codebook.is_contiguous():
         raise ValueError("codebook must be contiguous")
+    dt = torch.uint8 if u8 else torch.int16
     if idx is None:
-        idx = torch.empty((L, T, H, D // sub_dim), dtype=torch.int16, device=x.device)
-    _need(idx, torch.int16, "idx")
+        idx = torch.empty((L, T, H, D // sub_dim), dtype=dt, device=x.device)
+    _need(idx, dt, "idx")
     pl, ps = _params(lam, signs, L, H, D)
-    _check(lib().kvq_vq_encode(_shape(x, D), _view(x), pl, ps, ctypes.c_void_p(codebook.data_ptr()),
-                               int(codebook_layer_stride), int(K), int(sub_dim), _view(idx), _stream(stream)))
+    fn = lib().kvq_vq_encode_u8 if u8 else lib().kvq_vq_encode
+    _check(fn(_shape(x, D), _view(x), pl, ps, ctypes.c_void_p(codebook.data_ptr()), int(codebook_layer_stride),
+              int(K), int(sub_dim), _view(idx), _stream(stream)))
     return idx
 
 
-def vq_decode(idx, codebook, lam, signs, sub_dim: int = 8, out=None, codebook_layer_stride: int = 0,
-              stream=None):
-    """Product-VQ decode: indices [L, T, H, D/sub_dim] -> fp16 [L, T, H, D]."""
+def _vq_decode(idx, codebook, lam, signs, sub_dim, out, codebook_layer_stride, stream, u8):
     torch = _torch()
-    _need(idx, torch.int16, "idx")
+    _need(idx, torch.uint8 if u8 else torch.int16, "idx")
     _need(codebook, torch.float16, "codebook")
     L, T, H, nsub = idx.shape
     D = nsub * sub_dim
@@ -295,10 +295,37 @@ def vq_decode(idx, codebook, lam, signs, sub_dim: int = 8, out=None, codebook_la
         out = torch.empty((L, T, H, D), dtype=torch.float16, device=idx.device)
     _need(out, torch.float16, "out")
     pl, ps = _params(lam, signs, L, H, D)
-    _check(lib().kvq_vq_decode(_shape(idx, D), _view(idx), ctypes.c_void_p(codebook.data_ptr()),
-                               int(codebook_layer_stride), int(K), int(sub_dim), pl, ps, _view(out),
-                               _stream(stream)))
+    fn = lib().kvq_vq_decode_u8 if u8 else lib().kvq_vq_decode
+    _check(fn(_shape(idx, D), _view(idx), ctypes.c_void_p(codebook.data_ptr()), int(codebook_layer_stride), int(K),
+              int(sub_dim), pl, ps, _view(out), _stream(stream)))
     return out
+
+
+def vq_encode(x, lam, signs, codebook, sub_dim: int = 8, idx=None, codebook_layer_stride: int = 0,
+              stream=None):
+    """Product-VQ encode of x [L, T, H, D] fp16 against codebook [H, K, sub_dim]
+    fp16 (or [L, H, K, sub_dim] with codebook_layer_stride = H*K*sub_dim) ->
+    indices [L, T, H, D/sub_dim] stored in an int16 tensor (read as uint16)."""
+    return _vq_encode(x, lam, signs, codebook, sub_dim, idx, codebook_layer_stride, stream, False)
+
+
+def vq_decode(idx, codebook, lam, signs, sub_dim: int = 8, out=None, codebook_layer_stride: int = 0,
+              stream=None):
+    """Product-VQ decode: indices [L, T, H, D/sub_dim] -> fp16 [L, T, H, D]."""
+    return _vq_decode(idx, codebook, lam, signs, sub_dim, out, codebook_layer_stride, stream, False)
+
+
+def vq_encode_u8(x, lam, signs, codebook, sub_dim: int = 8, idx=None, codebook_layer_stride: int = 0,
+                 stream=None):
+    """vq_encode with one-byte indices (codebooks of at most 256 centroids) ->
+    uint8 [L, T, H, D/sub_dim]."""
+    return _vq_encode(x, lam, signs, codebook, sub_dim, idx, codebook_layer_stride, stream, True)
+
+
+def vq_decode_u8(idx, codebook, lam, signs, sub_dim: int = 8, out=None, codebook_layer_stride: int = 0,
+                 stream=None):
+    """vq_decode of uint8 indices -> fp16 [L, T, H, D]."""
+    return _vq_decode(idx, codebook, lam, signs, sub_dim, out, codebook_layer_stride, stream, True)
 
 
 # -------------------------------------------------------- decode attention

@@ -177,10 +177,11 @@ kvq_status int4_common(const kvq_shape& shape, const kvq_view& x, const float* l
 
 kvq_status vq_common(const kvq_shape& shape, const kvq_view& x, const float* lambda, const int8_t* signs,
                      const void* codebook, int64_t cb_layer_stride, int32_t K, int32_t sub,
-                     const kvq_view& idx, kvq::VqArgs& a, bool x_is_output)
+                     const kvq_view& idx, kvq::VqArgs& a, bool x_is_output, bool idx8 = false)
 {
     KVQ_TRY(check_shape(shape));
     if (K < 1 || K > 65536) return fail(KVQ_ERR_SHAPE, "n_centroids=%d; must be in 1..65536", K);
+    if (idx8 && K > 256) return fail(KVQ_ERR_SHAPE, "n_centroids=%d; one-byte indices need at most 256", K);
     if (sub <= 0 || shape.head_dim % sub) return fail(KVQ_ERR_SHAPE, "sub_dim=%d must divide head_dim", sub);
     if (sub != 8) return fail(KVQ_ERR_UNSUPPORTED, "sub_dim=%d; only 8 is instantiated", sub);
     if (empty(shape)) return KVQ_OK;
@@ -191,7 +192,8 @@ kvq_status vq_common(const kvq_shape& shape, const kvq_view& x, const float* lam
     if ((cb_layer_stride * 2) % 16) return fail(KVQ_ERR_ALIGN, "codebook_layer_stride*2 bytes must be a multiple of 16");
     const int64_t D = shape.head_dim;
     KVQ_TRY(check_view(x_is_output ? "out_f16" : "x_f16", x, 2, D, 16, shape));
-    KVQ_TRY(check_view("idx_u16", idx, 2, D / sub, 4, shape));
+    KVQ_TRY(check_view(idx8 ? "idx_u8" : "idx_u16", idx, idx8 ? 1 : 2, D / sub, 4, shape));
+    a.idx8 = idx8 ? 1 : 0;
     a.L = (int32_t)shape.layers;
     a.T = (int32_t)shape.tokens;
     a.H = (int32_t)shape.heads;
@@ -259,6 +261,54 @@ kvq_status attn_check(const kvq_shape& shape, int32_t R)
 
 }  // namespace
 
+namespace {
+
+kvq_status vq_encode_any(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,
+                         const void* codebook_f16, int64_t codebook_layer_stride, int32_t n_centroids,
+                         int32_t sub_dim, kvq_view idx, void* stream, bool idx8)
+{
+    g_err[0] = 0;
+    kvq::VqArgs a;
+    KVQ_TRY(vq_common(shape, x_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
+                      idx, a, false, idx8));
+    if (empty(shape)) return KVQ_OK;
+    // one block per CU holds the 144 KB of LDS; four blocks' worth of units
+    // per CU balance the tail
+    const int64_t blocks = std::min<int64_t>(a.enc_n_units, 4 * (int64_t)device_cus());
+    a.enc_units_per_block = (int32_t)((a.enc_n_units + blocks - 1) / blocks);
+    return hip_status(kvq::launch_vq_encode(a, static_cast<hipStream_t>(stream)), "kvq_vq_encode launch");
+}
+
+kvq_status vq_decode_any(kvq_shape shape, kvq_view idx, const void* codebook_f16,
+                         int64_t codebook_layer_stride, int32_t n_centroids, int32_t sub_dim,
+                         const float* lambda, const int8_t* signs, kvq_view out_f16, void* stream, bool idx8)
+{
+    g_err[0] = 0;
+    kvq::VqArgs a;
+    KVQ_TRY(vq_common(shape, out_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
+                      idx, a, true, idx8));
+    if (empty(shape)) return KVQ_OK;
+    a.dec_rows_per_range = 0;
+    a.dec_range_groups = 0;
+    if (n_centroids <= kvq::kVqChunk) {
+        // codebook in LDS: one block per CU.  The (layer, 16-token tile) rows
+        // are cut into ranges; each range is decoded by H blocks, one per
+        // head, placed on the same XCD so that the heads' indices of a token,
+        // which share cache lines, are fetched from HBM once.
+        a.token_major = 0;
+        a.tok_per_item = kvq::kTokensPerTile;
+        a.items_per_group = (int32_t)((shape.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
+        a.n_items = shape.layers * shape.heads * (int64_t)a.items_per_group;
+        const int64_t rows = shape.layers * (int64_t)a.items_per_group;
+        a.dec_range_groups = (int32_t)std::max<int64_t>(1, device_cus() / (8 * shape.heads));
+        const int64_t ranges = 8 * (int64_t)a.dec_range_groups;
+        a.dec_rows_per_range = (rows + ranges - 1) / ranges;
+    }
+    return hip_status(kvq::launch_vq_decode(a, static_cast<hipStream_t>(stream)), "kvq_vq_decode launch");
+}
+
+}  // namespace
+
 extern "C" {
 
 kvq_status kvq_quantize(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,
@@ -321,48 +371,37 @@ kvq_status kvq_dequantize_mxfp4(kvq_shape shape, kvq_view codes_u8, kvq_view sca
     return hip_status(kvq::launch_dequantize(a, static_cast<hipStream_t>(stream)), "kvq_dequantize_mxfp4 launch");
 }
 
+
 kvq_status kvq_vq_encode(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,
                          const void* codebook_f16, int64_t codebook_layer_stride, int32_t n_centroids,
                          int32_t sub_dim, kvq_view idx_u16, void* stream)
 {
-    g_err[0] = 0;
-    kvq::VqArgs a;
-    KVQ_TRY(vq_common(shape, x_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
-                      idx_u16, a, false));
-    if (empty(shape)) return KVQ_OK;
-    // one block per CU holds the 144 KB of LDS; four blocks' worth of units
-    // per CU balance the tail
-    const int64_t blocks = std::min<int64_t>(a.enc_n_units, 4 * (int64_t)device_cus());
-    a.enc_units_per_block = (int32_t)((a.enc_n_units + blocks - 1) / blocks);
-    return hip_status(kvq::launch_vq_encode(a, static_cast<hipStream_t>(stream)), "kvq_vq_encode launch");
+    return vq_encode_any(shape, x_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
+                         idx_u16, stream, false);
 }
 
 kvq_status kvq_vq_decode(kvq_shape shape, kvq_view idx_u16, const void* codebook_f16,
                          int64_t codebook_layer_stride, int32_t n_centroids, int32_t sub_dim,
                          const float* lambda, const int8_t* signs, kvq_view out_f16, void* stream)
 {
-    g_err[0] = 0;
-    kvq::VqArgs a;
-    KVQ_TRY(vq_common(shape, out_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
-                      idx_u16, a, true));
-    if (empty(shape)) return KVQ_OK;
-    a.dec_rows_per_range = 0;
-    a.dec_range_groups = 0;
-    if (n_centroids <= kvq::kVqChunk) {
-        // codebook in LDS: one block per CU.  The (layer, 16-token tile) rows
-        // are cut into ranges; each range is decoded by H blocks, one per
-        // head, placed on the same XCD so that the heads' indices of a token,
-        // which share cache lines, are fetched from HBM once.
-        a.token_major = 0;
-        a.tok_per_item = kvq::kTokensPerTile;
-        a.items_per_group = (int32_t)((shape.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
-        a.n_items = shape.layers * shape.heads * (int64_t)a.items_per_group;
-        const int64_t rows = shape.layers * (int64_t)a.items_per_group;
-        a.dec_range_groups = (int32_t)std::max<int64_t>(1, device_cus() / (8 * shape.heads));
-        const int64_t ranges = 8 * (int64_t)a.dec_range_groups;
-        a.dec_rows_per_range = (rows + ranges - 1) / ranges;
-    }
-    return hip_status(kvq::launch_vq_decode(a, static_cast<hipStream_t>(stream)), "kvq_vq_decode launch");
+    return vq_decode_any(shape, idx_u16, codebook_f16, codebook_layer_stride, n_centroids, sub_dim, lambda, signs,
+                         out_f16, stream, false);
+}
+
+kvq_status kvq_vq_encode_u8(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,
+                            const void* codebook_f16, int64_t codebook_layer_stride, int32_t n_centroids,
+                            int32_t sub_dim, kvq_view idx_u8, void* stream)
+{
+    return vq_encode_any(shape, x_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
+                         idx_u8, stream, true);
+}
+
+kvq_status kvq_vq_decode_u8(kvq_shape shape, kvq_view idx_u8, const void* codebook_f16,
+                            int64_t codebook_layer_stride, int32_t n_centroids, int32_t sub_dim,
+                            const float* lambda, const int8_t* signs, kvq_view out_f16, void* stream)
+{
+    return vq_decode_any(shape, idx_u8, codebook_f16, codebook_layer_stride, n_centroids, sub_dim, lambda, signs,
+                         out_f16, stream, true);
 }
 
 kvq_status kvq_attend_decode_workspace(kvq_shape shape, int32_t q_per_kv, int64_t* bytes)

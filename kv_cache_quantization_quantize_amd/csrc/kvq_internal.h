@@ -43,7 +43,8 @@ struct Int4Args {
 struct VqArgs {
     int32_t L, T, H, D, sub, K;
     Tensor4 x;              // fp16 keys (encode) / fp16 output (decode)
-    Tensor4 idx;            // u16, D/sub per vector
+    Tensor4 idx;            // u16 (or u8 when idx8), D/sub per vector
+    int32_t idx8;           // one-byte indices (K <= 256)
     const float* lambda;    // [L, H, D]
     const int8_t* signs;    // [D]
     const uint16_t* codebook;   // fp16 bits, [H, K, sub] per layer

@@ -71,9 +71,11 @@ __device__ __forceinline__ int stage_slot(int v, int s) { return v * NS + (s ^ (
 
 }  // namespace
 
-template <int D>
+// IDX8: one-byte indices (codebooks of at most 256 centroids), else u16.
+template <int D, bool IDX8>
 __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs a)
 {
+    typedef typename std::conditional<IDX8, uint8_t, uint16_t>::type idx_t;
     using C = VqCfg<D>;
     constexpr int NS = C::NS, NJ = C::NJ, N = C::N, GPR = C::GPR, ROUNDS = C::ROUNDS, WAVES = C::WAVES;
 
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
     int cur_cb = -1;
 
     const _Float16* __restrict__ xg = static_cast<const _Float16*>(a.x.data);
-    uint16_t* __restrict__ ig = static_cast<uint16_t*>(a.idx.data);
+    idx_t* __restrict__ ig = static_cast<idx_t*>(a.idx.data);
 
     for (int64_t u = ubeg; u < uend; ++u) {
         // ---- unit -> (layer, head, token chunk); codebook-major order ----------
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
                 const int key = sv / NS, s = sv % NS;
                 const int tk = t0 + key;
                 if (half == 0 && tk < a.T)
-                    ig[(int64_t)l * a.idx.sl + (int64_t)h * a.idx.sh + (int64_t)tk * a.idx.st + s] = (uint16_t)idx;
+                    ig[(int64_t)l * a.idx.sl + (int64_t)h * a.idx.sh + (int64_t)tk * a.idx.st + s] = (idx_t)idx;
             }
         }
     }
@@ -482,7 +484,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void vq_decode_kernel(VqArgs a
 // layer's part of the range into contiguous runs.  The centroid gathers are
 // LDS reads rather than 16-byte pieces of L2 lines.  Each wavefront keeps the
 // indices of its next three items in flight.
-template <int D>
+template <int D, bool IDX8>
 __global__ __launch_bounds__(64 * VqDecLds<D>::WAVES) void vq_decode_lds_kernel(VqArgs a)
 {
     constexpr int WAVES = VqDecLds<D>::WAVES;
@@ -490,7 +492,8 @@ __global__ __launch_bounds__(64 * VqDecLds<D>::WAVES) void vq_decode_lds_kernel(
     constexpr int N = NJ * 8;
     constexpr int CV = D / 8;
     constexpr int VPK = 1024 / (2 * D);
-    constexpr int NIW = D / 64;
+    constexpr int IB = (D / 8) * (IDX8 ? 1 : 2);   // index bytes per key
+    constexpr int NIW = (IB + 15) / 16;           // 16-byte loads (8 bytes: one 8-byte load)
 
     __shared__ uint4 cb_lds[kVqChunk];
     __shared__ uint4 lds_out[WAVES][16 * CV];
@@ -505,13 +508,16 @@ __global__ __launch_bounds__(64 * VqDecLds<D>::WAVES) void vq_decode_lds_kernel(
     const float lane_sign = (__builtin_popcount(q) & 1) ? -1.0f : 1.0f;
     const bool hi_pair = (q & 2) != 0;
     const uint32_t half_shift = (q & 1) * 16;
+    const uint32_t byte_shift = q * 8;
     const uint32_t kmax = (uint32_t)(a.K - 1);
 
     _Float16* __restrict__ og = static_cast<_Float16*>(a.x.data);
-    const uint16_t* __restrict__ ig = static_cast<const uint16_t*>(a.idx.data);
+    const uint8_t* __restrict__ ig = static_cast<const uint8_t*>(a.idx.data);
+    constexpr int ISZ = IDX8 ? 1 : 2;             // index strides are in elements
     uint4* my_out = lds_out[wid];
     const int row_c = lane % CV;
     typedef uint4 uint4_a4 __attribute__((aligned(4)));
+    typedef uint2 uint2_a4 __attribute__((aligned(4)));
 
     // Block b runs on XCD b % 8.  Its head is (b / 8) % H and its row range
     // is ((b / 8) / H) * 8 + b % 8, so the H blocks of a range share an XCD
@@ -548,13 +554,18 @@ __global__ __launch_bounds__(64 * VqDecLds<D>::WAVES) void vq_decode_lds_kernel(
         const int end = min(begin + per_wave, i1);
         if (begin >= end) continue;
 
-        const uint16_t* ig_lh = ig + (int64_t)l * a.idx.sl + (int64_t)h * a.idx.sh;
-        // the quad's index block; tokens past the end read the last token's
+        const uint8_t* ig_lh = ig + ((int64_t)l * a.idx.sl + (int64_t)h * a.idx.sh) * ISZ;
+        // the quad's index row; tokens past the end read the last token's
         auto load_idx = [&](int item, uint4 (&W)[NIW]) {
             const int t = min(item * kTokensPerTile + slot, a.T - 1);
-            const uint16_t* ip = ig_lh + (int64_t)t * a.idx.st;
+            const uint8_t* ip = ig_lh + (int64_t)t * a.idx.st * ISZ;
+            if constexpr (IB >= 16) {
 #pragma unroll
-            for (int i = 0; i < NIW; i++) W[i] = *reinterpret_cast<const uint4_a4*>(ip + 8 * i);
+                for (int i = 0; i < NIW; i++) W[i] = *reinterpret_cast<const uint4_a4*>(ip + 16 * i);
+            } else {
+                const uint2 w2 = *reinterpret_cast<const uint2_a4*>(ip);
+                W[0] = make_uint4(w2.x, w2.y, 0u, 0u);
+            }
         };
 
         float m[N];
@@ -569,9 +580,18 @@ __global__ __launch_bounds__(64 * VqDecLds<D>::WAVES) void vq_decode_lds_kernel(
             uint4 cv[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; j++) {
-                const uint4 wd = W[j / 2];
-                const uint32_t d = (j & 1) ? (hi_pair ? wd.w : wd.z) : (hi_pair ? wd.y : wd.x);
-                cv[j] = cb_lds[min(__builtin_amdgcn_ubfe(d, half_shift, 16), kmax)];
+                uint32_t k;
+                if constexpr (IDX8) {
+                    // sub-vector 4j + q is byte q of word j % 4 of 16-byte piece j / 4
+                    const uint4 wd = W[j / 4];
+                    const uint32_t d = (j & 3) == 0 ? wd.x : (j & 3) == 1 ? wd.y : (j & 3) == 2 ? wd.z : wd.w;
+                    k = __builtin_amdgcn_ubfe(d, byte_shift, 8);
+                } else {
+                    const uint4 wd = W[j / 2];
+                    const uint32_t d = (j & 1) ? (hi_pair ? wd.w : wd.z) : (hi_pair ? wd.y : wd.x);
+                    k = __builtin_amdgcn_ubfe(d, half_shift, 16);
+                }
+                cv[j] = cb_lds[min(k, kmax)];
             }
             load_idx(min(item + 3, end - 1), W);
             __builtin_amdgcn_sched_barrier(0);   // issue the indices before the compute
@@ -636,7 +656,8 @@ template <int D>
 hipError_t launch_enc(const VqArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)((a.enc_n_units + a.enc_units_per_block - 1) / a.enc_units_per_block));
-    hipLaunchKernelGGL((vq_encode_kernel<D>), grid, dim3(64 * VqCfg<D>::WAVES), 0, s, a);
+    if (a.idx8) hipLaunchKernelGGL((vq_encode_kernel<D, true>), grid, dim3(64 * VqCfg<D>::WAVES), 0, s, a);
+    else hipLaunchKernelGGL((vq_encode_kernel<D, false>), grid, dim3(64 * VqCfg<D>::WAVES), 0, s, a);
     return hipGetLastError();
 }
 
@@ -645,9 +666,11 @@ hipError_t launch_dec(const VqArgs& a, hipStream_t s)
 {
     if (a.dec_rows_per_range > 0) {
         const dim3 grid((unsigned)(8 * a.H * a.dec_range_groups));
-        hipLaunchKernelGGL((vq_decode_lds_kernel<D>), grid, dim3(64 * VqDecLds<D>::WAVES), 0, s, a);
+        if (a.idx8) hipLaunchKernelGGL((vq_decode_lds_kernel<D, true>), grid, dim3(64 * VqDecLds<D>::WAVES), 0, s, a);
+        else hipLaunchKernelGGL((vq_decode_lds_kernel<D, false>), grid, dim3(64 * VqDecLds<D>::WAVES), 0, s, a);
         return hipGetLastError();
     }
+    if (a.idx8) return hipErrorInvalidValue;   // one-byte indices imply K <= 256: the LDS path
     const dim3 grid((unsigned)((a.dec_n_waves + kWavesPerBlock - 1) / kWavesPerBlock));
     if (a.token_major) hipLaunchKernelGGL((vq_decode_kernel<D, true>), grid, dim3(64 * kWavesPerBlock), 0, s, a);
     else hipLaunchKernelGGL((vq_decode_kernel<D, false>), grid, dim3(64 * kWavesPerBlock), 0, s, a);

@@ -10,7 +10,7 @@ from the device), so neither side needs to regenerate them.
 
 Seeds: seed(config i, purpose p) = 1000 * i + p with p = 1 K data, 2 V data,
 3 K calibration, 4 V calibration, 5 signs, 6 outlier-channel / channel-scale
-choice, 7 codebook.
+choice, 7 key codebook, 8 value codebook.
 
 Calibration (input recipe, not part of the quantizer): for every (layer,
 head, channel) lambda = 1 / sqrt(mean over 16 calibration tokens of x^2),
@@ -27,7 +27,7 @@ from dataclasses import dataclass, field
 import torch
 
 CALIB_TOKENS = 16
-P_KDATA, P_VDATA, P_KCAL, P_VCAL, P_SIGNS, P_CHAN, P_CODEBOOK = 1, 2, 3, 4, 5, 6, 7
+P_KDATA, P_VDATA, P_KCAL, P_VCAL, P_SIGNS, P_CHAN, P_CODEBOOK, P_VCODEBOOK = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def seed(config: int, purpose: int) -> int:
@@ -135,6 +135,7 @@ class Config:
     v_dist: Dist | None            # None = keys only
     vq: bool = False
     n_centroids: int = 4096
+    v_centroids: int = 256             # value codebooks (one-byte indices)
     sub_dim: int = 8
     notes: str = ""
     extra: dict = field(default_factory=dict)
@@ -162,7 +163,8 @@ def config(name: str, T: int | None = None) -> Config:
                       Dist("normal", lognormal_channels=True))
     if name == "vq":
         return Config(4, name, 36, 8192 if T is None else T, 8, 128, 0,
-                      Dist("normal", lognormal_channels=True), None, vq=True)
+                      Dist("normal", lognormal_channels=True), Dist("normal", lognormal_channels=True), vq=True,
+                      notes="keys: 4096-centroid codebooks (12-bit); values: 256-centroid codebooks (8-bit)")
     raise KeyError(name)
 
 
@@ -171,7 +173,8 @@ CONFIG_NAMES = ("tiny", "qwen2.5-1.5b", "gemma-3-1b", "qwen3-8b", "vq")
 
 def make_inputs(cfg: Config, device="cpu", want_v: bool = True) -> dict:
     """Draw one config: K (and V), their lambdas, the sign vector and, for the
-    VQ config, the per-head codebook [H, K, sub] fp16 ~ N(0, 1)."""
+    VQ config, the per-head key codebook [H, K, sub] and value codebook
+    [H, 256, sub], fp16 ~ N(0, 1)."""
     i = cfg.index
     out = {"cfg": cfg}
     out["K"] = draw(cfg.L, cfg.T, cfg.H, cfg.D, cfg.k_dist, seed(i, P_KDATA), seed(i, P_CHAN), device)
@@ -187,6 +190,9 @@ def make_inputs(cfg: Config, device="cpu", want_v: bool = True) -> dict:
         g = _gen(seed(i, P_CODEBOOK), "cpu")
         cb = torch.randn((cfg.H, cfg.n_centroids, cfg.sub_dim), generator=g, dtype=torch.float32)
         out["codebook"] = cb.to(torch.float16).to(device)
+        g = _gen(seed(i, P_VCODEBOOK), "cpu")
+        cb = torch.randn((cfg.H, cfg.v_centroids, cfg.sub_dim), generator=g, dtype=torch.float32)
+        out["codebook_V"] = cb.to(torch.float16).to(device)
     return out
 
 

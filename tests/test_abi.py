@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "kvq_quantize", "kvq_dequantize", "kvq_vq_encode", "kvq_vq_decode",
         "kvq_attend_decode", "kvq_attend_decode_workspace", "kvq_quantize_int8", "kvq_dequantize_int8",
-        "kvq_quantize_mxfp4", "kvq_dequantize_mxfp4",
+        "kvq_quantize_mxfp4", "kvq_dequantize_mxfp4", "kvq_vq_encode_u8", "kvq_vq_decode_u8",
         "kvq_status_string", "kvq_last_error", "kvq_version"])
 
 
@@ -143,6 +143,24 @@ def test_vq_validation(lib):
     assert enc(ix=view(addr=A + 2, row=16)) == ALIGN
     assert lib.kvq_vq_decode(sh, idx, P(A), 0, 4096, 8, P(A), P(A), view(addr=0), None) == NULL
     assert lib.kvq_vq_decode(shape(T=0), idx, P(A), 0, 4096, 8, P(A), P(A), x, None) == OK
+
+
+def test_vq_u8_validation(lib):
+    P = ctypes.c_void_p
+    sh = shape()
+    x = view()
+    idx = view(row=16)
+
+    def enc(K=256, ix=idx, shp=sh):
+        return lib.kvq_vq_encode_u8(shp, x, P(A), P(A), P(A), 0, K, 8, ix, None)
+
+    assert enc(shp=shape(T=0)) == OK
+    assert enc(K=257) == SHAPE
+    assert enc(K=0) == SHAPE
+    assert enc(ix=view(addr=A + 2, row=16)) == ALIGN          # one-byte rows still need 4-byte alignment
+    assert lib.kvq_vq_decode_u8(sh, idx, P(A), 0, 300, 8, P(A), P(A), x, None) == SHAPE
+    assert lib.kvq_vq_decode_u8(sh, idx, P(A), 0, 256, 8, P(A), P(A), view(addr=0), None) == NULL
+    assert lib.kvq_vq_decode_u8(shape(T=0), idx, P(A), 0, 256, 8, P(A), P(A), x, None) == OK
 
 
 def test_binding_raises_without_gpu_tensors():
