@@ -210,6 +210,34 @@ kvq_status kvq_vq_decode_u8(kvq_shape shape, kvq_view idx_u8, const void* codebo
                             int32_t sub_dim, const float* lambda, const int8_t* signs,
                             kvq_view out_f16, void* stream);
 
+/* Codebook training (VecInfer blog, "What VecInfer does, and the calibration
+ * caveat up front": codebooks trained k-means style on synthetic samples):
+ * one Lloyd iteration over per-head codebooks [heads, n_centroids, sub_dim]
+ * shared by all layers.  Every vector of x (all layers of head h train
+ * codebook h) is rotated as kvq_vq_encode does and split into sub-vectors;
+ *   1. assignment: idx_u16 receives, per sub-vector, the lowest index of a
+ *      nearest centroid of codebook_f16 (exactly kvq_vq_encode's output);
+ *   2. update: new_codebook_f16[h, k] = fp16 (round to nearest even) of the
+ *      mean of the rotated sub-vectors assigned to centroid k of head h;
+ *      a centroid with none keeps its value; counts[h, k] = how many.
+ *   n_centroids   1 .. 4096;  sub_dim 8;
+ *   new_codebook  16-byte aligned, may be codebook_f16 itself (in place);
+ *   counts        uint32 [heads, n_centroids], 4-byte aligned;
+ *   workspace     device scratch of at least kvq_kmeans_step_workspace()
+ *                 bytes, 16-byte aligned, owned by the caller; no state is
+ *                 kept in it between calls.
+ * The sums are taken in fp32 per block of work and across blocks in fp64;
+ * the order of the fp32 additions inside a block is not fixed, so the last
+ * bit of a centroid can differ between runs.  Views and errors as for
+ * kvq_vq_encode; KVQ_ERR_SHAPE for a short workspace. */
+kvq_status kvq_kmeans_step_workspace(kvq_shape shape, int32_t n_centroids, int32_t sub_dim,
+                                     int64_t* bytes);
+kvq_status kvq_kmeans_step(kvq_shape shape, kvq_view x_f16, const float* lambda,
+                           const int8_t* signs, const void* codebook_f16, int32_t n_centroids,
+                           int32_t sub_dim, kvq_view idx_u16, void* new_codebook_f16,
+                           uint32_t* counts, void* workspace, int64_t workspace_bytes,
+                           void* stream);
+
 /* Decode attention straight from the int4 cache (VeloxQuant-MLX package
  * description, "Fused group-affine (KIVI-style) attention": one query per
  * head, online softmax accumulated in fp32, codes turned into values in

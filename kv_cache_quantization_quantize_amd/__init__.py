@@ -78,6 +78,10 @@ def lib():
     L.kvq_vq_encode.argtypes = [Shape, View, P, P, P, I64, I32, I32, View, P]
     L.kvq_vq_decode.restype = ctypes.c_int
     L.kvq_vq_decode.argtypes = [Shape, View, P, I64, I32, I32, P, P, View, P]
+    L.kvq_kmeans_step_workspace.restype = ctypes.c_int
+    L.kvq_kmeans_step_workspace.argtypes = [Shape, I32, I32, ctypes.POINTER(ctypes.c_int64)]
+    L.kvq_kmeans_step.restype = ctypes.c_int
+    L.kvq_kmeans_step.argtypes = [Shape, View, P, P, P, I32, I32, View, P, P, P, I64, P]
     L.kvq_vq_encode_u8.restype = ctypes.c_int
     L.kvq_vq_encode_u8.argtypes = [Shape, View, P, P, P, I64, I32, I32, View, P]
     L.kvq_vq_decode_u8.restype = ctypes.c_int
@@ -326,6 +330,53 @@ def vq_decode_u8(idx, codebook, lam, signs, sub_dim: int = 8, out=None, codebook
                  stream=None):
     """vq_decode of uint8 indices -> fp16 [L, T, H, D]."""
     return _vq_decode(idx, codebook, lam, signs, sub_dim, out, codebook_layer_stride, stream, True)
+
+
+# ------------------------------------------------------ codebook training
+def kmeans_step_workspace_bytes(L: int, T: int, H: int, D: int, n_centroids: int, sub_dim: int = 8) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().kvq_kmeans_step_workspace(Shape(L, T, H, D), int(n_centroids), int(sub_dim), ctypes.byref(n)))
+    return int(n.value)
+
+
+def kmeans_step(x, lam, signs, codebook, sub_dim: int = 8, idx=None, new_codebook=None, counts=None,
+                workspace=None, stream=None):
+    """One Lloyd iteration for the per-head codebooks [H, K, sub_dim] (fp16)
+    on the samples x [L, T, H, D] fp16 -> (idx int16 [L, T, H, D/sub_dim]
+    assignments to the input codebook, new codebook fp16 [H, K, sub_dim],
+    counts int32 [H, K] (read as uint32))."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(codebook, torch.float16, "codebook")
+    if not codebook.is_contiguous():
+        raise ValueError("codebook must be contiguous")
+    L, T, H, D = x.shape
+    K = codebook.shape[-2]
+    if idx is None:
+        idx = torch.empty((L, T, H, D // sub_dim), dtype=torch.int16, device=x.device)
+    _need(idx, torch.int16, "idx")
+    if new_codebook is None:
+        new_codebook = torch.empty_like(codebook)
+    _need(new_codebook, torch.float16, "new_codebook")
+    if not new_codebook.is_contiguous():
+        raise ValueError("new_codebook must be contiguous")
+    if counts is None:
+        counts = torch.empty((H, K), dtype=torch.int32, device=x.device)
+    _need(counts, torch.int32, "counts")
+    if tuple(counts.shape) != (H, K) or not counts.is_contiguous():
+        raise ValueError("counts must be a contiguous int32 [heads, n_centroids] tensor")
+    if tuple(new_codebook.shape) != tuple(codebook.shape):
+        raise ValueError("new_codebook must have the codebook's shape")
+    need = kmeans_step_workspace_bytes(L, T, H, D, K, sub_dim)
+    if workspace is None:
+        workspace = torch.empty(max(16, need), dtype=torch.uint8, device=x.device)
+    _need(workspace, torch.uint8, "workspace")
+    pl, ps = _params(lam, signs, L, H, D)
+    _check(lib().kvq_kmeans_step(_shape(x, D), _view(x), pl, ps, ctypes.c_void_p(codebook.data_ptr()), int(K),
+                                 int(sub_dim), _view(idx), ctypes.c_void_p(new_codebook.data_ptr()),
+                                 ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+                                 int(workspace.numel()), _stream(stream)))
+    return idx, new_codebook, counts
 
 
 # -------------------------------------------------------- decode attention

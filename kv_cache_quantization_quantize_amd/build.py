@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libkvq.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["kvq_int4.hip", "kvq_vq.hip", "kvq_attend.hip", "kvq_api.cpp"]
+SOURCES = ["kvq_int4.hip", "kvq_vq.hip", "kvq_attend.hip", "kvq_kmeans.hip", "kvq_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -307,6 +307,42 @@ kvq_status vq_decode_any(kvq_shape shape, kvq_view idx, const void* codebook_f16
     return hip_status(kvq::launch_vq_decode(a, static_cast<hipStream_t>(stream)), "kvq_vq_decode launch");
 }
 
+// Work split of the k-means update: per head, 8 * range_groups ranges of
+// (layer, 16-token tile) rows, one block per (head, range).  A function of
+// the shape and the current device only, so that the workspace query and the
+// call agree.
+struct KmPlan {
+    int32_t tiles, range_groups;
+    int64_t rows_per_range;
+};
+
+KmPlan km_plan(const kvq_shape& s)
+{
+    KmPlan p;
+    p.tiles = (int32_t)((s.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
+    p.range_groups = (int32_t)std::max<int64_t>(1, device_cus() / (8 * std::max<int64_t>(1, s.heads)));
+    const int64_t rows = s.layers * (int64_t)p.tiles;
+    const int64_t ranges = 8 * (int64_t)p.range_groups;
+    p.rows_per_range = (rows + ranges - 1) / ranges;
+    return p;
+}
+
+int64_t km_workspace_bytes(const kvq_shape& s, int32_t K, const KmPlan& p)
+{
+    // fp32 sums (8 per centroid) and a u32 count per centroid, per (head, range)
+    return s.heads * 8 * (int64_t)p.range_groups * (int64_t)K * 36;
+}
+
+kvq_status km_check(const kvq_shape& s, int32_t K, int32_t sub)
+{
+    KVQ_TRY(check_shape(s));
+    if (K < 1 || K > kvq::kKmMaxCentroids)
+        return fail(KVQ_ERR_SHAPE, "n_centroids=%d; k-means update supports 1..%d", K, kvq::kKmMaxCentroids);
+    if (sub <= 0 || s.head_dim % sub) return fail(KVQ_ERR_SHAPE, "sub_dim=%d must divide head_dim", sub);
+    if (sub != 8) return fail(KVQ_ERR_UNSUPPORTED, "sub_dim=%d; only 8 is instantiated", sub);
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -402,6 +438,63 @@ kvq_status kvq_vq_decode_u8(kvq_shape shape, kvq_view idx_u8, const void* codebo
 {
     return vq_decode_any(shape, idx_u8, codebook_f16, codebook_layer_stride, n_centroids, sub_dim, lambda, signs,
                          out_f16, stream, true);
+}
+
+kvq_status kvq_kmeans_step_workspace(kvq_shape shape, int32_t n_centroids, int32_t sub_dim, int64_t* bytes)
+{
+    g_err[0] = 0;
+    if (!bytes) return fail(KVQ_ERR_NULL, "bytes is NULL");
+    *bytes = 0;
+    KVQ_TRY(km_check(shape, n_centroids, sub_dim));
+    *bytes = km_workspace_bytes(shape, n_centroids, km_plan(shape));
+    return KVQ_OK;
+}
+
+kvq_status kvq_kmeans_step(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,
+                           const void* codebook_f16, int32_t n_centroids, int32_t sub_dim, kvq_view idx_u16,
+                           void* new_codebook_f16, uint32_t* counts, void* workspace, int64_t workspace_bytes,
+                           void* stream)
+{
+    g_err[0] = 0;
+    KVQ_TRY(km_check(shape, n_centroids, sub_dim));
+    if (shape.heads == 0) return KVQ_OK;
+    if (!codebook_f16) return fail(KVQ_ERR_NULL, "codebook is NULL");
+    if (!new_codebook_f16) return fail(KVQ_ERR_NULL, "new_codebook is NULL");
+    if (!counts) return fail(KVQ_ERR_NULL, "counts is NULL");
+    if (!aligned(codebook_f16, 16) || !aligned(new_codebook_f16, 16))
+        return fail(KVQ_ERR_ALIGN, "codebook and new_codebook must be 16-byte aligned");
+    if (!aligned(counts, 4)) return fail(KVQ_ERR_ALIGN, "counts must be 4-byte aligned");
+    const KmPlan p = km_plan(shape);
+    const int64_t need = km_workspace_bytes(shape, n_centroids, p);
+    if (!workspace) return fail(KVQ_ERR_NULL, "workspace is NULL (%lld bytes needed)", (long long)need);
+    if (!aligned(workspace, 16)) return fail(KVQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(KVQ_ERR_SHAPE, "workspace_bytes=%lld; %lld needed", (long long)workspace_bytes, (long long)need);
+    if (!empty(shape)) {
+        // assignment: the product-VQ encoder against the current codebook
+        KVQ_TRY(vq_encode_any(shape, x_f16, lambda, signs, codebook_f16, 0, n_centroids, sub_dim, idx_u16, stream,
+                              false));
+    }
+    kvq::KmArgs a;
+    a.L = (int32_t)shape.layers;
+    a.T = (int32_t)shape.tokens;
+    a.H = (int32_t)shape.heads;
+    a.D = (int32_t)shape.head_dim;
+    a.K = n_centroids;
+    a.x = t4(x_f16);
+    a.idx = t4(idx_u16);
+    a.lambda = lambda;
+    a.signs = signs;
+    a.codebook = static_cast<const uint16_t*>(codebook_f16);
+    a.new_codebook = static_cast<uint16_t*>(new_codebook_f16);
+    a.counts = counts;
+    const int64_t slots = shape.heads * 8 * (int64_t)p.range_groups * n_centroids;
+    a.part_sums = static_cast<float*>(workspace);
+    a.part_counts = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + slots * 32);
+    a.tiles = p.tiles;
+    a.range_groups = p.range_groups;
+    a.rows_per_range = p.rows_per_range;
+    return hip_status(kvq::launch_kmeans_update(a, static_cast<hipStream_t>(stream)), "kvq_kmeans_step launch");
 }
 
 kvq_status kvq_attend_decode_workspace(kvq_shape shape, int32_t q_per_kv, int64_t* bytes)

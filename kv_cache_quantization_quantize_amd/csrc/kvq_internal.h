@@ -92,6 +92,26 @@ constexpr int kAttnWaves = 4;       // wavefronts per attention block
 // Centroids staged in LDS at a time by the VQ encoder (64 KB of fp16).
 constexpr int kVqChunk = 4096;
 
+// One Lloyd (k-means) update of per-head codebooks [H, K, 8] shared by all
+// layers: per-block sums of the rotated sub-vectors assigned to each
+// centroid, then a fixed-order reduction of the blocks' partials.
+struct KmArgs {
+    int32_t L, T, H, D, K;
+    Tensor4 x;                      // fp16 samples [L, T, H, D]
+    Tensor4 idx;                    // u16 assignments, D/8 per vector
+    const float* lambda;            // [L, H, D]
+    const int8_t* signs;            // [D]
+    const uint16_t* codebook;       // fp16 bits [H, K, 8] (input)
+    uint16_t* new_codebook;         // fp16 bits [H, K, 8] (output, may alias codebook)
+    uint32_t* counts;               // [H, K]
+    float* part_sums;               // [H, ranges, K, 8]
+    uint32_t* part_counts;          // [H, ranges, K]
+    int32_t tiles;                  // 16-token tiles per layer
+    int32_t range_groups;           // ranges per head = 8 * range_groups
+    int64_t rows_per_range;         // (layer, tile) rows per range
+};
+constexpr int kKmMaxCentroids = 4096;   // LDS: 36 bytes per centroid
+
 // Wavefronts per VQ-encode block for a head dim (each stages 16 keys).
 int vq_encode_waves(int D);
 
@@ -102,5 +122,6 @@ hipError_t launch_dequantize(const Int4Args& a, hipStream_t stream);
 hipError_t launch_vq_encode(const VqArgs& a, hipStream_t stream);
 hipError_t launch_vq_decode(const VqArgs& a, hipStream_t stream);
 hipError_t launch_attend_decode(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_kmeans_update(const KmArgs& a, hipStream_t stream);
 
 }  // namespace kvq

@@ -254,3 +254,59 @@ def mxfp4_parity(x_bits, lam_rows, signs, codes_gpu, scales_gpu, out_gpu=None):
             _raise("mxfp4 dequant", rd, "first bad [row, coord]: %s gpu=%s ora=%s" % (
                 i.tolist(), f16(out_gpu)[tuple(i.T)], x64[tuple(i.T)]))
     return rep
+
+
+# ------------------------------------------------------- k-means update step
+U32 = 2.0 ** -24
+KM_ROT = 2.0 ** -19
+
+
+def kmeans_parity(x_bits, lam_rows, signs, codebook_bits, idx_gpu, new_gpu, counts_gpu, sub=8):
+    """One Lloyd step on n training vectors of one head against its codebook
+    [K, sub] (fp16 bits).
+    assignments  idx_gpu [n, D/sub] under the VQ index contract;
+    counts       exactly the oracle's counts of the GPU's own assignments;
+    centroids    the oracle's update from the GPU's own assignments: an empty
+                 centroid keeps its exact old bits; otherwise the GPU's fp16
+                 value must lie between fp16(m - delta) and fp16(m + delta),
+                 m the fp64 mean, delta = 2^-24 * n_k * mean|y| (worst-case
+                 error of an n_k-term fp32 sum) + 2^-19 * the largest
+                 per-vector RMS of y (fp32 rotation error)."""
+    x_bits = np.ascontiguousarray(x_bits, np.uint16)
+    lam_rows = np.ascontiguousarray(lam_rows, np.float32)
+    cb = np.ascontiguousarray(codebook_bits, np.uint16)
+    K = cb.shape[0]
+    idx_gpu = np.ascontiguousarray(idx_gpu, np.uint16)
+    idx_o, y64 = oracle.vq_encode(x_bits, lam_rows, signs, cb[None], np.zeros(len(x_bits), np.int32), sub)
+    if (idx_gpu >= K).any():
+        raise ParityError("GPU assignment out of range: max %d >= %d" % (idx_gpu.max(), K))
+    rep = {"assign": check_vq(y64, cb[None], np.zeros(len(x_bits), np.int32), idx_gpu, idx_o, sub)}
+    if rep["assign"]["bad"]:
+        i = np.argwhere(rep["assign"]["bad_mask"])[:5]
+        _raise("k-means assignment", rep["assign"], "first bad [vector, sub]: %s gpu=%s ora=%s" % (
+            i.tolist(), idx_gpu[tuple(i.T)], idx_o[tuple(i.T)]))
+    ysub = y64.reshape(-1, sub)
+    new_o, m64, cnt_o, am = oracle.kmeans_update(ysub, idx_gpu.reshape(-1), cb)
+    cg = np.ascontiguousarray(counts_gpu).astype(np.int64).reshape(K)
+    cbad = cg != cnt_o.astype(np.int64)
+    rep["counts"] = {"n": K, "bad": int(cbad.sum()), "total": int(cg.sum())}
+    if cbad.any():
+        i = np.flatnonzero(cbad)[:5]
+        _raise("k-means counts", rep["counts"], "first bad centroids %s gpu=%s ora=%s" % (
+            i.tolist(), cg[i], cnt_o[i]))
+    ng = np.ascontiguousarray(new_gpu, np.uint16).reshape(K, sub)
+    ymax = float(np.sqrt((y64 ** 2).mean(axis=1)).max()) if len(y64) else 0.0
+    delta = U32 * cnt_o[:, None].astype(np.float64) * am + KM_ROT * ymax
+    lo = f16(oracle.f64_to_f16(m64 - delta))
+    hi = f16(oracle.f64_to_f16(m64 + delta))
+    g = f16(ng)
+    empty = cnt_o == 0
+    ok = np.where(empty[:, None], ng == cb, (g >= lo) & (g <= hi))
+    exact = np.where(empty[:, None], ng == cb, ng == new_o)
+    rep["centroids"] = {"n": int(ng.size), "empty": int(empty.sum()), "exact": int(exact.sum()),
+                        "bad": int((~ok).sum()), "bad_mask": ~ok}
+    if (~ok).any():
+        i = np.argwhere(~ok)[:5]
+        _raise("k-means centroid", rep["centroids"], "first bad [k, t]: %s gpu=%s mean64=%s delta=%s" % (
+            i.tolist(), g[tuple(i.T)], m64[tuple(i.T)], delta[tuple(i.T)]))
+    return rep

@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
         "kvq_quantize", "kvq_dequantize", "kvq_vq_encode", "kvq_vq_decode",
         "kvq_attend_decode", "kvq_attend_decode_workspace", "kvq_quantize_int8", "kvq_dequantize_int8",
         "kvq_quantize_mxfp4", "kvq_dequantize_mxfp4", "kvq_vq_encode_u8", "kvq_vq_decode_u8",
+        "kvq_kmeans_step", "kvq_kmeans_step_workspace",
         "kvq_status_string", "kvq_last_error", "kvq_version"])
 
 
@@ -161,6 +162,37 @@ def test_vq_u8_validation(lib):
     assert lib.kvq_vq_decode_u8(sh, idx, P(A), 0, 300, 8, P(A), P(A), x, None) == SHAPE
     assert lib.kvq_vq_decode_u8(sh, idx, P(A), 0, 256, 8, P(A), P(A), view(addr=0), None) == NULL
     assert lib.kvq_vq_decode_u8(shape(T=0), idx, P(A), 0, 256, 8, P(A), P(A), x, None) == OK
+
+
+def test_kmeans_workspace_query_and_validation(lib):
+    P = ctypes.c_void_p
+    n = ctypes.c_int64(-1)
+    assert lib.kvq_kmeans_step_workspace(shape(), 4096, 8, ctypes.byref(n)) == OK
+    assert n.value > 0 and n.value % (3 * 8 * 4096 * 36) == 0      # H * 8 ranges-per-group * K * 36 bytes
+    assert lib.kvq_kmeans_step_workspace(shape(), 4097, 8, ctypes.byref(n)) == SHAPE
+    assert lib.kvq_kmeans_step_workspace(shape(), 16, 3, ctypes.byref(n)) == SHAPE
+    assert lib.kvq_kmeans_step_workspace(shape(), 16, 16, ctypes.byref(n)) == UNSUP
+    assert lib.kvq_kmeans_step_workspace(shape(), 16, 8, None) == NULL
+    need = ctypes.c_int64(0)
+    assert lib.kvq_kmeans_step_workspace(shape(), 256, 8, ctypes.byref(need)) == OK
+    x, idx = view(), view(row=16)
+
+    def step(sh=None, cb=A, K=256, new=A, cnt=A, ws=A, wsb=None):
+        return lib.kvq_kmeans_step(sh or shape(), x, P(A), P(A), P(cb), K, 8, idx, P(new), P(cnt), P(ws),
+                                   need.value if wsb is None else wsb, None)
+
+    assert step(sh=shape(H=0)) == OK                                # nothing to train
+    assert step(K=5000) == SHAPE
+    assert step(cb=0) == NULL
+    assert step(new=0) == NULL
+    assert step(cnt=0) == NULL
+    assert step(ws=0) == NULL
+    assert step(cb=A + 8) == ALIGN
+    assert step(new=A + 8) == ALIGN
+    assert step(cnt=A + 2) == ALIGN
+    assert step(ws=A + 8) == ALIGN
+    assert step(wsb=need.value - 1) == SHAPE
+    assert b"needed" in lib.kvq_last_error()
 
 
 def test_binding_raises_without_gpu_tensors():

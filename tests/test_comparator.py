@@ -2,6 +2,7 @@
 classified as the contract says -- accepted where a legitimate fp32/fp64
 difference can produce them, rejected otherwise."""
 import numpy as np
+import pytest
 
 import oracle
 from tests import parity
@@ -87,3 +88,38 @@ def test_vq_classification():
     assert parity.check_vq(y, cbb, book, tie, ora, sub)["bad"] == 1
     far = np.array([[3, 0]], np.uint16)
     assert parity.check_vq(y, cbb, book, far, ora, sub)["bad"] == 1
+
+
+def _km_case(n=40, D=64, K=24):
+    x = RNG.standard_normal((n, D)).astype(np.float16).view(np.uint16)
+    lam = np.exp(RNG.standard_normal((n, D)) * 0.3).astype(np.float32)
+    s = (RNG.integers(0, 2, D) * 2 - 1).astype(np.int8)
+    cb = RNG.standard_normal((K, 8))
+    cb[7] = 40.0                                   # never the nearest: stays empty
+    cbb = cb.astype(np.float16).view(np.uint16)
+    idx, new, m64, cnt, am, ysub = oracle.kmeans_step(x, lam, s, cbb, 8)
+    return x, lam, s, cbb, idx, new, cnt
+
+
+def test_kmeans_classification():
+    x, lam, s, cbb, idx, new, cnt = _km_case()
+    rep = parity.kmeans_parity(x, lam, s, cbb, idx, new, cnt)
+    assert rep["centroids"]["bad"] == 0 and rep["centroids"]["empty"] >= 1
+    assert rep["centroids"]["exact"] == rep["centroids"]["n"]
+    # a count off by one is rejected
+    c2 = cnt.copy()
+    c2[int(np.argmax(cnt))] -= 1
+    with pytest.raises(parity.ParityError):
+        parity.kmeans_parity(x, lam, s, cbb, idx, new, c2)
+    # a centroid two fp16 ulps away is rejected; so is a moved empty centroid
+    k = int(np.argmax(cnt))
+    for kk, t in ((k, 3), (7, 0)):
+        n2 = new.copy()
+        n2[kk, t] += 2
+        with pytest.raises(parity.ParityError):
+            parity.kmeans_parity(x, lam, s, cbb, idx, n2, cnt)
+    # a non-nearest assignment is rejected
+    i2 = idx.copy()
+    i2[0, 0] = 7
+    with pytest.raises(parity.ParityError):
+        parity.kmeans_parity(x, lam, s, cbb, i2, new, cnt)
