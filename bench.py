@@ -107,12 +107,17 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
         "dequantize_mxfp4": ("kvq::dequantize_kernel<128, 32, true, 4, true>", nv * (2 * D + D // 2 + D // 32)),
         "attend_partial": ("kvq::attend_partial_kernel<128, 4, false>", att),
         "attend_combine": ("kvq::attend_combine_kernel<128>", None),
-        "vq_encode": ("kvq::vq_encode_kernel<128>", nk * (2 * D + 2 * (D // 8))),
-        "vq_decode": ("kvq::vq_decode_lds_kernel<128>", nk * (2 * D + 2 * (D // 8))),
+        "vq_encode": ("kvq::vq_encode_kernel<128, false>", nk * (2 * D + 2 * (D // 8))),
+        "vq_decode": ("kvq::vq_decode_lds_kernel<128, false>", nk * (2 * D + 2 * (D // 8))),
+        "vq_encode_u8": ("kvq::vq_encode_kernel<128, true>", nk * (2 * D + D // 8)),
+        "vq_decode_u8": ("kvq::vq_decode_lds_kernel<128, true>", nk * (2 * D + D // 8)),
+        # reads the keys and their assignments, writes one partial slot per block
+        "kmeans_accum": ("kvq::kmeans_accum_kernel<128>", nk * (2 * D + 2 * (D // 8)) + 256 * 4096 * 36),
+        "kmeans_finalize": ("kvq::kmeans_finalize_kernel", 256 * 4096 * 36 + 8 * 4096 * (16 + 4)),
     }
     out = {"workload": "qwen3-8b-shaped cache [36, 262144, 8, 128] fp16, group 32, one tensor per launch; "
                        "decode attention over it as 288 sequences of 32768 tokens, 4 query heads per KV head; "
-                       "vecinfer-shaped keys [36, 8192, 8, 128] for vq",
+                       "vecinfer-shaped keys and values [36, 8192, 8, 128] for vq (4096 / 256 centroids)",
            "source_hash": kernel_source_hash(), "copy_reference_bytes": copy_bytes,
            "fetch_scale": round(f_scale, 6), "write_scale": round(w_scale, 6)}
     for key, (name, alg) in kernels.items():
@@ -544,27 +549,45 @@ def bench_attend(torch, kvq, codes, scales, lamK, lamV, signs, dims, args):
 
 
 def bench_vq(torch, kvq, synth, dev, args):
-    """Time VQ encode and decode of the VecInfer-shaped key cache."""
+    """Time the product-VQ paths on the VecInfer-shaped caches: key encode and
+    decode (4096-centroid codebooks, u16 indices), value encode and decode
+    (256-centroid codebooks, one-byte indices) and one k-means codebook
+    training step on the keys."""
     cfg = synth.config("vq")
     try:
         inp = synth.make_inputs(cfg, dev)
     except RuntimeError:
         return None
     x, lam, s, cb = inp["K"], inp["lam_K"], inp["signs"], inp["codebook"]
+    v, lam_v, cb_v = inp["V"], inp["lam_V"], inp["codebook_V"]
     L, T, H, D = x.shape
-    idx = torch.empty((L, T, H, D // cfg.sub_dim), dtype=torch.int16, device=dev)
+    sub = cfg.sub_dim
+    idx = torch.empty((L, T, H, D // sub), dtype=torch.int16, device=dev)
+    idx8 = torch.empty((L, T, H, D // sub), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x)
+    new_cb = torch.empty_like(cb)
+    counts = torch.empty((H, cfg.n_centroids), dtype=torch.int32, device=dev)
+    ws = torch.empty(kvq.kmeans_step_workspace_bytes(L, T, H, D, cfg.n_centroids, sub), dtype=torch.uint8,
+                     device=dev)
     stream = torch.cuda.current_stream()
+    legs = (
+        ("encode", lambda: kvq.vq_encode(x, lam, s, cb, sub, idx=idx, stream=stream)),
+        ("decode", lambda: kvq.vq_decode(idx, cb, lam, s, sub, out=out, stream=stream)),
+        ("value_encode_u8", lambda: kvq.vq_encode_u8(v, lam_v, s, cb_v, sub, idx=idx8, stream=stream)),
+        ("value_decode_u8", lambda: kvq.vq_decode_u8(idx8, cb_v, lam_v, s, sub, out=out, stream=stream)),
+        ("kmeans_step", lambda: kvq.kmeans_step(x, lam, s, cb, sub, idx=idx, new_codebook=new_cb, counts=counts,
+                                                workspace=ws, stream=stream)),
+    )
     try:
-        kvq.vq_encode(x, lam, s, cb, cfg.sub_dim, idx=idx, stream=stream)
-        kvq.vq_decode(idx, cb, lam, s, cfg.sub_dim, out=out, stream=stream)
+        for _, fn in legs:
+            fn()
         torch.cuda.synchronize()
     except kvq.KvqError as e:
         return {"status": "unavailable", "error": str(e)}
     res = {}
     reps = max(3, min(args.steps, 10))
-    for name, fn in (("encode", lambda: kvq.vq_encode(x, lam, s, cb, cfg.sub_dim, idx=idx, stream=stream)),
-                     ("decode", lambda: kvq.vq_decode(idx, cb, lam, s, cfg.sub_dim, out=out, stream=stream))):
+    nkeys = L * T * H
+    for name, fn in legs:
         fn()
         ms = []
         for _ in range(reps):
@@ -575,24 +598,28 @@ def bench_vq(torch, kvq, synth, dev, args):
             torch.cuda.synchronize()
             ms.append(a.elapsed_time(b))
         avg = sum(ms) / len(ms)
-        nkeys = L * T * H
         r = {"avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "ns_per_key": round(avg * 1e6 / nkeys, 4)}
-        if name == "encode":
-            flop = nkeys * (D // cfg.sub_dim) * cfg.n_centroids * cfg.sub_dim * 2
+        if name in ("encode", "kmeans_step"):
+            flop = nkeys * (D // sub) * cfg.n_centroids * sub * 2
             tf = flop / (avg * 1e-3) / 1e12
             r.update({"algorithmic_TFLOP": round(flop / 1e12, 4), "TFLOP_per_s": round(tf, 2),
-                      "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
-                      # per 32-centroid tile and 4 groups of 32 sub-vectors: four
-                      # 32x32x16 MFMAs on the fp16 hi/lo split plus one 32x32x8
-                      # norm MFMA, against 4 x 32 x 32 x 8 algorithmic MACs
-                      "executed_mfma_flop_factor": 2.25,
-                      "executed_frac_of_fp16_mfma_peak": round(2.25 * tf / FP16_MFMA_PEAK_TFLOPS, 4)})
+                      "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)})
+            if name == "encode":
+                # per 32-centroid tile and 4 groups of 32 sub-vectors: four
+                # 32x32x16 MFMAs on the fp16 hi/lo split plus one 32x32x8
+                # norm MFMA, against 4 x 32 x 32 x 8 algorithmic MACs
+                r.update({"executed_mfma_flop_factor": 2.25,
+                          "executed_frac_of_fp16_mfma_peak": round(2.25 * tf / FP16_MFMA_PEAK_TFLOPS, 4)})
+            else:
+                r["includes"] = "assignment (the encoder) + accumulate + finalize"
         else:
-            byt = nkeys * (2 * D + 2 * (D // cfg.sub_dim))
+            ib = 2 if name == "decode" else 1
+            byt = nkeys * (2 * D + ib * (D // sub))
             r.update({"GB_per_s": round(byt / (avg * 1e-3) / 1e9, 1),
                       "frac_of_hbm_peak": round(byt / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
         res[name] = r
-    res["workload"] = "vecinfer-shaped keys [36, 8192, 8, 128], codebook [8, 4096, 8] fp16, sub_dim 8"
+    res["workload"] = ("vecinfer-shaped keys and values [36, 8192, 8, 128]; key codebooks [8, 4096, 8] fp16, "
+                       "value codebooks [8, 256, 8] fp16, sub_dim 8")
     return res
 
 

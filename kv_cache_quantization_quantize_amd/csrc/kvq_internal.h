@@ -104,7 +104,7 @@ struct KmArgs {
     const uint16_t* codebook;       // fp16 bits [H, K, 8] (input)
     uint16_t* new_codebook;         // fp16 bits [H, K, 8] (output, may alias codebook)
     uint32_t* counts;               // [H, K]
-    float* part_sums;               // [H, ranges, K, 8]
+    float* part_sums;               // [H, ranges, 8, K]
     uint32_t* part_counts;          // [H, ranges, K]
     int32_t tiles;                  // 16-token tiles per layer
     int32_t range_groups;           // ranges per head = 8 * range_groups

@@ -13,7 +13,10 @@
 // its vectors exactly as the encoder does (4 lanes per vector, Walsh-Hadamard
 // in registers), reads each sub-vector's assignment and adds the sub-vector
 // and a count into per-centroid fp32 sums in LDS (ds_add_f32; 36 bytes per
-// centroid, at most 4096 centroids).  The block then writes its sums and
+// centroid, at most 4096 centroids).  The sums are stored coordinate-major,
+// [8][K]: the 64 lanes of one atomic instruction add coordinate e of their
+// own centroids, and consecutive centroids fall in consecutive banks (a
+// centroid-major [K][8] layout would put them all in 4 of the 32 banks).  The block then writes its sums and
 // counts to a workspace slot of its own.  As in the decoder, the H blocks of
 // one range are dispatched to the same XCD so that the heads' assignments of a
 // token, which share cache lines, are fetched from HBM once.
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(64 * KmCfg<D>::WAVES) void kmeans_accum_kernel(KmAr
     constexpr int NJ = D / 32;
     constexpr int N = D / 4;
 
-    __shared__ float sums[kKmMaxCentroids * 8];
+    __shared__ float sums[8 * kKmMaxCentroids];      // [8][K]
     __shared__ uint32_t cnts[kKmMaxCentroids];
 
     const int lane = threadIdx.x & 63;
@@ -126,9 +129,8 @@ __global__ __launch_bounds__(64 * KmCfg<D>::WAVES) void kmeans_accum_kernel(KmAr
         if (valid) {
 #pragma unroll
             for (int j = 0; j < NJ; j++) {
-                float* sp = sums + kk[j] * 8;
 #pragma unroll
-                for (int e = 0; e < 8; e++) atomicAdd(sp + e, v[j * 8 + e] * lane_sign);
+                for (int e = 0; e < 8; e++) atomicAdd(sums + e * a.K + kk[j], v[j * 8 + e] * lane_sign);
                 atomicAdd(cnts + kk[j], 1u);
             }
         }
@@ -136,9 +138,8 @@ __global__ __launch_bounds__(64 * KmCfg<D>::WAVES) void kmeans_accum_kernel(KmAr
     __syncthreads();
 
     const int64_t slot_base = (int64_t)h * ranges + range;
-    float4* ps = reinterpret_cast<float4*>(a.part_sums + slot_base * a.K * 8);
-    const float4* sl4 = reinterpret_cast<const float4*>(sums);
-    for (int i = threadIdx.x; i < a.K * 2; i += 64 * WAVES) ps[i] = sl4[i];
+    float* ps = a.part_sums + slot_base * a.K * 8;
+    for (int i = threadIdx.x; i < a.K * 8; i += 64 * WAVES) ps[i] = sums[i];
     uint32_t* pc = a.part_counts + slot_base * a.K;
     for (int i = threadIdx.x; i < a.K; i += 64 * WAVES) pc[i] = cnts[i];
 }
@@ -154,10 +155,9 @@ __global__ __launch_bounds__(256) void kmeans_finalize_kernel(KmArgs a)
     uint64_t n = 0;
     for (int r = 0; r < ranges; r++) {
         const int64_t sl = (int64_t)h * ranges + r;
-        const float4* ps = reinterpret_cast<const float4*>(a.part_sums + (sl * a.K + k) * 8);
-        const float4 p0 = ps[0], p1 = ps[1];
-        s[0] += p0.x; s[1] += p0.y; s[2] += p0.z; s[3] += p0.w;
-        s[4] += p1.x; s[5] += p1.y; s[6] += p1.z; s[7] += p1.w;
+        const float* ps = a.part_sums + sl * a.K * 8 + k;     // [8][K] per slot
+#pragma unroll
+        for (int e = 0; e < 8; e++) s[e] += ps[(int64_t)e * a.K];
         n += a.part_counts[sl * a.K + k];
     }
     a.counts[i] = (uint32_t)n;

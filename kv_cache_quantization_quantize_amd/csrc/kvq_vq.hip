@@ -79,8 +79,11 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
     using C = VqCfg<D>;
     constexpr int NS = C::NS, NJ = C::NJ, N = C::N, GPR = C::GPR, ROUNDS = C::ROUNDS, WAVES = C::WAVES;
 
-    __shared__ uint4 cb_lds[kVqChunk];                 // centroid k: 8 fp16
-    __shared__ uint32_t nrm_lds[kVqChunk];             // packed (n_hi, n_lo)
+    // one-byte indices imply at most 256 centroids: a small codebook area
+    // lets two blocks share a CU
+    constexpr int CHUNK = IDX8 ? 256 : kVqChunk;
+    __shared__ uint4 cb_lds[CHUNK];                    // centroid k: 8 fp16
+    __shared__ uint32_t nrm_lds[CHUNK];                // packed (n_hi, n_lo)
     __shared__ uint4 stage[WAVES][2][16 * NS];         // [wave][hi/lo][key, sub-vector]
 
     const int lane = threadIdx.x & 63;
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
     const uint32_t mhalf2 = 0xB800B800u;               // two fp16 -0.5
     const h4_t b2 = as_h4(make_uint2(half == 0 ? mhalf2 : 0u, 0u));
 
-    const int nchunks = (a.K + kVqChunk - 1) / kVqChunk;
+    const int nchunks = (a.K + CHUNK - 1) / CHUNK;
     const int64_t ubeg = (int64_t)blockIdx.x * a.enc_units_per_block;
     const int64_t uend = min(ubeg + a.enc_units_per_block, a.enc_n_units);
     int cur_cb = -1;
@@ -183,12 +186,12 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
             }
 
             for (int ch = 0; ch < nchunks; ch++) {
-                const int kbase = ch * kVqChunk;
-                const int kc = min(kVqChunk, a.K - kbase);
+                const int kbase = ch * CHUNK;
+                const int kc = min(CHUNK, a.K - kbase);
                 if (nchunks > 1 || cbkey != cur_cb) {
                     // ---- stage codebook chunk + split norms (whole block) ----------
                     __syncthreads();
-                    for (int k = threadIdx.x; k < kVqChunk; k += 64 * WAVES) {
+                    for (int k = threadIdx.x; k < CHUNK; k += 64 * WAVES) {
                         uint4 cv = make_uint4(0, 0, 0, 0);
                         // padding: n_hi = 65504 (largest finite fp16) gives a score of
                         // -32752, below any in-domain centroid; finite so that the
