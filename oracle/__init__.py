@@ -62,6 +62,10 @@ def bind(path: str):
         "kvqo_codes_given_scales": (I32, [I64, I32, I32, P, P, P]),
         "kvqo_quantize_rows": (I64, [I64, I32, I32, P, P, P, P, P, P]),
         "kvqo_dequantize_rows": (I32, [I64, I32, I32, P, P, P, P, P, P]),
+        "kvqo_srft_rows": (I32, [I64, I32, P, P, P, P]),
+        "kvqo_isrft_rows": (I32, [I64, I32, P, P, P, P, P]),
+        "kvqo_quantize_srft_rows": (I64, [I64, I32, I32, P, P, P, P, P, P]),
+        "kvqo_dequantize_srft_rows": (I32, [I64, I32, I32, P, P, P, P, P, P]),
         "kvqo_vq_encode_rows": (I32, [I64, I32, I32, I32, P, P, P, P, P, P, P]),
         "kvqo_vq_distances": (I32, [I64, I32, I32, I32, P, P, P, P, P]),
         "kvqo_kmeans_update": (I32, [I64, I32, I32, P, P, P, P, P, P, P]),
@@ -145,6 +149,34 @@ def unrotate(yhat, lam, signs):
     return x64, x16
 
 
+def srft(x_bits, lam, signs):
+    """SRFT rotation of every row: y = pack(unitary DFT of s * lambda * x),
+    pack = [X_0, X_{D/2}, sqrt2 Re X_1, sqrt2 Im X_1, ...]; D even."""
+    x, px = _c(x_bits, np.uint16)
+    D = x.shape[-1]
+    lam, pl = _c(np.broadcast_to(lam, x.shape), np.float32)
+    s, ps = _c(signs, np.int8)
+    y, py = _out(x.shape, np.float64)
+    rc = _load().kvqo_srft_rows(_rows(x, D), D, px, pl, ps, py)
+    if rc:
+        raise ValueError("oracle srft rejected D=%d" % D)
+    return y
+
+
+def isrft(yhat, lam, signs):
+    """(x64, x16bits) = unscale(inverse SRFT of yhat) for every row."""
+    yh, py = _c(yhat, np.float64)
+    D = yh.shape[-1]
+    lam, pl = _c(np.broadcast_to(lam, yh.shape), np.float32)
+    s, ps = _c(signs, np.int8)
+    x64, p64 = _out(yh.shape, np.float64)
+    x16, p16 = _out(yh.shape, np.uint16)
+    rc = _load().kvqo_isrft_rows(_rows(yh, D), D, py, pl, ps, p64, p16)
+    if rc:
+        raise ValueError("oracle isrft rejected D=%d" % D)
+    return x64, x16
+
+
 # ---------------------------------------------------------------- nibbles
 def pack_nibbles(q):
     q, pq = _c(q, np.int8)
@@ -201,6 +233,37 @@ def dequantize(codes, scales_bits, lam, signs, G):
     rc = _load().kvqo_dequantize_rows(_rows(x64, D), D, int(G), pc, psc, pl, ps, p64, p16)
     if rc:
         raise ValueError("oracle dequantize rejected D=%d G=%d" % (D, G))
+    return x64, x16
+
+
+def quantize_srft(x_bits, lam, signs, G):
+    """quantize() on the SRFT rotation (D even)."""
+    x, px = _c(x_bits, np.uint16)
+    D = x.shape[-1]
+    lam, pl = _c(np.broadcast_to(lam, x.shape), np.float32)
+    s, ps = _c(signs, np.int8)
+    codes, pc = _out(x.shape[:-1] + (D // 2,), np.uint8)
+    scales, psc = _out(x.shape[:-1] + (D // G,), np.uint16)
+    y, py = _out(x.shape, np.float64)
+    bad = _load().kvqo_quantize_srft_rows(_rows(x, D), D, int(G), px, pl, ps, pc, psc, py)
+    if bad < 0:
+        raise ValueError("oracle quantize_srft rejected D=%d G=%d" % (D, G))
+    return codes, scales, y, int(bad)
+
+
+def dequantize_srft(codes, scales_bits, lam, signs, G):
+    """dequantize() with the inverse SRFT."""
+    c, pc = _c(codes, np.uint8)
+    D = c.shape[-1] * 2
+    sc, psc = _c(scales_bits, np.uint16)
+    shape = c.shape[:-1] + (D,)
+    lam, pl = _c(np.broadcast_to(lam, shape), np.float32)
+    s, ps = _c(signs, np.int8)
+    x64, p64 = _out(shape, np.float64)
+    x16, p16 = _out(shape, np.uint16)
+    rc = _load().kvqo_dequantize_srft_rows(_rows(x64, D), D, int(G), pc, psc, pl, ps, p64, p16)
+    if rc:
+        raise ValueError("oracle dequantize_srft rejected D=%d G=%d" % (D, G))
     return x64, x16
 
 

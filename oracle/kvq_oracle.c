@@ -52,6 +52,9 @@
  *    byte k [GIST s.2 "two int4 values in one byte"].
  *  - VQ: contiguous sub-vectors, squared Euclidean distance on the unrounded
  *    rotated key, lowest index on ties [README "Metal kernels"; VQ-blog].
+ *  - SRFT (the Fourier alternative to the Hadamard rotation) [GIST s.1, s.2]:
+ *    unitary DFT of s * lambda * x, real-packed as [X_0, X_{D/2}, sqrt2 Re X_1,
+ *    sqrt2 Im X_1, ...], an orthonormal map; D any even number.
  *  - codebook training is Lloyd's k-means on the rotated sub-vectors of
  *    synthetic samples: assign each to its nearest centroid (the encode
  *    above), then move each centroid to the mean of its samples; a centroid
@@ -192,6 +195,101 @@ int kvqo_unrotate_rows(int64_t n, int D, const double* yhat, const float* lam,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Sign-randomized real Fourier rotation (SRFT) [GIST s.1, s.2]               */
+/* ------------------------------------------------------------------------ */
+
+/* cos and sin of 2*pi*t/D for t = 0 .. D-1 (the phase j*k is reduced modulo
+   D before the lookup, so no large argument reaches cos or sin). */
+static void dft_table(int D, double* c, double* sn)
+{
+    const double pi = 3.14159265358979323846;
+    for (int t = 0; t < D; t++) {
+        double a = 2.0 * pi * (double)t / (double)D;
+        c[t] = cos(a);
+        sn[t] = sin(a);
+    }
+}
+
+/* Forward SRFT of one vector, D even:
+     v_j = s_j * lambda_j * x_j;
+     X_k = D^-1/2 * sum_j v_j * exp(-2 pi i j k / D)    (unitary DFT);
+   v is real, so X_{D-k} = conj(X_k) and X_0, X_{D/2} are real.  The real
+   packing keeps one copy of each conjugate pair, scaled so that the map is
+   orthonormal:
+     y_0 = X_0,  y_1 = X_{D/2},
+     y_{2k} = sqrt(2) Re X_k,  y_{2k+1} = sqrt(2) Im X_k   (0 < k < D/2). */
+static void srft_one(int D, const uint16_t* x, const float* lam, const int8_t* s,
+                     double* v, double* y, const double* c, const double* sn)
+{
+    for (int j = 0; j < D; j++)
+        v[j] = (double)s[j] * (double)lam[j] * kvqo_f16_to_f64(x[j]);
+    double norm = 1.0 / sqrt((double)D);
+    for (int k = 0; k <= D / 2; k++) {
+        double re = 0.0, im = 0.0;
+        for (int j = 0; j < D; j++) {
+            int t = (int)(((int64_t)j * k) % D);
+            re += v[j] * c[t];
+            im -= v[j] * sn[t];
+        }
+        re *= norm;
+        im *= norm;
+        if (k == 0) y[0] = re;
+        else if (k == D / 2) y[1] = re;
+        else { y[2 * k] = sqrt(2.0) * re; y[2 * k + 1] = sqrt(2.0) * im; }
+    }
+}
+
+/* Inverse: rebuild X from the packing (X_k = (y_{2k} + i y_{2k+1}) / sqrt 2)
+   and take the unitary inverse DFT, whose result is real:
+     v_j = D^-1/2 [ y_0 + (-1)^j y_1
+                    + sqrt(2) sum_{0<k<D/2} (y_{2k} cos(2 pi jk/D) - y_{2k+1} sin(2 pi jk/D)) ];
+   then unscale: xhat_j = (s_j / lambda_j) v_j. */
+static void isrft_one(int D, const double* yhat, const float* lam, const int8_t* s,
+                      double* xhat, const double* c, const double* sn)
+{
+    double norm = 1.0 / sqrt((double)D);
+    for (int j = 0; j < D; j++) {
+        double acc = yhat[0] + ((j & 1) ? -yhat[1] : yhat[1]);
+        for (int k = 1; k < D / 2; k++) {
+            int t = (int)(((int64_t)j * k) % D);
+            acc += sqrt(2.0) * (yhat[2 * k] * c[t] - yhat[2 * k + 1] * sn[t]);
+        }
+        xhat[j] = ((double)s[j] / (double)lam[j]) * (acc * norm);
+    }
+}
+
+int kvqo_srft_rows(int64_t n, int D, const uint16_t* x, const float* lam,
+                   const int8_t* s, double* y)
+{
+    if (D < 2 || (D & 1)) return -1;
+    double* v = (double*)malloc(sizeof(double) * (size_t)D * 3);
+    double* c = v + D;
+    double* sn = c + D;
+    dft_table(D, c, sn);
+    for (int64_t r = 0; r < n; r++)
+        srft_one(D, x + r * D, lam + r * D, s, v, y + r * D, c, sn);
+    free(v);
+    return 0;
+}
+
+int kvqo_isrft_rows(int64_t n, int D, const double* yhat, const float* lam,
+                    const int8_t* s, double* xhat64, uint16_t* xhat16)
+{
+    if (D < 2 || (D & 1)) return -1;
+    double* c = (double*)malloc(sizeof(double) * (size_t)D * 2);
+    double* sn = c + D;
+    dft_table(D, c, sn);
+    for (int64_t r = 0; r < n; r++) {
+        isrft_one(D, yhat + r * D, lam + r * D, s, xhat64 + r * D, c, sn);
+        if (xhat16)
+            for (int j = 0; j < D; j++)
+                xhat16[r * D + j] = kvqo_f64_to_f16(xhat64[r * D + j]);
+    }
+    free(c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Group quantizer and nibble format [ABSTRACT; GIST s.2, s.3]                 */
 /* ------------------------------------------------------------------------ */
 
@@ -248,21 +346,26 @@ int kvqo_codes_given_scales(int64_t n, int D, int G, const double* y,
      q_i = clamp(rne(y_i / scale), -7, 7)  (0 when scale == 0).
    Returns the number of vectors outside the domain (a non-finite input or a
    scale that overflows binary16); their outputs are set to zero. */
-int64_t kvqo_quantize_rows(int64_t n, int D, int G, const uint16_t* x,
-                           const float* lam, const int8_t* s, uint8_t* codes,
-                           uint16_t* scales, double* y_out)
+static int64_t quantize_rows_with(int fourier, int64_t n, int D, int G, const uint16_t* x,
+                                  const float* lam, const int8_t* s, uint8_t* codes,
+                                  uint16_t* scales, double* y_out)
 {
-    if (!is_pow2(D) || G <= 0 || D % G || (G & 1)) return -1;
+    if (fourier ? (D < 2 || (D & 1)) : !is_pow2(D)) return -1;
+    if (G <= 0 || D % G || (G & 1)) return -1;
     int ng = D / G;
     double* v = (double*)malloc(sizeof(double) * (size_t)D);
     double* y = (double*)malloc(sizeof(double) * (size_t)D);
+    double* c = (double*)malloc(sizeof(double) * (size_t)D * 2);
+    double* sn = c + D;
     int8_t* q = (int8_t*)malloc((size_t)D);
+    if (fourier) dft_table(D, c, sn);
     int64_t bad = 0;
     for (int64_t r = 0; r < n; r++) {
         int ok = 1;
         for (int j = 0; j < D; j++)
             if (!isfinite(kvqo_f16_to_f64(x[r * D + j]))) ok = 0;
-        if (ok) rotate_one(D, x + r * D, lam + r * D, s, v, y);
+        if (ok && fourier) srft_one(D, x + r * D, lam + r * D, s, v, y, c, sn);
+        else if (ok) rotate_one(D, x + r * D, lam + r * D, s, v, y);
         for (int g = 0; ok && g < ng; g++) {
             double amax = 0.0;
             for (int i = g * G; i < (g + 1) * G; i++)
@@ -283,8 +386,23 @@ int64_t kvqo_quantize_rows(int64_t n, int D, int G, const uint16_t* x,
         kvqo_pack_nibbles(D, q, codes + r * (D / 2));
         if (y_out) memcpy(y_out + r * D, y, sizeof(double) * (size_t)D);
     }
-    free(v); free(y); free(q);
+    free(v); free(y); free(c); free(q);
     return bad;
+}
+
+int64_t kvqo_quantize_rows(int64_t n, int D, int G, const uint16_t* x,
+                           const float* lam, const int8_t* s, uint8_t* codes,
+                           uint16_t* scales, double* y_out)
+{
+    return quantize_rows_with(0, n, D, G, x, lam, s, codes, scales, y_out);
+}
+
+/* The same group quantizer on the SRFT rotation (D even). */
+int64_t kvqo_quantize_srft_rows(int64_t n, int D, int G, const uint16_t* x,
+                                const float* lam, const int8_t* s, uint8_t* codes,
+                                uint16_t* scales, double* y_out)
+{
+    return quantize_rows_with(1, n, D, G, x, lam, s, codes, scales, y_out);
 }
 
 /* Dequantize n vectors from packed codes [n, D/2] and binary16 scales
@@ -292,25 +410,46 @@ int64_t kvqo_quantize_rows(int64_t n, int D, int G, const uint16_t* x,
      yhat_i = q_i * scale_g;  xhat = unrotate(yhat);
    xhat64 [n, D] receives the exact fp64 result and xhat16 [n, D] (may be
    NULL) its binary16 rounding. */
-int kvqo_dequantize_rows(int64_t n, int D, int G, const uint8_t* codes,
-                         const uint16_t* scales, const float* lam,
-                         const int8_t* s, double* xhat64, uint16_t* xhat16)
+static int dequantize_rows_with(int fourier, int64_t n, int D, int G, const uint8_t* codes,
+                                const uint16_t* scales, const float* lam,
+                                const int8_t* s, double* xhat64, uint16_t* xhat16)
 {
-    if (!is_pow2(D) || G <= 0 || D % G || (G & 1)) return -1;
+    if (fourier ? (D < 2 || (D & 1)) : !is_pow2(D)) return -1;
+    if (G <= 0 || D % G || (G & 1)) return -1;
     int ng = D / G;
     int8_t* q = (int8_t*)malloc((size_t)D);
     double* yh = (double*)malloc(sizeof(double) * (size_t)D);
+    double* c = (double*)malloc(sizeof(double) * (size_t)D * 2);
+    double* sn = c + D;
+    if (fourier) dft_table(D, c, sn);
     for (int64_t r = 0; r < n; r++) {
         kvqo_unpack_nibbles(D / 2, codes + r * (D / 2), q);
         for (int i = 0; i < D; i++)
             yh[i] = (double)q[i] * kvqo_f16_to_f64(scales[r * ng + i / G]);
-        unrotate_one(D, yh, lam + r * D, s, xhat64 + r * D);
+        if (fourier) isrft_one(D, yh, lam + r * D, s, xhat64 + r * D, c, sn);
+        else unrotate_one(D, yh, lam + r * D, s, xhat64 + r * D);
         if (xhat16)
             for (int j = 0; j < D; j++)
                 xhat16[r * D + j] = kvqo_f64_to_f16(xhat64[r * D + j]);
     }
-    free(q); free(yh);
+    free(q); free(yh); free(c);
     return 0;
+}
+
+int kvqo_dequantize_rows(int64_t n, int D, int G, const uint8_t* codes,
+                         const uint16_t* scales, const float* lam,
+                         const int8_t* s, double* xhat64, uint16_t* xhat16)
+{
+    return dequantize_rows_with(0, n, D, G, codes, scales, lam, s, xhat64, xhat16);
+}
+
+/* Mirror of kvqo_quantize_srft_rows: yhat_i = q_i * scale_g, then the inverse
+   SRFT and unscale. */
+int kvqo_dequantize_srft_rows(int64_t n, int D, int G, const uint8_t* codes,
+                              const uint16_t* scales, const float* lam,
+                              const int8_t* s, double* xhat64, uint16_t* xhat16)
+{
+    return dequantize_rows_with(1, n, D, G, codes, scales, lam, s, xhat64, xhat16);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -365,6 +365,134 @@ def test_byte_accounting_3_56x():
     assert nbytes == 72 and abs(2 * D / nbytes - 3.56) < 0.005
 
 
+# -------------------------------------------------------------------- SRFT
+def srft_numpy(x_bits, lam, s):
+    """numpy's orthonormal FFT of s * lambda * x, packed [X_0, X_{D/2},
+    sqrt2 Re X_1, sqrt2 Im X_1, ...]."""
+    v = s * lam.astype(np.float64) * bits_to_f64(x_bits)
+    D = v.shape[-1]
+    X = np.fft.fft(v, norm="ortho", axis=-1)
+    y = np.empty_like(v)
+    y[..., 0] = X[..., 0].real
+    y[..., 1] = X[..., D // 2].real
+    y[..., 2::2] = np.sqrt(2) * X[..., 1:D // 2].real
+    y[..., 3::2] = np.sqrt(2) * X[..., 1:D // 2].imag
+    return y
+
+
+@pytest.mark.parametrize("D", [2, 6, 8, 64, 96, 128, 256])
+def test_srft_matches_numpy_fft(D):
+    n = 20
+    x = rand_x(n, D, 3.0)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    y = oracle.srft(x, lam, s)
+    want = srft_numpy(x, lam, s)
+    assert np.allclose(y, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    # the real FFT of scipy gives the same half spectrum
+    import scipy.fft
+    R = scipy.fft.rfft(s * lam.astype(np.float64) * bits_to_f64(x), norm="ortho", axis=-1)
+    assert np.allclose(y[:, 1], R[:, D // 2].real, atol=1e-12 * np.abs(want).max())
+    assert np.allclose(y[:, 3::2], np.sqrt(2) * R[:, 1:D // 2].imag, atol=1e-12 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("D", [8, 96, 128])
+def test_srft_orthonormal_parseval_and_roundtrip(D):
+    # the packed map is an orthogonal matrix: rotate exact unit vectors
+    eye = np.eye(D).astype(np.float16).view(np.uint16)
+    Q = oracle.srft(eye, np.ones(D, np.float32), np.ones(D, np.int8)).T     # column j = image of e_j
+    assert np.allclose(Q @ Q.T, np.eye(D), atol=1e-13)
+    n = 50
+    x = rand_x(n, D)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    y = oracle.srft(x, lam, s)
+    v = lam * bits_to_f64(x)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(v, axis=1), rtol=1e-12)
+    x64, x16 = oracle.isrft(y, lam, s)
+    assert np.abs(x64 - bits_to_f64(x)).max() <= 1e-12 * np.abs(bits_to_f64(x)).max()
+    assert np.array_equal(x16, x)
+
+
+def test_srft_closed_forms():
+    D = 16
+    one, plus = np.ones(D, np.float32), np.ones(D, np.int8)
+    j = np.arange(D)
+    # impulse: flat spectrum X_k = D^-1/2
+    imp = np.zeros((1, D))
+    imp[0, 0] = 1
+    y = oracle.srft(f16bits(imp), one, plus)[0]
+    want = np.full(D, np.sqrt(2.0 / D))
+    want[0] = want[1] = 1 / np.sqrt(D)
+    want[3::2] = 0
+    assert np.allclose(y, want, atol=1e-15)
+    # alternating signs: everything in X_{D/2}
+    y = oracle.srft(f16bits(((-1.0) ** j)[None]), one, plus)[0]
+    want = np.zeros(D)
+    want[1] = np.sqrt(D)
+    assert np.allclose(y, want, atol=1e-14)
+    # cos / sin at frequency D/4 (exact in fp16): sqrt(D/2) in Re / -sqrt(D/2) in Im of X_{D/4}
+    k0 = D // 4
+    c = np.round(np.cos(2 * np.pi * k0 * j / D))
+    sn = np.round(np.sin(2 * np.pi * k0 * j / D))
+    y = oracle.srft(f16bits(np.stack([c, sn])), one, plus)
+    wc, ws = np.zeros(D), np.zeros(D)
+    wc[2 * k0] = np.sqrt(D / 2)
+    ws[2 * k0 + 1] = -np.sqrt(D / 2)
+    assert np.allclose(y[0], wc, atol=1e-14) and np.allclose(y[1], ws, atol=1e-14)
+
+
+@pytest.mark.parametrize("D,G", [(128, 32), (96, 32), (256, 64)])
+def test_srft_quantizer_invariants_and_roundtrip(D, G):
+    n = 300
+    x = rand_x(n, D, 2.0)
+    lam = rand_lambda(n, D)
+    s = rand_signs(D)
+    codes, scales, y, bad = oracle.quantize_srft(x, lam, s, G)
+    assert bad == 0
+    assert np.allclose(y, srft_numpy(x, lam, s), atol=1e-12 * np.abs(y).max())
+    q = oracle.unpack_nibbles(codes).astype(np.float64)
+    sb = bits_to_f64(scales)
+    sbe = np.repeat(sb, G, axis=1)
+    assert np.abs(q).max() <= 7
+    assert (np.abs(y - q * sbe) <= sbe / 2 * (1 + 1e-12)).all()
+    amax = np.abs(y).reshape(n, D // G, G).max(axis=2)
+    assert np.array_equal(scales, (amax / 7).astype(np.float16).view(np.uint16))
+    assert np.array_equal(oracle.codes_given_scales(y, scales, G), q.astype(np.int8))
+    # round trip: ||lambda (xhat - x)|| = ||yhat - y|| <= 1/2 sqrt(G sum scale^2)
+    x64, x16 = oracle.dequantize_srft(codes, scales, lam, s, G)
+    err = np.linalg.norm(lam * (x64 - bits_to_f64(x)), axis=1)
+    assert (err <= 0.5 * np.sqrt(G * (sb ** 2).sum(axis=1)) * (1 + 1e-9)).all()
+    assert np.array_equal(x16, x64.astype(np.float16).view(np.uint16))
+
+
+def test_srft_dequant_single_code_closed_form():
+    """One code at packed position 2k (or 2k+1) decodes to sqrt(2/D) times a
+    cosine (or minus a sine) at frequency k; positions 0 and 1 to a constant
+    and an alternating vector."""
+    D, G = 64, 16
+    lam = rand_lambda(1, D)[0]
+    s = rand_signs(D)
+    j = np.arange(D)
+    for pos, c in ((0, 7), (1, -2), (10, 3), (11, -5), (63, 1)):
+        q = np.zeros((1, D), np.int8)
+        q[0, pos] = c
+        scales = np.zeros((1, D // G), np.uint16)
+        scales[0, pos // G] = np.float16(0.3125).view(np.uint16)
+        x64, _ = oracle.dequantize_srft(oracle.pack_nibbles(q), scales, lam, s, G)
+        k = pos // 2
+        if pos == 0:
+            basis = np.ones(D) / np.sqrt(D)
+        elif pos == 1:
+            basis = (-1.0) ** j / np.sqrt(D)
+        elif pos % 2 == 0:
+            basis = np.sqrt(2.0 / D) * np.cos(2 * np.pi * j * k / D)
+        else:
+            basis = -np.sqrt(2.0 / D) * np.sin(2 * np.pi * j * k / D)
+        want = (s / lam.astype(np.float64)) * c * 0.3125 * basis
+        assert np.allclose(x64[0], want, rtol=0, atol=1e-14)
+
+
 # ---------------------------------------------------------------------- VQ
 @pytest.mark.parametrize("sub", [1, 2, 4, 8])
 @pytest.mark.parametrize("K", [1, 3, 16])

@@ -17,11 +17,17 @@ import tests.test_oracle as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "kvq_oracle.c")
 
+# context that tells the Hadamard rotation's input line from the SRFT's
+_H = ";\n    double norm = 1.0 / sqrt((double)D);\n    for (int i = 0; i < D; i++) {"
+_F = ";\n    double norm = 1.0 / sqrt((double)D);\n    for (int k = 0; k <= D / 2; k++) {"
+
 MUTANTS = {
-    "lambda_divides_on_quantize": ("(double)s[j] * (double)lam[j] * kvqo_f16_to_f64(x[j])",
-                                   "(double)s[j] / (double)lam[j] * kvqo_f16_to_f64(x[j])"),
-    "signs_dropped": ("(double)s[j] * (double)lam[j] * kvqo_f16_to_f64(x[j])",
-                      "(double)lam[j] * kvqo_f16_to_f64(x[j])"),
+    "lambda_divides_on_quantize": ("(double)s[j] * (double)lam[j] * kvqo_f16_to_f64(x[j])" + _H,
+                                   "(double)s[j] / (double)lam[j] * kvqo_f16_to_f64(x[j])" + _H),
+    "signs_dropped": ("(double)s[j] * (double)lam[j] * kvqo_f16_to_f64(x[j])" + _H,
+                      "(double)lam[j] * kvqo_f16_to_f64(x[j])" + _H),
+    "srft_lambda_divides": ("(double)s[j] * (double)lam[j] * kvqo_f16_to_f64(x[j])" + _F,
+                            "(double)s[j] / (double)lam[j] * kvqo_f16_to_f64(x[j])" + _F),
     "no_normalisation": ("y[i] = acc * norm;", "y[i] = acc;"),
     "hadamard_sign_flipped": ("& 1) ? -1 : 1;", "& 1) ? 1 : -1;"),
     "hadamard_or_index": ("popcount((unsigned)(i & j))", "popcount((unsigned)(i | j))"),
@@ -38,8 +44,10 @@ MUTANTS = {
                                 "code_of(y[r * D + i],\n                                           kvqo_f16_to_f64(scales[r * ng + i % ng]));"),
     "dequant_group_interleaved": ("(double)q[i] * kvqo_f16_to_f64(scales[r * ng + i / G]);",
                                   "(double)q[i] * kvqo_f16_to_f64(scales[r * ng + i % ng]);"),
-    "unscale_multiplies": ("((double)s[j] / (double)lam[j]) * (acc * norm)",
-                           "((double)s[j] * (double)lam[j]) * (acc * norm)"),
+    "unscale_multiplies": ("* yhat[i];\n        xhat[j] = ((double)s[j] / (double)lam[j]) * (acc * norm)",
+                           "* yhat[i];\n        xhat[j] = ((double)s[j] * (double)lam[j]) * (acc * norm)"),
+    "isrft_unscale_multiplies": ("}\n        xhat[j] = ((double)s[j] / (double)lam[j]) * (acc * norm)",
+                                 "}\n        xhat[j] = ((double)s[j] * (double)lam[j]) * (acc * norm)"),
     "vq_ties_to_highest": ("if (d < bd) { bd = d; best = k; }", "if (d <= bd) { bd = d; best = k; }"),
     "vq_abs_distance": ("d += diff * diff;", "d += fabs(diff);"),
     "f16_truncates": ("double n = nearbyint((2.0 * m - 1.0) * 1024.0);",
@@ -59,6 +67,16 @@ MUTANTS = {
                                   "for (int64_t i = 1; i < n; i++) {\n        int k = idx[i];"),
     "kmeans_coordinate_shifted": ("mean64[(int64_t)k * sub + t] += ysub[i * sub + t];",
                                   "mean64[(int64_t)k * sub + t] += ysub[i * sub + (t + 1) % sub];"),
+    "srft_imag_sign_flipped": ("            im -= v[j] * sn[t];", "            im += v[j] * sn[t];"),
+    "srft_sqrt2_dropped": ("else { y[2 * k] = sqrt(2.0) * re; y[2 * k + 1] = sqrt(2.0) * im; }",
+                           "else { y[2 * k] = re; y[2 * k + 1] = im; }"),
+    "srft_re_im_swapped": ("else { y[2 * k] = sqrt(2.0) * re; y[2 * k + 1] = sqrt(2.0) * im; }",
+                           "else { y[2 * k] = sqrt(2.0) * im; y[2 * k + 1] = sqrt(2.0) * re; }"),
+    "srft_nyquist_dropped": ("else if (k == D / 2) y[1] = re;", "else if (k == D / 2) y[1] = 0.0;"),
+    "isrft_alternating_sign": ("double acc = yhat[0] + ((j & 1) ? -yhat[1] : yhat[1]);",
+                               "double acc = yhat[0] + yhat[1];"),
+    "isrft_sine_sign": ("acc += sqrt(2.0) * (yhat[2 * k] * c[t] - yhat[2 * k + 1] * sn[t]);",
+                        "acc += sqrt(2.0) * (yhat[2 * k] * c[t] + yhat[2 * k + 1] * sn[t]);"),
     "attend_no_max_shift": ("double w = exp(a[t] - amax);", "double w = exp(a[t]);"),
     "attend_scale_dropped": ("a[t] = scale * dot;", "a[t] = dot;"),
     "attend_values_from_keys": ("o[c] += w * vh[(int64_t)t * D + c];", "o[c] += w * kh[(int64_t)t * D + c];"),
@@ -97,6 +115,11 @@ BATTERY = [
     ("test_e2m1_rounding_ties_even_and_saturation", {"golden_dir": None}),
     ("test_mxfp4_block_scale_rule_and_invariants", {"D": 128, "golden_dir": None}),
     ("test_mxfp4_zero_block_and_single_spike", {"golden_dir": None}),
+    ("test_srft_matches_numpy_fft", {"D": 96}),
+    ("test_srft_orthonormal_parseval_and_roundtrip", {"D": 96}),
+    ("test_srft_closed_forms", {}),
+    ("test_srft_quantizer_invariants_and_roundtrip", {"D": 128, "G": 32}),
+    ("test_srft_dequant_single_code_closed_form", {}),
     ("test_kmeans_step_matches_scipy_lloyd_iteration", {}),
     ("test_kmeans_update_closed_form_clusters", {}),
     ("test_kmeans_update_is_the_sse_minimiser_and_lloyd_descends", {}),
