@@ -126,6 +126,25 @@ kvq_status kvq_dequantize(kvq_shape shape, kvq_view codes_u8, kvq_view scales_f1
                           const float* lambda, const int8_t* signs, int32_t group,
                           kvq_view out_f16, void* stream);
 
+/* SRFT variant of kvq_quantize (gist.science summary, "Methodologie" s.1:
+ * the sign-randomized Fourier transform as the rotation): the same group
+ * quantizer and formats on
+ *   y = pack(F diag(s) diag(lambda) x),  F the unitary DFT of length D,
+ *   pack = [X_0, X_{D/2}, sqrt2 Re X_1, sqrt2 Im X_1, ..., sqrt2 Im X_{D/2-1}],
+ * an orthonormal real representation of the real input's half spectrum.
+ * Computed as a D/2-point complex radix-2 FFT of (v_2m + i v_2m+1) and its
+ * Hermitian unpacking.  Shapes, views, lambda, signs, group and errors as
+ * for kvq_quantize. */
+kvq_status kvq_quantize_srft(kvq_shape shape, kvq_view x_f16, const float* lambda,
+                             const int8_t* signs, int32_t group, kvq_view codes_u8,
+                             kvq_view scales_f16, void* stream);
+
+/* Mirror of kvq_quantize_srft: unpack, scale, inverse SRFT, unscale, fp16.
+ * Arguments as for kvq_dequantize. */
+kvq_status kvq_dequantize_srft(kvq_shape shape, kvq_view codes_u8, kvq_view scales_f16,
+                               const float* lambda, const int8_t* signs, int32_t group,
+                               kvq_view out_f16, void* stream);
+
 /* int8 variant of kvq_quantize (gist.science summary, "Methodologie" s.2:
  * the fused kernel rounds to signed int4 or int8): the same rotation and
  * groups, scale = fp16_rne(amax / 127), q = clamp(rne(y / scale), -127, 127)

@@ -66,6 +66,10 @@ def lib():
     L.kvq_quantize.argtypes = [Shape, View, P, P, I32, View, View, P]
     L.kvq_dequantize.restype = ctypes.c_int
     L.kvq_dequantize.argtypes = [Shape, View, View, P, P, I32, View, P]
+    L.kvq_quantize_srft.restype = ctypes.c_int
+    L.kvq_quantize_srft.argtypes = [Shape, View, P, P, I32, View, View, P]
+    L.kvq_dequantize_srft.restype = ctypes.c_int
+    L.kvq_dequantize_srft.argtypes = [Shape, View, View, P, P, I32, View, P]
     L.kvq_quantize_int8.restype = ctypes.c_int
     L.kvq_quantize_int8.argtypes = [Shape, View, P, P, I32, View, View, P]
     L.kvq_dequantize_int8.restype = ctypes.c_int
@@ -155,7 +159,7 @@ def _params(lam, signs, L, H, D):
 
 
 # ------------------------------------------------------------------ int4
-def quantize(x, lam, signs, group: int, codes=None, scales=None, stream=None):
+def quantize(x, lam, signs, group: int, codes=None, scales=None, stream=None, _fn="kvq_quantize"):
     """Fused rotate + int4 quantize of x [L, T, H, D] fp16 -> (codes [L, T, H, D/2]
     uint8, scales [L, T, H, D/group] fp16)."""
     torch = _torch()
@@ -168,12 +172,12 @@ def quantize(x, lam, signs, group: int, codes=None, scales=None, stream=None):
     _need(codes, torch.uint8, "codes")
     _need(scales, torch.float16, "scales")
     pl, ps = _params(lam, signs, L, H, D)
-    _check(lib().kvq_quantize(_shape(x, D), _view(x), pl, ps, int(group), _view(codes), _view(scales),
-                              _stream(stream)))
+    _check(getattr(lib(), _fn)(_shape(x, D), _view(x), pl, ps, int(group), _view(codes), _view(scales),
+                               _stream(stream)))
     return codes, scales
 
 
-def dequantize(codes, scales, lam, signs, group: int, out=None, stream=None):
+def dequantize(codes, scales, lam, signs, group: int, out=None, stream=None, _fn="kvq_dequantize"):
     """Mirror of quantize: (codes, scales) -> fp16 [L, T, H, D]."""
     torch = _torch()
     _need(codes, torch.uint8, "codes")
@@ -184,9 +188,20 @@ def dequantize(codes, scales, lam, signs, group: int, out=None, stream=None):
         out = torch.empty((L, T, H, D), dtype=torch.float16, device=codes.device)
     _need(out, torch.float16, "out")
     pl, ps = _params(lam, signs, L, H, D)
-    _check(lib().kvq_dequantize(_shape(codes, D), _view(codes), _view(scales), pl, ps, int(group), _view(out),
-                                _stream(stream)))
+    _check(getattr(lib(), _fn)(_shape(codes, D), _view(codes), _view(scales), pl, ps, int(group), _view(out),
+                               _stream(stream)))
     return out
+
+
+def quantize_srft(x, lam, signs, group: int, codes=None, scales=None, stream=None):
+    """quantize() with the SRFT rotation (real-packed unitary DFT) instead of
+    the Walsh-Hadamard one."""
+    return quantize(x, lam, signs, group, codes, scales, stream, _fn="kvq_quantize_srft")
+
+
+def dequantize_srft(codes, scales, lam, signs, group: int, out=None, stream=None):
+    """Mirror of quantize_srft."""
+    return dequantize(codes, scales, lam, signs, group, out, stream, _fn="kvq_dequantize_srft")
 
 
 def append_quantize(x_tok, cache_codes, cache_scales, t: int, lam, signs, group: int, stream=None):

@@ -148,7 +148,7 @@ kvq_status hip_status(hipError_t e, const char* what)
 kvq_status int4_common(const kvq_shape& shape, const kvq_view& x, const float* lambda,
                        const int8_t* signs, int32_t group, const kvq_view& codes,
                        const kvq_view& scales, kvq::Int4Args& a, bool x_is_output, int bits = 4,
-                       bool mx = false)
+                       bool mx = false, bool fourier = false)
 {
     KVQ_TRY(check_shape(shape));
     KVQ_TRY(check_group(group, shape.head_dim));
@@ -166,6 +166,7 @@ kvq_status int4_common(const kvq_shape& shape, const kvq_view& x, const float* l
     a.G = group;
     a.bits = bits;
     a.mx = mx ? 1 : 0;
+    a.fourier = fourier ? 1 : 0;
     a.x = t4(x);
     a.codes = t4(codes);
     a.scales = t4(scales);
@@ -365,6 +366,26 @@ kvq_status kvq_dequantize(kvq_shape shape, kvq_view codes_u8, kvq_view scales_f1
     KVQ_TRY(int4_common(shape, out_f16, lambda, signs, group, codes_u8, scales_f16, a, true));
     if (empty(shape)) return KVQ_OK;
     return hip_status(kvq::launch_dequantize(a, static_cast<hipStream_t>(stream)), "kvq_dequantize launch");
+}
+
+kvq_status kvq_quantize_srft(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,
+                             int32_t group, kvq_view codes_u8, kvq_view scales_f16, void* stream)
+{
+    g_err[0] = 0;
+    kvq::Int4Args a;
+    KVQ_TRY(int4_common(shape, x_f16, lambda, signs, group, codes_u8, scales_f16, a, false, 4, false, true));
+    if (empty(shape)) return KVQ_OK;
+    return hip_status(kvq::launch_quantize(a, static_cast<hipStream_t>(stream)), "kvq_quantize_srft launch");
+}
+
+kvq_status kvq_dequantize_srft(kvq_shape shape, kvq_view codes_u8, kvq_view scales_f16, const float* lambda,
+                               const int8_t* signs, int32_t group, kvq_view out_f16, void* stream)
+{
+    g_err[0] = 0;
+    kvq::Int4Args a;
+    KVQ_TRY(int4_common(shape, out_f16, lambda, signs, group, codes_u8, scales_f16, a, true, 4, false, true));
+    if (empty(shape)) return KVQ_OK;
+    return hip_status(kvq::launch_dequantize(a, static_cast<hipStream_t>(stream)), "kvq_dequantize_srft launch");
 }
 
 kvq_status kvq_quantize_int8(kvq_shape shape, kvq_view x_f16, const float* lambda, const int8_t* signs,

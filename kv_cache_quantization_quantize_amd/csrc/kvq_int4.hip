@@ -13,7 +13,9 @@
 // equivalent to the FFT, and lambda applied before the rotation as in the
 // VecInfer blog ("What VecInfer does": smooth scale, then rotation).
 // Dequantize is the mirror ("The kernel toggle": dequantize, inverse
-// transform, unscale).
+// transform, unscale).  With FT the rotation is the sign-randomized real
+// Fourier transform instead (same gist, "Methodologie" s.1: the SRFT), whose
+// register layout and sign conventions match the Walsh-Hadamard path's.
 //
 // Work decomposition.  An item is 16 head vectors, one per quad of a
 // wavefront.  When the head count divides 16 the item is 16 consecutive
@@ -29,6 +31,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_srft.h"
 
 namespace kvq {
 
@@ -215,10 +218,11 @@ __device__ __forceinline__ void run_pipeline(int begin, int end, Load&& load, Fi
 //   2. issues the previous item's stores and the next item's loads,
 //   3. computes the rest of the current item,
 // and a scheduling barrier keeps step 2 between steps 1 and 3.
-template <int D, int G, bool TM, int BITS, bool MX>
+template <int D, int G, bool TM, int BITS, bool MX, bool FT>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args a)
 {
     static_assert(!MX || (BITS == 4 && G == 32), "MXFP4: 4-bit codes in blocks of 32");
+    static_assert(!FT || (BITS == 4 && !MX), "SRFT: int4 codes");
     using S = QuantShape<D, G>;
     using F = CodeFmt<BITS>;
     constexpr int WPJ = BITS / 4;        // code dwords per 8-coordinate chunk
@@ -250,6 +254,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
 
     float m[N];
     int cur_key = -1;
+    // SRFT: one LDS row of D/2 complex points (+1 against bank conflicts) per quad
+    __shared__ float2 lds_fft[FT ? kWavesPerBlock * 16 * (D / 2 + 1) : 1];
+    float2* fft_row = lds_fft + (FT ? ((threadIdx.x >> 6) * 16 + slot) * (D / 2 + 1) : 0);
 
     struct Out {
         uint32_t word[NJ * WPJ];
@@ -337,6 +344,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
     };
 
     // step 1: lambda/sign scaling fused with the butterfly on register bit 0
+    // (SRFT: the scaling alone)
     auto first_stage = [&](int item, const uint4(&buf)[NJ], float(&v)[N]) {
         const Item it = decode_item<TM>(item, a);
         if (it.key != cur_key) {
@@ -349,16 +357,22 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
 #pragma unroll
             for (int k = 0; k < 4; k++) {
                 const int r = j * 8 + 2 * k;
-                const float b = fmaf(hi_half(w[k]), m[r + 1], 0.0f);   // one v_fma_mix
-                v[r] = fmaf(lo_half(w[k]), m[r], b);
-                v[r + 1] = fmaf(lo_half(w[k]), m[r], -b);
+                if constexpr (FT) {
+                    v[r] = lo_half(w[k]) * m[r];
+                    v[r + 1] = hi_half(w[k]) * m[r + 1];
+                } else {
+                    const float b = fmaf(hi_half(w[k]), m[r + 1], 0.0f);   // one v_fma_mix
+                    v[r] = fmaf(lo_half(w[k]), m[r], b);
+                    v[r + 1] = fmaf(lo_half(w[k]), m[r], -b);
+                }
             }
         }
     };
 
     // step 3: rest of the transform, scales, codes, packing
     auto finish = [&](float(&v)[N], Out& o) {
-        fwht_rest(v, c1, c2);
+        if constexpr (FT) srft::forward<D>(v, fft_row, q);
+        else fwht_rest(v, c1, c2);
 
         float amax[LG];
 #pragma unroll
@@ -452,16 +466,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
         }
     };
 
-    run_pipeline<uint4[NJ], Out, N, (D <= 128)>(begin, end, load, first_stage, store, finish);
+    run_pipeline<uint4[NJ], Out, N, (D <= 128 && !FT)>(begin, end, load, first_stage, store, finish);
 }
 
 // ---------------------------------------------------------------------------
 // Dequantize
 // ---------------------------------------------------------------------------
-template <int D, int G, bool TM, int BITS, bool MX>
+template <int D, int G, bool TM, int BITS, bool MX, bool FT>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Args a)
 {
     static_assert(!MX || (BITS == 4 && G == 32), "MXFP4: 4-bit codes in blocks of 32");
+    static_assert(!FT || (BITS == 4 && !MX), "SRFT: int4 codes");
     constexpr int WPJ = BITS / 4;        // code dwords per 8-coordinate chunk
     constexpr int NJ = D / 32;
     constexpr int N = NJ * 8;
@@ -489,6 +504,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
 
     float m[N];
     int cur_key = -1;
+    __shared__ float2 lds_fft[FT ? kWavesPerBlock * 16 * (D / 2 + 1) : 1];
+    float2* fft_row = lds_fft + (FT ? ((threadIdx.x >> 6) * 16 + slot) * (D / 2 + 1) : 0);
 
     // Raw inputs of one item: the lane's NJ code words and its vector's whole
     // scale row as packed 32-bit words.
@@ -639,6 +656,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
             const uint32_t wb = raw.w[j] ^ 0x88888888u;
             const uint32_t lo = wb & 0x0f0f0f0fu;            // n of elements 0,2,4,6
             const uint32_t hi = (wb >> 4) & 0x0f0f0f0fu;     // n of elements 1,3,5,7
+            if constexpr (FT) {
+                // the plain values yhat = (n - 8) * sc
+                const float off8 = -8.0f * sc;
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    v[j * 8 + 2 * k] = fmaf((float)((lo >> (8 * k)) & 0xffu), sc, off8);
+                    v[j * 8 + 2 * k + 1] = fmaf((float)((hi >> (8 * k)) & 0xffu), sc, off8);
+                }
+                continue;
+            }
             const uint32_t sum = lo + hi;                    // bytewise, <= 30
             const uint32_t dif = (lo | 0x10101010u) - hi;    // bytewise, 1..31
 #pragma unroll
@@ -653,7 +680,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
 
     // step 3: rest of the inverse transform, unscale, round to fp16
     auto finish = [&](float(&v)[N], Out& o) {
-        fwht_rest(v, c1, c2);
+        if constexpr (FT) srft::inverse<D>(v, fft_row, q);
+        else fwht_rest(v, c1, c2);
 #pragma unroll
         for (int j = 0; j < NJ; j++) {
             o.o[j].x = pack_half2(v[j * 8 + 0] * m[j * 8 + 0], v[j * 8 + 1] * m[j * 8 + 1]);
@@ -663,7 +691,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
         }
     };
 
-    run_pipeline<Raw, Out, N, (D <= 128)>(begin, end, load, first_stage, store, finish);
+    run_pipeline<Raw, Out, N, (D <= 128 && !FT)>(begin, end, load, first_stage, store, finish);
 }
 
 // ---------------------------------------------------------------------------
@@ -671,18 +699,18 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int D, int G, int BITS, bool MX = false>
+template <int D, int G, int BITS, bool MX = false, bool FT = false>
 hipError_t launch_qb(const Int4Args& a, hipStream_t s, bool inverse)
 {
     const int64_t waves = (a.n_items + a.items_per_wave - 1) / a.items_per_wave;
     const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
     const dim3 block(64 * kWavesPerBlock);
     if (inverse) {
-        if (a.token_major) hipLaunchKernelGGL((dequantize_kernel<D, G, true, BITS, MX>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((dequantize_kernel<D, G, false, BITS, MX>), grid, block, 0, s, a);
+        if (a.token_major) hipLaunchKernelGGL((dequantize_kernel<D, G, true, BITS, MX, FT>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((dequantize_kernel<D, G, false, BITS, MX, FT>), grid, block, 0, s, a);
     } else {
-        if (a.token_major) hipLaunchKernelGGL((quantize_kernel<D, G, true, BITS, MX>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((quantize_kernel<D, G, false, BITS, MX>), grid, block, 0, s, a);
+        if (a.token_major) hipLaunchKernelGGL((quantize_kernel<D, G, true, BITS, MX, FT>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((quantize_kernel<D, G, false, BITS, MX, FT>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -690,6 +718,7 @@ hipError_t launch_qb(const Int4Args& a, hipStream_t s, bool inverse)
 template <int D, int G>
 hipError_t launch_q(const Int4Args& a, hipStream_t s, bool inverse)
 {
+    if (a.fourier) return launch_qb<D, G, 4, false, true>(a, s, inverse);
     if constexpr (G == 32)
         if (a.mx) return launch_qb<D, 32, 4, true>(a, s, inverse);
     return a.bits == 8 ? launch_qb<D, G, 8>(a, s, inverse) : launch_qb<D, G, 4>(a, s, inverse);

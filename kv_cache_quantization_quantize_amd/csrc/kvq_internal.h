@@ -22,6 +22,7 @@ struct Int4Args {
     int32_t L, T, H, D, G;
     int32_t bits;           // code width: 4 (nibbles) or 8 (bytes)
     int32_t mx;             // 1: block-scaled E2M1 codes with E8M0 byte scales (group 32)
+    int32_t fourier;        // 1: SRFT rotation instead of Walsh-Hadamard (int4 codes)
     Tensor4 x;              // fp16 input (quantize) / fp16 output (dequantize)
     Tensor4 codes;          // u8, D/2 per vector
     Tensor4 scales;         // fp16, D/G per vector

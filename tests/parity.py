@@ -86,13 +86,15 @@ def _raise(what, rep, extra=""):
     raise ParityError("%s parity failed: %s %s" % (what, r, extra))
 
 
-def int4_parity(x_bits, lam_rows, signs, G, codes_gpu, scales_gpu, out_gpu=None):
+def int4_parity(x_bits, lam_rows, signs, G, codes_gpu, scales_gpu, out_gpu=None, fourier=False):
     """Full int4 check of n vectors.  x_bits [n, D] fp16 bits, lam_rows [n, D]
     fp32, codes_gpu [n, D/2] u8, scales_gpu [n, D/G] fp16 bits, out_gpu
-    (optional) [n, D] fp16 bits of the GPU dequantization of its own codes."""
+    (optional) [n, D] fp16 bits of the GPU dequantization of its own codes.
+    fourier: the SRFT rotation instead of the Walsh-Hadamard one."""
     x_bits = np.ascontiguousarray(x_bits, np.uint16)
     lam_rows = np.ascontiguousarray(lam_rows, np.float32)
-    codes_o, scales_o, y64, nbad = oracle.quantize(x_bits, lam_rows, signs, G)
+    quant = oracle.quantize_srft if fourier else oracle.quantize
+    codes_o, scales_o, y64, nbad = quant(x_bits, lam_rows, signs, G)
     if nbad:
         raise ParityError("%d input vectors are outside the quantizer's domain" % nbad)
     rep = {}
@@ -111,7 +113,7 @@ def int4_parity(x_bits, lam_rows, signs, G, codes_gpu, scales_gpu, out_gpu=None)
             i.tolist(), q_gpu[tuple(i.T)], rc["q_cond"][tuple(i.T)],
             (y64 / np.repeat(f16(scales_gpu), G, axis=1))[tuple(i.T)]))
     if out_gpu is not None:
-        x64, _ = oracle.dequantize(codes_gpu, scales_gpu, lam_rows, signs, G)
+        x64, _ = (oracle.dequantize_srft if fourier else oracle.dequantize)(codes_gpu, scales_gpu, lam_rows, signs, G)
         rd = check_dequant(out_gpu, x64, lam_rows)
         rep["dequant"] = rd
         if rd["bad"]:

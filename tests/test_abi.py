@@ -36,6 +36,7 @@ def test_header_declares_the_boundary():
         "kvq_attend_decode", "kvq_attend_decode_workspace", "kvq_quantize_int8", "kvq_dequantize_int8",
         "kvq_quantize_mxfp4", "kvq_dequantize_mxfp4", "kvq_vq_encode_u8", "kvq_vq_decode_u8",
         "kvq_kmeans_step", "kvq_kmeans_step_workspace",
+        "kvq_quantize_srft", "kvq_dequantize_srft",
         "kvq_status_string", "kvq_last_error", "kvq_version"])
 
 
@@ -193,6 +194,19 @@ def test_kmeans_workspace_query_and_validation(lib):
     assert step(ws=A + 8) == ALIGN
     assert step(wsb=need.value - 1) == SHAPE
     assert b"needed" in lib.kvq_last_error()
+
+
+def test_srft_validation(lib):
+    P = ctypes.c_void_p
+    sh = shape()
+    x, codes, scales = view(), view(row=64), view(row=4)
+    assert lib.kvq_quantize_srft(shape(T=0), x, P(A), P(A), 32, codes, scales, None) == OK
+    assert lib.kvq_quantize_srft(shape(D=96), x, P(A), P(A), 32, codes, scales, None) == UNSUP
+    assert lib.kvq_quantize_srft(sh, x, P(A), P(A), 12, codes, scales, None) == UNSUP
+    assert lib.kvq_quantize_srft(sh, x, P(0), P(A), 32, codes, scales, None) == NULL
+    assert lib.kvq_quantize_srft(sh, view(addr=A + 2), P(A), P(A), 32, codes, scales, None) == ALIGN
+    assert lib.kvq_dequantize_srft(sh, codes, scales, P(A), P(A), 32, view(addr=0), None) == NULL
+    assert lib.kvq_dequantize_srft(shape(T=0), codes, scales, P(A), P(A), 32, x, None) == OK
 
 
 def test_binding_raises_without_gpu_tensors():
