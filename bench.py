@@ -99,12 +99,14 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
     att = 2 * L * T * H * (D // 2 + 2 * (D // G)) + 2 * (L * B) * H * R * D * 2
     nk = 36 * 8192 * 8
     kernels = {
-        "quantize": ("kvq::quantize_kernel<128, 32, true, 4, false>", nv * bytes_per_vector(D, G)),
-        "dequantize": ("kvq::dequantize_kernel<128, 32, true, 4, false>", nv * bytes_per_vector(D, G)),
-        "quantize_int8": ("kvq::quantize_kernel<128, 32, true, 8, false>", nv * (3 * D + 2 * (D // G))),
-        "dequantize_int8": ("kvq::dequantize_kernel<128, 32, true, 8, false>", nv * (3 * D + 2 * (D // G))),
-        "quantize_mxfp4": ("kvq::quantize_kernel<128, 32, true, 4, true>", nv * (2 * D + D // 2 + D // 32)),
-        "dequantize_mxfp4": ("kvq::dequantize_kernel<128, 32, true, 4, true>", nv * (2 * D + D // 2 + D // 32)),
+        "quantize": ("kvq::quantize_kernel<128, 32, true, 4, false, false>", nv * bytes_per_vector(D, G)),
+        "dequantize": ("kvq::dequantize_kernel<128, 32, true, 4, false, false>", nv * bytes_per_vector(D, G)),
+        "quantize_int8": ("kvq::quantize_kernel<128, 32, true, 8, false, false>", nv * (3 * D + 2 * (D // G))),
+        "dequantize_int8": ("kvq::dequantize_kernel<128, 32, true, 8, false, false>", nv * (3 * D + 2 * (D // G))),
+        "quantize_mxfp4": ("kvq::quantize_kernel<128, 32, true, 4, true, false>", nv * (2 * D + D // 2 + D // 32)),
+        "dequantize_mxfp4": ("kvq::dequantize_kernel<128, 32, true, 4, true, false>", nv * (2 * D + D // 2 + D // 32)),
+        "quantize_srft": ("kvq::quantize_kernel<128, 32, true, 4, false, true>", nv * bytes_per_vector(D, G)),
+        "dequantize_srft": ("kvq::dequantize_kernel<128, 32, true, 4, false, true>", nv * bytes_per_vector(D, G)),
         "attend_partial": ("kvq::attend_partial_kernel<128, 4, false>", att),
         "attend_combine": ("kvq::attend_combine_kernel<128>", None),
         "vq_encode": ("kvq::vq_encode_kernel<128, false>", nk * (2 * D + 2 * (D // 8))),
@@ -219,6 +221,7 @@ def main():
     ap.add_argument("--no-attend", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--no-mxfp4", action="store_true")
+    ap.add_argument("--no-srft", action="store_true")
     ap.add_argument("--no-small", action="store_true", help="skip the Qwen2.5 / Gemma cache timings")
     ap.add_argument("--attend-seqs", type=int, default=8,
                     help="sequences the int4 cache's token axis is split into for the decode-attention leg")
@@ -340,6 +343,9 @@ def main():
     mxfp4 = None
     if not args.no_mxfp4:
         mxfp4 = bench_variant(torch, kvq, K, lamK, signs, (L, T, H, D, G), args, "mxfp4")
+    srft = None
+    if not args.no_srft:
+        srft = bench_variant(torch, kvq, K, lamK, signs, (L, T, H, D, G), args, "srft")
 
     attend = None
     if not args.no_attend:
@@ -379,6 +385,7 @@ def main():
         "attend": attend,
         "int8": int8,
         "mxfp4": mxfp4,
+        "srft": srft,
         "small_workloads": small,
         "frac_of_hbm_peak_step": round(value / HBM_PEAK_GBPS, 4),
     }
@@ -454,10 +461,18 @@ def bench_small(torch, kvq, synth, dev, args):
 
 def bench_variant(torch, kvq, K, lamK, signs, dims, args, kind):
     """Time one code variant of the fused quantizer (quantize, then dequantize)
-    on the K cache: "int8" (127 levels, fp16 group scales) or "mxfp4"
-    (E2M1 elements, one E8M0 scale byte per 32 coordinates)."""
+    on the K cache: "int8" (127 levels, fp16 group scales), "mxfp4" (E2M1
+    elements, one E8M0 scale byte per 32 coordinates) or "srft" (int4 codes
+    on the sign-randomized real Fourier rotation)."""
     L, T, H, D, G = dims
-    if kind == "int8":
+    if kind == "srft":
+        codes = torch.empty((L, T, H, D // 2), dtype=torch.uint8, device=K.device)
+        scales = torch.empty((L, T, H, D // G), dtype=torch.float16, device=K.device)
+        bpv = bytes_per_vector(D, G)
+        what = "group %d, int4 codes, SRFT rotation" % G
+        qf = lambda: kvq.quantize_srft(K, lamK, signs, G, codes=codes, scales=scales, stream=stream)
+        df = lambda: kvq.dequantize_srft(codes, scales, lamK, signs, G, out=out, stream=stream)
+    elif kind == "int8":
         codes = torch.empty((L, T, H, D), dtype=torch.int8, device=K.device)
         scales = torch.empty((L, T, H, D // G), dtype=torch.float16, device=K.device)
         bpv = 2 * D + D + 2 * (D // G)
