@@ -355,6 +355,372 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core partial kernel: head_dim 128, group 32
+// ---------------------------------------------------------------------------
+// Same block decomposition, query rotation, log2-domain online softmax and
+// partial format as attend_partial_kernel, with both contractions on
+// v_mfma_f32_16x16x32_f16 (A 16x32, B 32x16, fp32 accumulate; lane l holds
+// A row l%16 / B column l%16 and k-slice l/16, eight k per slice; the result
+// holds rows 4*(l/16)..+3 of column l%16).  A wavefront takes 32 tokens per
+// step.
+//
+// Scores.  Rows are 16 tokens; columns are (group g, query r) = 4g + r; the
+// k-slice of lane row-slice sl is group sl, so B column (g, r) is the rotated
+// query r restricted to group g (zero on the other slices) and the result is
+// the per-group partial dot products, which the group scales then weight
+// (scaled by columns, summed over g with two row rotations).  The query is
+// split into fp16 hi + lo halves (two MFMAs), so the dot products are fp32
+// accurate; the codes (integers -7..7) are exact in fp16.  A lane's 16 code
+// bytes of group sl feed four MFMAs, one dword each.
+//
+// Values.  Rows are (group g', query r) = 4g' + r, k is the 32 tokens, and
+// columns are coordinates: tile m, column j is coordinate 8j + m.  A row
+// (g', r) is p_r * vscale_g' over the tokens (hi + lo halves), so the result's
+// row (g(c), r) is query r's weighted sum of coordinate c; the other rows are
+// discarded.  A lane loads one dword (coordinates 8j..8j+7) of each of its
+// slice's 8 tokens and regroups nibbles with v_perm.
+//
+// Within every 8-element operand the k order is (0,4,1,5,2,6,3,7), the order
+// in which nibble pairs come out of a masked dword; A and B use the same order.
+// Scores, weights and scales cross between the two layouts through small
+// wave-private LDS tiles.
+namespace {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kPermK[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+
+// fp16 of (n - 8) for two offset-binary nibbles n held in bits 0-3 and 16-19
+__device__ __forceinline__ uint32_t nib2_h2(uint32_t x)
+{
+    const uint32_t b = (x & 0x000F000Fu) | 0x64006400u;          // fp16 1024 + n
+    const h2_t r = __builtin_bit_cast(h2_t, b) + h2_t{(_Float16)-1032.0f, (_Float16)-1032.0f};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight two's-complement codes of a dword (nibble e = element e) as an fp16
+// operand in the order (0,4,1,5,2,6,3,7).
+__device__ __forceinline__ h8_t codes8(uint32_t w)
+{
+    const uint32_t x = w ^ 0x88888888u;
+    const uint4 o = make_uint4(nib2_h2(x), nib2_h2(x >> 4), nib2_h2(x >> 8), nib2_h2(x >> 12));
+    return __builtin_bit_cast(h8_t, o);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, h2_t{(_Float16)a, (_Float16)b});
+}
+
+}  // namespace
+
+template <int D, int RP>
+__device__ __forceinline__ void rotate_queries(const AttnArgs& a, int l, int h, int r0, int lane, float (&qt)[RP][D])
+{
+    constexpr int NJ = D / 32;
+    constexpr int N = D / 4;
+    const int qd = lane >> 2, qq = lane & 3;
+    const int rr = min(qd, RP - 1);
+    const int qi = min(r0 + rr, a.R - 1);
+    const _Float16* qp = a.q + (((int64_t)l * a.H + h) * a.R + qi) * D;
+    const float* lk = a.lam_k + ((int64_t)l * a.H + h) * D;
+    float v[N];
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+        const int c0 = 32 * j + 8 * qq;
+        const uint4 qw = *reinterpret_cast<const uint4*>(qp + c0);
+        const float4 l0 = *reinterpret_cast<const float4*>(lk + c0);
+        const float4 l1 = *reinterpret_cast<const float4*>(lk + c0 + 4);
+        const uint2 sg = *reinterpret_cast<const uint2*>(a.signs + c0);
+        const uint32_t w[4] = {qw.x, qw.y, qw.z, qw.w};
+        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const uint32_t word = e < 4 ? sg.x : sg.y;
+            const int sv = (int)(int8_t)((word >> (8 * (e & 3))) & 0xff);
+            const float qv = (e & 1) ? hi_half(w[e / 2]) : lo_half(w[e / 2]);
+            x[e] = (sv < 0 ? -qv : qv) / (lv[e] * SqrtD<D>::v);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            v[8 * j + 2 * k] = x[2 * k] + x[2 * k + 1];
+            v[8 * j + 2 * k + 1] = x[2 * k] - x[2 * k + 1];
+        }
+    }
+    fwht_rest(v, (qq & 1) ? -1.0f : 1.0f, (qq & 2) ? -1.0f : 1.0f);
+    const float f = ((__builtin_popcount(qq) & 1) ? -1.0f : 1.0f) * a.qscale;
+    if (qd < RP) {
+#pragma unroll
+        for (int j = 0; j < NJ; j++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) qt[rr][32 * j + 8 * qq + e] = v[8 * j + e] * f;
+    }
+}
+
+__global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(AttnArgs a)
+{
+    constexpr int D = 128, RP = 4, STEP = 32, TS = 1024 / D;
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    int l, h, split;
+    {
+        const int b = blockIdx.x;
+        int u;
+        if (a.xcd_map) {
+            const int k = b >> 3;
+            u = ((k / a.H) << 3) + (b & 7);
+            h = k - (k / a.H) * a.H;
+        } else {
+            u = b / a.H;
+            h = b - u * a.H;
+        }
+        l = uniform(u / a.S);
+        split = u - l * a.S;
+        h = uniform(h);
+    }
+    const int lh = l * a.H + h;
+    const int r0 = blockIdx.y * a.rp;
+    const int n = a.lengths ? min(max(a.lengths[l], 0), a.T) : a.T;
+
+    __shared__ float qt[RP][D];
+    if (wid == 0) rotate_queries<D, RP>(a, l, h, r0, lane, qt);
+    __syncthreads();
+
+    const int j16 = lane & 15;   // MFMA row (A) / column (B, result)
+    const int sl = lane >> 4;    // MFMA k-slice; result row block
+
+    // score B operands: column (g, r) = 4g + r, slice sl = group sl
+    h8_t bq_hi[4], bq_lo[4];
+    {
+        const int r = j16 & 3, g = j16 >> 2;
+        const bool on = g == sl;
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const float v0 = on ? qt[r][32 * sl + 8 * m + kPermK[2 * k]] : 0.0f;
+                const float v1 = on ? qt[r][32 * sl + 8 * m + kPermK[2 * k + 1]] : 0.0f;
+                const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+                hw[k] = __builtin_bit_cast(uint32_t, h2_t{h0, h1});
+                lw[k] = pack_h2(v0 - (float)h0, v1 - (float)h1);
+            }
+            bq_hi[m] = __builtin_bit_cast(h8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+            bq_lo[m] = __builtin_bit_cast(h8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
+    }
+
+    // wave-private exchange tiles
+    __shared__ _Float16 ksT[kAttnWaves][4][STEP], vsT[kAttnWaves][4][STEP];
+    __shared__ float pL[kAttnWaves][RP][STEP];
+    __shared__ float aL[kAttnWaves][RP];
+
+    const int cb = split * a.chunk;
+    const int ce = min(cb + a.chunk, n);
+    const int per_wave = ((a.chunk + kAttnWaves * STEP - 1) / (kAttnWaves * STEP)) * STEP;
+    const int wb = cb + wid * per_wave;
+    const int we = min(wb + per_wave, ce);
+    const int nsteps = we > wb ? (we - wb + STEP - 1) / STEP : 0;
+
+    const uint8_t* kcg = static_cast<const uint8_t*>(a.kc.data) + (int64_t)l * a.kc.sl + (int64_t)h * a.kc.sh;
+    const uint8_t* vcg = static_cast<const uint8_t*>(a.vc.data) + (int64_t)l * a.vc.sl + (int64_t)h * a.vc.sh;
+    const uint16_t* ksg = static_cast<const uint16_t*>(a.ks.data) + (int64_t)l * a.ks.sl + (int64_t)h * a.ks.sh;
+    const uint16_t* vsg = static_cast<const uint16_t*>(a.vs.data) + (int64_t)l * a.vs.sl + (int64_t)h * a.vs.sh;
+    typedef uint32_t u32_a2 __attribute__((aligned(2)));
+
+    struct Buf {
+        uint4 k[2];       // token 16 tau + j16, group sl: 32 codes
+        uint32_t v[8];    // token 8 sl + t', coordinates 8 j16 .. 8 j16 + 7
+        uint32_t ks, vs;  // token lane / 2, groups 2 (lane & 1), +1
+    };
+    // every load is in range: token indices are clamped to the wave's last token
+    auto load = [&](int step, Buf& b) {
+        const int tb = wb + step * STEP;
+        const int last = we - 1;
+#pragma unroll
+        for (int tau = 0; tau < 2; tau++) {
+            const int t = min(tb + 16 * tau + j16, last);
+            b.k[tau] = *reinterpret_cast<const uint4*>(kcg + (int64_t)t * a.kc.st + 16 * sl);
+        }
+#pragma unroll
+        for (int tp = 0; tp < 8; tp++) {
+            const int t = min(tb + 8 * sl + tp, last);
+            b.v[tp] = *reinterpret_cast<const uint32_t*>(vcg + (int64_t)t * a.vc.st + 4 * j16);
+        }
+        const int ts = min(tb + (lane >> 1), last);
+        b.ks = *reinterpret_cast<const u32_a2*>(ksg + (int64_t)ts * a.ks.st + 2 * (lane & 1));
+        b.vs = *reinterpret_cast<const u32_a2*>(vsg + (int64_t)ts * a.vs.st + 2 * (lane & 1));
+    };
+
+    float m_run = -__builtin_inff();   // running max of query j16 & 3 (log2 domain)
+    float l_run = 0.0f;                // this lane's share of the weight sum
+    f4_t acc[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; mt++) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](int step, const Buf& b) {
+        const int tb = wb + step * STEP;
+        // scale tiles, transposed to [group][token]
+        {
+            const int tl = lane >> 1, g0 = 2 * (lane & 1);
+            ksT[wid][g0][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.ks & 0xffffu));
+            ksT[wid][g0 + 1][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.ks >> 16));
+            vsT[wid][g0][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.vs & 0xffffu));
+            vsT[wid][g0 + 1][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.vs >> 16));
+        }
+        // per-group partial scores of 2 x 16 tokens
+        f4_t c[2];
+#pragma unroll
+        for (int tau = 0; tau < 2; tau++) {
+            c[tau] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            const uint32_t kw[4] = {b.k[tau].x, b.k[tau].y, b.k[tau].z, b.k[tau].w};
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                const h8_t am = codes8(kw[m]);
+                c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bq_hi[m], c[tau], 0, 0, 0);
+                c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bq_lo[m], c[tau], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // weight by the group scales, sum over the 4 groups (columns 4g + r)
+        const int g = j16 >> 2, r = j16 & 3;
+        float sc[2][4];
+        float smax = -__builtin_inff();
+#pragma unroll
+        for (int tau = 0; tau < 2; tau++) {
+            const uint2 kq = *reinterpret_cast<const uint2*>(&ksT[wid][g][16 * tau + 4 * sl]);
+            const float kv[4] = {lo_half(kq.x), hi_half(kq.x), lo_half(kq.y), hi_half(kq.y)};
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                float x = c[tau][v] * kv[v];
+                x += dpp_mov<0x124>(x);            // row_ror:4
+                x += dpp_mov<0x128>(x);            // row_ror:8
+                const bool valid = tb + 16 * tau + 4 * sl + v < we;
+                sc[tau][v] = valid ? x : -__builtin_inff();
+                smax = fmaxf(smax, sc[tau][v]);
+            }
+        }
+        smax = fmaxf(smax, __shfl_xor(smax, 16));
+        smax = fmaxf(smax, __shfl_xor(smax, 32));
+        const float m_new = fmaxf(m_run, smax);
+        const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        float psum = 0.0f;
+        float pv[2][4];
+#pragma unroll
+        for (int tau = 0; tau < 2; tau++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                pv[tau][v] = (sc[tau][v] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(sc[tau][v] - m_new);
+                psum += pv[tau][v];
+            }
+        l_run = fmaf(l_run, alpha, psum);
+        if (g == 0) {
+#pragma unroll
+            for (int tau = 0; tau < 2; tau++)
+                *reinterpret_cast<float4*>(&pL[wid][r][16 * tau + 4 * sl]) =
+                    make_float4(pv[tau][0], pv[tau][1], pv[tau][2], pv[tau][3]);
+            if (sl == 0) aL[wid][r] = alpha;
+        }
+        __builtin_amdgcn_wave_barrier();
+        // value operands: A row (g', r') = (j16 >> 2, j16 & 3), tokens 8 sl + (0,4,1,5,...)
+        h8_t ap_hi, ap_lo;
+        {
+            const float4 p0 = *reinterpret_cast<const float4*>(&pL[wid][r][8 * sl]);
+            const float4 p1 = *reinterpret_cast<const float4*>(&pL[wid][r][8 * sl + 4]);
+            const uint4 vq = *reinterpret_cast<const uint4*>(&vsT[wid][g][8 * sl]);
+            const float pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            const float vv[8] = {lo_half(vq.x), hi_half(vq.x), lo_half(vq.y), hi_half(vq.y),
+                                 lo_half(vq.z), hi_half(vq.z), lo_half(vq.w), hi_half(vq.w)};
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const float x0 = pp[k] * vv[k], x1 = pp[k + 4] * vv[k + 4];
+                const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+                hw[k] = __builtin_bit_cast(uint32_t, h2_t{h0, h1});
+                lw[k] = pack_h2(x0 - (float)h0, x1 - (float)h1);
+            }
+            ap_hi = __builtin_bit_cast(h8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+            ap_lo = __builtin_bit_cast(h8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
+        // rescale: result rows 4 sl + v are queries v
+        {
+            const float4 al = *reinterpret_cast<const float4*>(&aL[wid][0]);
+            const float av[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+            for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc[mt][v] *= av[v];
+        }
+        // value B operands: tile 2q' / 2q'+1 from byte q' of the 8 tokens' dwords
+#pragma unroll
+        for (int qb = 0; qb < 4; qb++) {
+            const uint32_t sel = (uint32_t)qb | (0x0cu << 8) | ((uint32_t)(4 + qb) << 16) | (0x0cu << 24);
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const uint32_t w = __builtin_amdgcn_perm(b.v[k + 4], b.v[k], sel) ^ 0x00880088u;
+                lo[k] = nib2_h2(w);
+                hi[k] = nib2_h2(w >> 4);
+            }
+            const h8_t bl = __builtin_bit_cast(h8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+            const h8_t bh = __builtin_bit_cast(h8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+            acc[2 * qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_hi, bl, acc[2 * qb], 0, 0, 0);
+            acc[2 * qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_lo, bl, acc[2 * qb], 0, 0, 0);
+            acc[2 * qb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_hi, bh, acc[2 * qb + 1], 0, 0, 0);
+            acc[2 * qb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_lo, bh, acc[2 * qb + 1], 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    if (nsteps > 0) {
+        Buf A, B;
+        load(0, A);
+        for (int st = 0;; st += 2) {
+            load(min(st + 1, nsteps - 1), B);
+            compute(st, A);
+            if (st + 1 >= nsteps) break;
+            load(min(st + 2, nsteps - 1), A);
+            compute(st + 1, B);
+            if (st + 2 >= nsteps) break;
+        }
+    }
+
+    // ---- partials: the wave's state in slot 0, empty headers in the others --
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    const int part0 = (split * kAttnWaves + wid) * TS;
+    const int nr = min(a.rp, a.R - r0);
+    {
+        const int r = j16 & 3, g = j16 >> 2;
+        if (g == 0 && sl == 0 && r < nr) {
+            float* P = a.ws + ((((int64_t)lh * a.R + r0 + r) * a.parts) + part0) * (D + 4);
+            *reinterpret_cast<float2*>(P) = make_float2(m_run, l_run);
+        }
+        if (lane >= 1 && lane < TS) {
+            for (int rr = 0; rr < nr; rr++) {
+                float* P = a.ws + ((((int64_t)lh * a.R + r0 + rr) * a.parts) + part0 + lane) * (D + 4);
+                *reinterpret_cast<float2*>(P) = make_float2(-__builtin_inff(), 0.0f);
+            }
+        }
+    }
+    // result rows 4 sl + v = (group sl, query v); column j16 of tile mt is
+    // coordinate 8 j16 + mt, which belongs to group j16 / 4
+    if (sl == (j16 >> 2)) {
+#pragma unroll
+        for (int v = 0; v < RP; v++) {
+            if (v >= nr) break;
+            float* P = a.ws + ((((int64_t)lh * a.R + r0 + v) * a.parts) + part0) * (D + 4) + 4 + 8 * j16;
+            *reinterpret_cast<float4*>(P) = make_float4(acc[0][v], acc[1][v], acc[2][v], acc[3][v]);
+            *reinterpret_cast<float4*>(P + 4) = make_float4(acc[4][v], acc[5][v], acc[6][v], acc[7][v]);
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kAttnWaves) void attend_combine_kernel(AttnArgs a)
 {
@@ -431,6 +797,12 @@ template <int D, int RP>
 hipError_t launch_part(const AttnArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)((int64_t)a.L * a.H * a.S), (unsigned)((a.R + RP - 1) / RP));
+    if constexpr (D == 128) {
+        if (a.g_shift == 5) {
+            hipLaunchKernelGGL(attend_partial_mfma_kernel, grid, dim3(64 * kAttnWaves), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     if (a.g_shift == 3) hipLaunchKernelGGL((attend_partial_kernel<D, RP, true>), grid, dim3(64 * kAttnWaves), 0, s, a);
     else hipLaunchKernelGGL((attend_partial_kernel<D, RP, false>), grid, dim3(64 * kAttnWaves), 0, s, a);
     return hipGetLastError();
