@@ -28,6 +28,8 @@
 //
 // Combine kernel.  One quad per (outer index, query head): merges the
 // partials, normalises, applies the inverse rotation and unscale, writes fp16.
+#include <algorithm>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -393,20 +395,25 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPermK[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 
-// fp16 of (n - 8) for two offset-binary nibbles n held in bits 0-3 and 16-19
-__device__ __forceinline__ uint32_t nib2_h2(uint32_t x)
+// fp16 of (n - 8) for two offset-binary nibbles n held in bits 0-3 and 16-19:
+// one v_and_or_b32 builds the fp16 patterns of 1024 + n (magic = 0x64006400
+// held in a VGPR, the mask in an SGPR: one constant-bus read), one packed
+// fp16 add subtracts 1032 exactly.
+__device__ __forceinline__ uint32_t nib2_h2(uint32_t x, uint32_t magic)
 {
-    const uint32_t b = (x & 0x000F000Fu) | 0x64006400u;          // fp16 1024 + n
+    uint32_t b;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(b) : "v"(x), "s"(0x000F000Fu), "v"(magic));
     const h2_t r = __builtin_bit_cast(h2_t, b) + h2_t{(_Float16)-1032.0f, (_Float16)-1032.0f};
     return __builtin_bit_cast(uint32_t, r);
 }
 
 // Eight two's-complement codes of a dword (nibble e = element e) as an fp16
 // operand in the order (0,4,1,5,2,6,3,7).
-__device__ __forceinline__ h8_t codes8(uint32_t w)
+__device__ __forceinline__ h8_t codes8(uint32_t w, uint32_t magic)
 {
     const uint32_t x = w ^ 0x88888888u;
-    const uint4 o = make_uint4(nib2_h2(x), nib2_h2(x >> 4), nib2_h2(x >> 8), nib2_h2(x >> 12));
+    const uint4 o = make_uint4(nib2_h2(x, magic), nib2_h2(x >> 4, magic), nib2_h2(x >> 8, magic),
+                               nib2_h2(x >> 12, magic));
     return __builtin_bit_cast(h8_t, o);
 }
 
@@ -465,7 +472,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
 {
     constexpr int D = 128, RP = 4, STEP = 32, TS = 1024 / D;
     const int lane = threadIdx.x & 63;
-    const int wid = threadIdx.x >> 6;
+    const int wid = uniform(threadIdx.x >> 6);
     int l, h, split;
     {
         const int b = blockIdx.x;
@@ -537,25 +544,46 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
         uint32_t v[8];    // token 8 sl + t', coordinates 8 j16 .. 8 j16 + 7
         uint32_t ks, vs;  // token lane / 2, groups 2 (lane & 1), +1
     };
-    // every load is in range: token indices are clamped to the wave's last token
+    // A step's loads address a wave-uniform base (the step's first token)
+    // plus 32-bit per-lane byte offsets (the host guarantees 32 token rows fit
+    // in 2^31 bytes).  In the last step, tokens past the wave's range are
+    // clamped to its last token, so every load is in range.
+    const uint32_t kst = (uint32_t)a.kc.st, vst = (uint32_t)a.vc.st;
+    const uint32_t kss = 2u * (uint32_t)a.ks.st, vss = 2u * (uint32_t)a.vs.st;
+    struct Off {
+        uint32_t k[2], v[8], ks, vs;
+    };
+    // byte offsets of the lane's loads from the step's first token, for steps
+    // whose last in-range token is `lim`
+    auto offsets = [&](int lim) {
+        Off o;
+#pragma unroll
+        for (int tau = 0; tau < 2; tau++) o.k[tau] = (uint32_t)min(16 * tau + j16, lim) * kst + 16u * sl;
+#pragma unroll
+        for (int tp = 0; tp < 8; tp++) o.v[tp] = (uint32_t)min(8 * sl + tp, lim) * vst + 4u * j16;
+        const uint32_t ts = (uint32_t)min(lane >> 1, lim);
+        o.ks = ts * kss + 4u * (lane & 1);
+        o.vs = ts * vss + 4u * (lane & 1);
+        return o;
+    };
+    Off off = offsets(STEP - 1);
     auto load = [&](int step, Buf& b) {
         const int tb = wb + step * STEP;
-        const int last = we - 1;
+        if (tb + STEP > we) off = offsets(we - 1 - tb);      // the wave's last, partial step
+        const uint8_t* kb = kcg + (int64_t)tb * a.kc.st;
+        const uint8_t* vb = vcg + (int64_t)tb * a.vc.st;
+        const uint8_t* ksb = reinterpret_cast<const uint8_t*>(ksg + (int64_t)tb * a.ks.st);
+        const uint8_t* vsb = reinterpret_cast<const uint8_t*>(vsg + (int64_t)tb * a.vs.st);
 #pragma unroll
-        for (int tau = 0; tau < 2; tau++) {
-            const int t = min(tb + 16 * tau + j16, last);
-            b.k[tau] = *reinterpret_cast<const uint4*>(kcg + (int64_t)t * a.kc.st + 16 * sl);
-        }
+        for (int tau = 0; tau < 2; tau++) b.k[tau] = *reinterpret_cast<const uint4*>(kb + off.k[tau]);
 #pragma unroll
-        for (int tp = 0; tp < 8; tp++) {
-            const int t = min(tb + 8 * sl + tp, last);
-            b.v[tp] = *reinterpret_cast<const uint32_t*>(vcg + (int64_t)t * a.vc.st + 4 * j16);
-        }
-        const int ts = min(tb + (lane >> 1), last);
-        b.ks = *reinterpret_cast<const u32_a2*>(ksg + (int64_t)ts * a.ks.st + 2 * (lane & 1));
-        b.vs = *reinterpret_cast<const u32_a2*>(vsg + (int64_t)ts * a.vs.st + 2 * (lane & 1));
+        for (int tp = 0; tp < 8; tp++) b.v[tp] = *reinterpret_cast<const uint32_t*>(vb + off.v[tp]);
+        b.ks = *reinterpret_cast<const u32_a2*>(ksb + off.ks);
+        b.vs = *reinterpret_cast<const u32_a2*>(vsb + off.vs);
     };
 
+    uint32_t magic = 0x64006400u;      // fp16 1024 in both halves, kept in a VGPR
+    asm volatile("" : "+v"(magic));
     float m_run = -__builtin_inff();   // running max of query j16 & 3 (log2 domain)
     float l_run = 0.0f;                // this lane's share of the weight sum
     f4_t acc[8];
@@ -580,7 +608,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
             const uint32_t kw[4] = {b.k[tau].x, b.k[tau].y, b.k[tau].z, b.k[tau].w};
 #pragma unroll
             for (int m = 0; m < 4; m++) {
-                const h8_t am = codes8(kw[m]);
+                const h8_t am = codes8(kw[m], magic);
                 c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bq_hi[m], c[tau], 0, 0, 0);
                 c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bq_lo[m], c[tau], 0, 0, 0);
             }
@@ -606,25 +634,40 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
         }
         smax = fmaxf(smax, __shfl_xor(smax, 16));
         smax = fmaxf(smax, __shfl_xor(smax, 32));
-        const float m_new = fmaxf(m_run, smax);
-        const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
+        // The weights are taken relative to a reference max that moves only
+        // when a score exceeds it by more than 2^8 (weights stay below 256,
+        // well inside fp16), so the accumulators are rescaled a few times per
+        // wave rather than every step.
+        if (__builtin_amdgcn_ballot_w64(smax > m_run + 8.0f)) {
+            const float m_new = fmaxf(m_run, smax);
+            const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+            if (g == 0 && sl == 0) aL[wid][r] = alpha;
+            __builtin_amdgcn_wave_barrier();
+            // result rows 4 sl + v are queries v
+            const float4 al = *reinterpret_cast<const float4*>(&aL[wid][0]);
+            const float av[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+            for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc[mt][v] *= av[v];
+        }
         float psum = 0.0f;
         float pv[2][4];
 #pragma unroll
         for (int tau = 0; tau < 2; tau++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                pv[tau][v] = (sc[tau][v] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(sc[tau][v] - m_new);
+                pv[tau][v] = (sc[tau][v] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(sc[tau][v] - m_run);
                 psum += pv[tau][v];
             }
-        l_run = fmaf(l_run, alpha, psum);
+        l_run += psum;
         if (g == 0) {
 #pragma unroll
             for (int tau = 0; tau < 2; tau++)
                 *reinterpret_cast<float4*>(&pL[wid][r][16 * tau + 4 * sl]) =
                     make_float4(pv[tau][0], pv[tau][1], pv[tau][2], pv[tau][3]);
-            if (sl == 0) aL[wid][r] = alpha;
         }
         __builtin_amdgcn_wave_barrier();
         // value operands: A row (g', r') = (j16 >> 2, j16 & 3), tokens 8 sl + (0,4,1,5,...)
@@ -647,15 +690,6 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
             ap_hi = __builtin_bit_cast(h8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
             ap_lo = __builtin_bit_cast(h8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
         }
-        // rescale: result rows 4 sl + v are queries v
-        {
-            const float4 al = *reinterpret_cast<const float4*>(&aL[wid][0]);
-            const float av[4] = {al.x, al.y, al.z, al.w};
-#pragma unroll
-            for (int mt = 0; mt < 8; mt++)
-#pragma unroll
-                for (int v = 0; v < 4; v++) acc[mt][v] *= av[v];
-        }
         // value B operands: tile 2q' / 2q'+1 from byte q' of the 8 tokens' dwords
 #pragma unroll
         for (int qb = 0; qb < 4; qb++) {
@@ -664,8 +698,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
 #pragma unroll
             for (int k = 0; k < 4; k++) {
                 const uint32_t w = __builtin_amdgcn_perm(b.v[k + 4], b.v[k], sel) ^ 0x00880088u;
-                lo[k] = nib2_h2(w);
-                hi[k] = nib2_h2(w >> 4);
+                lo[k] = nib2_h2(w, magic);
+                hi[k] = nib2_h2(w >> 4, magic);
             }
             const h8_t bl = __builtin_bit_cast(h8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
             const h8_t bh = __builtin_bit_cast(h8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
@@ -677,6 +711,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
         __builtin_amdgcn_wave_barrier();
     };
 
+    // the next step's loads in flight while a step is computed
     if (nsteps > 0) {
         Buf A, B;
         load(0, A);
@@ -798,7 +833,9 @@ hipError_t launch_part(const AttnArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)((int64_t)a.L * a.H * a.S), (unsigned)((a.R + RP - 1) / RP));
     if constexpr (D == 128) {
-        if (a.g_shift == 5) {
+        // the matrix-core kernel addresses 32 token rows with 32-bit offsets
+        const int64_t row = std::max(std::max(a.kc.st, a.vc.st), 2 * std::max(a.ks.st, a.vs.st));
+        if (a.g_shift == 5 && 32 * row + 64 < ((int64_t)1 << 31)) {
             hipLaunchKernelGGL(attend_partial_mfma_kernel, grid, dim3(64 * kAttnWaves), 0, s, a);
             return hipGetLastError();
         }
