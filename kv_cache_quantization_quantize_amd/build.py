@@ -35,7 +35,11 @@ COMMON = [
 # Per-file extra flags.  The VQ search takes maxima of MFMA results; without
 # -fno-honor-nans every fmaxf first canonicalises its (possibly signalling-NaN)
 # inputs.  Non-finite inputs are outside the library's documented domain.
-EXTRA = {"kvq_vq.hip": ["-fno-honor-nans"]}
+# The attention kernel rescales its MFMA accumulators on the VALU; keeping
+# MFMA operands and results in VGPRs (rather than AGPRs) avoids copying the
+# accumulators between the two register files every step.
+EXTRA = {"kvq_vq.hip": ["-fno-honor-nans"],
+         "kvq_attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

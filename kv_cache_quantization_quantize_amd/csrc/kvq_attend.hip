@@ -500,9 +500,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
     const int j16 = lane & 15;   // MFMA row (A) / column (B, result)
     const int sl = lane >> 4;    // MFMA k-slice; result row block
 
-    // score B operands: column (g, r) = 4g + r, slice sl = group sl
-    h8_t bq_hi[4], bq_lo[4];
-    {
+    // score B operands, [hi/lo][MFMA m][lane]: column (g, r) = 4g + r, slice
+    // sl = group sl.  The same for every wavefront; kept in LDS and read at
+    // each use rather than held in 32 VGPRs.
+    __shared__ uint4 bqL[2][4][64];
+    if (wid == 0) {
         const int r = j16 & 3, g = j16 >> 2;
         const bool on = g == sl;
 #pragma unroll
@@ -516,10 +518,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
                 hw[k] = __builtin_bit_cast(uint32_t, h2_t{h0, h1});
                 lw[k] = pack_h2(v0 - (float)h0, v1 - (float)h1);
             }
-            bq_hi[m] = __builtin_bit_cast(h8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-            bq_lo[m] = __builtin_bit_cast(h8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+            bqL[0][m][lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            bqL[1][m][lane] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
     }
+    __syncthreads();
 
     // wave-private exchange tiles
     __shared__ _Float16 ksT[kAttnWaves][4][STEP], vsT[kAttnWaves][4][STEP];
@@ -609,8 +612,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
 #pragma unroll
             for (int m = 0; m < 4; m++) {
                 const h8_t am = codes8(kw[m], magic);
-                c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bq_hi[m], c[tau], 0, 0, 0);
-                c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bq_lo[m], c[tau], 0, 0, 0);
+                const h8_t bh = __builtin_bit_cast(h8_t, bqL[0][m][lane]);
+                const h8_t bl = __builtin_bit_cast(h8_t, bqL[1][m][lane]);
+                c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bh, c[tau], 0, 0, 0);
+                c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bl, c[tau], 0, 0, 0);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -691,13 +696,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
             ap_lo = __builtin_bit_cast(h8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
         }
         // value B operands: tile 2q' / 2q'+1 from byte q' of the 8 tokens' dwords
+        uint32_t vx[8];
+#pragma unroll
+        for (int tp = 0; tp < 8; tp++) vx[tp] = b.v[tp] ^ 0x88888888u;      // offset binary
 #pragma unroll
         for (int qb = 0; qb < 4; qb++) {
             const uint32_t sel = (uint32_t)qb | (0x0cu << 8) | ((uint32_t)(4 + qb) << 16) | (0x0cu << 24);
             uint32_t lo[4], hi[4];
 #pragma unroll
             for (int k = 0; k < 4; k++) {
-                const uint32_t w = __builtin_amdgcn_perm(b.v[k + 4], b.v[k], sel) ^ 0x00880088u;
+                const uint32_t w = __builtin_amdgcn_perm(vx[k + 4], vx[k], sel);
                 lo[k] = nib2_h2(w, magic);
                 hi[k] = nib2_h2(w >> 4, magic);
             }
