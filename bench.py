@@ -107,7 +107,7 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
         "dequantize_mxfp4": ("kvq::dequantize_kernel<128, 32, true, 4, true, false>", nv * (2 * D + D // 2 + D // 32)),
         "quantize_srft": ("kvq::quantize_kernel<128, 32, true, 4, false, true>", nv * bytes_per_vector(D, G)),
         "dequantize_srft": ("kvq::dequantize_kernel<128, 32, true, 4, false, true>", nv * bytes_per_vector(D, G)),
-        "attend_partial": ("kvq::attend_partial_kernel<128, 4, false>", att),
+        "attend_partial": ("kvq::attend_partial_mfma_kernel", att),
         "attend_combine": ("kvq::attend_combine_kernel<128>", None),
         "vq_encode": ("kvq::vq_encode_kernel<128, false>", nk * (2 * D + 2 * (D // 8))),
         "vq_decode": ("kvq::vq_decode_lds_kernel<128, false>", nk * (2 * D + 2 * (D // 8))),

@@ -178,3 +178,32 @@ def test_qwen3_8b_decode_step_full_size_sampled():
                                      s.cpu().numpy(), cfg.G, 1.0 / cfg.D ** 0.5)
         compare(out[o:o + 1, h * R:(h + 1) * R], out64, lv[o:o + 1, h:h + 1], 1, R,
                 "qwen3-8b decode step (outer %d, head %d)" % (o, h))
+
+
+@pytest.mark.parametrize("stride_mb", [60, 70])
+def test_attend_huge_token_stride(stride_mb):
+    """K codes stored with a token stride of tens of MB: 60 MB keeps 32 token
+    rows under 2^31 bytes (matrix-core kernel, 32-bit per-lane offsets near
+    their limit); 70 MB goes past it, and the host must pick the VALU kernel.
+    Both agree with the oracle."""
+    dev = device()
+    L, T, H, R, D, G = 1, 40, 1, 4, 128, 32
+    c = make_cache(L, T, H, D, G, 60 + stride_mb, dev)
+    kc, ks, lk = c["k"]
+    vc, vs, lv = c["v"]
+    st = stride_mb << 20
+    buf = torch.zeros(T * st, dtype=torch.uint8, device=dev)
+    big = buf.as_strided((L, T, H, D // 2), (T * st, st, D // 2, 1))
+    big.copy_(kc)
+    g = torch.Generator(device="cpu").manual_seed(stride_mb)
+    q = torch.randn((L, H * R, D), generator=g).to(torch.float16).to(dev)
+    out = kvq.attend_decode(q, big, ks, vc, vs, lk, lv, c["s"], G)
+    ref = kvq.attend_decode(q, kc, ks, vc, vs, lk, lv, c["s"], G)
+    torch.cuda.synchronize()
+    out64 = oracle.attend_decode(bits(q), kc.cpu().numpy(), bits(ks), vc.cpu().numpy(), bits(vs),
+                                 lk.cpu().numpy(), lv.cpu().numpy(), c["s"].cpu().numpy(), G, 1.0 / D ** 0.5)
+    compare(out, out64, lv, H, R, "huge token stride %d MB" % stride_mb)
+    if stride_mb == 60:
+        assert torch.equal(out, ref)        # same kernel, same arithmetic
+    del buf, big
+    torch.cuda.empty_cache()
