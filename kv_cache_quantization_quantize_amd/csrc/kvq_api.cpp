@@ -246,9 +246,50 @@ AttnPlan attn_plan(const kvq_shape& s, int32_t R)
     return p;
 }
 
-int64_t attn_workspace_bytes(const kvq_shape& s, int32_t R, const AttnPlan& p)
+// Plan of the matrix-core kernel (head_dim 128, group 32).  A block is one
+// (outer index, split) and a group of hb KV heads, hb the largest of 8, 4, 2,
+// 1 that divides H; its eight wavefronts are the hb heads times 8 / hb
+// consecutive sub-ranges of the split.  The heads of a group read
+// interleaved rows of the same 128-byte lines (two heads' codes, all heads'
+// scales), so one block reads each line once.  One block fills a CU; the
+// splits give about eight blocks per CU, with at least four 32-token steps
+// per wavefront.  parts = splits x sub-ranges, one partial per wavefront.
+struct MfmaPlan {
+    int32_t hb, S, chunk, parts;
+};
+
+MfmaPlan attn_plan_mfma(const kvq_shape& s, int32_t R)
 {
-    return s.layers * s.heads * (int64_t)R * p.parts * (s.head_dim + 4) * (int64_t)sizeof(float);
+    MfmaPlan p;
+    p.hb = s.heads % 8 == 0 ? 8 : (s.heads % 4 == 0 ? 4 : (s.heads % 2 == 0 ? 2 : 1));
+    const int64_t nsub = kvq::kAttnMfmaWaves / p.hb;
+    const int64_t step = nsub * 32;                        // tokens per block step
+    const int64_t passes = (R + 3) / 4;
+    const int64_t base = std::max<int64_t>(1, s.layers * (s.heads / p.hb) * passes);
+    const int64_t target = 8LL * device_cus();
+    int64_t S = (target + base - 1) / base;
+    S = std::min<int64_t>(S, std::max<int64_t>(1, (s.tokens + 4 * step - 1) / (4 * step)));
+    int64_t chunk = std::max<int64_t>(1, (s.tokens + S - 1) / S);
+    chunk = (chunk + step - 1) / step * step;
+    S = std::max<int64_t>(1, (s.tokens + chunk - 1) / chunk);
+    p.S = (int32_t)S;
+    p.chunk = (int32_t)chunk;
+    p.parts = (int32_t)(S * nsub);
+    return p;
+}
+
+// Partial states per (outer index, query head) the workspace holds: enough
+// for whichever kernel the call picks.
+int64_t attn_parts_capacity(const kvq_shape& s, int32_t R)
+{
+    int64_t parts = attn_plan(s, R).parts;
+    if (s.head_dim == 128) parts = std::max<int64_t>(parts, attn_plan_mfma(s, R).parts);
+    return parts;
+}
+
+int64_t attn_workspace_bytes(const kvq_shape& s, int32_t R)
+{
+    return s.layers * s.heads * (int64_t)R * attn_parts_capacity(s, R) * (s.head_dim + 4) * (int64_t)sizeof(float);
 }
 
 kvq_status attn_check(const kvq_shape& shape, int32_t R)
@@ -525,7 +566,7 @@ kvq_status kvq_attend_decode_workspace(kvq_shape shape, int32_t q_per_kv, int64_
     *bytes = 0;
     KVQ_TRY(attn_check(shape, q_per_kv));
     if (shape.layers == 0 || shape.heads == 0) return KVQ_OK;
-    *bytes = attn_workspace_bytes(shape, q_per_kv, attn_plan(shape, q_per_kv));
+    *bytes = attn_workspace_bytes(shape, q_per_kv);
     return KVQ_OK;
 }
 
@@ -552,8 +593,7 @@ kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f1
         KVQ_TRY(check_view("v_codes_u8", v_codes_u8, 1, D / 2, 16, shape));
         KVQ_TRY(check_view("v_scales_f16", v_scales_f16, 2, D / group, 2, shape));
     }
-    const AttnPlan p = attn_plan(shape, q_per_kv);
-    const int64_t need = attn_workspace_bytes(shape, q_per_kv, p);
+    const int64_t need = attn_workspace_bytes(shape, q_per_kv);
     if (!workspace) return fail(KVQ_ERR_NULL, "workspace is NULL (%lld bytes needed)", (long long)need);
     if (!aligned(workspace, 16)) return fail(KVQ_ERR_ALIGN, "workspace must be 16-byte aligned");
     if (workspace_bytes < need)
@@ -566,11 +606,29 @@ kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f1
     a.R = q_per_kv;
     a.g_shift = 0;
     while ((1 << a.g_shift) < group) a.g_shift++;
-    a.rp = p.rp;
-    a.S = p.S;
-    a.chunk = p.chunk;
-    a.parts = p.parts;
-    a.xcd_map = ((int64_t)a.L * a.S) % 8 == 0;
+    // The matrix-core kernel serves head_dim 128 with groups of 32, where 32
+    // token rows of every view span less than 2^31 bytes (it addresses a
+    // step's loads with 32-bit offsets); the VALU kernel serves the rest.
+    const int64_t row = std::max(std::max(k_codes_u8.stride_token, v_codes_u8.stride_token),
+                                 2 * std::max(k_scales_f16.stride_token, v_scales_f16.stride_token));
+    a.mfma = D == 128 && group == 32 && 32 * row + 64 < ((int64_t)1 << 31);
+    if (a.mfma) {
+        const MfmaPlan p = attn_plan_mfma(shape, q_per_kv);
+        a.rp = 4;
+        a.hb = p.hb;
+        a.S = p.S;
+        a.chunk = p.chunk;
+        a.parts = p.parts;
+        a.xcd_map = 0;
+    } else {
+        const AttnPlan p = attn_plan(shape, q_per_kv);
+        a.rp = p.rp;
+        a.hb = 1;
+        a.S = p.S;
+        a.chunk = p.chunk;
+        a.parts = p.parts;
+        a.xcd_map = ((int64_t)a.L * a.S) % 8 == 0;
+    }
     a.q = static_cast<const _Float16*>(q_f16);
     a.out = static_cast<_Float16*>(out_f16);
     a.kc = t4(k_codes_u8);

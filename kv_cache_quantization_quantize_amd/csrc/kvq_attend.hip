@@ -468,43 +468,44 @@ __device__ __forceinline__ void rotate_queries(const AttnArgs& a, int l, int h, 
     }
 }
 
-__global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(AttnArgs a)
+__global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kernel(AttnArgs a)
 {
-    constexpr int D = 128, RP = 4, STEP = 32, TS = 1024 / D;
+    constexpr int D = 128, RP = 4, STEP = 32, W = kAttnMfmaWaves;
     const int lane = threadIdx.x & 63;
     const int wid = uniform(threadIdx.x >> 6);
-    int l, h, split;
+    // Block -> (outer index l, head group, split); wavefront -> (head of the
+    // group, sub-range of the split).  The heads of a group read interleaved
+    // rows of the same cache lines ([T, H, D/2] codes, [T, H, D/G] scales),
+    // and its wavefronts walk the same tokens together, so each line is
+    // fetched once.
+    const int hb = a.hb, nsub = W / hb;
+    int l, h, split, sub;
     {
-        const int b = blockIdx.x;
-        int u;
-        if (a.xcd_map) {
-            const int k = b >> 3;
-            u = ((k / a.H) << 3) + (b & 7);
-            h = k - (k / a.H) * a.H;
-        } else {
-            u = b / a.H;
-            h = b - u * a.H;
-        }
-        l = uniform(u / a.S);
-        split = u - l * a.S;
-        h = uniform(h);
+        int b = blockIdx.x;
+        split = b % a.S;
+        b /= a.S;
+        const int ng = a.H / hb;
+        l = uniform(b / ng);
+        h = uniform((b - l * ng) * hb + (wid & (hb - 1)));
+        split = uniform(split);
+        sub = uniform(wid / hb);
     }
     const int lh = l * a.H + h;
-    const int r0 = blockIdx.y * a.rp;
+    const int r0 = blockIdx.y * RP;
     const int n = a.lengths ? min(max(a.lengths[l], 0), a.T) : a.T;
 
-    __shared__ float qt[RP][D];
-    if (wid == 0) rotate_queries<D, RP>(a, l, h, r0, lane, qt);
-    __syncthreads();
+    __shared__ float qt[W][RP][D];
+    rotate_queries<D, RP>(a, l, h, r0, lane, qt[wid]);
+    __builtin_amdgcn_wave_barrier();
 
     const int j16 = lane & 15;   // MFMA row (A) / column (B, result)
     const int sl = lane >> 4;    // MFMA k-slice; result row block
 
-    // score B operands, [hi/lo][MFMA m][lane]: column (g, r) = 4g + r, slice
-    // sl = group sl.  The same for every wavefront; kept in LDS and read at
-    // each use rather than held in 32 VGPRs.
-    __shared__ uint4 bqL[2][4][64];
-    if (wid == 0) {
+    // score B operands of the wavefront's head, [hi/lo][MFMA m][lane]: column
+    // (g, r) = 4g + r, slice sl = group sl.  Kept in LDS and read at each use
+    // rather than held in 32 VGPRs.
+    __shared__ uint4 bqL[W][2][4][64];
+    {
         const int r = j16 & 3, g = j16 >> 2;
         const bool on = g == sl;
 #pragma unroll
@@ -512,27 +513,27 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int k = 0; k < 4; k++) {
-                const float v0 = on ? qt[r][32 * sl + 8 * m + kPermK[2 * k]] : 0.0f;
-                const float v1 = on ? qt[r][32 * sl + 8 * m + kPermK[2 * k + 1]] : 0.0f;
+                const float v0 = on ? qt[wid][r][32 * sl + 8 * m + kPermK[2 * k]] : 0.0f;
+                const float v1 = on ? qt[wid][r][32 * sl + 8 * m + kPermK[2 * k + 1]] : 0.0f;
                 const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
                 hw[k] = __builtin_bit_cast(uint32_t, h2_t{h0, h1});
                 lw[k] = pack_h2(v0 - (float)h0, v1 - (float)h1);
             }
-            bqL[0][m][lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            bqL[1][m][lane] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            bqL[wid][0][m][lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            bqL[wid][1][m][lane] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
 
     // wave-private exchange tiles
-    __shared__ _Float16 ksT[kAttnWaves][4][STEP], vsT[kAttnWaves][4][STEP];
-    __shared__ float pL[kAttnWaves][RP][STEP];
-    __shared__ float aL[kAttnWaves][RP];
+    __shared__ _Float16 ksT[W][4][STEP], vsT[W][4][STEP];
+    __shared__ float pL[W][RP][STEP];
+    __shared__ float aL[W][RP];
 
     const int cb = split * a.chunk;
     const int ce = min(cb + a.chunk, n);
-    const int per_wave = ((a.chunk + kAttnWaves * STEP - 1) / (kAttnWaves * STEP)) * STEP;
-    const int wb = cb + wid * per_wave;
+    const int per_wave = ((a.chunk + nsub * STEP - 1) / (nsub * STEP)) * STEP;
+    const int wb = cb + sub * per_wave;
     const int we = min(wb + per_wave, ce);
     const int nsteps = we > wb ? (we - wb + STEP - 1) / STEP : 0;
 
@@ -612,8 +613,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
 #pragma unroll
             for (int m = 0; m < 4; m++) {
                 const h8_t am = codes8(kw[m], magic);
-                const h8_t bh = __builtin_bit_cast(h8_t, bqL[0][m][lane]);
-                const h8_t bl = __builtin_bit_cast(h8_t, bqL[1][m][lane]);
+                const h8_t bh = __builtin_bit_cast(h8_t, bqL[wid][0][m][lane]);
+                const h8_t bl = __builtin_bit_cast(h8_t, bqL[wid][1][m][lane]);
                 c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bh, c[tau], 0, 0, 0);
                 c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bl, c[tau], 0, 0, 0);
             }
@@ -733,22 +734,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_mfma_kernel(At
         }
     }
 
-    // ---- partials: the wave's state in slot 0, empty headers in the others --
+    // ---- partial: one per wavefront ------------------------------------------
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-    const int part0 = (split * kAttnWaves + wid) * TS;
-    const int nr = min(a.rp, a.R - r0);
+    const int part0 = split * nsub + sub;
+    const int nr = min(RP, a.R - r0);
     {
         const int r = j16 & 3, g = j16 >> 2;
         if (g == 0 && sl == 0 && r < nr) {
             float* P = a.ws + ((((int64_t)lh * a.R + r0 + r) * a.parts) + part0) * (D + 4);
             *reinterpret_cast<float2*>(P) = make_float2(m_run, l_run);
-        }
-        if (lane >= 1 && lane < TS) {
-            for (int rr = 0; rr < nr; rr++) {
-                float* P = a.ws + ((((int64_t)lh * a.R + r0 + rr) * a.parts) + part0 + lane) * (D + 4);
-                *reinterpret_cast<float2*>(P) = make_float2(-__builtin_inff(), 0.0f);
-            }
         }
     }
     // result rows 4 sl + v = (group sl, query v); column j16 of tile mt is
@@ -841,10 +836,9 @@ hipError_t launch_part(const AttnArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)((int64_t)a.L * a.H * a.S), (unsigned)((a.R + RP - 1) / RP));
     if constexpr (D == 128) {
-        // the matrix-core kernel addresses 32 token rows with 32-bit offsets
-        const int64_t row = std::max(std::max(a.kc.st, a.vc.st), 2 * std::max(a.ks.st, a.vs.st));
-        if (a.g_shift == 5 && 32 * row + 64 < ((int64_t)1 << 31)) {
-            hipLaunchKernelGGL(attend_partial_mfma_kernel, grid, dim3(64 * kAttnWaves), 0, s, a);
+        if (a.mfma) {
+            const dim3 mgrid((unsigned)((int64_t)a.L * (a.H / a.hb) * a.S), (unsigned)((a.R + 3) / 4));
+            hipLaunchKernelGGL(attend_partial_mfma_kernel, mgrid, dim3(64 * kAttnMfmaWaves), 0, s, a);
             return hipGetLastError();
         }
     }

@@ -78,6 +78,8 @@ struct AttnArgs {
     int32_t chunk;                  // tokens per split
     int32_t parts;                  // partial states per (outer index, query head)
     int32_t xcd_map;                // (L*S) % 8 == 0: heads of one (l, split) on one XCD
+    int32_t mfma;                   // use the matrix-core kernel (D 128, group 32)
+    int32_t hb;                     // matrix-core kernel: KV heads per block
     const _Float16* q;              // [L, H*R, D]
     _Float16* out;                  // [L, H*R, D]
     Tensor4 kc, ks, vc, vs;         // codes u8 (D/2), scales fp16 (D/G)
@@ -89,6 +91,7 @@ struct AttnArgs {
     float* ws;                      // partials: [L*H][R][parts][D + 4] floats
 };
 constexpr int kAttnWaves = 4;       // wavefronts per attention block
+constexpr int kAttnMfmaWaves = 8;   // wavefronts per matrix-core attention block
 
 // Centroids staged in LDS at a time by the VQ encoder (64 KB of fp16).
 constexpr int kVqChunk = 4096;
