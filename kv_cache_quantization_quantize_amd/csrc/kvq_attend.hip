@@ -360,12 +360,22 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
 // ---------------------------------------------------------------------------
 // Matrix-core partial kernel: head_dim 128, group 32
 // ---------------------------------------------------------------------------
-// Same block decomposition, query rotation, log2-domain online softmax and
-// partial format as attend_partial_kernel, with both contractions on
+// Same query rotation, log2-domain online softmax and partial format as
+// attend_partial_kernel, with both contractions on
 // v_mfma_f32_16x16x32_f16 (A 16x32, B 32x16, fp32 accumulate; lane l holds
 // A row l%16 / B column l%16 and k-slice l/16, eight k per slice; the result
-// holds rows 4*(l/16)..+3 of column l%16).  A wavefront takes 32 tokens per
-// step.
+// holds rows 4*(l/16)..+3 of column l%16).  A block is eight wavefronts: the
+// KV heads of a head group times sub-ranges of one token split, so the heads
+// that share cache lines read them together.  A wavefront takes 32 tokens
+// per step and writes one partial.
+//
+// Codes enter both contractions as fp16 72 + c: one v_and_or_b32 puts two
+// offset-binary nibbles (c + 8) into the mantissas of 64.0 (bits 4-7 of each
+// half), and the constant part is removed from the results: 72 times the
+// group sum of the query from each score, 72 times the running sum of the
+// weight operand from each value row.  The biased operands are exact in fp16
+// and the constant is small next to the codes, so the results stay fp32
+// accurate.
 //
 // Scores.  Rows are 16 tokens; columns are (group g, query r) = 4g + r; the
 // k-slice of lane row-slice sl is group sl, so B column (g, r) is the rotated
@@ -373,7 +383,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
 // the per-group partial dot products, which the group scales then weight
 // (scaled by columns, summed over g with two row rotations).  The query is
 // split into fp16 hi + lo halves (two MFMAs), so the dot products are fp32
-// accurate; the codes (integers -7..7) are exact in fp16.  A lane's 16 code
+// accurate.  A lane's 16 code
 // bytes of group sl feed four MFMAs, one dword each.
 //
 // Values.  Rows are (group g', query r) = 4g' + r, k is the 32 tokens, and
@@ -395,25 +405,22 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPermK[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 
-// fp16 of (n - 8) for two offset-binary nibbles n held in bits 0-3 and 16-19:
-// one v_and_or_b32 builds the fp16 patterns of 1024 + n (magic = 0x64006400
-// held in a VGPR, the mask in an SGPR: one constant-bus read), one packed
-// fp16 add subtracts 1032 exactly.
-__device__ __forceinline__ uint32_t nib2_h2(uint32_t x, uint32_t magic)
+// fp16 of 64 + n for two offset-binary nibbles n held in bits 4-7 and 20-23:
+// one v_and_or_b32 (magic = 0x54005400, fp16 64 in both halves, in a VGPR).
+__device__ __forceinline__ uint32_t nib2_b64(uint32_t x, uint32_t magic)
 {
     uint32_t b;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(b) : "v"(x), "s"(0x000F000Fu), "v"(magic));
-    const h2_t r = __builtin_bit_cast(h2_t, b) + h2_t{(_Float16)-1032.0f, (_Float16)-1032.0f};
-    return __builtin_bit_cast(uint32_t, r);
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(b) : "v"(x), "s"(0x00F000F0u), "v"(magic));
+    return b;
 }
 
-// Eight two's-complement codes of a dword (nibble e = element e) as an fp16
-// operand in the order (0,4,1,5,2,6,3,7).
-__device__ __forceinline__ h8_t codes8(uint32_t w, uint32_t magic)
+// Eight two's-complement codes c of a dword as fp16 72 + c (nibble e =
+// element e), in the order (0,4,1,5,2,6,3,7).
+__device__ __forceinline__ h8_t codes8_b72(uint32_t w, uint32_t magic)
 {
     const uint32_t x = w ^ 0x88888888u;
-    const uint4 o = make_uint4(nib2_h2(x, magic), nib2_h2(x >> 4, magic), nib2_h2(x >> 8, magic),
-                               nib2_h2(x >> 12, magic));
+    const uint4 o = make_uint4(nib2_b64(x << 4, magic), nib2_b64(x, magic), nib2_b64(x >> 4, magic),
+                               nib2_b64(x >> 8, magic));
     return __builtin_bit_cast(h8_t, o);
 }
 
@@ -525,6 +532,17 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     }
     __builtin_amdgcn_wave_barrier();
 
+    // The codes enter the MFMAs as 72 + c: the score column (g, r) carries
+    // 72 times the sum of query r over group g, removed before scaling.
+    float kb;
+    {
+        const int r = j16 & 3, g = j16 >> 2;
+        float sq = 0.0f;
+#pragma unroll 8
+        for (int c = 0; c < 32; c++) sq += qt[wid][r][32 * g + c];
+        kb = 72.0f * sq;
+    }
+
     // wave-private exchange tiles
     __shared__ _Float16 ksT[W][4][STEP], vsT[W][4][STEP];
     __shared__ float pL[W][RP][STEP];
@@ -586,10 +604,11 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
         b.vs = *reinterpret_cast<const u32_a2*>(vsb + off.vs);
     };
 
-    uint32_t magic = 0x64006400u;      // fp16 1024 in both halves, kept in a VGPR
+    uint32_t magic = 0x54005400u;      // fp16 64 in both halves, kept in a VGPR
     asm volatile("" : "+v"(magic));
     float m_run = -__builtin_inff();   // running max of query j16 & 3 (log2 domain)
     float l_run = 0.0f;                // this lane's share of the weight sum
+    float vb = 0.0f;                   // sum of the lane's value-operand entries
     f4_t acc[8];
 #pragma unroll
     for (int mt = 0; mt < 8; mt++) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -612,7 +631,7 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             const uint32_t kw[4] = {b.k[tau].x, b.k[tau].y, b.k[tau].z, b.k[tau].w};
 #pragma unroll
             for (int m = 0; m < 4; m++) {
-                const h8_t am = codes8(kw[m], magic);
+                const h8_t am = codes8_b72(kw[m], magic);
                 const h8_t bh = __builtin_bit_cast(h8_t, bqL[wid][0][m][lane]);
                 const h8_t bl = __builtin_bit_cast(h8_t, bqL[wid][1][m][lane]);
                 c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bh, c[tau], 0, 0, 0);
@@ -630,7 +649,7 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             const float kv[4] = {lo_half(kq.x), hi_half(kq.x), lo_half(kq.y), hi_half(kq.y)};
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                float x = c[tau][v] * kv[v];
+                float x = (c[tau][v] - kb) * kv[v];
                 x += dpp_mov<0x124>(x);            // row_ror:4
                 x += dpp_mov<0x128>(x);            // row_ror:8
                 const bool valid = tb + 16 * tau + 4 * sl + v < we;
@@ -651,6 +670,7 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             l_run *= alpha;
             if (g == 0 && sl == 0) aL[wid][r] = alpha;
             __builtin_amdgcn_wave_barrier();
+            vb *= aL[wid][r];
             // result rows 4 sl + v are queries v
             const float4 al = *reinterpret_cast<const float4*>(&aL[wid][0]);
             const float av[4] = {al.x, al.y, al.z, al.w};
@@ -689,6 +709,7 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
 #pragma unroll
             for (int k = 0; k < 4; k++) {
                 const float x0 = pp[k] * vv[k], x1 = pp[k + 4] * vv[k + 4];
+                vb += x0 + x1;
                 const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
                 hw[k] = __builtin_bit_cast(uint32_t, h2_t{h0, h1});
                 lw[k] = pack_h2(x0 - (float)h0, x1 - (float)h1);
@@ -707,8 +728,8 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
 #pragma unroll
             for (int k = 0; k < 4; k++) {
                 const uint32_t w = __builtin_amdgcn_perm(vx[k + 4], vx[k], sel);
-                lo[k] = nib2_h2(w, magic);
-                hi[k] = nib2_h2(w >> 4, magic);
+                lo[k] = nib2_b64(w << 4, magic);
+                hi[k] = nib2_b64(w, magic);
             }
             const h8_t bl = __builtin_bit_cast(h8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
             const h8_t bh = __builtin_bit_cast(h8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
@@ -748,6 +769,16 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     }
     // result rows 4 sl + v = (group sl, query v); column j16 of tile mt is
     // coordinate 8 j16 + mt, which belongs to group j16 / 4
+    // value codes entered as 72 + c: remove 72 times row (g, v)'s operand sum
+    vb += __shfl_xor(vb, 16);
+    vb += __shfl_xor(vb, 32);
+    float vbias[RP];
+#pragma unroll
+    for (int v = 0; v < RP; v++) vbias[v] = 72.0f * __shfl(vb, 4 * sl + v);
+#pragma unroll
+    for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+        for (int v = 0; v < RP; v++) acc[mt][v] -= vbias[v];
     if (sl == (j16 >> 2)) {
 #pragma unroll
         for (int v = 0; v < RP; v++) {
