@@ -19,9 +19,10 @@
 // tile by a 32x32x8 MFMA and shared by every group of sub-vectors.  Each lane then holds the
 // scores of 16 centroids for one sub-vector: a max3 tree gives the tile
 // maximum, and only the best tile is tracked (strict >, so the earliest tile
-// wins ties).  After a sweep, the lanes that improved re-score the 16
-// candidates of their best tile on VALU to find the position (first maximum,
-// so the lowest index wins), and the two lanes that share a sub-vector (rows
+// wins ties; with one-byte indices, the best quarter of a tile).  After a
+// sweep, the lanes that improved re-score the 16 (4) candidates of their best
+// tile (quarter) on VALU to find the position (first maximum, so the lowest
+// index wins), and the two lanes that share a sub-vector (rows
 // 0-3,8-11,.. and 4-7,12-15,..) merge (value, index) lexicographically.
 //
 // The codebook (<= 4096 centroids at a time, 64 KB) and its norms live in
@@ -82,6 +83,14 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
     // one-byte indices imply at most 256 centroids: a small codebook area
     // lets two blocks share a CU
     constexpr int CHUNK = IDX8 ? 256 : kVqChunk;
+    // Best-score tracking granularity: sub-blocks of 16 / NSUB of a lane's 16
+    // tile scores.  A 256-centroid codebook is eight tiles, so re-scoring all
+    // 16 candidates of the best tile would cost more than the sweep; tracking
+    // the best 4-score sub-block costs about ten more VALU operations per tile
+    // and leaves four candidates (1.45 -> 0.96 ms for 2.4 M keys; sub-blocks
+    // of 8 or 2 scores, or single scores, were slower).
+    constexpr int NSUB = IDX8 ? 4 : 1, SUBW = 16 / NSUB;
+    constexpr int EPI_OPS = NSUB == 1 ? 10 : 20;           // VALU operations per group and tile
     __shared__ uint4 cb_lds[CHUNK];                    // centroid k: 8 fp16
     __shared__ uint32_t nrm_lds[CHUNK];                // packed (n_hi, n_lo)
     __shared__ uint4 stage[WAVES][2][16 * NS];         // [wave][hi/lo][key, sub-vector]
@@ -243,13 +252,26 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
                 auto epilogue = [&](const f32x16_t (&acc)[GPR], int tl) {
 #pragma unroll
                     for (int gg = 0; gg < GPR; gg++) {
-                        float mx = fmaxf(fmaxf(acc[gg][0], acc[gg][1]), acc[gg][2]);
+                        if constexpr (NSUB == 1) {
+                            float mx = fmaxf(fmaxf(acc[gg][0], acc[gg][1]), acc[gg][2]);
 #pragma unroll
-                        for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[gg][r]), acc[gg][r + 1]);
-                        mx = fmaxf(mx, acc[gg][15]);
-                        if (mx > best_val[gg]) {
-                            best_val[gg] = mx;
-                            best_tile[gg] = tl;
+                            for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[gg][r]), acc[gg][r + 1]);
+                            mx = fmaxf(mx, acc[gg][15]);
+                            if (mx > best_val[gg]) {
+                                best_val[gg] = mx;
+                                best_tile[gg] = tl;
+                            }
+                        } else {
+#pragma unroll
+                            for (int sb = 0; sb < NSUB; sb++) {
+                                float mx = acc[gg][SUBW * sb];
+#pragma unroll
+                                for (int r = 1; r < SUBW; r++) mx = fmaxf(mx, acc[gg][SUBW * sb + r]);
+                                if (mx > best_val[gg]) {
+                                    best_val[gg] = mx;
+                                    best_tile[gg] = tl * NSUB + sb;
+                                }
+                            }
                         }
                     }
                 };
@@ -259,11 +281,11 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
                 auto interleave = [&]() {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // norm MFMA
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // operand reads
-                    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, EPI_OPS, 0);
 #pragma unroll
                     for (int gg = 0; gg < GPR; gg++) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, EPI_OPS, 0);
                     }
                 };
                 f32x16_t acc0[GPR], acc1[GPR];
@@ -302,10 +324,12 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
                         }
                         float bs = -__builtin_inff();
                         int bk = 0;
+                        const int bt = best_tile[gg] / NSUB, r0 = SUBW * (best_tile[gg] % NSUB);
 #pragma unroll
-                        for (int r = 0; r < 16; r++) {
+                        for (int rr = 0; rr < SUBW; rr++) {
+                            const int r = r0 + rr;
                             const int row = 8 * (r / 4) + 4 * half + (r % 4);
-                            const int k = best_tile[gg] * 32 + row;
+                            const int k = bt * 32 + row;
                             const uint4 cv = cb_lds[k];
                             const uint32_t nw = nrm_lds[k];
                             const uint32_t w[4] = {cv.x, cv.y, cv.z, cv.w};
