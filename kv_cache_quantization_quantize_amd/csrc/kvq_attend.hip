@@ -377,11 +377,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
 // and the constant is small next to the codes, so the results stay fp32
 // accurate.
 //
-// Scores.  Rows are 16 tokens; columns are (group g, query r) = 4g + r; the
+// Scores.  Rows are 16 tokens; columns are (group g, query r) = 4r + g; the
 // k-slice of lane row-slice sl is group sl, so B column (g, r) is the rotated
 // query r restricted to group g (zero on the other slices) and the result is
-// the per-group partial dot products, which the group scales then weight
-// (scaled by columns, summed over g with two row rotations).  The query is
+// the per-group partial dot products, which the group scales then weight and
+// a reduce-scatter over the quad of a query's four groups sums, leaving one
+// token's score per lane for the softmax.  The query is
 // split into fp16 hi + lo halves (two MFMAs), so the dot products are fp32
 // accurate.  A lane's 16 code
 // bytes of group sl feed four MFMAs, one dword each.
@@ -509,11 +510,11 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     const int sl = lane >> 4;    // MFMA k-slice; result row block
 
     // score B operands of the wavefront's head, [hi/lo][MFMA m][lane]: column
-    // (g, r) = 4g + r, slice sl = group sl.  Kept in LDS and read at each use
+    // (g, r) = 4r + g, slice sl = group sl.  Kept in LDS and read at each use
     // rather than held in 32 VGPRs.
     __shared__ uint4 bqL[W][2][4][64];
     {
-        const int r = j16 & 3, g = j16 >> 2;
+        const int r = j16 >> 2, g = j16 & 3;
         const bool on = g == sl;
 #pragma unroll
         for (int m = 0; m < 4; m++) {
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     // 72 times the sum of query r over group g, removed before scaling.
     float kb;
     {
-        const int r = j16 & 3, g = j16 >> 2;
+        const int r = j16 >> 2, g = j16 & 3;
         float sq = 0.0f;
 #pragma unroll 8
         for (int c = 0; c < 32; c++) sq += qt[wid][r][32 * g + c];
@@ -639,24 +640,33 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             }
         }
         __builtin_amdgcn_wave_barrier();
-        // weight by the group scales, sum over the 4 groups (columns 4g + r)
-        const int g = j16 >> 2, r = j16 & 3;
-        float sc[2][4];
+        // Weight by the group scales and sum over the 4 groups, which are the
+        // four lanes of a quad (columns 4r + g): a reduce-scatter leaves lane
+        // g with the score of token 4 sl + g, so each lane carries on with
+        // one score per 16 tokens.
+        const int gS = j16 & 3, rS = j16 >> 2;     // score column: group, query
+        const int g = j16 >> 2, r = j16 & 3;       // value-operand row: group, query
+        const bool h1 = (gS & 1) != 0, h2 = (gS & 2) != 0;
+        float sc[2];
         float smax = -__builtin_inff();
 #pragma unroll
         for (int tau = 0; tau < 2; tau++) {
-            const uint2 kq = *reinterpret_cast<const uint2*>(&ksT[wid][g][16 * tau + 4 * sl]);
+            const uint2 kq = *reinterpret_cast<const uint2*>(&ksT[wid][gS][16 * tau + 4 * sl]);
             const float kv[4] = {lo_half(kq.x), hi_half(kq.x), lo_half(kq.y), hi_half(kq.y)};
+            float x[4];
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                float x = (c[tau][v] - kb) * kv[v];
-                x += dpp_mov<0x124>(x);            // row_ror:4
-                x += dpp_mov<0x128>(x);            // row_ror:8
-                const bool valid = tb + 16 * tau + 4 * sl + v < we;
-                sc[tau][v] = valid ? x : -__builtin_inff();
-                smax = fmaxf(smax, sc[tau][v]);
-            }
+            for (int v = 0; v < 4; v++) x[v] = (c[tau][v] - kb) * kv[v];
+            // keep tokens 2 (g >> 1) + {0, 1}, add the partner's (lane g ^ 2)
+            const float y0 = (h2 ? x[2] : x[0]) + dpp_mov<kDppXor2>(h2 ? x[0] : x[2]);
+            const float y1 = (h2 ? x[3] : x[1]) + dpp_mov<kDppXor2>(h2 ? x[1] : x[3]);
+            // keep token g, add lane g ^ 1's
+            const float sv = (h1 ? y1 : y0) + dpp_mov<kDppXor1>(h1 ? y0 : y1);
+            const bool valid = tb + 16 * tau + 4 * sl + gS < we;
+            sc[tau] = valid ? sv : -__builtin_inff();
+            smax = fmaxf(smax, sc[tau]);
         }
+        smax = fmaxf(smax, dpp_mov<kDppXor1>(smax));
+        smax = fmaxf(smax, dpp_mov<kDppXor2>(smax));
         smax = fmaxf(smax, __shfl_xor(smax, 16));
         smax = fmaxf(smax, __shfl_xor(smax, 32));
         // The weights are taken relative to a reference max that moves only
@@ -668,7 +678,7 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
-            if (g == 0 && sl == 0) aL[wid][r] = alpha;
+            if (gS == 0 && sl == 0) aL[wid][rS] = alpha;
             __builtin_amdgcn_wave_barrier();
             vb *= aL[wid][r];
             // result rows 4 sl + v are queries v
@@ -679,21 +689,11 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
 #pragma unroll
                 for (int v = 0; v < 4; v++) acc[mt][v] *= av[v];
         }
-        float psum = 0.0f;
-        float pv[2][4];
 #pragma unroll
-        for (int tau = 0; tau < 2; tau++)
-#pragma unroll
-            for (int v = 0; v < 4; v++) {
-                pv[tau][v] = (sc[tau][v] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(sc[tau][v] - m_run);
-                psum += pv[tau][v];
-            }
-        l_run += psum;
-        if (g == 0) {
-#pragma unroll
-            for (int tau = 0; tau < 2; tau++)
-                *reinterpret_cast<float4*>(&pL[wid][r][16 * tau + 4 * sl]) =
-                    make_float4(pv[tau][0], pv[tau][1], pv[tau][2], pv[tau][3]);
+        for (int tau = 0; tau < 2; tau++) {
+            const float pv = (sc[tau] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(sc[tau] - m_run);
+            l_run += pv;
+            pL[wid][rS][16 * tau + 4 * sl + gS] = pv;
         }
         __builtin_amdgcn_wave_barrier();
         // value operands: A row (g', r') = (j16 >> 2, j16 & 3), tokens 8 sl + (0,4,1,5,...)
@@ -756,14 +756,16 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     }
 
     // ---- partial: one per wavefront ------------------------------------------
+    l_run += dpp_mov<kDppXor1>(l_run);
+    l_run += dpp_mov<kDppXor2>(l_run);
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
     const int part0 = split * nsub + sub;
     const int nr = min(RP, a.R - r0);
     {
-        const int r = j16 & 3, g = j16 >> 2;
-        if (g == 0 && sl == 0 && r < nr) {
-            float* P = a.ws + ((((int64_t)lh * a.R + r0 + r) * a.parts) + part0) * (D + 4);
+        const int rS = j16 >> 2, gS = j16 & 3;     // score-column lanes hold query rS's state
+        if (gS == 0 && sl == 0 && rS < nr) {
+            float* P = a.ws + ((((int64_t)lh * a.R + r0 + rS) * a.parts) + part0) * (D + 4);
             *reinterpret_cast<float2*>(P) = make_float2(m_run, l_run);
         }
     }
