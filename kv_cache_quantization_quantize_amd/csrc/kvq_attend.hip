@@ -562,8 +562,12 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     const uint16_t* vsg = static_cast<const uint16_t*>(a.vs.data) + (int64_t)l * a.vs.sl + (int64_t)h * a.vs.sh;
     typedef uint32_t u32_a2 __attribute__((aligned(2)));
 
-    struct Buf {
+    // Loads are split by what consumes them: the key codes of a step feed its
+    // score MFMAs one step before its values and scales are needed.
+    struct KBuf {
         uint4 k[2];       // token 16 tau + j16, group sl: 32 codes
+    };
+    struct VBuf {
         uint32_t v[8];    // token 8 sl + t', coordinates 8 j16 .. 8 j16 + 7
         uint32_t ks, vs;  // token lane / 2, groups 2 (lane & 1), +1
     };
@@ -573,15 +577,22 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     // clamped to its last token, so every load is in range.
     const uint32_t kst = (uint32_t)a.kc.st, vst = (uint32_t)a.vc.st;
     const uint32_t kss = 2u * (uint32_t)a.ks.st, vss = 2u * (uint32_t)a.vs.st;
-    struct Off {
-        uint32_t k[2], v[8], ks, vs;
+    struct OffK {
+        uint32_t k[2];
+    };
+    struct OffV {
+        uint32_t v[8], ks, vs;
     };
     // byte offsets of the lane's loads from the step's first token, for steps
     // whose last in-range token is `lim`
-    auto offsets = [&](int lim) {
-        Off o;
+    auto offsets_k = [&](int lim) {
+        OffK o;
 #pragma unroll
         for (int tau = 0; tau < 2; tau++) o.k[tau] = (uint32_t)min(16 * tau + j16, lim) * kst + 16u * sl;
+        return o;
+    };
+    auto offsets_v = [&](int lim) {
+        OffV o;
 #pragma unroll
         for (int tp = 0; tp < 8; tp++) o.v[tp] = (uint32_t)min(8 * sl + tp, lim) * vst + 4u * j16;
         const uint32_t ts = (uint32_t)min(lane >> 1, lim);
@@ -589,20 +600,27 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
         o.vs = ts * vss + 4u * (lane & 1);
         return o;
     };
-    Off off = offsets(STEP - 1);
-    auto load = [&](int step, Buf& b) {
+    // Each loader visits steps in increasing order, so its offsets switch to
+    // the clamped ones once, at the wave's last (partial) step.
+    OffK offk = offsets_k(STEP - 1);
+    OffV offv = offsets_v(STEP - 1);
+    auto load_k = [&](int step, KBuf& b) {
         const int tb = wb + step * STEP;
-        if (tb + STEP > we) off = offsets(we - 1 - tb);      // the wave's last, partial step
-        const uint8_t* kb = kcg + (int64_t)tb * a.kc.st;
-        const uint8_t* vb = vcg + (int64_t)tb * a.vc.st;
+        if (tb + STEP > we) offk = offsets_k(we - 1 - tb);
+        const uint8_t* kbase = kcg + (int64_t)tb * a.kc.st;
+#pragma unroll
+        for (int tau = 0; tau < 2; tau++) b.k[tau] = *reinterpret_cast<const uint4*>(kbase + offk.k[tau]);
+    };
+    auto load_v = [&](int step, VBuf& b) {
+        const int tb = wb + step * STEP;
+        if (tb + STEP > we) offv = offsets_v(we - 1 - tb);
+        const uint8_t* vbase = vcg + (int64_t)tb * a.vc.st;
         const uint8_t* ksb = reinterpret_cast<const uint8_t*>(ksg + (int64_t)tb * a.ks.st);
         const uint8_t* vsb = reinterpret_cast<const uint8_t*>(vsg + (int64_t)tb * a.vs.st);
 #pragma unroll
-        for (int tau = 0; tau < 2; tau++) b.k[tau] = *reinterpret_cast<const uint4*>(kb + off.k[tau]);
-#pragma unroll
-        for (int tp = 0; tp < 8; tp++) b.v[tp] = *reinterpret_cast<const uint32_t*>(vb + off.v[tp]);
-        b.ks = *reinterpret_cast<const u32_a2*>(ksb + off.ks);
-        b.vs = *reinterpret_cast<const u32_a2*>(vsb + off.vs);
+        for (int tp = 0; tp < 8; tp++) b.v[tp] = *reinterpret_cast<const uint32_t*>(vbase + offv.v[tp]);
+        b.ks = *reinterpret_cast<const u32_a2*>(ksb + offv.ks);
+        b.vs = *reinterpret_cast<const u32_a2*>(vsb + offv.vs);
     };
 
     uint32_t magic = 0x54005400u;      // fp16 64 in both halves, kept in a VGPR
@@ -614,18 +632,8 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
 #pragma unroll
     for (int mt = 0; mt < 8; mt++) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto compute = [&](int step, const Buf& b) {
-        const int tb = wb + step * STEP;
-        // scale tiles, transposed to [group][token]
-        {
-            const int tl = lane >> 1, g0 = 2 * (lane & 1);
-            ksT[wid][g0][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.ks & 0xffffu));
-            ksT[wid][g0 + 1][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.ks >> 16));
-            vsT[wid][g0][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.vs & 0xffffu));
-            vsT[wid][g0 + 1][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.vs >> 16));
-        }
-        // per-group partial scores of 2 x 16 tokens
-        f4_t c[2];
+    // per-group partial scores of a step's 2 x 16 tokens
+    auto scores = [&](const KBuf& b, f4_t (&c)[2]) {
 #pragma unroll
         for (int tau = 0; tau < 2; tau++) {
             c[tau] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -638,6 +646,18 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
                 c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bh, c[tau], 0, 0, 0);
                 c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bl, c[tau], 0, 0, 0);
             }
+        }
+    };
+    // softmax and value accumulation of a step, from its partial scores
+    auto finish = [&](int step, const VBuf& b, const f4_t (&c)[2]) {
+        const int tb = wb + step * STEP;
+        // scale tiles, transposed to [group][token]
+        {
+            const int tl = lane >> 1, g0 = 2 * (lane & 1);
+            ksT[wid][g0][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.ks & 0xffffu));
+            ksT[wid][g0 + 1][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.ks >> 16));
+            vsT[wid][g0][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.vs & 0xffffu));
+            vsT[wid][g0 + 1][tl] = __builtin_bit_cast(_Float16, (uint16_t)(b.vs >> 16));
         }
         __builtin_amdgcn_wave_barrier();
         // Weight by the group scales and sum over the 4 groups, which are the
@@ -741,16 +761,29 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
         __builtin_amdgcn_wave_barrier();
     };
 
-    // the next step's loads in flight while a step is computed
+    // Software pipeline: while step st is finished, the score MFMAs of step
+    // st + 1 run on the matrix cores, the key codes of steps st + 2 and st + 3
+    // and the values and scales of step st + 1 are in flight.  Steps past
+    // the last one repeat it (in range; their results are never used).
     if (nsteps > 0) {
-        Buf A, B;
-        load(0, A);
+        KBuf K0, K1;
+        VBuf V0, V1;
+        f4_t c0[2], c1[2];
+        load_k(0, K0);
+        load_v(0, V0);
+        load_k(min(1, nsteps - 1), K1);
+        scores(K0, c0);
+        load_k(min(2, nsteps - 1), K0);
         for (int st = 0;; st += 2) {
-            load(min(st + 1, nsteps - 1), B);
-            compute(st, A);
+            load_v(min(st + 1, nsteps - 1), V1);
+            scores(K1, c1);
+            load_k(min(st + 3, nsteps - 1), K1);
+            finish(st, V0, c0);
             if (st + 1 >= nsteps) break;
-            load(min(st + 2, nsteps - 1), A);
-            compute(st + 1, B);
+            load_v(min(st + 2, nsteps - 1), V0);
+            scores(K0, c0);
+            load_k(min(st + 4, nsteps - 1), K0);
+            finish(st + 1, V1, c1);
             if (st + 2 >= nsteps) break;
         }
     }
