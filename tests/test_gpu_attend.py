@@ -84,6 +84,13 @@ def test_attend_query_groups_over_passes(R):
     run_case(2, 257, 3, R, 128, 32, seed=40 + R)
 
 
+@pytest.mark.parametrize("H", [1, 4, 6, 8, 12, 16])
+def test_attend_head_groups(H):
+    # head_dim 128 / group 32 blocks hold hb = 8, 4, 2 or 1 KV heads (the
+    # largest dividing H) times 8 / hb token sub-ranges
+    run_case(2, 333, H, 4, 128, 32, seed=60 + H, lengths=[333, 97])
+
+
 def test_attend_ragged_lengths_and_empty():
     run_case(5, 200, 2, 4, 128, 32, seed=50, lengths=[200, 0, 1, 77, 13])
 
