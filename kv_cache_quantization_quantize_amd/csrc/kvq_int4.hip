@@ -257,6 +257,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
     // SRFT: one LDS row of D/2 complex points (+1 against bank conflicts) per quad
     __shared__ float2 lds_fft[FT ? kWavesPerBlock * 16 * (D / 2 + 1) : 1];
     float2* fft_row = lds_fft + (FT ? ((threadIdx.x >> 6) * 16 + slot) * (D / 2 + 1) : 0);
+    srft::Tw<D, -1> tw;
+    if constexpr (FT) tw = srft::make_twiddles<D, -1>(q);
 
     struct Out {
         uint32_t word[NJ * WPJ];
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
 
     // step 3: rest of the transform, scales, codes, packing
     auto finish = [&](float(&v)[N], Out& o) {
-        if constexpr (FT) srft::forward<D>(v, fft_row, q);
+        if constexpr (FT) srft::forward<D>(v, fft_row, q, tw);
         else fwht_rest(v, c1, c2);
 
         float amax[LG];
@@ -506,6 +508,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
     int cur_key = -1;
     __shared__ float2 lds_fft[FT ? kWavesPerBlock * 16 * (D / 2 + 1) : 1];
     float2* fft_row = lds_fft + (FT ? ((threadIdx.x >> 6) * 16 + slot) * (D / 2 + 1) : 0);
+    srft::Tw<D, 1> tw;
+    if constexpr (FT) tw = srft::make_twiddles<D, 1>(q);
 
     // Raw inputs of one item: the lane's NJ code words and its vector's whole
     // scale row as packed 32-bit words.
@@ -680,7 +684,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
 
     // step 3: rest of the inverse transform, unscale, round to fp16
     auto finish = [&](float(&v)[N], Out& o) {
-        if constexpr (FT) srft::inverse<D>(v, fft_row, q);
+        if constexpr (FT) srft::inverse<D>(v, fft_row, q, tw);
         else fwht_rest(v, c1, c2);
 #pragma unroll
         for (int j = 0; j < NJ; j++) {

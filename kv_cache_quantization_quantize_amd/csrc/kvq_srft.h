@@ -151,11 +151,74 @@ __device__ __forceinline__ void to_bit_reversed(float (&c)[D / 4], float2* row, 
     });
 }
 
+// The lane-dependent twiddles of the FFT stages, computed once per kernel
+// and kept in registers (they depend only on the lane and on compile-time
+// register indices): the two lane-bit stages' factors (1 on the lower lane of
+// a pair) and the register-bit stages' twiddles omega^((f + 16 (j mod hj))
+// step + 4 q step).  SIGN as in fft_dit.
+template <int D, int SIGN>
+struct Tw {
+    static constexpr int N = D / 2, LOGN = ilog2(N);
+    static constexpr int NJT = LOGN > 4 ? 4 * ((1 << (LOGN - 4)) - 1) : 0;
+    float l0r[3], l0i[3];            // lane bit 0 stage, f = 1..3
+    float l1r[4], l1i[4];            // lane bit 1 stage, f = 0..3
+    float jr[NJT > 0 ? NJT : 1], ji[NJT > 0 ? NJT : 1];
+};
+
+// the first twiddle of register-bit stage b in Tw::jr / Tw::ji
+constexpr int tw_j_base(int b) { return 4 * ((1 << (b - 4)) - 1); }
+
+template <int D, int SIGN>
+__device__ __forceinline__ Tw<D, SIGN> make_twiddles(int q)
+{
+    using T = Tw<D, SIGN>;
+    constexpr int N = T::N, LOGN = T::LOGN;
+    T t;
+    const bool up0 = (q & 1) != 0, up1 = (q & 2) != 0, odd = (q & 1) != 0;
+    static_for<1, 4>([&](auto kk) {
+        constexpr int k = decltype(kk)::value;
+        constexpr int e = k * (N / 8);
+        t.l0r[k - 1] = up0 ? (float)cos2pi(e, N) : 1.0f;
+        t.l0i[k - 1] = up0 ? (float)(SIGN * sin2pi(e, N)) : 0.0f;
+    });
+    static_for<0, 4>([&](auto kk) {
+        constexpr int k = decltype(kk)::value;
+        constexpr int e0 = k * (N / 16), e1 = (k + 4) * (N / 16);
+        t.l1r[k] = up1 ? (odd ? (float)cos2pi(e1, N) : (float)cos2pi(e0, N)) : 1.0f;
+        t.l1i[k] = up1 ? (odd ? (float)(SIGN * sin2pi(e1, N)) : (float)(SIGN * sin2pi(e0, N))) : 0.0f;
+    });
+    static_for<4, LOGN>([&](auto bb) {
+        constexpr int b = decltype(bb)::value;
+        constexpr int hj = 1 << (b - 4);
+        constexpr int step = N >> (b + 1);
+        const float lr = by_lane(q, 1.0f, (float)cos2pi(4 * step, N), (float)cos2pi(8 * step, N),
+                                 (float)cos2pi(12 * step, N));
+        const float li = by_lane(q, 0.0f, (float)(SIGN * sin2pi(4 * step, N)), (float)(SIGN * sin2pi(8 * step, N)),
+                                 (float)(SIGN * sin2pi(12 * step, N)));
+        static_for<0, 4 * hj>([&](auto xx) {
+            constexpr int x = decltype(xx)::value;
+            constexpr int e = (x % 4 + 16 * (x / 4)) * step;
+            const float cr = (float)cos2pi(e, N), ci = (float)(SIGN * sin2pi(e, N));
+            t.jr[tw_j_base(b) + x] = fmaf(lr, cr, -li * ci);
+            t.ji[tw_j_base(b) + x] = fmaf(lr, ci, li * cr);
+        });
+    });
+    // opaque to the optimiser, so that the values stay in registers across
+    // the caller's loop instead of being rebuilt from constants per use
+#pragma unroll
+    for (int k = 0; k < 3; k++) asm volatile("" : "+v"(t.l0r[k]), "+v"(t.l0i[k]));
+#pragma unroll
+    for (int k = 0; k < 4; k++) asm volatile("" : "+v"(t.l1r[k]), "+v"(t.l1i[k]));
+#pragma unroll
+    for (int k = 0; k < T::NJT; k++) asm volatile("" : "+v"(t.jr[k]), "+v"(t.ji[k]));
+    return t;
+}
+
 // Radix-2 decimation-in-time FFT of N = D/2 points held by a quad, from
 // bit-reversed order to natural order, times sigma(q).  SIGN = -1: forward
 // (omega = exp(-2 pi i / N)); +1: inverse without the 1/N.
 template <int D, int SIGN>
-__device__ __forceinline__ void fft_dit(float (&c)[D / 4], int q)
+__device__ __forceinline__ void fft_dit(float (&c)[D / 4], int q, const Tw<D, SIGN>& tw)
 {
     constexpr int P = D / 8, N = D / 2, NJ = D / 32, LOGN = ilog2(N);
     // stage on point bit 0 (f bit 0): twiddle 1
@@ -185,53 +248,34 @@ __device__ __forceinline__ void fft_dit(float (&c)[D / 4], int q)
     }
     // point bit 2 (lane bit 0): upper lanes (q & 1) multiply by omega^(f N/8)
     {
-        const bool up = (q & 1) != 0;
         static_for<0, P>([&](auto ii) {
             constexpr int i = decltype(ii)::value;
-            constexpr int e = (i % 4) * (N / 8);
-            if constexpr (e != 0) {
-                const float wr = up ? (float)cos2pi(e, N) : 1.0f;
-                const float wi = up ? (float)(SIGN * sin2pi(e, N)) : 0.0f;
-                cmul(c[i], c[P + i], wr, wi);
-            }
+            if constexpr (i % 4 != 0) cmul(c[i], c[P + i], tw.l0r[i % 4 - 1], tw.l0i[i % 4 - 1]);
         });
-        bfly_quad1(c, up ? -1.0f : 1.0f);
+        bfly_quad1(c, (q & 1) ? -1.0f : 1.0f);
     }
     // point bit 3 (lane bit 1): upper lanes (q & 2) multiply by
     // omega^((f + 4 (q & 1)) N / 16)
     {
-        const bool up = (q & 2) != 0;
-        const bool odd = (q & 1) != 0;
         static_for<0, P>([&](auto ii) {
             constexpr int i = decltype(ii)::value;
-            constexpr int e0 = (i % 4) * (N / 16), e1 = ((i % 4) + 4) * (N / 16);
-            const float wr = up ? (odd ? (float)cos2pi(e1, N) : (float)cos2pi(e0, N)) : 1.0f;
-            const float wi = up ? (odd ? (float)(SIGN * sin2pi(e1, N)) : (float)(SIGN * sin2pi(e0, N))) : 0.0f;
-            if constexpr (e0 != 0) cmul(c[i], c[P + i], wr, wi);
-            else if (odd) cmul(c[i], c[P + i], wr, wi);
+            cmul(c[i], c[P + i], tw.l1r[i % 4], tw.l1i[i % 4]);
         });
-        bfly_quad2(c, up ? -1.0f : 1.0f);
+        bfly_quad2(c, (q & 2) ? -1.0f : 1.0f);
     }
     // point bits 4 .. LOGN-1 (register j bits)
     static_for<4, LOGN>([&](auto bb) {
         constexpr int b = decltype(bb)::value;
         constexpr int hj = 1 << (b - 4);          // pair distance in j
-        constexpr int step = N >> (b + 1);        // twiddle exponent per unit of (p mod 2^b)
-        // lane part of the twiddle: omega^(4 q step)
-        const float lr = by_lane(q, 1.0f, (float)cos2pi(4 * step, N), (float)cos2pi(8 * step, N),
-                                 (float)cos2pi(12 * step, N));
-        const float li = by_lane(q, 0.0f, (float)(SIGN * sin2pi(4 * step, N)), (float)(SIGN * sin2pi(8 * step, N)),
-                                 (float)(SIGN * sin2pi(12 * step, N)));
+        // twiddle omega^((f + 16 (j mod hj)) step + 4 q step), step = N / 2^(b+1)
         static_for<0, P>([&](auto ii) {
             constexpr int i = decltype(ii)::value;
             constexpr int j = i / 4, f = i % 4;
             if constexpr ((j & hj) == 0) {
                 constexpr int ib = i + 4 * hj;
-                constexpr int e = (f + 16 * (j % hj)) * step;
-                const float cr = (float)cos2pi(e, N), ci = (float)(SIGN * sin2pi(e, N));
-                const float wr = fmaf(lr, cr, -li * ci), wi = fmaf(lr, ci, li * cr);
+                constexpr int x = tw_j_base(b) + f + 4 * (j % hj);
                 float tr = c[ib], ti = c[P + ib];
-                cmul(tr, ti, wr, wi);
+                cmul(tr, ti, tw.jr[x], tw.ji[x]);
                 const float ar = c[i], ai = c[P + i];
                 c[i] = ar + tr; c[P + i] = ai + ti;
                 c[ib] = ar - tr; c[P + ib] = ai - ti;
@@ -283,7 +327,7 @@ __device__ __forceinline__ void unpack_twiddle(int q, float scale, float& cw, fl
 // already multiplied by s * lambda / sqrt(D)): afterwards v holds y times
 // sigma(q).  row: the quad's LDS row of N float2.
 template <int D>
-__device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q)
+__device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, const Tw<D, -1>& tw)
 {
     constexpr int P = D / 8;
     float c[D / 4];
@@ -293,7 +337,7 @@ __device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q)
         c[P + i] = v[8 * (i / 4) + 2 * (i % 4) + 1];
     }
     to_bit_reversed<D>(c, row, q);
-    fft_dit<D, -1>(c, q);
+    fft_dit<D, -1>(c, q, tw);
     float pc[D / 4];
     hermitian_partners<D>(c, pc, q, true);
     constexpr float r = 0.70710678118654752440f;
@@ -322,7 +366,7 @@ __device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q)
 // vector s * lambda * xhat, times sigma(q); the consumer multiplies by
 // s / (lambda sqrt(D)) and sigma(q).
 template <int D>
-__device__ __forceinline__ void inverse(float (&v)[D / 4], float2* row, int q)
+__device__ __forceinline__ void inverse(float (&v)[D / 4], float2* row, int q, const Tw<D, 1>& tw)
 {
     constexpr int P = D / 8;
     float y[D / 4];
@@ -353,7 +397,7 @@ __device__ __forceinline__ void inverse(float (&v)[D / 4], float2* row, int q)
         c[P + i] = zi;
     });
     to_bit_reversed<D>(c, row, q);
-    fft_dit<D, 1>(c, q);
+    fft_dit<D, 1>(c, q, tw);
 #pragma unroll
     for (int i = 0; i < P; i++) {
         v[8 * (i / 4) + 2 * (i % 4)] = c[i];
