@@ -440,17 +440,37 @@ def bench_small(torch, kvq, synth, dev, args):
             tok = {t: inp[t][:, T - 1:T].contiguous() for t in ("K", "V")}
             lam1 = {t: [inp["lam_" + t][l:l + 1].contiguous() for l in range(L)] for t in ("K", "V")}
 
-            def step():
+            def step(st=stream):
                 for l in range(L):
                     for t in ("K", "V"):
                         c, sc = caches[t]
                         kvq.quantize(tok[t][l:l + 1], lam1[t][l], inp["signs"], G, codes=c[l:l + 1, T - 1:T],
-                                     scales=sc[l:l + 1, T - 1:T], stream=stream)
+                                     scales=sc[l:l + 1, T - 1:T], stream=st)
+
+            def graph_step():
+                step(torch.cuda.current_stream())
             step()
             torch.cuda.synchronize()
             sms = timed(step, 10, False)
+            # the same launches captured once in a HIP graph and replayed
+            # (no Python or per-launch host work in the timed region)
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                graph_step()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                graph_step()
+            g.replay()
+            torch.cuda.synchronize()
+            gms = timed(g.replay, 20, False)
             r["decode_append"] = {"us_per_layer_K_and_V": round(sms * 1e3 / L, 2), "us_per_step": round(sms * 1e3, 1),
-                                  "layers": L, "note": "two launches per layer; launch-bound"}
+                                  "layers": L, "note": "two launches per layer; launch-bound",
+                                  "hip_graph_us_per_step": round(gms * 1e3, 1),
+                                  "hip_graph_us_per_layer_K_and_V": round(gms * 1e3 / L, 2)}
+            del g
         res[name] = r
         del inp
         torch.cuda.empty_cache()

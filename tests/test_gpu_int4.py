@@ -91,6 +91,57 @@ def test_gemma_decode_append():
                    "gemma append " + name)
 
 
+def test_decode_append_replayed_from_hip_graph():
+    """The per-layer appends of a decode step captured once in a HIP graph
+    (the library allocates nothing and never synchronizes, so its launches
+    are capturable) and replayed for successive token slots: every replay,
+    with eager work and synchronizations between replays, must write exactly
+    what eager calls write."""
+    dev = device()
+    cfg = synth.config("gemma-3-1b", T=64)
+    inp = synth.make_inputs(cfg, dev)
+    G, Tmax = cfg.G, 64
+    L, _, H, D = inp["K"].shape
+    s = inp["signs"]
+    caches = {t: (torch.zeros((L, Tmax, H, D // 2), dtype=torch.uint8, device=dev),
+                  torch.zeros((L, Tmax, H, D // G), dtype=torch.float16, device=dev)) for t in "KV"}
+    tok = {t: torch.empty((L, 1, H, D), dtype=torch.float16, device=dev) for t in "KV"}
+    slot = {t: (torch.empty((L, 1, H, D // 2), dtype=torch.uint8, device=dev),
+                torch.empty((L, 1, H, D // G), dtype=torch.float16, device=dev)) for t in "KV"}
+    lam1 = {t: [inp["lam_" + t][l:l + 1].contiguous() for l in range(L)] for t in "KV"}
+
+    def step():      # one launch per (layer, K/V), into the staging slot
+        for l in range(L):
+            for t in "KV":
+                kvq.quantize(tok[t][l:l + 1], lam1[t][l], s, G, codes=slot[t][0][l:l + 1],
+                             scales=slot[t][1][l:l + 1])
+
+    for t in "KV":
+        tok[t].copy_(inp[t][:, 0:1])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for pos in range(5, 9):
+        for t in "KV":
+            tok[t].copy_(inp[t][:, pos:pos + 1])
+        g.replay()
+        for t in "KV":                # eager copy into the cache slot
+            caches[t][0][:, pos:pos + 1].copy_(slot[t][0])
+            caches[t][1][:, pos:pos + 1].copy_(slot[t][1])
+        torch.cuda.synchronize()
+        for t in "KV":
+            want_c, want_s = kvq.quantize(inp[t][:, pos:pos + 1], inp["lam_" + t], s, G)
+            torch.cuda.synchronize()
+            assert torch.equal(caches[t][0][:, pos:pos + 1], want_c), (pos, t)
+            assert torch.equal(caches[t][1][:, pos:pos + 1], want_s), (pos, t)
+
+
 # ------------------------------------------------------- instantiations
 @pytest.mark.parametrize("H", [2, 3])           # token-major (H | 16) and head-major items
 @pytest.mark.parametrize("D,G", [(D, G) for D in (64, 128, 256) for G in (8, 16, 32, 64, 128, 256) if G <= D])
