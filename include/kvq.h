@@ -245,9 +245,11 @@ kvq_status kvq_vq_decode_u8(kvq_shape shape, kvq_view idx_u8, const void* codebo
  *   workspace     device scratch of at least kvq_kmeans_step_workspace()
  *                 bytes, 16-byte aligned, owned by the caller; no state is
  *                 kept in it between calls.
- * The sums are taken in fp32 per block of work and across blocks in fp64;
- * the order of the fp32 additions inside a block is not fixed, so the last
- * bit of a centroid can differ between runs.  Views and errors as for
+ * The sums are exact: each rotated coordinate is rounded to a multiple of
+ * 2^-24 and added as a 64-bit integer, so the result does not depend on the
+ * order of the additions and is the same on every run (|y| * n_k < 2^39 for
+ * every centroid, n_k its sample count, keeps the sums in range); each mean
+ * is then formed in fp64 and rounded once to fp16.  Views and errors as for
  * kvq_vq_encode; KVQ_ERR_SHAPE for a short workspace. */
 kvq_status kvq_kmeans_step_workspace(kvq_shape shape, int32_t n_centroids, int32_t sub_dim,
                                      int64_t* bytes);

@@ -350,7 +350,8 @@ kvq_status vq_decode_any(kvq_shape shape, kvq_view idx, const void* codebook_f16
 }
 
 // Work split of the k-means update: per head, 8 * range_groups ranges of
-// (layer, 16-token tile) rows, one block per (head, range).  A function of
+// (layer, 16-token tile) rows, two blocks per (head, range) (coordinates
+// 0-3 and 4-7 of the sub-vectors).  A function of
 // the shape and the current device only, so that the workspace query and the
 // call agree.
 struct KmPlan {
@@ -371,8 +372,9 @@ KmPlan km_plan(const kvq_shape& s)
 
 int64_t km_workspace_bytes(const kvq_shape& s, int32_t K, const KmPlan& p)
 {
-    // fp32 sums (8 per centroid) and a u32 count per centroid, per (head, range)
-    return s.heads * 8 * (int64_t)p.range_groups * (int64_t)K * 36;
+    // int64 fixed-point sums (8 per centroid) and a u32 count per centroid,
+    // per (head, range)
+    return s.heads * 8 * (int64_t)p.range_groups * (int64_t)K * 68;
 }
 
 kvq_status km_check(const kvq_shape& s, int32_t K, int32_t sub)
@@ -551,8 +553,8 @@ kvq_status kvq_kmeans_step(kvq_shape shape, kvq_view x_f16, const float* lambda,
     a.new_codebook = static_cast<uint16_t*>(new_codebook_f16);
     a.counts = counts;
     const int64_t slots = shape.heads * 8 * (int64_t)p.range_groups * n_centroids;
-    a.part_sums = static_cast<float*>(workspace);
-    a.part_counts = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + slots * 32);
+    a.part_sums = static_cast<int64_t*>(workspace);
+    a.part_counts = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + slots * 64);
     a.tiles = p.tiles;
     a.range_groups = p.range_groups;
     a.rows_per_range = p.rows_per_range;

@@ -108,10 +108,10 @@ struct KmArgs {
     const uint16_t* codebook;       // fp16 bits [H, K, 8] (input)
     uint16_t* new_codebook;         // fp16 bits [H, K, 8] (output, may alias codebook)
     uint32_t* counts;               // [H, K]
-    float* part_sums;               // [H, ranges, 8, K]
+    int64_t* part_sums;             // [H, ranges, 8, K], fixed point (2^24 per unit)
     uint32_t* part_counts;          // [H, ranges, K]
     int32_t tiles;                  // 16-token tiles per layer
-    int32_t range_groups;           // ranges per head = 8 * range_groups
+    int32_t range_groups;           // ranges per head = 8 * range_groups (two blocks each)
     int64_t rows_per_range;         // (layer, tile) rows per range
 };
 constexpr int kKmMaxCentroids = 4096;   // LDS: 36 bytes per centroid

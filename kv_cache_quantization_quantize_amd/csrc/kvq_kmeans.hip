@@ -9,24 +9,28 @@
 // assigned to it; a centroid with none keeps its place.
 //
 // Accumulate.  The training vectors of one head (all layers) are cut into
-// ranges of (layer, 16-token tile) rows; one block per (head, range) rotates
-// its vectors exactly as the encoder does (4 lanes per vector, Walsh-Hadamard
-// in registers), reads each sub-vector's assignment and adds the sub-vector
-// and a count into per-centroid fp32 sums in LDS (ds_add_f32; 36 bytes per
-// centroid, at most 4096 centroids).  The sums are stored coordinate-major,
-// [8][K]: the 64 lanes of one atomic instruction add coordinate e of their
-// own centroids, and consecutive centroids fall in consecutive banks (a
-// centroid-major [K][8] layout would put them all in 4 of the 32 banks).  The block then writes its sums and
-// counts to a workspace slot of its own.  As in the decoder, the H blocks of
-// one range are dispatched to the same XCD so that the heads' assignments of a
-// token, which share cache lines, are fetched from HBM once.
+// ranges of (layer, 16-token tile) rows; two blocks per (head, range), one
+// for coordinates 0-3 and one for 4-7 of the sub-vectors, rotate the range's
+// vectors exactly as the encoder does (4 lanes per vector, Walsh-Hadamard in
+// registers), read each sub-vector's assignment and add its coordinates into
+// per-centroid sums in LDS, plus a count (first block only).  The sums are
+// fixed point: each coordinate is rounded to a multiple of 2^-24 and added
+// as a 64-bit integer with ds_add_u64 (4 x 8 bytes per centroid and block,
+// at most 4096 centroids: 128 KB, with the counts 144 KB).  Integer LDS
+// atomics cost about 13 cycles per wavefront instruction on this GPU against
+// about 200 for ds_add_f32, and integer sums are exact, so the result does
+// not depend on the order of the additions.  The sums are stored
+// coordinate-major, [4][K]: the 64 lanes of one atomic instruction add
+// coordinate e of their own centroids, which spread over the banks.  Each
+// block writes its sums (and counts) to the range's workspace slot.  As in
+// the decoder, the H blocks of one range are dispatched to the same XCD (and
+// the two blocks of a (head, range) one after the other) so that shared
+// cache lines are fetched from HBM once.
 //
-// Finalize.  One thread per (head, centroid) adds the blocks' partials in a
-// fixed order in fp64, divides by the count and rounds the mean to fp16
+// Finalize.  One thread per (head, centroid) adds the ranges' integer sums
+// (exact), scales to fp64, divides by the count and rounds the mean to fp16
 // (round to odd into fp32, then round to nearest even into fp16, which is the
-// correctly rounded fp16 of the fp64 mean).  The order of the LDS additions
-// inside a block is not fixed, so the fp32 partial sums -- and rarely the last
-// fp16 bit of a centroid -- may differ between runs.
+// correctly rounded fp16 of the fp64 mean).
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -38,6 +42,17 @@ template <int D>
 struct KmCfg {
     static constexpr int WAVES = (D == 256) ? 8 : 16;
 };
+
+// round(y * 2^24) as a 64-bit integer, exactly (|y| < 2^23): the product is
+// exact, its part above 2^16 converts through a truncation, and the
+// remainder below 2^16 is exact in fp32 and rounds to nearest even.
+__device__ __forceinline__ int64_t to_fixed24(float y)
+{
+    const float t = y * 16777216.0f;
+    const float th = __builtin_truncf(t * (1.0f / 65536.0f));
+    const float tl = fmaf(th, -65536.0f, t);
+    return (int64_t)(int32_t)th * 65536 + (int64_t)(int32_t)__builtin_rintf(tl);
+}
 
 // fp64 -> fp16 with one rounding: round to odd into fp32 (24 significant
 // bits, more than 11 + 2), then the hardware's round to nearest even.
@@ -61,7 +76,7 @@ __global__ __launch_bounds__(64 * KmCfg<D>::WAVES) void kmeans_accum_kernel(KmAr
     constexpr int NJ = D / 32;
     constexpr int N = D / 4;
 
-    __shared__ float sums[8 * kKmMaxCentroids];      // [8][K]
+    __shared__ unsigned long long sums[4 * kKmMaxCentroids];   // [4][K], fixed point
     __shared__ uint32_t cnts[kKmMaxCentroids];
 
     const int lane = threadIdx.x & 63;
@@ -73,9 +88,11 @@ __global__ __launch_bounds__(64 * KmCfg<D>::WAVES) void kmeans_accum_kernel(KmAr
     const float lane_sign = (__builtin_popcount(q) & 1) ? -1.0f : 1.0f;
     const uint32_t kmax = (uint32_t)(a.K - 1);
 
-    // block b runs on XCD b % 8; head (b / 8) % H, range ((b / 8) / H) * 8 + b % 8
+    // block b runs on XCD b % 8; coordinate half (b / 8) % 2, head
+    // (b / 16) % H, range ((b / 16) / H) * 8 + b % 8
     const int xcd = blockIdx.x & 7;
-    const int kx = blockIdx.x >> 3;
+    const int half = (blockIdx.x >> 3) & 1;
+    const int kx = blockIdx.x >> 4;
     const int grp = kx / a.H;
     const int h = kx - grp * a.H;
     const int range = grp * 8 + xcd;
@@ -84,7 +101,7 @@ __global__ __launch_bounds__(64 * KmCfg<D>::WAVES) void kmeans_accum_kernel(KmAr
     const int64_t r0 = (int64_t)range * a.rows_per_range;
     const int64_t r1 = min(r0 + a.rows_per_range, rows);
 
-    for (int i = threadIdx.x; i < a.K * 8; i += 64 * WAVES) sums[i] = 0.0f;
+    for (int i = threadIdx.x; i < a.K * 4; i += 64 * WAVES) sums[i] = 0ull;
     for (int i = threadIdx.x; i < a.K; i += 64 * WAVES) cnts[i] = 0u;
     __syncthreads();
 
@@ -130,18 +147,24 @@ __global__ __launch_bounds__(64 * KmCfg<D>::WAVES) void kmeans_accum_kernel(KmAr
 #pragma unroll
             for (int j = 0; j < NJ; j++) {
 #pragma unroll
-                for (int e = 0; e < 8; e++) atomicAdd(sums + e * a.K + kk[j], v[j * 8 + e] * lane_sign);
-                atomicAdd(cnts + kk[j], 1u);
+                for (int e = 0; e < 4; e++) {
+                    // coordinate 4 half + e of the sub-vector (half is wave-uniform)
+                    const float y = (half ? v[j * 8 + 4 + e] : v[j * 8 + e]) * lane_sign;
+                    atomicAdd(sums + e * a.K + kk[j], (unsigned long long)to_fixed24(y));
+                }
+                if (half == 0) atomicAdd(cnts + kk[j], 1u);
             }
         }
     }
     __syncthreads();
 
     const int64_t slot_base = (int64_t)h * ranges + range;
-    float* ps = a.part_sums + slot_base * a.K * 8;
-    for (int i = threadIdx.x; i < a.K * 8; i += 64 * WAVES) ps[i] = sums[i];
-    uint32_t* pc = a.part_counts + slot_base * a.K;
-    for (int i = threadIdx.x; i < a.K; i += 64 * WAVES) pc[i] = cnts[i];
+    int64_t* ps = a.part_sums + (slot_base * 8 + 4 * half) * a.K;
+    for (int i = threadIdx.x; i < a.K * 4; i += 64 * WAVES) ps[i] = (int64_t)sums[i];
+    if (half == 0) {
+        uint32_t* pc = a.part_counts + slot_base * a.K;
+        for (int i = threadIdx.x; i < a.K; i += 64 * WAVES) pc[i] = cnts[i];
+    }
 }
 
 __global__ __launch_bounds__(256) void kmeans_finalize_kernel(KmArgs a)
@@ -151,15 +174,18 @@ __global__ __launch_bounds__(256) void kmeans_finalize_kernel(KmArgs a)
     const int h = (int)(i / a.K);
     const int k = (int)(i - (int64_t)h * a.K);
     const int ranges = 8 * a.range_groups;
-    double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int64_t si[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     uint64_t n = 0;
     for (int r = 0; r < ranges; r++) {
         const int64_t sl = (int64_t)h * ranges + r;
-        const float* ps = a.part_sums + sl * a.K * 8 + k;     // [8][K] per slot
+        const int64_t* ps = a.part_sums + sl * a.K * 8 + k;   // [8][K] per slot
 #pragma unroll
-        for (int e = 0; e < 8; e++) s[e] += ps[(int64_t)e * a.K];
+        for (int e = 0; e < 8; e++) si[e] += ps[(int64_t)e * a.K];
         n += a.part_counts[sl * a.K + k];
     }
+    double s[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) s[e] = (double)si[e] * (1.0 / 16777216.0);
     a.counts[i] = (uint32_t)n;
     uint4 o;
     if (n == 0) {
@@ -180,7 +206,7 @@ namespace {
 template <int D>
 hipError_t launch_km(const KmArgs& a, hipStream_t s)
 {
-    const dim3 grid((unsigned)(8 * a.H * a.range_groups));
+    const dim3 grid((unsigned)(16 * a.H * a.range_groups));
     hipLaunchKernelGGL((kmeans_accum_kernel<D>), grid, dim3(64 * KmCfg<D>::WAVES), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -259,7 +259,7 @@ def mxfp4_parity(x_bits, lam_rows, signs, codes_gpu, scales_gpu, out_gpu=None):
 
 
 # ------------------------------------------------------- k-means update step
-U32 = 2.0 ** -24
+KM_FIX = 2.0 ** -25
 KM_ROT = 2.0 ** -19
 
 
@@ -271,8 +271,9 @@ def kmeans_parity(x_bits, lam_rows, signs, codebook_bits, idx_gpu, new_gpu, coun
     centroids    the oracle's update from the GPU's own assignments: an empty
                  centroid keeps its exact old bits; otherwise the GPU's fp16
                  value must lie between fp16(m - delta) and fp16(m + delta),
-                 m the fp64 mean, delta = 2^-24 * n_k * mean|y| (worst-case
-                 error of an n_k-term fp32 sum) + 2^-19 * the largest
+                 m the fp64 mean, delta = 2^-25 (the sums are exact sums of
+                 the coordinates rounded to multiples of 2^-24, so the mean
+                 is off by at most half that) + 2^-19 * the largest
                  per-vector RMS of y (fp32 rotation error)."""
     x_bits = np.ascontiguousarray(x_bits, np.uint16)
     lam_rows = np.ascontiguousarray(lam_rows, np.float32)
@@ -298,7 +299,7 @@ def kmeans_parity(x_bits, lam_rows, signs, codebook_bits, idx_gpu, new_gpu, coun
             i.tolist(), cg[i], cnt_o[i]))
     ng = np.ascontiguousarray(new_gpu, np.uint16).reshape(K, sub)
     ymax = float(np.sqrt((y64 ** 2).mean(axis=1)).max()) if len(y64) else 0.0
-    delta = U32 * cnt_o[:, None].astype(np.float64) * am + KM_ROT * ymax
+    delta = np.full(m64.shape, KM_FIX + KM_ROT * ymax)
     lo = f16(oracle.f64_to_f16(m64 - delta))
     hi = f16(oracle.f64_to_f16(m64 + delta))
     g = f16(ng)

@@ -169,7 +169,7 @@ def test_kmeans_workspace_query_and_validation(lib):
     P = ctypes.c_void_p
     n = ctypes.c_int64(-1)
     assert lib.kvq_kmeans_step_workspace(shape(), 4096, 8, ctypes.byref(n)) == OK
-    assert n.value > 0 and n.value % (3 * 8 * 4096 * 36) == 0      # H * 8 ranges-per-group * K * 36 bytes
+    assert n.value > 0 and n.value % (3 * 8 * 4096 * 68) == 0      # H * 8 ranges-per-group * K * 68 bytes
     assert lib.kvq_kmeans_step_workspace(shape(), 4097, 8, ctypes.byref(n)) == SHAPE
     assert lib.kvq_kmeans_step_workspace(shape(), 16, 3, ctypes.byref(n)) == SHAPE
     assert lib.kvq_kmeans_step_workspace(shape(), 16, 16, ctypes.byref(n)) == UNSUP
