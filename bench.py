@@ -113,9 +113,10 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
         "vq_decode": ("kvq::vq_decode_lds_kernel<128, false>", nk * (2 * D + 2 * (D // 8))),
         "vq_encode_u8": ("kvq::vq_encode_kernel<128, true>", nk * (2 * D + D // 8)),
         "vq_decode_u8": ("kvq::vq_decode_lds_kernel<128, true>", nk * (2 * D + D // 8)),
-        # reads the keys and their assignments, writes one partial slot per block
-        "kmeans_accum": ("kvq::kmeans_accum_kernel<128>", nk * (2 * D + 2 * (D // 8)) + 256 * 4096 * 36),
-        "kmeans_finalize": ("kvq::kmeans_finalize_kernel", 256 * 4096 * 36 + 8 * 4096 * (16 + 4)),
+        # reads the keys and their assignments, writes the 256 (head, range)
+        # workspace slots (8 int64 sums and a u32 count per centroid)
+        "kmeans_accum": ("kvq::kmeans_accum_kernel<128>", nk * (2 * D + 2 * (D // 8)) + 256 * 4096 * 68),
+        "kmeans_finalize": ("kvq::kmeans_finalize_kernel", 256 * 4096 * 68 + 8 * 4096 * (16 + 4)),
     }
     out = {"workload": "qwen3-8b-shaped cache [36, 262144, 8, 128] fp16, group 32, one tensor per launch; "
                        "decode attention over it as 288 sequences of 32768 tokens, 4 query heads per KV head; "
