@@ -509,6 +509,22 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     const int j16 = lane & 15;   // MFMA row (A) / column (B, result)
     const int sl = lane >> 4;    // MFMA k-slice; result row block
 
+    // The rotated queries enter the MFMAs as fp16 hi + lo halves, scaled by
+    // 2^-qe so that the largest stays below 2^14 (qe = 0 unless the queries
+    // are huge; the scaling is exact), and each score is multiplied back by
+    // 2^qe.
+    int qe;
+    {
+        float qm = 0.0f;
+        const float* qf = &qt[wid][0][0] + 8 * lane;
+#pragma unroll
+        for (int i = 0; i < 8; i++) qm = fmaxf(qm, fabsf(qf[i]));
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) qm = fmaxf(qm, __shfl_xor(qm, o));
+        qe = uniform(qm > 0.0f ? max(0, ilogbf(qm) - 13) : 0);
+    }
+    const float sfac = ldexpf(1.0f, qe);
+
     // score B operands of the wavefront's head, [hi/lo][MFMA m][lane]: column
     // (g, r) = 4r + g, slice sl = group sl.  Kept in LDS and read at each use
     // rather than held in 32 VGPRs.
@@ -521,8 +537,8 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int k = 0; k < 4; k++) {
-                const float v0 = on ? qt[wid][r][32 * sl + 8 * m + kPermK[2 * k]] : 0.0f;
-                const float v1 = on ? qt[wid][r][32 * sl + 8 * m + kPermK[2 * k + 1]] : 0.0f;
+                const float v0 = on ? ldexpf(qt[wid][r][32 * sl + 8 * m + kPermK[2 * k]], -qe) : 0.0f;
+                const float v1 = on ? ldexpf(qt[wid][r][32 * sl + 8 * m + kPermK[2 * k + 1]], -qe) : 0.0f;
                 const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
                 hw[k] = __builtin_bit_cast(uint32_t, h2_t{h0, h1});
                 lw[k] = pack_h2(v0 - (float)h0, v1 - (float)h1);
@@ -540,7 +556,7 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
         const int r = j16 >> 2, g = j16 & 3;
         float sq = 0.0f;
 #pragma unroll 8
-        for (int c = 0; c < 32; c++) sq += qt[wid][r][32 * g + c];
+        for (int c = 0; c < 32; c++) sq += ldexpf(qt[wid][r][32 * g + c], -qe);
         kb = 72.0f * sq;
     }
 
@@ -682,7 +698,7 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             // keep token g, add lane g ^ 1's
             const float sv = (h1 ? y1 : y0) + dpp_mov<kDppXor1>(h1 ? y0 : y1);
             const bool valid = tb + 16 * tau + 4 * sl + gS < we;
-            sc[tau] = valid ? sv : -__builtin_inff();
+            sc[tau] = valid ? sv * sfac : -__builtin_inff();
             smax = fmaxf(smax, sc[tau]);
         }
         smax = fmaxf(smax, dpp_mov<kDppXor1>(smax));
@@ -690,10 +706,14 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
         smax = fmaxf(smax, __shfl_xor(smax, 16));
         smax = fmaxf(smax, __shfl_xor(smax, 32));
         // The weights are taken relative to a reference max that moves only
-        // when a score exceeds it by more than 2^8 (weights stay below 256,
-        // well inside fp16), so the accumulators are rescaled a few times per
-        // wave rather than every step.
-        if (__builtin_amdgcn_ballot_w64(smax > m_run + 8.0f)) {
+        // when a score exceeds it by more than 2^8 (weights stay below 256),
+        // so the accumulators are rescaled a few times per wave rather than
+        // every step.  The value operand p * vscale must stay finite in fp16:
+        // in a step with a value scale of 128 or more the reference moves to
+        // the step's max, so that p <= 1.
+        const uint32_t vsb = b.vs & 0x7fff7fffu;
+        const bool big = __builtin_amdgcn_ballot_w64((vsb & 0xffffu) >= 0x5800u || (vsb >> 16) >= 0x5800u) != 0;
+        if (__builtin_amdgcn_ballot_w64(smax > m_run + (big ? 0.0f : 8.0f))) {
             const float m_new = fmaxf(m_run, smax);
             const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;

@@ -38,11 +38,12 @@ def make_cache(L, T, H, D, G, seed, dev, spread=0.5):
     return out
 
 
-def compare(out, out64, lam_v, H, R, what):
-    """out [L, H*R, D] fp16 (GPU), out64 [L, H*R, D], lam_v [L, H, D]."""
+def compare(out, out64, lam_v, H, R, what, unit=1.0):
+    """out [L, H*R, D] fp16 (GPU), out64 [L, H*R, D], lam_v [L, H, D].  unit:
+    the RMS of the lambda-scaled values when it is not about 1."""
     g = bits(out).view(np.float16).astype(np.float64)
     lam = np.repeat(lam_v.cpu().numpy().astype(np.float64), R, axis=1)       # [L, H*R, D]
-    tol = ATOL / lam + RTOL * np.abs(out64)
+    tol = ATOL * unit / lam + RTOL * np.abs(out64)
     err = np.abs(g - out64)
     bad = ~(err <= tol)
     rep = {"n": int(g.size), "bad": int(bad.sum()), "max_err_over_tol": float((err / tol).max()),
@@ -214,3 +215,56 @@ def test_attend_huge_token_stride(stride_mb):
         assert torch.equal(out, ref)        # same kernel, same arithmetic
     del buf, big
     torch.cuda.empty_cache()
+
+
+def _cache(x, lam, s, G):
+    codes, scales = kvq.quantize(x, lam, s, G)
+    return codes, scales
+
+
+def test_attend_large_value_scales():
+    """Values whose lambda-scaled magnitude is in the thousands (value
+    scales far above 128): the matrix-core kernel keeps its fp16 value
+    operand p * scale finite by moving the softmax reference to each such
+    step's maximum (p <= 1).  Tolerance relative to the values' RMS."""
+    dev = device()
+    L, T, H, R, D, G = 2, 300, 2, 4, 128, 32
+    g = torch.Generator(device="cpu").manual_seed(71)
+    s = (torch.randint(0, 2, (D,), generator=g) * 2 - 1).to(torch.int8).to(dev)
+    xk = torch.randn((L, T, H, D), generator=g).to(torch.float16).to(dev)
+    xv = (torch.randn((L, T, H, D), generator=g) * 2000.0).to(torch.float16).to(dev)
+    lk = torch.ones((L, H, D), dtype=torch.float32, device=dev)
+    lv = torch.ones((L, H, D), dtype=torch.float32, device=dev)
+    kc, ks = _cache(xk, lk, s, G)
+    vc, vs = _cache(xv, lv, s, G)
+    assert float(vs.float().max()) > 128.0
+    q = (torch.randn((L, H * R, D), generator=g) * 3.0).to(torch.float16).to(dev)
+    out = kvq.attend_decode(q, kc, ks, vc, vs, lk, lv, s, G)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    out64 = oracle.attend_decode(bits(q), kc.cpu().numpy(), bits(ks), vc.cpu().numpy(), bits(vs),
+                                 lk.cpu().numpy(), lv.cpu().numpy(), s.cpu().numpy(), G, 1.0 / D ** 0.5)
+    compare(out, out64, lv, H, R, "large value scales", unit=2000.0)
+
+
+def test_attend_huge_rotated_queries():
+    """A tiny key lambda makes the rotated query (q / lambda_K) exceed the
+    fp16 range: the matrix-core kernel scales its query operand by a power
+    of two and the scores back, exactly."""
+    dev = device()
+    L, T, H, R, D, G = 2, 300, 2, 4, 128, 32
+    g = torch.Generator(device="cpu").manual_seed(72)
+    s = (torch.randint(0, 2, (D,), generator=g) * 2 - 1).to(torch.int8).to(dev)
+    xk = (torch.randn((L, T, H, D), generator=g) * 16.0).to(torch.float16).to(dev)
+    xv = torch.randn((L, T, H, D), generator=g).to(torch.float16).to(dev)
+    lk = torch.full((L, H, D), 2.0 ** -14, dtype=torch.float32, device=dev)
+    lv = torch.ones((L, H, D), dtype=torch.float32, device=dev)
+    kc, ks = _cache(xk, lk, s, G)
+    vc, vs = _cache(xv, lv, s, G)
+    q = (torch.randn((L, H * R, D), generator=g) * 10.0).to(torch.float16).to(dev)
+    out = kvq.attend_decode(q, kc, ks, vc, vs, lk, lv, s, G)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    out64 = oracle.attend_decode(bits(q), kc.cpu().numpy(), bits(ks), vc.cpu().numpy(), bits(vs),
+                                 lk.cpu().numpy(), lv.cpu().numpy(), s.cpu().numpy(), G, 1.0 / D ** 0.5)
+    compare(out, out64, lv, H, R, "huge rotated queries")
