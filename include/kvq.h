@@ -199,7 +199,10 @@ kvq_status kvq_dequantize_mxfp4(kvq_shape shape, kvq_view codes_u8, kvq_view sca
  *   idx_u16                 output view of D/sub_dim uint16 rows; 4-byte
  *                           aligned data, even strides.
  * The codebook must be 16-byte aligned.  Distances use the unrounded fp32
- * rotated key. */
+ * rotated key.  Domain: rotated coordinates below 65504 in magnitude and
+ * squared centroid norms below 65504 (both enter the matrix cores as fp16
+ * hi + lo halves); outside it the indices are unspecified, and no access
+ * goes out of bounds. */
 kvq_status kvq_vq_encode(kvq_shape shape, kvq_view x_f16, const float* lambda,
                          const int8_t* signs, const void* codebook_f16,
                          int64_t codebook_layer_stride, int32_t n_centroids,
