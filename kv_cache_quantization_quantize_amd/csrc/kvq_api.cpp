@@ -246,7 +246,7 @@ AttnPlan attn_plan(const kvq_shape& s, int32_t R)
     return p;
 }
 
-// Plan of the matrix-core kernel (head_dim 128, group 32).  A block is one
+// Plan of the matrix-core kernel (head_dim 128 or 256, four groups).  A block is one
 // (outer index, split) and a group of hb KV heads, hb the largest of 8, 4, 2,
 // 1 that divides H; its eight wavefronts are the hb heads times 8 / hb
 // consecutive sub-ranges of the split.  The heads of a group read
@@ -283,7 +283,7 @@ MfmaPlan attn_plan_mfma(const kvq_shape& s, int32_t R)
 int64_t attn_parts_capacity(const kvq_shape& s, int32_t R)
 {
     int64_t parts = attn_plan(s, R).parts;
-    if (s.head_dim == 128) parts = std::max<int64_t>(parts, attn_plan_mfma(s, R).parts);
+    if (s.head_dim == 128 || s.head_dim == 256) parts = std::max<int64_t>(parts, attn_plan_mfma(s, R).parts);
     return parts;
 }
 
@@ -608,12 +608,13 @@ kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f1
     a.R = q_per_kv;
     a.g_shift = 0;
     while ((1 << a.g_shift) < group) a.g_shift++;
-    // The matrix-core kernel serves head_dim 128 with groups of 32, where 32
-    // token rows of every view span less than 2^31 bytes (it addresses a
-    // step's loads with 32-bit offsets); the VALU kernel serves the rest.
+    // The matrix-core kernel serves head_dim 128 with groups of 32 and
+    // head_dim 256 with groups of 64 (four groups per vector), where 32 token
+    // rows of every view span less than 2^31 bytes (it addresses a step's
+    // loads with 32-bit offsets); the VALU kernel serves the rest.
     const int64_t row = std::max(std::max(k_codes_u8.stride_token, v_codes_u8.stride_token),
                                  2 * std::max(k_scales_f16.stride_token, v_scales_f16.stride_token));
-    a.mfma = D == 128 && group == 32 && 32 * row + 64 < ((int64_t)1 << 31);
+    a.mfma = ((D == 128 && group == 32) || (D == 256 && group == 64)) && 32 * row + 64 < ((int64_t)1 << 31);
     if (a.mfma) {
         const MfmaPlan p = attn_plan_mfma(shape, q_per_kv);
         a.rp = 4;

@@ -358,7 +358,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core partial kernel: head_dim 128, group 32
+// Matrix-core partial kernel: head_dim 128 with groups of 32, head_dim 256
+// with groups of 64
 // ---------------------------------------------------------------------------
 // Same query rotation, log2-domain online softmax and partial format as
 // attend_partial_kernel, with both contractions on
@@ -476,9 +477,15 @@ __device__ __forceinline__ void rotate_queries(const AttnArgs& a, int l, int h, 
     }
 }
 
+template <int D>
 __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kernel(AttnArgs a)
 {
-    constexpr int D = 128, RP = 4, STEP = 32, W = kAttnMfmaWaves;
+    // D = 128 with groups of 32 or D = 256 with groups of 64: four groups per
+    // vector either way.  NM MFMAs of k = 32 per group, KW 16-byte code loads
+    // per (token, group), NVD value dwords per (token, lane).
+    constexpr int RP = 4, STEP = 32, W = kAttnMfmaWaves;
+    constexpr int G = D / 4, NM = G / 8, KW = G / 32, NVD = D / 128;
+    static_assert(D == 128 || D == 256, "head_dim 128 or 256");
     const int lane = threadIdx.x & 63;
     const int wid = uniform(threadIdx.x >> 6);
     // Block -> (outer index l, head group, split); wavefront -> (head of the
@@ -516,38 +523,43 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     int qe;
     {
         float qm = 0.0f;
-        const float* qf = &qt[wid][0][0] + 8 * lane;
+        const float* qf = &qt[wid][0][0] + (RP * D / 64) * lane;
 #pragma unroll
-        for (int i = 0; i < 8; i++) qm = fmaxf(qm, fabsf(qf[i]));
+        for (int i = 0; i < RP * D / 64; i++) qm = fmaxf(qm, fabsf(qf[i]));
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) qm = fmaxf(qm, __shfl_xor(qm, o));
         qe = uniform(qm > 0.0f ? max(0, ilogbf(qm) - 13) : 0);
     }
     const float sfac = ldexpf(1.0f, qe);
 
-    // score B operands of the wavefront's head, [hi/lo][MFMA m][lane]: column
-    // (g, r) = 4r + g, slice sl = group sl.  Kept in LDS and read at each use
-    // rather than held in 32 VGPRs.
-    __shared__ uint4 bqL[W][2][4][64];
-    {
+    // Score B operands of the wavefront's head: column (g, r) = 4r + g of
+    // k-slice sl holds query r's coordinates of group g when g == sl, zeros
+    // otherwise.  The 16 non-zero columns of each MFMA are kept in LDS,
+    // [hi/lo][MFMA m][column], and read at each use; a lane whose column is
+    // zero in its slice reads a block of zeros laid out the same way.
+    __shared__ uint4 bqL[W][2][NM][16];
+    __shared__ uint4 bqZero[2][NM][16];
+    for (int i = threadIdx.x; i < 2 * NM * 16; i += 64 * W) (&bqZero[0][0][0])[i] = make_uint4(0, 0, 0, 0);
+    const bool bq_on = (j16 & 3) == sl;
+    if (bq_on) {
         const int r = j16 >> 2, g = j16 & 3;
-        const bool on = g == sl;
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
+        for (int m = 0; m < NM; m++) {
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int k = 0; k < 4; k++) {
-                const float v0 = on ? ldexpf(qt[wid][r][32 * sl + 8 * m + kPermK[2 * k]], -qe) : 0.0f;
-                const float v1 = on ? ldexpf(qt[wid][r][32 * sl + 8 * m + kPermK[2 * k + 1]], -qe) : 0.0f;
+                const float v0 = ldexpf(qt[wid][r][G * g + 8 * m + kPermK[2 * k]], -qe);
+                const float v1 = ldexpf(qt[wid][r][G * g + 8 * m + kPermK[2 * k + 1]], -qe);
                 const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
                 hw[k] = __builtin_bit_cast(uint32_t, h2_t{h0, h1});
                 lw[k] = pack_h2(v0 - (float)h0, v1 - (float)h1);
             }
-            bqL[wid][0][m][lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            bqL[wid][1][m][lane] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            bqL[wid][0][m][j16] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            bqL[wid][1][m][j16] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
     }
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();     // the zero block is shared by the block's wavefronts
+    const uint4* bqp = bq_on ? &bqL[wid][0][0][j16] : &bqZero[0][0][j16];
 
     // The codes enter the MFMAs as 72 + c: the score column (g, r) carries
     // 72 times the sum of query r over group g, removed before scaling.
@@ -556,7 +568,7 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
         const int r = j16 >> 2, g = j16 & 3;
         float sq = 0.0f;
 #pragma unroll 8
-        for (int c = 0; c < 32; c++) sq += ldexpf(qt[wid][r][32 * g + c], -qe);
+        for (int c = 0; c < G; c++) sq += ldexpf(qt[wid][r][G * g + c], -qe);
         kb = 72.0f * sq;
     }
 
@@ -576,67 +588,77 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     const uint8_t* vcg = static_cast<const uint8_t*>(a.vc.data) + (int64_t)l * a.vc.sl + (int64_t)h * a.vc.sh;
     const uint16_t* ksg = static_cast<const uint16_t*>(a.ks.data) + (int64_t)l * a.ks.sl + (int64_t)h * a.ks.sh;
     const uint16_t* vsg = static_cast<const uint16_t*>(a.vs.data) + (int64_t)l * a.vs.sl + (int64_t)h * a.vs.sh;
-    typedef uint32_t u32_a2 __attribute__((aligned(2)));
-
     // Loads are split by what consumes them: the key codes of a step feed its
     // score MFMAs one step before its values and scales are needed.
     struct KBuf {
-        uint4 k[2];       // token 16 tau + j16, group sl: 32 codes
+        uint4 k[2][KW];   // token 16 tau + j16, group sl: G codes
     };
     struct VBuf {
-        uint32_t v[8];    // token 8 sl + t', coordinates 8 j16 .. 8 j16 + 7
-        uint32_t ks, vs;  // token lane / 2, groups 2 (lane & 1), +1
+        uint32_t v[NVD][8];   // token 8 sl + t', coordinates 128 hv + 8 j16 .. + 7
+        uint32_t ks, vs;      // token lane / 2, groups 2 (lane & 1), +1
     };
-    // A step's loads address a wave-uniform base (the step's first token)
-    // plus 32-bit per-lane byte offsets (the host guarantees 32 token rows fit
-    // in 2^31 bytes).  In the last step, tokens past the wave's range are
-    // clamped to its last token, so every load is in range.
+    // Loads are raw buffer loads: each stream's resource starts at the step's
+    // first token (scalar arithmetic), each lane keeps one fixed 32-bit offset
+    // per stream, and the per-load parts are scalar offsets, so a step's
+    // addressing costs no vector instructions (the host guarantees 32 token
+    // rows span less than 2^31 bytes).  In the wave's last step, rows past
+    // its range are clamped to its last token, so every load stays in the
+    // cache.
     const uint32_t kst = (uint32_t)a.kc.st, vst = (uint32_t)a.vc.st;
     const uint32_t kss = 2u * (uint32_t)a.ks.st, vss = 2u * (uint32_t)a.vs.st;
-    struct OffK {
-        uint32_t k[2];
+    constexpr int kRawBufferFlags = 0x00020000;     // gfx9 descriptor word 3 for raw dword access
+    auto rsrc = [](const void* p) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, kRawBufferFlags);
     };
-    struct OffV {
-        uint32_t v[8], ks, vs;
-    };
-    // byte offsets of the lane's loads from the step's first token, for steps
-    // whose last in-range token is `lim`
-    auto offsets_k = [&](int lim) {
-        OffK o;
-#pragma unroll
-        for (int tau = 0; tau < 2; tau++) o.k[tau] = (uint32_t)min(16 * tau + j16, lim) * kst + 16u * sl;
-        return o;
-    };
-    auto offsets_v = [&](int lim) {
-        OffV o;
-#pragma unroll
-        for (int tp = 0; tp < 8; tp++) o.v[tp] = (uint32_t)min(8 * sl + tp, lim) * vst + 4u * j16;
-        const uint32_t ts = (uint32_t)min(lane >> 1, lim);
-        o.ks = ts * kss + 4u * (lane & 1);
-        o.vs = ts * vss + 4u * (lane & 1);
-        return o;
-    };
-    // Each loader visits steps in increasing order, so its offsets switch to
-    // the clamped ones once, at the wave's last (partial) step.
-    OffK offk = offsets_k(STEP - 1);
-    OffV offv = offsets_v(STEP - 1);
+    const uint32_t klane = (uint32_t)j16 * kst + 16u * (uint32_t)(KW * sl);
+    const uint32_t vlane = (uint32_t)(8 * sl) * vst + 4u * (uint32_t)j16;
+    const uint32_t kslane = (uint32_t)(lane >> 1) * kss + 4u * (uint32_t)(lane & 1);
+    const uint32_t vslane = (uint32_t)(lane >> 1) * vss + 4u * (uint32_t)(lane & 1);
     auto load_k = [&](int step, KBuf& b) {
         const int tb = wb + step * STEP;
-        if (tb + STEP > we) offk = offsets_k(we - 1 - tb);
-        const uint8_t* kbase = kcg + (int64_t)tb * a.kc.st;
+        const auto r = rsrc(kcg + (int64_t)tb * a.kc.st);
+        if (tb + STEP > we) {
+            const int lim = we - 1 - tb;
 #pragma unroll
-        for (int tau = 0; tau < 2; tau++) b.k[tau] = *reinterpret_cast<const uint4*>(kbase + offk.k[tau]);
+            for (int tau = 0; tau < 2; tau++)
+#pragma unroll
+                for (int kw = 0; kw < KW; kw++)
+                    b.k[tau][kw] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                        r, (uint32_t)min(16 * tau + j16, lim) * kst + 16u * (uint32_t)(KW * sl + kw), 0, 0));
+        } else {
+#pragma unroll
+            for (int tau = 0; tau < 2; tau++)
+#pragma unroll
+                for (int kw = 0; kw < KW; kw++)
+                    b.k[tau][kw] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                        r, klane, 16u * (uint32_t)tau * kst + 16u * (uint32_t)kw, 0));
+        }
     };
     auto load_v = [&](int step, VBuf& b) {
         const int tb = wb + step * STEP;
-        if (tb + STEP > we) offv = offsets_v(we - 1 - tb);
-        const uint8_t* vbase = vcg + (int64_t)tb * a.vc.st;
-        const uint8_t* ksb = reinterpret_cast<const uint8_t*>(ksg + (int64_t)tb * a.ks.st);
-        const uint8_t* vsb = reinterpret_cast<const uint8_t*>(vsg + (int64_t)tb * a.vs.st);
+        const auto rv = rsrc(vcg + (int64_t)tb * a.vc.st);
+        const auto rks = rsrc(ksg + (int64_t)tb * a.ks.st);
+        const auto rvs = rsrc(vsg + (int64_t)tb * a.vs.st);
+        if (tb + STEP > we) {
+            const int lim = we - 1 - tb;
 #pragma unroll
-        for (int tp = 0; tp < 8; tp++) b.v[tp] = *reinterpret_cast<const uint32_t*>(vbase + offv.v[tp]);
-        b.ks = *reinterpret_cast<const u32_a2*>(ksb + offv.ks);
-        b.vs = *reinterpret_cast<const u32_a2*>(vsb + offv.vs);
+            for (int hv = 0; hv < NVD; hv++)
+#pragma unroll
+                for (int tp = 0; tp < 8; tp++)
+                    b.v[hv][tp] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rv, (uint32_t)min(8 * sl + tp, lim) * vst + 4u * (uint32_t)j16 + 64u * (uint32_t)hv, 0, 0);
+            const uint32_t ts = (uint32_t)min(lane >> 1, lim);
+            b.ks = __builtin_amdgcn_raw_buffer_load_b32(rks, ts * kss + 4u * (uint32_t)(lane & 1), 0, 0);
+            b.vs = __builtin_amdgcn_raw_buffer_load_b32(rvs, ts * vss + 4u * (uint32_t)(lane & 1), 0, 0);
+        } else {
+#pragma unroll
+            for (int hv = 0; hv < NVD; hv++)
+#pragma unroll
+                for (int tp = 0; tp < 8; tp++)
+                    b.v[hv][tp] = __builtin_amdgcn_raw_buffer_load_b32(rv, vlane, (uint32_t)tp * vst + 64u * (uint32_t)hv, 0);
+            b.ks = __builtin_amdgcn_raw_buffer_load_b32(rks, kslane, 0, 0);
+            b.vs = __builtin_amdgcn_raw_buffer_load_b32(rvs, vslane, 0, 0);
+        }
     };
 
     uint32_t magic = 0x54005400u;      // fp16 64 in both halves, kept in a VGPR
@@ -644,23 +666,29 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     float m_run = -__builtin_inff();   // running max of query j16 & 3 (log2 domain)
     float l_run = 0.0f;                // this lane's share of the weight sum
     float vb = 0.0f;                   // sum of the lane's value-operand entries
-    f4_t acc[8];
+    f4_t acc[NVD][8];
 #pragma unroll
-    for (int mt = 0; mt < 8; mt++) acc[mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int hv = 0; hv < NVD; hv++)
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++) acc[hv][mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // per-group partial scores of a step's 2 x 16 tokens
     auto scores = [&](const KBuf& b, f4_t (&c)[2]) {
 #pragma unroll
         for (int tau = 0; tau < 2; tau++) {
             c[tau] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            const uint32_t kw[4] = {b.k[tau].x, b.k[tau].y, b.k[tau].z, b.k[tau].w};
 #pragma unroll
-            for (int m = 0; m < 4; m++) {
-                const h8_t am = codes8_b72(kw[m], magic);
-                const h8_t bh = __builtin_bit_cast(h8_t, bqL[wid][0][m][lane]);
-                const h8_t bl = __builtin_bit_cast(h8_t, bqL[wid][1][m][lane]);
-                c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bh, c[tau], 0, 0, 0);
-                c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bl, c[tau], 0, 0, 0);
+            for (int kq = 0; kq < KW; kq++) {
+                const uint32_t kw[4] = {b.k[tau][kq].x, b.k[tau][kq].y, b.k[tau][kq].z, b.k[tau][kq].w};
+#pragma unroll
+                for (int d = 0; d < 4; d++) {
+                    const int m = 4 * kq + d;
+                    const h8_t am = codes8_b72(kw[d], magic);
+                    const h8_t bh = __builtin_bit_cast(h8_t, bqp[m * 16]);
+                    const h8_t bl = __builtin_bit_cast(h8_t, bqp[(NM + m) * 16]);
+                    c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bh, c[tau], 0, 0, 0);
+                    c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bl, c[tau], 0, 0, 0);
+                }
             }
         }
     };
@@ -725,9 +753,11 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             const float4 al = *reinterpret_cast<const float4*>(&aL[wid][0]);
             const float av[4] = {al.x, al.y, al.z, al.w};
 #pragma unroll
-            for (int mt = 0; mt < 8; mt++)
+            for (int hv = 0; hv < NVD; hv++)
 #pragma unroll
-                for (int v = 0; v < 4; v++) acc[mt][v] *= av[v];
+                for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+                    for (int v = 0; v < 4; v++) acc[hv][mt][v] *= av[v];
         }
 #pragma unroll
         for (int tau = 0; tau < 2; tau++) {
@@ -758,51 +788,56 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             ap_lo = __builtin_bit_cast(h8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
         }
         // value B operands: tile 2q' / 2q'+1 from byte q' of the 8 tokens' dwords
-        uint32_t vx[8];
 #pragma unroll
-        for (int tp = 0; tp < 8; tp++) vx[tp] = b.v[tp] ^ 0x88888888u;      // offset binary
+        for (int hv = 0; hv < NVD; hv++) {
+            uint32_t vx[8];
 #pragma unroll
-        for (int qb = 0; qb < 4; qb++) {
-            const uint32_t sel = (uint32_t)qb | (0x0cu << 8) | ((uint32_t)(4 + qb) << 16) | (0x0cu << 24);
-            uint32_t lo[4], hi[4];
+            for (int tp = 0; tp < 8; tp++) vx[tp] = b.v[hv][tp] ^ 0x88888888u;      // offset binary
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const uint32_t w = __builtin_amdgcn_perm(vx[k + 4], vx[k], sel);
-                lo[k] = nib2_b64(w << 4, magic);
-                hi[k] = nib2_b64(w, magic);
+            for (int qb = 0; qb < 4; qb++) {
+                const uint32_t sel = (uint32_t)qb | (0x0cu << 8) | ((uint32_t)(4 + qb) << 16) | (0x0cu << 24);
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const uint32_t w = __builtin_amdgcn_perm(vx[k + 4], vx[k], sel);
+                    lo[k] = nib2_b64(w << 4, magic);
+                    hi[k] = nib2_b64(w, magic);
+                }
+                const h8_t bl = __builtin_bit_cast(h8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+                const h8_t bh = __builtin_bit_cast(h8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                f4_t& a0 = acc[hv][2 * qb];
+                f4_t& a1 = acc[hv][2 * qb + 1];
+                a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_hi, bl, a0, 0, 0, 0);
+                a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_lo, bl, a0, 0, 0, 0);
+                a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_hi, bh, a1, 0, 0, 0);
+                a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_lo, bh, a1, 0, 0, 0);
             }
-            const h8_t bl = __builtin_bit_cast(h8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
-            const h8_t bh = __builtin_bit_cast(h8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-            acc[2 * qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_hi, bl, acc[2 * qb], 0, 0, 0);
-            acc[2 * qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_lo, bl, acc[2 * qb], 0, 0, 0);
-            acc[2 * qb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_hi, bh, acc[2 * qb + 1], 0, 0, 0);
-            acc[2 * qb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_lo, bh, acc[2 * qb + 1], 0, 0, 0);
         }
         __builtin_amdgcn_wave_barrier();
     };
 
     // Software pipeline: while step st is finished, the score MFMAs of step
-    // st + 1 run on the matrix cores, the key codes of steps st + 2 and st + 3
-    // and the values and scales of step st + 1 are in flight.  Steps past
+    // st + 1 run on the matrix cores, and the key codes of step st + 2 and
+    // the values and scales of step st + 1 are in flight (the key buffer is
+    // refilled as soon as its codes have become MFMA operands).  Steps past
     // the last one repeat it (in range; their results are never used).
     if (nsteps > 0) {
-        KBuf K0, K1;
+        KBuf K;
         VBuf V0, V1;
         f4_t c0[2], c1[2];
-        load_k(0, K0);
+        load_k(0, K);
         load_v(0, V0);
-        load_k(min(1, nsteps - 1), K1);
-        scores(K0, c0);
-        load_k(min(2, nsteps - 1), K0);
+        scores(K, c0);
+        load_k(min(1, nsteps - 1), K);
         for (int st = 0;; st += 2) {
             load_v(min(st + 1, nsteps - 1), V1);
-            scores(K1, c1);
-            load_k(min(st + 3, nsteps - 1), K1);
+            scores(K, c1);
+            load_k(min(st + 2, nsteps - 1), K);
             finish(st, V0, c0);
             if (st + 1 >= nsteps) break;
             load_v(min(st + 2, nsteps - 1), V0);
-            scores(K0, c0);
-            load_k(min(st + 4, nsteps - 1), K0);
+            scores(K, c0);
+            load_k(min(st + 3, nsteps - 1), K);
             finish(st + 1, V1, c1);
             if (st + 2 >= nsteps) break;
         }
@@ -822,25 +857,30 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             *reinterpret_cast<float2*>(P) = make_float2(m_run, l_run);
         }
     }
-    // result rows 4 sl + v = (group sl, query v); column j16 of tile mt is
-    // coordinate 8 j16 + mt, which belongs to group j16 / 4
-    // value codes entered as 72 + c: remove 72 times row (g, v)'s operand sum
+    // result rows 4 sl + v = (group sl, query v); column j16 of tile (hv, mt)
+    // is coordinate 128 hv + 8 j16 + mt, of group (128 hv + 8 j16) / G.
+    // Value codes entered as 72 + c: remove 72 times row (g, v)'s operand sum.
     vb += __shfl_xor(vb, 16);
     vb += __shfl_xor(vb, 32);
     float vbias[RP];
 #pragma unroll
     for (int v = 0; v < RP; v++) vbias[v] = 72.0f * __shfl(vb, 4 * sl + v);
 #pragma unroll
-    for (int mt = 0; mt < 8; mt++)
+    for (int hv = 0; hv < NVD; hv++) {
 #pragma unroll
-        for (int v = 0; v < RP; v++) acc[mt][v] -= vbias[v];
-    if (sl == (j16 >> 2)) {
+        for (int mt = 0; mt < 8; mt++)
 #pragma unroll
-        for (int v = 0; v < RP; v++) {
-            if (v >= nr) break;
-            float* P = a.ws + ((((int64_t)lh * a.R + r0 + v) * a.parts) + part0) * (D + 4) + 4 + 8 * j16;
-            *reinterpret_cast<float4*>(P) = make_float4(acc[0][v], acc[1][v], acc[2][v], acc[3][v]);
-            *reinterpret_cast<float4*>(P + 4) = make_float4(acc[4][v], acc[5][v], acc[6][v], acc[7][v]);
+            for (int v = 0; v < RP; v++) acc[hv][mt][v] -= vbias[v];
+        if (sl == (128 * hv + 8 * j16) / G) {
+#pragma unroll
+            for (int v = 0; v < RP; v++) {
+                if (v >= nr) break;
+                float* P = a.ws + ((((int64_t)lh * a.R + r0 + v) * a.parts) + part0) * (D + 4) + 4 + 128 * hv + 8 * j16;
+                *reinterpret_cast<float4*>(P) =
+                    make_float4(acc[hv][0][v], acc[hv][1][v], acc[hv][2][v], acc[hv][3][v]);
+                *reinterpret_cast<float4*>(P + 4) =
+                    make_float4(acc[hv][4][v], acc[hv][5][v], acc[hv][6][v], acc[hv][7][v]);
+            }
         }
     }
 }
@@ -921,10 +961,10 @@ template <int D, int RP>
 hipError_t launch_part(const AttnArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)((int64_t)a.L * a.H * a.S), (unsigned)((a.R + RP - 1) / RP));
-    if constexpr (D == 128) {
+    if constexpr (D == 128 || D == 256) {
         if (a.mfma) {
             const dim3 mgrid((unsigned)((int64_t)a.L * (a.H / a.hb) * a.S), (unsigned)((a.R + 3) / 4));
-            hipLaunchKernelGGL(attend_partial_mfma_kernel, mgrid, dim3(64 * kAttnMfmaWaves), 0, s, a);
+            hipLaunchKernelGGL((attend_partial_mfma_kernel<D>), mgrid, dim3(64 * kAttnMfmaWaves), 0, s, a);
             return hipGetLastError();
         }
     }

@@ -85,11 +85,18 @@ def test_attend_query_groups_over_passes(R):
     run_case(2, 257, 3, R, 128, 32, seed=40 + R)
 
 
+@pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("H", [1, 4, 6, 8, 12, 16])
-def test_attend_head_groups(H):
-    # head_dim 128 / group 32 blocks hold hb = 8, 4, 2 or 1 KV heads (the
-    # largest dividing H) times 8 / hb token sub-ranges
-    run_case(2, 333, H, 4, 128, 32, seed=60 + H, lengths=[333, 97])
+def test_attend_head_groups(H, D):
+    # matrix-core blocks (head_dim 128 / group 32, head_dim 256 / group 64)
+    # hold hb = 8, 4, 2 or 1 KV heads (the largest dividing H) times 8 / hb
+    # token sub-ranges
+    run_case(2, 333, H, 4, D, D // 4, seed=60 + H + D, lengths=[333, 97])
+
+
+@pytest.mark.parametrize("R", [3, 8])
+def test_attend_head_dim_256_query_passes(R):
+    run_case(2, 257, 2, R, 256, 64, seed=80 + R)
 
 
 def test_attend_ragged_lengths_and_empty():
