@@ -107,7 +107,7 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
         "dequantize_mxfp4": ("kvq::dequantize_kernel<128, 32, true, 4, true, false>", nv * (2 * D + D // 2 + D // 32)),
         "quantize_srft": ("kvq::quantize_kernel<128, 32, true, 4, false, true>", nv * bytes_per_vector(D, G)),
         "dequantize_srft": ("kvq::dequantize_kernel<128, 32, true, 4, false, true>", nv * bytes_per_vector(D, G)),
-        "attend_partial": ("kvq::attend_partial_mfma_kernel", att),
+        "attend_partial": ("kvq::attend_partial_mfma_kernel<128>", att),
         "attend_combine": ("kvq::attend_combine_kernel<128>", None),
         "vq_encode": ("kvq::vq_encode_kernel<128, false>", nk * (2 * D + 2 * (D // 8))),
         "vq_decode": ("kvq::vq_decode_lds_kernel<128, false>", nk * (2 * D + 2 * (D // 8))),
@@ -472,6 +472,27 @@ def bench_small(torch, kvq, synth, dev, args):
                                   "hip_graph_us_per_step": round(gms * 1e3, 1),
                                   "hip_graph_us_per_layer_K_and_V": round(gms * 1e3 / L, 2)}
             del g
+            # decode attention over the whole cache: 4 query heads on the one
+            # KV head, all layers in one call (matrix-core kernel, head_dim 256)
+            R = 4
+            qg = torch.Generator(device="cpu").manual_seed(2026)
+            q = torch.randn((L, H * R, D), generator=qg).to(torch.float16).to(dev)
+            kc, ks = caches["K"]
+            vc, vs = caches["V"]
+            ws = torch.empty(kvq.attend_decode_workspace_bytes(L, T, H, D, R), dtype=torch.uint8, device=dev)
+            ao = torch.empty((L, H * R, D), dtype=torch.float16, device=dev)
+
+            def attend():
+                kvq.attend_decode(q, kc, ks, vc, vs, inp["lam_K"], inp["lam_V"], inp["signs"], G, out=ao,
+                                  workspace=ws, stream=stream)
+            attend()
+            torch.cuda.synchronize()
+            ams = timed(attend, 20, False)
+            abytes = 2 * L * T * H * (D // 2 + 2 * (D // G))
+            r["decode_attention"] = {"layers": L, "tokens": T, "q_per_kv": R, "ms": round(ams, 4),
+                                     "GB_per_s": round(abytes / (ams * 1e-3) / 1e9, 1),
+                                     "note": "one call over all layers; small, so launch and tail bound"}
+            del ws, ao
         res[name] = r
         del inp
         torch.cuda.empty_cache()
