@@ -276,7 +276,11 @@ kvq_status kvq_kmeans_step(kvq_shape shape, kvq_view x_f16, const float* lambda,
  *   gets zeros.
  * It runs in the rotated domain: each query is rotated once (by the key
  * cache's lambda and signs), keys are never inverse-transformed, and the
- * weighted value sum is inverse-transformed once per query.
+ * weighted value sum is inverse-transformed once per query.  Scores,
+ * weights and sums are fp32-accurate: for head_dim 128 with groups of 32 and
+ * head_dim 256 with groups of 64 both contractions run on the matrix cores
+ * with the query and the weights split into fp16 hi + lo halves and the
+ * codes as exact fp16 integers; other shapes run on the vector ALUs in fp32.
  *   shape        layers = outer index (layers, or sequences sharing one
  *                layer), tokens = context capacity T, heads = KV heads,
  *                head_dim = D.
