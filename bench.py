@@ -467,11 +467,42 @@ def bench_small(torch, kvq, synth, dev, args):
             g.replay()
             torch.cuda.synchronize()
             gms = timed(g.replay, 20, False)
+            # K and V in one launch per layer: a cache laid out [L, T, 2H, .]
+            # holds K in heads 0..H-1 and V in heads H..2H-1 (attention takes
+            # the two halves as strided views), lambda [L, 2H, D] likewise
+            kv_codes = torch.empty((L, T, 2 * H, D // 2), dtype=torch.uint8, device=dev)
+            kv_scales = torch.empty((L, T, 2 * H, D // G), dtype=torch.float16, device=dev)
+            tok_kv = torch.cat([tok["K"], tok["V"]], dim=2).contiguous()
+            lam_kv = [torch.cat([lam1["K"][l], lam1["V"][l]], dim=1).contiguous() for l in range(L)]
+
+            def step_kv(st=stream):
+                for l in range(L):
+                    kvq.quantize(tok_kv[l:l + 1], lam_kv[l], inp["signs"], G, codes=kv_codes[l:l + 1, T - 1:T],
+                                 scales=kv_scales[l:l + 1, T - 1:T], stream=st)
+
+            def graph_step_kv():
+                step_kv(torch.cuda.current_stream())
+            step_kv()
+            torch.cuda.synchronize()
+            kms = timed(step_kv, 10, False)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                graph_step_kv()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2):
+                graph_step_kv()
+            g2.replay()
+            torch.cuda.synchronize()
+            kgms = timed(g2.replay, 20, False)
             r["decode_append"] = {"us_per_layer_K_and_V": round(sms * 1e3 / L, 2), "us_per_step": round(sms * 1e3, 1),
                                   "layers": L, "note": "two launches per layer; launch-bound",
                                   "hip_graph_us_per_step": round(gms * 1e3, 1),
-                                  "hip_graph_us_per_layer_K_and_V": round(gms * 1e3 / L, 2)}
-            del g
+                                  "hip_graph_us_per_layer_K_and_V": round(gms * 1e3 / L, 2),
+                                  "kv_in_one_launch_us_per_step": round(kms * 1e3, 1),
+                                  "kv_in_one_launch_hip_graph_us_per_step": round(kgms * 1e3, 1)}
+            del g, g2, kv_codes, kv_scales
             # decode attention over the whole cache: 4 query heads on the one
             # KV head, all layers in one call (matrix-core kernel, head_dim 256)
             R = 4

@@ -112,6 +112,11 @@ typedef struct kvq_view {
  *   group      G, a power of two with 8 <= G <= head_dim.
  *   codes_u8   output view of D/2-byte rows; 16-byte aligned data and strides.
  *   scales_f16 output view of D/G-element fp16 rows; 2-byte aligned.
+ * Heads are independent, so a layer's K and V can go through one call: with
+ * the cache laid out [layers, tokens, 2*heads, .] (K in heads 0..H-1, V in
+ * heads H..2H-1) and lambda [layers, 2*heads, head_dim], one decode-time
+ * append per layer replaces two; kvq_attend_decode takes the two halves as
+ * views with the same strides.
  */
 kvq_status kvq_quantize(kvq_shape shape, kvq_view x_f16, const float* lambda,
                         const int8_t* signs, int32_t group, kvq_view codes_u8,

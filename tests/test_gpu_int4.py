@@ -142,6 +142,42 @@ def test_decode_append_replayed_from_hip_graph():
             assert torch.equal(caches[t][1][:, pos:pos + 1], want_s), (pos, t)
 
 
+def test_decode_append_k_and_v_in_one_call():
+    """K and V of a new token appended by one call per layer into a cache
+    laid out [L, T, 2H, .] (K in heads 0..H-1, V in heads H..2H-1, lambda
+    [L, 2H, D]): each half equals the separate K and V appends, and the
+    attention entry point reads the halves as strided views."""
+    dev = device()
+    cfg = synth.config("gemma-3-1b", T=40)
+    inp = synth.make_inputs(cfg, dev)
+    G, t = cfg.G, 33
+    L, T, H, D = inp["K"].shape
+    s = inp["signs"]
+    kv_codes = torch.zeros((L, T, 2 * H, D // 2), dtype=torch.uint8, device=dev)
+    kv_scales = torch.zeros((L, T, 2 * H, D // G), dtype=torch.float16, device=dev)
+    tok = torch.cat([inp["K"][:, t:t + 1], inp["V"][:, t:t + 1]], dim=2).contiguous()
+    lam = torch.cat([inp["lam_K"], inp["lam_V"]], dim=1).contiguous()
+    for l in range(L):
+        kvq.append_quantize(tok[l:l + 1], kv_codes[l:l + 1], kv_scales[l:l + 1], t, lam[l:l + 1], s, G)
+    kc, ks = kvq.quantize(inp["K"][:, t:t + 1], inp["lam_K"], s, G)
+    vc, vs = kvq.quantize(inp["V"][:, t:t + 1], inp["lam_V"], s, G)
+    torch.cuda.synchronize()
+    assert torch.equal(kv_codes[:, t:t + 1, :H], kc) and torch.equal(kv_scales[:, t:t + 1, :H], ks)
+    assert torch.equal(kv_codes[:, t:t + 1, H:], vc) and torch.equal(kv_scales[:, t:t + 1, H:], vs)
+    # the whole prefix through the same layout, then attention over the halves
+    full = torch.cat([inp["K"], inp["V"]], dim=2).contiguous()
+    kvq.quantize(full, lam, s, G, codes=kv_codes, scales=kv_scales)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    q = torch.randn((L, H * 4, D), generator=g).to(torch.float16).to(dev)
+    o1 = kvq.attend_decode(q, kv_codes[:, :, :H], kv_scales[:, :, :H], kv_codes[:, :, H:], kv_scales[:, :, H:],
+                           inp["lam_K"], inp["lam_V"], s, G)
+    kc, ks = kvq.quantize(inp["K"], inp["lam_K"], s, G)
+    vc, vs = kvq.quantize(inp["V"], inp["lam_V"], s, G)
+    o2 = kvq.attend_decode(q, kc, ks, vc, vs, inp["lam_K"], inp["lam_V"], s, G)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
 # ------------------------------------------------------- instantiations
 @pytest.mark.parametrize("H", [2, 3])           # token-major (H | 16) and head-major items
 @pytest.mark.parametrize("D,G", [(D, G) for D in (64, 128, 256) for G in (8, 16, 32, 64, 128, 256) if G <= D])
