@@ -352,6 +352,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
         if (it.key != cur_key) {
             cur_key = it.key;
             load_fwd_mult<D>(a.lambda + lambda_row<TM>(it, lm, a), a.signs, q, m);
+            if constexpr (FT) {
+#pragma unroll
+                for (int i = 0; i < N; i++) m[i] *= 0.70710678118654752440f;   // the SRFT's 1/sqrt2
+            }
         }
 #pragma unroll
         for (int j = 0; j < NJ; j++) {
@@ -360,8 +364,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
             for (int k = 0; k < 4; k++) {
                 const int r = j * 8 + 2 * k;
                 if constexpr (FT) {
-                    v[r] = lo_half(w[k]) * m[r];
-                    v[r + 1] = hi_half(w[k]) * m[r + 1];
+                    v[r] = fmaf(lo_half(w[k]), m[r], 0.0f);           // one v_fma_mix each
+                    v[r + 1] = fmaf(hi_half(w[k]), m[r + 1], 0.0f);
                 } else {
                     const float b = fmaf(hi_half(w[k]), m[r + 1], 0.0f);   // one v_fma_mix
                     v[r] = fmaf(lo_half(w[k]), m[r], b);
@@ -619,6 +623,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
         if (it.key != cur_key) {
             cur_key = it.key;
             load_inv_mult<D>(a.lambda + lambda_row<TM>(it, lm, a), a.signs, q, lane_sign, m);
+            if constexpr (FT) {
+#pragma unroll
+                for (int i = 0; i < N; i++) m[i] *= 0.70710678118654752440f;   // the SRFT's 1/sqrt2
+            }
         }
 #pragma unroll
         for (int j = 0; j < NJ; j++) {

@@ -324,7 +324,8 @@ __device__ __forceinline__ void unpack_twiddle(int q, float scale, float& cw, fl
 }
 
 // Forward SRFT of the quad's vector, in place on v (natural layout, values
-// already multiplied by s * lambda / sqrt(D)): afterwards v holds y times
+// already multiplied by s * lambda / sqrt(D), and by 1/sqrt2, which the
+// unpacking's weights would otherwise apply): afterwards v holds y times
 // sigma(q).  row: the quad's LDS row of N float2.
 template <int D>
 __device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, const Tw<D, -1>& tw)
@@ -340,20 +341,20 @@ __device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, c
     fft_dit<D, -1>(c, q, tw);
     float pc[D / 4];
     hermitian_partners<D>(c, pc, q, true);
-    constexpr float r = 0.70710678118654752440f;
+    constexpr float sqrt2 = 1.41421356237309504880f;
     static_for<0, P>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
         float cw, sw;
-        unpack_twiddle<D, i>(q, r, cw, sw);
+        unpack_twiddle<D, i>(q, 1.0f, cw, sw);
         const float a = c[i], b = c[P + i], cc = pc[i], d = pc[P + i];
         const float s1 = a + cc, d1 = a - cc, s2 = b + d, d2 = b - d;
-        float y0 = fmaf(cw, s2, fmaf(-sw, d1, s1 * r));
-        float y1 = fmaf(-cw, d1, fmaf(-sw, s2, d2 * r));
+        float y0 = fmaf(cw, s2, fmaf(-sw, d1, s1));
+        float y1 = fmaf(-cw, d1, fmaf(-sw, s2, d2));
         if constexpr (i == 0) {
             // k = 0 (lane 0): X_0 and X_{D/2} are real, from Z_0 alone
             if (q == 0) {
-                y0 = a + b;
-                y1 = a - b;
+                y0 = (a + b) * sqrt2;
+                y1 = (a - b) * sqrt2;
             }
         }
         v[8 * (i / 4) + 2 * (i % 4)] = y0;
@@ -362,9 +363,9 @@ __device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, c
 }
 
 // Inverse SRFT of the quad's vector, in place on v (natural layout, true
-// rotated-domain values): afterwards v holds sqrt(D) times the unscaled
+// rotated-domain values): afterwards v holds sqrt(2 D) times the unscaled
 // vector s * lambda * xhat, times sigma(q); the consumer multiplies by
-// s / (lambda sqrt(D)) and sigma(q).
+// s / (lambda sqrt(2 D)) and sigma(q).
 template <int D>
 __device__ __forceinline__ void inverse(float (&v)[D / 4], float2* row, int q, const Tw<D, 1>& tw)
 {
@@ -377,20 +378,20 @@ __device__ __forceinline__ void inverse(float (&v)[D / 4], float2* row, int q, c
     }
     float py[D / 4];
     hermitian_partners<D>(y, py, q, false);
-    constexpr float r = 0.70710678118654752440f;
+    constexpr float sqrt2 = 1.41421356237309504880f;
     float c[D / 4];
     static_for<0, P>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
         float cw, sw;
-        unpack_twiddle<D, i>(q, r, cw, sw);
+        unpack_twiddle<D, i>(q, 1.0f, cw, sw);
         const float p = y[i], rr = y[P + i], u = py[i], w = py[P + i];
         const float sp = p + u, dp = p - u, sr = rr + w, dr = rr - w;
-        float zr = fmaf(-sw, dp, fmaf(-cw, sr, sp * r));
-        float zi = fmaf(cw, dp, fmaf(-sw, sr, dr * r));
+        float zr = fmaf(-sw, dp, fmaf(-cw, sr, sp));
+        float zi = fmaf(cw, dp, fmaf(-sw, sr, dr));
         if constexpr (i == 0) {
             if (q == 0) {
-                zr = p + rr;
-                zi = p - rr;
+                zr = (p + rr) * sqrt2;
+                zi = (p - rr) * sqrt2;
             }
         }
         c[i] = zr;
