@@ -702,6 +702,14 @@ def bench_vq(torch, kvq, synth, dev, args):
                 r["includes"] = "assignment (the encoder) + accumulate + finalize"
         else:
             ib = 2 if name == "decode" else 1
+            if name == "value_encode_u8":
+                # a search against 256 centroids: MFMA contraction plus the
+                # VALU argmax, not an HBM stream
+                flop = nkeys * (D // sub) * cfg.v_centroids * sub * 2
+                tf = flop / (avg * 1e-3) / 1e12
+                r.update({"algorithmic_TFLOP": round(flop / 1e12, 4), "TFLOP_per_s": round(tf, 2),
+                          "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+                          "executed_frac_of_fp16_mfma_peak": round(2.25 * tf / FP16_MFMA_PEAK_TFLOPS, 4)})
             byt = nkeys * (2 * D + ib * (D // sub))
             r.update({"GB_per_s": round(byt / (avg * 1e-3) / 1e9, 1),
                       "frac_of_hbm_peak": round(byt / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
