@@ -680,13 +680,14 @@ def test_attend_zero_query_is_mean_of_values():
         assert np.allclose(out[0, j], want[0, j // 3], rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("D,G", [(128, 32), (256, 64)])
 @pytest.mark.parametrize("R", [1, 2, 4])
-def test_attend_matches_torch_sdpa(R):
+def test_attend_matches_torch_sdpa(R, D, G):
     # the attention step against torch's scaled_dot_product_attention in
     # float64 on the (separately pinned) dequantized cache; GQA maps query
     # head j to KV head j // R; ragged lengths attend to a prefix
     import torch
-    L, T, H, D, G = 3, 50, 3, 128, 32
+    L, T, H = 3, 50, 3
     c = attn_case(L, T, H, R, D, G, seed=10 + R)
     lengths = np.array([50, 17, 1], np.int32)
     scale = 0.0883
