@@ -275,3 +275,23 @@ def test_attend_huge_rotated_queries():
     out64 = oracle.attend_decode(bits(q), kc.cpu().numpy(), bits(ks), vc.cpu().numpy(), bits(vs),
                                  lk.cpu().numpy(), lv.cpu().numpy(), s.cpu().numpy(), G, 1.0 / D ** 0.5)
     compare(out, out64, lv, H, R, "huge rotated queries")
+
+
+def test_attend_seeded_shape_sweep():
+    """Twenty seeded random shapes (head dims 64/128/256 with every group the
+    kernels take, 1-16 KV heads, 1-9 query heads per KV head, short and
+    ragged contexts, random lengths including zero) against the oracle: both
+    kernel versions, every head-group size and pass count, partial steps."""
+    rng = np.random.default_rng(2024)
+    for case in range(20):
+        D = int(rng.choice([64, 128, 256]))
+        G = D // 4 if case % 2 == 0 else int(rng.choice([g for g in (8, 16, 32, 64, 128, 256) if g <= D]))
+        H = int(rng.integers(1, 17))
+        R = int(rng.integers(1, 10))
+        L = int(rng.integers(1, 4))
+        T = int(rng.integers(1, 400))
+        lengths = [int(rng.integers(0, T + 1)) for _ in range(L)]
+        if case % 5 == 0:
+            lengths[0] = 0
+        log("sweep case %d: L=%d T=%d H=%d R=%d D=%d G=%d lengths=%s" % (case, L, T, H, R, D, G, lengths))
+        run_case(L, T, H, R, D, G, seed=900 + case, lengths=lengths)
