@@ -383,17 +383,18 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
 // query r restricted to group g (zero on the other slices) and the result is
 // the per-group partial dot products, which the group scales then weight and
 // a reduce-scatter over the quad of a query's four groups sums, leaving one
-// token's score per lane for the softmax.  The query is
-// split into fp16 hi + lo halves (two MFMAs), so the dot products are fp32
-// accurate.  A lane's 16 code
-// bytes of group sl feed four MFMAs, one dword each.
+// token's score per lane for the softmax.  The query is split into fp16
+// hi + lo halves (two MFMAs), so the dot products are fp32 accurate.  A
+// lane's G/2 code bytes of group sl feed G/8 MFMAs, one dword each (four at
+// head_dim 128, eight at 256).
 //
 // Values.  Rows are (group g', query r) = 4g' + r, k is the 32 tokens, and
-// columns are coordinates: tile m, column j is coordinate 8j + m.  A row
-// (g', r) is p_r * vscale_g' over the tokens (hi + lo halves), so the result's
-// row (g(c), r) is query r's weighted sum of coordinate c; the other rows are
-// discarded.  A lane loads one dword (coordinates 8j..8j+7) of each of its
-// slice's 8 tokens and regroups nibbles with v_perm.
+// columns are coordinates: tile (h, m), column j is coordinate
+// 128h + 8j + m (h = 0 only at head_dim 128).  A row (g', r) is
+// p_r * vscale_g' over the tokens (hi + lo halves), so the result's row
+// (g(c), r) is query r's weighted sum of coordinate c; the other rows are
+// discarded.  A lane loads one dword (coordinates 128h + 8j .. + 7) of each of
+// its slice's 8 tokens and regroups nibbles with v_perm.
 //
 // Within every 8-element operand the k order is (0,4,1,5,2,6,3,7), the order
 // in which nibble pairs come out of a masked dword; A and B use the same order.
