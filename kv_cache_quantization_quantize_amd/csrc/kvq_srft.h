@@ -132,6 +132,16 @@ __device__ __forceinline__ void cmul(float& xr, float& xi, float wr, float wi)
     xr = r;
 }
 
+// (xr, xi) *= SIGN * i where `on`, else unchanged: a select per part, exact.
+template <int SIGN>
+__device__ __forceinline__ void times_i_where(float& xr, float& xi, bool on)
+{
+    const float r = on ? (SIGN < 0 ? xi : -xi) : xr;
+    const float i = on ? (SIGN < 0 ? -xr : xr) : xi;
+    xr = r;
+    xi = i;
+}
+
 // Natural order -> bit-reversed order through the quad's LDS row (N entries).
 template <int D>
 __device__ __forceinline__ void to_bit_reversed(float (&c)[D / 4], float2* row, int q)
@@ -160,8 +170,8 @@ template <int D, int SIGN>
 struct Tw {
     static constexpr int N = D / 2, LOGN = ilog2(N);
     static constexpr int NJT = LOGN > 4 ? 4 * ((1 << (LOGN - 4)) - 1) : 0;
-    float l0r[3], l0i[3];            // lane bit 0 stage, f = 1..3
-    float l1r[4], l1i[4];            // lane bit 1 stage, f = 0..3
+    float l0r[2], l0i[2];            // lane bit 0 stage, f = 1 and 3
+    float l1r[3], l1i[3];            // lane bit 1 stage, f = 1..3
     float jr[NJT > 0 ? NJT : 1], ji[NJT > 0 ? NJT : 1];
 };
 
@@ -175,17 +185,18 @@ __device__ __forceinline__ Tw<D, SIGN> make_twiddles(int q)
     constexpr int N = T::N, LOGN = T::LOGN;
     T t;
     const bool up0 = (q & 1) != 0, up1 = (q & 2) != 0, odd = (q & 1) != 0;
+    // f = 2 of the lane bit 0 stage and f = 0 of the lane bit 1 stage
+    // multiply by SIGN * i or 1 (times_i_where), so they need no registers
+    static_for<0, 2>([&](auto kk) {
+        constexpr int e = (2 * decltype(kk)::value + 1) * (N / 8);
+        t.l0r[decltype(kk)::value] = up0 ? (float)cos2pi(e, N) : 1.0f;
+        t.l0i[decltype(kk)::value] = up0 ? (float)(SIGN * sin2pi(e, N)) : 0.0f;
+    });
     static_for<1, 4>([&](auto kk) {
         constexpr int k = decltype(kk)::value;
-        constexpr int e = k * (N / 8);
-        t.l0r[k - 1] = up0 ? (float)cos2pi(e, N) : 1.0f;
-        t.l0i[k - 1] = up0 ? (float)(SIGN * sin2pi(e, N)) : 0.0f;
-    });
-    static_for<0, 4>([&](auto kk) {
-        constexpr int k = decltype(kk)::value;
         constexpr int e0 = k * (N / 16), e1 = (k + 4) * (N / 16);
-        t.l1r[k] = up1 ? (odd ? (float)cos2pi(e1, N) : (float)cos2pi(e0, N)) : 1.0f;
-        t.l1i[k] = up1 ? (odd ? (float)(SIGN * sin2pi(e1, N)) : (float)(SIGN * sin2pi(e0, N))) : 0.0f;
+        t.l1r[k - 1] = up1 ? (odd ? (float)cos2pi(e1, N) : (float)cos2pi(e0, N)) : 1.0f;
+        t.l1i[k - 1] = up1 ? (odd ? (float)(SIGN * sin2pi(e1, N)) : (float)(SIGN * sin2pi(e0, N))) : 0.0f;
     });
     static_for<4, LOGN>([&](auto bb) {
         constexpr int b = decltype(bb)::value;
@@ -206,9 +217,9 @@ __device__ __forceinline__ Tw<D, SIGN> make_twiddles(int q)
     // opaque to the optimiser, so that the values stay in registers across
     // the caller's loop instead of being rebuilt from constants per use
 #pragma unroll
-    for (int k = 0; k < 3; k++) asm volatile("" : "+v"(t.l0r[k]), "+v"(t.l0i[k]));
+    for (int k = 0; k < 2; k++) asm volatile("" : "+v"(t.l0r[k]), "+v"(t.l0i[k]));
 #pragma unroll
-    for (int k = 0; k < 4; k++) asm volatile("" : "+v"(t.l1r[k]), "+v"(t.l1i[k]));
+    for (int k = 0; k < 3; k++) asm volatile("" : "+v"(t.l1r[k]), "+v"(t.l1i[k]));
 #pragma unroll
     for (int k = 0; k < T::NJT; k++) asm volatile("" : "+v"(t.jr[k]), "+v"(t.ji[k]));
     return t;
@@ -246,20 +257,23 @@ __device__ __forceinline__ void fft_dit(float (&c)[D / 4], int q, const Tw<D, SI
             c[b] = ar - tr; c[P + b] = ai - ti;
         }
     }
-    // point bit 2 (lane bit 0): upper lanes (q & 1) multiply by omega^(f N/8)
+    // point bit 2 (lane bit 0): upper lanes (q & 1) multiply by omega^(f N/8);
+    // omega^(N/4) = SIGN i
     {
         static_for<0, P>([&](auto ii) {
             constexpr int i = decltype(ii)::value;
-            if constexpr (i % 4 != 0) cmul(c[i], c[P + i], tw.l0r[i % 4 - 1], tw.l0i[i % 4 - 1]);
+            if constexpr (i % 4 == 2) times_i_where<SIGN>(c[i], c[P + i], (q & 1) != 0);
+            else if constexpr (i % 4 != 0) cmul(c[i], c[P + i], tw.l0r[i % 4 / 2], tw.l0i[i % 4 / 2]);
         });
         bfly_quad1(c, (q & 1) ? -1.0f : 1.0f);
     }
     // point bit 3 (lane bit 1): upper lanes (q & 2) multiply by
-    // omega^((f + 4 (q & 1)) N / 16)
+    // omega^((f + 4 (q & 1)) N / 16), which for f = 0 is 1 or SIGN i
     {
         static_for<0, P>([&](auto ii) {
             constexpr int i = decltype(ii)::value;
-            cmul(c[i], c[P + i], tw.l1r[i % 4], tw.l1i[i % 4]);
+            if constexpr (i % 4 == 0) times_i_where<SIGN>(c[i], c[P + i], q == 3);
+            else cmul(c[i], c[P + i], tw.l1r[i % 4 - 1], tw.l1i[i % 4 - 1]);
         });
         bfly_quad2(c, (q & 2) ? -1.0f : 1.0f);
     }
@@ -272,27 +286,30 @@ __device__ __forceinline__ void fft_dit(float (&c)[D / 4], int q, const Tw<D, SI
             constexpr int i = decltype(ii)::value;
             constexpr int j = i / 4, f = i % 4;
             if constexpr ((j & hj) == 0) {
+                // a + w b by two fmas per part, then a - w b = 2a - (a + w b):
+                // six operations instead of a complex multiply and four adds
                 constexpr int ib = i + 4 * hj;
                 constexpr int x = tw_j_base(b) + f + 4 * (j % hj);
-                float tr = c[ib], ti = c[P + ib];
-                cmul(tr, ti, tw.jr[x], tw.ji[x]);
-                const float ar = c[i], ai = c[P + i];
-                c[i] = ar + tr; c[P + i] = ai + ti;
-                c[ib] = ar - tr; c[P + ib] = ai - ti;
+                const float wr = tw.jr[x], wi = tw.ji[x];
+                const float ar = c[i], ai = c[P + i], br = c[ib], bi = c[P + ib];
+                const float yr = fmaf(-wi, bi, fmaf(wr, br, ar));
+                const float yi = fmaf(wi, br, fmaf(wr, bi, ai));
+                c[i] = yr; c[P + i] = yi;
+                c[ib] = fmaf(2.0f, ar, -yr); c[P + ib] = fmaf(2.0f, ai, -yi);
             }
         });
     });
 }
 
 // Fetch, for every register i of this lane (point k = 16j + 4q + f), the
-// value of point N - k from the quad (both parts), as the lane would see it
-// in its own sign convention when `signed_fix` (values carrying sigma(q)).
+// value of point N - k from the quad (both parts).  For values carrying
+// sigma(q), the f = 0 partners of lanes 1 and 3 come from a lane of the other
+// sign: the caller multiplies them by -1 there.
 template <int D>
-__device__ __forceinline__ void hermitian_partners(const float (&c)[D / 4], float (&pc)[D / 4], int q, bool signed_fix)
+__device__ __forceinline__ void hermitian_partners(const float (&c)[D / 4], float (&pc)[D / 4], int q)
 {
     constexpr int P = D / 8, NJ = D / 32;
     const bool q0 = q == 0;
-    const float fix = (signed_fix && (q & 1)) ? -1.0f : 1.0f;
     static_for<0, P>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
         constexpr int j = i / 4, f = i % 4;
@@ -304,8 +321,8 @@ __device__ __forceinline__ void hermitian_partners(const float (&c)[D / 4], floa
             constexpr int s1 = 4 * (NJ - 1 - j), s0 = 4 * ((NJ - j) % NJ);
             const float r1 = dpp<kQuadNegate>(c[s1]), i1 = dpp<kQuadNegate>(c[P + s1]);
             const float r0 = dpp<kQuadNegate>(c[s0]), i0 = dpp<kQuadNegate>(c[P + s0]);
-            pc[i] = (q0 ? r0 : r1) * fix;
-            pc[P + i] = (q0 ? i0 : i1) * fix;
+            pc[i] = q0 ? r0 : r1;
+            pc[P + i] = q0 ? i0 : i1;
         }
     });
 }
@@ -340,14 +357,21 @@ __device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, c
     to_bit_reversed<D>(c, row, q);
     fft_dit<D, -1>(c, q, tw);
     float pc[D / 4];
-    hermitian_partners<D>(c, pc, q, true);
+    hermitian_partners<D>(c, pc, q);
+    const float fix = (q & 1) ? -1.0f : 1.0f;      // f = 0 partners' sign
     constexpr float sqrt2 = 1.41421356237309504880f;
     static_for<0, P>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
         float cw, sw;
         unpack_twiddle<D, i>(q, 1.0f, cw, sw);
         const float a = c[i], b = c[P + i], cc = pc[i], d = pc[P + i];
-        const float s1 = a + cc, d1 = a - cc, s2 = b + d, d2 = b - d;
+        float s1, d1, s2, d2;
+        if constexpr (i % 4 == 0) {
+            s1 = fmaf(fix, cc, a); d1 = fmaf(-fix, cc, a);
+            s2 = fmaf(fix, d, b); d2 = fmaf(-fix, d, b);
+        } else {
+            s1 = a + cc; d1 = a - cc; s2 = b + d; d2 = b - d;
+        }
         float y0 = fmaf(cw, s2, fmaf(-sw, d1, s1));
         float y1 = fmaf(-cw, d1, fmaf(-sw, s2, d2));
         if constexpr (i == 0) {
@@ -377,7 +401,7 @@ __device__ __forceinline__ void inverse(float (&v)[D / 4], float2* row, int q, c
         y[P + i] = v[8 * (i / 4) + 2 * (i % 4) + 1];
     }
     float py[D / 4];
-    hermitian_partners<D>(y, py, q, false);
+    hermitian_partners<D>(y, py, q);
     constexpr float sqrt2 = 1.41421356237309504880f;
     float c[D / 4];
     static_for<0, P>([&](auto ii) {
