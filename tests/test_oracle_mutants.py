@@ -125,7 +125,7 @@ BATTERY = [
     ("test_kmeans_update_is_the_sse_minimiser_and_lloyd_descends", {}),
     ("test_attend_single_token_returns_its_value", {}),
     ("test_attend_zero_query_is_mean_of_values", {}),
-    ("test_attend_matches_torch_sdpa", {"R": 4}),
+    ("test_attend_matches_torch_sdpa", {"R": 4, "D": 128, "G": 32}),
     ("test_attend_large_scores_stay_finite", {}),
     ("test_attend_empty_context_gives_zeros", {}),
 ]
