@@ -157,9 +157,10 @@ struct QuantShape {
 
 // Item loop shared by both kernels (see the comment below).  With PREFETCH
 // the next item's loads are issued before the current item is finished,
-// using a second register buffer; without it (head_dim 256, where a second
-// buffer would not fit in registers) each item's loads are issued right
-// before its first stage, and only the stores are deferred.
+// using a second register buffer; without it (head_dim 256, and the SRFT
+// dequantizer, where a second buffer would cost a wave per SIMD) each item's
+// loads are issued right before its first stage, and only the stores are
+// deferred.
 template <typename Buf, typename Out, int N, bool PREFETCH, typename Load, typename First, typename Store,
           typename Finish>
 __device__ __forceinline__ void run_pipeline(int begin, int end, Load&& load, First&& first_stage,
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
         }
     };
 
-    run_pipeline<uint4[NJ], Out, N, (D <= 128 && !FT)>(begin, end, load, first_stage, store, finish);
+    run_pipeline<uint4[NJ], Out, N, (D <= 128)>(begin, end, load, first_stage, store, finish);
 }
 
 // ---------------------------------------------------------------------------
