@@ -670,12 +670,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
             const uint32_t lo = wb & 0x0f0f0f0fu;            // n of elements 0,2,4,6
             const uint32_t hi = (wb >> 4) & 0x0f0f0f0fu;     // n of elements 1,3,5,7
             if constexpr (FT) {
-                // the plain values yhat = (n - 8) * sc
+                // the plain values yhat = (n - 8) * sc.  With lo and hi opaque,
+                // each byte converts with one v_cvt_f32_ubyte<k> (the compiler
+                // would otherwise extract every nibble with a v_bfe first)
+                uint32_t lo8 = lo, hi8 = hi;
+                asm volatile("" : "+v"(lo8), "+v"(hi8));
                 const float off8 = -8.0f * sc;
 #pragma unroll
                 for (int k = 0; k < 4; k++) {
-                    v[j * 8 + 2 * k] = fmaf((float)((lo >> (8 * k)) & 0xffu), sc, off8);
-                    v[j * 8 + 2 * k + 1] = fmaf((float)((hi >> (8 * k)) & 0xffu), sc, off8);
+                    v[j * 8 + 2 * k] = fmaf((float)((lo8 >> (8 * k)) & 0xffu), sc, off8);
+                    v[j * 8 + 2 * k + 1] = fmaf((float)((hi8 >> (8 * k)) & 0xffu), sc, off8);
                 }
                 continue;
             }
