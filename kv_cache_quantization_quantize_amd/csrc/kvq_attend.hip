@@ -41,7 +41,9 @@ namespace {
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    // every control used here is a full permutation, so no lane keeps an old
+    // value (an old operand of 0 would cost a v_mov per use)
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]

@@ -119,7 +119,9 @@ __device__ __forceinline__ float by_lane(int q, float a0, float a1, float a2, fl
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+    // every lane has a source under a quad permutation, so no old value is
+    // needed (an old operand of 0 would cost a v_mov per use)
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
 constexpr int kQuadReverse = 0x1b;    // quad_perm [3, 2, 1, 0]
 constexpr int kQuadNegate = 0x6c;     // quad_perm [0, 3, 2, 1]: lane (4 - q) mod 4
