@@ -1,0 +1,87 @@
+"""Host-side logic of bench.py, on the CPU: the one-GPU guard, the gate that
+keeps a counter-derived traffic figure only while the kernel sources match
+the ones it was taken on, and the scaling of FETCH_SIZE / WRITE_SIZE
+counters by the plain-copy reference."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+COPY = "__amd_rocclr_copyBuffer"
+QUANT = "kvq::quantize_kernel<128, 32, true, 4, false, false>"
+
+
+def test_bytes_per_vector():
+    # fp16 vector + nibble codes + fp16 group scales
+    assert bench.bytes_per_vector(128, 32) == 256 + 64 + 8
+    assert bench.bytes_per_vector(256, 64) == 512 + 128 + 8
+    assert bench.bytes_per_vector(64, 8) == 128 + 32 + 16
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_more_than_one_gpu_is_refused(argv, env):
+    e = dict(os.environ, **env)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True,
+                       text=True, env=e, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_is_used_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    path = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    assert bench.load_traffic(1) is None                       # no file
+    path.write_text(json.dumps({"source_hash": "0" * 16, "traffic_bytes_per_launch": 123}))
+    assert bench.load_traffic(1) is None                       # other sources
+    path.write_text(json.dumps({"source_hash": bench.kernel_source_hash(), "traffic_bytes_per_launch": 123}))
+    assert bench.load_traffic(1) == 123
+    path.write_text("not json")
+    assert bench.load_traffic(1) is None
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (name, v) in enumerate(rows):
+            w.writerow([i, name, counter, v])
+
+
+def test_ingest_scales_by_the_copy_reference(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    copy_bytes = 1 << 30
+    kib = copy_bytes // 1024
+    # the reference copy reads and writes copy_bytes; FETCH_SIZE reports half
+    # of it (full-line reads), WRITE_SIZE all of it
+    fetch = [(COPY + "(void*)", kib / 2), (COPY + "(void*)", 3.0),          # a small unrelated copy
+             ("void " + QUANT + "(kvq::Int4Args)", 1000.0), ("void " + QUANT + "(kvq::Int4Args)", 1002.0)]
+    write = [(COPY + "(void*)", kib), (COPY + "(void*)", 3.0),
+             ("void " + QUANT + "(kvq::Int4Args)", 500.0), ("void " + QUANT + "(kvq::Int4Args)", 500.0)]
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(fp, "FETCH_SIZE", fetch)
+    _counter_csv(wp, "WRITE_SIZE", write)
+    out = bench.ingest_counters(str(fp), str(wp), copy_bytes)
+    assert out["fetch_scale"] == pytest.approx(2.0)
+    assert out["write_scale"] == pytest.approx(1.0)
+    q = out["quantize"]
+    assert q["dispatches"] == 2
+    assert q["traffic_bytes_per_launch"] == int(1001.0 * 1024 * 2.0 + 500.0 * 1024 * 1.0)
+    alg = 36 * 262144 * 8 * bench.bytes_per_vector(128, 32)
+    assert q["algorithmic_bytes_per_launch"] == alg
+    assert q["traffic_over_algorithmic"] == round(q["traffic_bytes_per_launch"] / alg, 5)
+    assert out["traffic_bytes_per_launch"] == q["traffic_bytes_per_launch"]
+    assert out["source_hash"] == bench.kernel_source_hash()
+    with open(bench.TRAFFIC_FILE) as f:
+        assert json.load(f) == out
+    # without the reference copy there is nothing to scale by
+    _counter_csv(wp, "WRITE_SIZE", write[2:])
+    with pytest.raises(SystemExit):
+        bench.ingest_counters(str(fp), str(wp), copy_bytes)
