@@ -156,48 +156,20 @@ struct QuantShape {
 };
 
 // Item loop shared by both kernels (see the comment below).  With PREFETCH
-// the next item's loads are issued before the current item is finished,
-// into a second register buffer, the loop unrolled by two.  PREFETCH1 does
-// the same with one buffer, refilled once the first stage has consumed it,
-// and no unrolling: the SRFT dequantizer, which the unrolled form takes past
-// 256 VGPRs (one wave per SIMD), stays at two waves per SIMD with it.
-// Without either (head_dim 256) each item's loads are issued right before
-// its first stage, and only the stores are deferred.
-template <typename Buf, typename Out, int N, bool PREFETCH, bool PREFETCH1 = false, typename Load, typename First,
-          typename Store, typename Finish>
+// the next item's loads are issued before the current item is finished, into
+// the item's one register buffer as soon as the first stage has consumed it
+// (a second buffer, with the loop unrolled by two, took 12 to 41 more VGPRs:
+// a wave per SIMD less for the quantizers and the SRFT dequantizer).
+// Without it (head_dim 256) each item's loads are issued right before its
+// first stage, and only the stores are deferred.
+template <typename Buf, typename Out, int N, bool PREFETCH, typename Load, typename First, typename Store,
+          typename Finish>
 __device__ __forceinline__ void run_pipeline(int begin, int end, Load&& load, First&& first_stage,
                                              Store&& store, Finish&& finish)
 {
     Out prev;
     int prev_item = -1;
     if constexpr (PREFETCH) {
-        Buf bufA, bufB;
-        load(begin, bufA);
-        for (int item = begin;;) {
-            {
-                float v[N];
-                first_stage(item, bufA, v);
-                pin(v);
-                if (prev_item >= 0) store(prev_item, prev);
-                if (item + 1 < end) load(item + 1, bufB);
-                __builtin_amdgcn_sched_barrier(0);
-                finish(v, prev);
-                prev_item = item;
-            }
-            if (++item >= end) break;
-            {
-                float v[N];
-                first_stage(item, bufB, v);
-                pin(v);
-                store(prev_item, prev);
-                if (item + 1 < end) load(item + 1, bufA);
-                __builtin_amdgcn_sched_barrier(0);
-                finish(v, prev);
-                prev_item = item;
-            }
-            if (++item >= end) break;
-        }
-    } else if constexpr (PREFETCH1) {
         Buf buf;
         load(begin, buf);
         for (int item = begin; item < end; ++item) {
@@ -723,7 +695,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
         }
     };
 
-    run_pipeline<Raw, Out, N, (D <= 128 && !FT), (D <= 128 && FT)>(begin, end, load, first_stage, store, finish);
+    run_pipeline<Raw, Out, N, (D <= 128)>(begin, end, load, first_stage, store, finish);
 }
 
 // ---------------------------------------------------------------------------
