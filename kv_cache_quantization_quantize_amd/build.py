@@ -42,8 +42,20 @@ EXTRA = {"kvq_vq.hip": ["-fno-honor-nans"],
          "kvq_attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
+def _up_to_date(src: str, obj: str) -> bool:
+    """The object is newer than its source and every header it may include."""
+    if not os.path.exists(obj):
+        return False
+    deps = [os.path.join(CSRC, src), os.path.join(ROOT, "include", "kvq.h")]
+    deps += [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    t = os.path.getmtime(obj)
+    return all(os.path.getmtime(d) < t for d in deps)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    if incremental and _up_to_date(src, obj):
+        return obj
     lang = ["-x", "hip"]
     cmd = [HIPCC, *lang, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,10 +65,12 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (incremental: only those whose object is older
+    than the source or a header) and link libkvq.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, incremental), SOURCES))
     tmp = OUT + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -80,4 +94,4 @@ def asm(src: str = "kvq_int4.hip", out: str | None = None) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)

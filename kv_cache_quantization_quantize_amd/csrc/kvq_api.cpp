@@ -561,6 +561,21 @@ kvq_status kvq_kmeans_step(kvq_shape shape, kvq_view x_f16, const float* lambda,
     return hip_status(kvq::launch_kmeans_update(a, static_cast<hipStream_t>(stream)), "kvq_kmeans_step launch");
 }
 
+kvq_status kvq_item_plan(kvq_shape shape, int32_t* token_major, int64_t* n_items, int32_t* items_per_wave)
+{
+    g_err[0] = 0;
+    if (!token_major || !n_items || !items_per_wave)
+        return fail(KVQ_ERR_NULL, "token_major, n_items and items_per_wave must not be NULL");
+    *token_major = 0;
+    *n_items = 0;
+    *items_per_wave = 0;
+    KVQ_TRY(check_shape(shape));
+    if (empty(shape)) return KVQ_OK;
+    int32_t h_shift, items_per_group, tok_per_item;
+    set_items(shape, *token_major, h_shift, items_per_group, tok_per_item, *items_per_wave, *n_items);
+    return KVQ_OK;
+}
+
 kvq_status kvq_attend_decode_workspace(kvq_shape shape, int32_t q_per_kv, int64_t* bytes)
 {
     g_err[0] = 0;

@@ -201,26 +201,24 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
                     // ---- stage codebook chunk + split norms (whole block) ----------
                     __syncthreads();
                     for (int k = threadIdx.x; k < CHUNK; k += 64 * WAVES) {
-                        uint4 cv = make_uint4(0, 0, 0, 0);
-                        // padding: n_hi = 65504 (largest finite fp16) gives a score of
-                        // -32752, below any in-domain centroid; finite so that the
-                        // zero B2 half never multiplies an infinity
-                        uint32_t nw = 0x00007BFFu;
-                        if (k < kc) {
-                            cv = *reinterpret_cast<const uint4*>(cbp + (int64_t)(kbase + k) * 8);
-                            const uint32_t w[4] = {cv.x, cv.y, cv.z, cv.w};
-                            float n = 0.0f;
+                        // Rows past the end of the codebook (only in the last tile of
+                        // the last chunk) repeat the chunk's last centroid, K - 1:
+                        // they score exactly as it does, so they never beat a real
+                        // centroid, and an index they yield is mapped back to K - 1
+                        // after the re-score.
+                        const int kk = min(k, kc - 1);
+                        const uint4 cv = *reinterpret_cast<const uint4*>(cbp + (int64_t)(kbase + kk) * 8);
+                        const uint32_t w[4] = {cv.x, cv.y, cv.z, cv.w};
+                        float n = 0.0f;
 #pragma unroll
-                            for (int e = 0; e < 4; e++) {
-                                n = fmaf(lo_half(w[e]), lo_half(w[e]), n);
-                                n = fmaf(hi_half(w[e]), hi_half(w[e]), n);
-                            }
-                            const _Float16 nh = (_Float16)n;
-                            const _Float16 nl = (_Float16)(n - (float)nh);
-                            nw = __builtin_bit_cast(uint32_t, half2_t{nh, nl});
+                        for (int e = 0; e < 4; e++) {
+                            n = fmaf(lo_half(w[e]), lo_half(w[e]), n);
+                            n = fmaf(hi_half(w[e]), hi_half(w[e]), n);
                         }
+                        const _Float16 nh = (_Float16)n;
+                        const _Float16 nl = (_Float16)(n - (float)nh);
                         cb_lds[k] = cv;
-                        nrm_lds[k] = nw;
+                        nrm_lds[k] = __builtin_bit_cast(uint32_t, half2_t{nh, nl});
                     }
                     __syncthreads();
                     cur_cb = nchunks > 1 ? -1 : cbkey;
@@ -344,7 +342,7 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
                                 bk = k;
                             }
                         }
-                        best_idx[gg] = kbase + bk;
+                        best_idx[gg] = min(kbase + bk, a.K - 1);     // a padded row is centroid K - 1
                     }
                 }
             }

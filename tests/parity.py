@@ -18,6 +18,9 @@ Contract (tolerances from the target statement; each check explained):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 
 import oracle
@@ -313,3 +316,51 @@ def kmeans_parity(x_bits, lam_rows, signs, codebook_bits, idx_gpu, new_gpu, coun
         _raise("k-means centroid", rep["centroids"], "first bad [k, t]: %s gpu=%s mean64=%s delta=%s" % (
             i.tolist(), g[tuple(i.T)], m64[tuple(i.T)], delta[tuple(i.T)]))
     return rep
+
+
+# ------------------------------------------------------- sharded checks
+def workers() -> int:
+    """Threads for sharded checks: the host cores this process may use, at
+    most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _merge(reps):
+    """Sum the counts of shard reports, take the maxima of their float
+    fields and concatenate their arrays."""
+    out = {}
+    for key in reps[0]:
+        parts = [r[key] for r in reps]
+        m = {}
+        for f, v in parts[0].items():
+            vals = [p[f] for p in parts]
+            if isinstance(v, np.ndarray):
+                m[f] = np.concatenate(vals)
+            elif isinstance(v, (bool, np.bool_)):
+                m[f] = any(vals)
+            elif isinstance(v, (int, np.integer)):
+                m[f] = int(sum(vals))
+            else:
+                m[f] = float(max(vals))
+        out[key] = m
+    return out
+
+
+def sharded(check, n: int, n_workers: int | None = None):
+    """Run check(row_slice) on disjoint row shards of n rows at once and
+    merge the reports.  Each shard is an independent call of the
+    single-threaded oracle (ctypes releases the GIL during the call), so
+    the arithmetic for every row is exactly that of one unsharded call; a
+    failing shard raises its own ParityError."""
+    w = max(1, min(n_workers or workers(), n))
+    bounds = np.linspace(0, n, w + 1).astype(int)
+    slices = [slice(int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    if len(slices) == 1:
+        return check(slices[0])
+    with cf.ThreadPoolExecutor(len(slices)) as ex:
+        reps = list(ex.map(check, slices))
+    return _merge(reps)

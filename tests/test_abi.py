@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
         "kvq_attend_decode", "kvq_attend_decode_workspace", "kvq_quantize_int8", "kvq_dequantize_int8",
         "kvq_quantize_mxfp4", "kvq_dequantize_mxfp4", "kvq_vq_encode_u8", "kvq_vq_decode_u8",
         "kvq_kmeans_step", "kvq_kmeans_step_workspace",
-        "kvq_quantize_srft", "kvq_dequantize_srft",
+        "kvq_quantize_srft", "kvq_dequantize_srft", "kvq_item_plan",
         "kvq_status_string", "kvq_last_error", "kvq_version"])
 
 
@@ -290,3 +290,24 @@ def test_mxfp4_validation(lib):
     assert lib.kvq_quantize_mxfp4(sh, x, A_, A_, codes, view(addr=A + 1, row=2), None) == SHAPE
     assert lib.kvq_dequantize_mxfp4(shape(2, 0, 3), codes, view(row=4), A_, A_, x, None) == OK
     assert lib.kvq_dequantize_mxfp4(shape(D=96), codes, view(row=4), A_, A_, x, None) == UNSUP
+
+
+def test_item_plan(lib):
+    """The work decomposition the multi-item parity tests rely on: several
+    items per wavefront, a partial last item, runs that cross a lambda key."""
+    # token-major: 16 / H tokens of all heads per item
+    assert kvq.item_plan(5, 80001, 2, 128) == (True, 5 * 10001, 3)
+    assert kvq.item_plan(4, 65540, 2, 128) == (True, 4 * 8193, 2)
+    assert kvq.item_plan(3, 200003, 1, 256) == (True, 3 * 12501, 2)
+    # head-major: 16 tokens of one (layer, head) per item
+    assert kvq.item_plan(3, 65541, 3, 128) == (False, 9 * 4097, 2)
+    assert kvq.item_plan(2, 87400, 3, 256) == (False, 6 * 5463, 2)
+    # small launches run one item per wavefront; long ones at most 64
+    assert kvq.item_plan(1, 64, 2, 128) == (True, 8, 1)
+    assert kvq.item_plan(28, 4096, 2, 128)[2] == 1
+    assert kvq.item_plan(36, 262144, 8, 128) == (True, 36 * 131072, 64)
+    assert kvq.item_plan(0, 5, 3, 128) == (False, 0, 0)
+    with pytest.raises(kvq.KvqError):
+        kvq.item_plan(1, 5, 3, 96)
+    tm, n, ipw = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
+    assert lib.kvq_item_plan(shape(), None, ctypes.byref(n), ctypes.byref(ipw)) == NULL

@@ -123,3 +123,21 @@ def test_kmeans_classification():
     i2[0, 0] = 7
     with pytest.raises(parity.ParityError):
         parity.kmeans_parity(x, lam, s, cbb, i2, new, cnt)
+
+
+def test_sharded_check_matches_unsharded_and_still_fails():
+    """The sharded runner gives the unsharded report's counts, and a planted
+    wrong code in one shard still fails the whole check."""
+    x, lam, s, G, codes, scales, y = _case(n=97)
+    _, x16 = oracle.dequantize(codes, scales, lam, s, G)
+    whole = parity.int4_parity(x, lam, s, G, codes, scales, x16)
+    rep = parity.sharded(lambda k: parity.int4_parity(x[k], lam[k], s, G, codes[k], scales[k], x16[k]), 97,
+                         n_workers=5)
+    for part in ("scales", "codes", "dequant"):
+        for f in ("n", "bad"):
+            assert rep[part][f] == whole[part][f], (part, f)
+    assert rep["codes"]["exact"] == 97 * 128
+    bad = codes.copy()
+    bad[80, 3] ^= 0x20                 # one nibble off by more than one step
+    with pytest.raises(parity.ParityError):
+        parity.sharded(lambda k: parity.int4_parity(x[k], lam[k], s, G, bad[k], scales[k]), 97, n_workers=5)

@@ -107,9 +107,10 @@ def test_vecinfer_keys_full_size_sampled():
     centroids per head), in the benchmark's launch configuration.  At any
     size: every head's counts sum to its sub-vector count and equal the
     histogram of the returned assignments, and empty centroids keep their
-    bits.  Sampled: 384 vectors' assignments under the VQ contract, and four
-    centroids' means recomputed by the oracle from every vector assigned to
-    them."""
+    bits.  Sampled: 4,608 vectors' assignments under the VQ contract.  Whole
+    head: for one seeded head, the oracle rotates all 294,912 of its vectors
+    and recomputes every one of its 4,096 centroids (counts and means) from
+    the GPU's assignments.  The oracle runs on disjoint shards in parallel."""
     dev = device()
     cfg = synth.config("vq")
     inp = synth.make_inputs(cfg, dev, want_v=False)
@@ -124,30 +125,37 @@ def test_vecinfer_keys_full_size_sampled():
     assert int(cnt.sum()) == L * T * H * D // 8
     empty = cnt == 0
     assert torch.equal(new[empty], cb[empty])
-    sel = synth.sample_rows(L, T, H, 384, 5151).numpy()
+    sv = s.cpu().numpy()
+
+    sel = synth.sample_rows(L, T, H, 4608, 5151).numpy()
     books = bits(cb).reshape(H, K, 8)
-    rep = parity.vq_parity(rows(x, sel), lam_rows(lam, sel), s.cpu().numpy(), books,
-                           sel[:, 2].astype(np.int32), 8, rows(idx, sel))
-    log("kmeans full-size assignments", parity.summary(rep))
-    rng = np.random.default_rng(61)
-    for h, k in zip(rng.integers(0, H, 4), rng.integers(0, K, 4)):
-        h, k = int(h), int(k)
-        hit = (idx[:, :, h].to(torch.int32) & 0xFFFF) == k                           # [L, T, D/8]
-        ltt = torch.nonzero(hit.any(dim=2))                          # vectors holding a hit
-        lt = ltt.cpu().numpy()
-        if len(lt) == 0:
-            continue
-        vsel = np.stack([lt[:, 0], lt[:, 1], np.full(len(lt), h)], axis=1)
-        y = oracle.rotate(rows(x, vsel), lam_rows(lam, vsel), s.cpu().numpy()).reshape(len(lt), -1, 8)
-        m = hit[ltt[:, 0], ltt[:, 1]].cpu().numpy()                  # [n, D/8]
-        ysub = y[m]
-        new_o, m64, cnt_o, am = oracle.kmeans_update(ysub, np.zeros(len(ysub), np.uint16), bits(cb[h, k:k + 1]))
-        assert int(cnt_o[0]) == int(cnt[h, k])
-        ymax = float(np.sqrt((y ** 2).mean(axis=2)).max())
-        delta = parity.KM_FIX + parity.KM_ROT * ymax
-        g = bits(new[h, k]).view(np.float16).astype(np.float64)
-        lo = parity.f16(oracle.f64_to_f16(m64[0] - delta))
-        hi = parity.f16(oracle.f64_to_f16(m64[0] + delta))
-        log("kmeans full-size centroid (%d, %d): n=%d exact=%d" % (h, k, int(cnt_o[0]),
-                                                                   int((bits(new[h, k]) == new_o[0]).sum())))
-        assert ((g >= lo) & (g <= hi)).all(), (h, k, g, m64[0], delta)
+    book = sel[:, 2].astype(np.int32)
+    xr, lr, ir = rows(x, sel), lam_rows(lam, sel), rows(idx, sel)
+    rep = parity.sharded(lambda k: parity.vq_parity(xr[k], lr[k], sv, books, book[k], 8, ir[k]), len(sel))
+    log("kmeans full-size assignments (%d vectors)" % len(sel), parity.summary(rep))
+
+    h = int(np.random.default_rng(61).integers(0, H))
+    hsel = all_idx(L, T, 1)
+    hsel[:, 2] = h
+    xh, lh = rows(x, hsel), lam_rows(lam, hsel)
+    y = np.empty((len(hsel), D))
+
+    def rot(k):
+        y[k] = oracle.rotate(xh[k], lh[k], sv)
+        return {}
+
+    parity.sharded(rot, len(hsel))
+    ih = rows(idx, hsel).reshape(-1)
+    new_o, m64, cnt_o, _ = oracle.kmeans_update(y.reshape(-1, 8), ih, bits(cb[h]))
+    assert np.array_equal(cnt_o.astype(np.int64), cnt[h].cpu().numpy().astype(np.int64)), "counts of head %d" % h
+    ymax = float(np.sqrt((y ** 2).mean(axis=1)).max())
+    delta = parity.KM_FIX + parity.KM_ROT * ymax
+    lo = parity.f16(oracle.f64_to_f16(m64 - delta))
+    hi = parity.f16(oracle.f64_to_f16(m64 + delta))
+    gb = bits(new[h])
+    g = parity.f16(gb)
+    e = cnt_o == 0
+    ok = np.where(e[:, None], gb == bits(cb[h]), (g >= lo) & (g <= hi))
+    log("kmeans full-size head %d: %d centroids (%d empty), %d of %d values bit-equal to the oracle's" % (
+        h, K, int(e.sum()), int((gb == new_o).sum()), gb.size))
+    assert ok.all(), np.argwhere(~ok)[:5].tolist()

@@ -84,6 +84,37 @@ def test_duplicate_centroids_resolve_to_lowest_index(K, dup):
     check(x, lam, s, cb, idx, out, all_idx(1, 48, 2), "dup K=%d" % K)
 
 
+@pytest.mark.parametrize("K,u8", [(33, False), (33, True), (4096 + 33, False), (1, False)])
+def test_far_codebook_partial_last_tile(K, u8):
+    """Every centroid lies far on the opposite side of every sub-vector
+    (rotated keys near +1414 per coordinate, centroids near -70 per
+    coordinate), so every score c.y - |c|^2/2 is about -8e5, far below any
+    fixed padding score: the rows past the end of the codebook in the
+    partial last tile (of the last LDS chunk) must never be chosen, and the
+    index must be the oracle's.  lambda = 1, s = 1 and x = 16000 e_0 + small
+    noise make every rotated coordinate about 16000 / sqrt(128)."""
+    dev = device()
+    g = torch.Generator(device="cpu").manual_seed(K + 7 * u8)
+    L, T, H, D = 1, 40, 2, 128
+    x = torch.randn((L, T, H, D), generator=g) * 20.0
+    x[..., 0] = 16000.0
+    lam = torch.ones((L, H, D), dtype=torch.float32)
+    s = torch.ones(D, dtype=torch.int8)
+    cb = -70.0 + 2.0 * torch.randn((H, K, 8), generator=g)
+    x, lam, s = x.to(torch.float16).to(dev), lam.to(dev), s.to(dev)
+    cb = cb.to(torch.float16).contiguous().to(dev)
+    if u8:
+        idx = kvq.vq_encode_u8(x, lam, s, cb, 8)
+        out = kvq.vq_decode_u8(idx, cb, lam, s, 8)
+        torch.cuda.synchronize()
+        assert int(idx.max()) < K
+        idx = idx.to(torch.int16)
+    else:
+        idx, out = run_vq(x, lam, s, cb)
+        assert int(bits(idx).max()) < K
+    check(x, lam, s, cb, idx, out, all_idx(L, T, H), "far codebook K=%d u8=%s" % (K, u8))
+
+
 def test_per_layer_codebooks_and_strided_views():
     dev = device()
     x0, lam, s, _ = rand_case(3, 21, 2, 128, 64, seed=9)
@@ -152,11 +183,18 @@ def test_decode_random_indices(K, L, T, H, D):
 def test_vecinfer_full_size_sampled():
     """The VecInfer-shaped key cache at full size ([36, 8192, 8, 128],
     per-head 4096-centroid fp16 codebooks), in the benchmark's launch
-    configuration; parity on a seeded sample of 384 keys."""
+    configuration; parity on a seeded sample of 4,608 keys (73,728
+    sub-vectors), 16 per (layer, head) on average, with the oracle run on
+    disjoint shards in parallel."""
     dev = device()
     cfg = synth.config("vq")
     inp = synth.make_inputs(cfg, dev)
     x, lam, s, cb = inp["K"], inp["lam_K"], inp["signs"], inp["codebook"]
     idx, out = run_vq(x, lam, s, cb)
-    sel = synth.sample_rows(cfg.L, cfg.T, cfg.H, 384, 4242).numpy()
-    check(x, lam, s, cb, idx, out, sel, "vecinfer full-size")
+    sel = synth.sample_rows(cfg.L, cfg.T, cfg.H, 4608, 4242).numpy()
+    xr, lr, ir, orow = rows(x, sel), lam_rows(lam, sel), rows(idx, sel), rows(out, sel)
+    books = bits(cb).reshape(cfg.H, cfg.n_centroids, 8)
+    book = sel[:, 2].astype(np.int32)
+    sv = s.cpu().numpy()
+    rep = parity.sharded(lambda k: parity.vq_parity(xr[k], lr[k], sv, books, book[k], 8, ir[k], orow[k]), len(sel))
+    log("vecinfer full-size (%d keys, %d oracle threads)" % (len(sel), parity.workers()), parity.summary(rep))
