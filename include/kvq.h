@@ -318,6 +318,29 @@ kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f1
  * current device (written to *bytes; 0 for an empty shape). */
 kvq_status kvq_attend_decode_workspace(kvq_shape shape, int32_t q_per_kv, int64_t* bytes);
 
+/* kvq_attend_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The partial states go to a static
+ * device array of 64 MiB that the library holds on every GPU it runs on
+ * until the process ends; nothing is allocated or freed by the call.
+ * Arguments, results and errors are kvq_attend_decode's, plus KVQ_ERR_SHAPE
+ * when the partial states of the kernel this call runs exceed 64 MiB (split
+ * the call, or pass a workspace to kvq_attend_decode; any shape whose
+ * kvq_attend_decode_workspace() is at most 64 MiB fits, and so do larger
+ * ones on the matrix-core kernel, e.g. 36 layers x 8 sequences of 32K tokens
+ * with 8 KV heads of 128 and 4 query heads each), and KVQ_ERR_HIP if the
+ * array's device address cannot be looked up (done once per device, on the
+ * first call with that device current).  All calls on one device share the
+ * array: calls that overlap in time on one device (concurrent streams, or
+ * threads) race and must be serialised by the caller; the array needs no
+ * clearing between calls. */
+kvq_status kvq_attend_decode_noalloc(kvq_shape shape, int32_t q_per_kv, const void* q_f16,
+                                     kvq_view k_codes_u8, kvq_view k_scales_f16,
+                                     kvq_view v_codes_u8, kvq_view v_scales_f16,
+                                     const float* lambda_k, const float* lambda_v,
+                                     const int8_t* signs, int32_t group, const int32_t* lengths,
+                                     float softmax_scale, void* out_f16, void* stream);
+
 /* Work decomposition of the quantize and dequantize kernels of every format
  * (int4, int8, MXFP4, SRFT) for a shape; host arithmetic only, no HIP call.
  * An item is 16 head vectors: 16/heads consecutive tokens of one layer (all

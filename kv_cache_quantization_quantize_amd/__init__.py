@@ -93,6 +93,9 @@ def lib():
     L.kvq_attend_decode.restype = ctypes.c_int
     L.kvq_attend_decode.argtypes = [Shape, I32, P, View, View, View, View, P, P, P, I32, P, ctypes.c_float, P, P,
                                     I64, P]
+    L.kvq_attend_decode_noalloc.restype = ctypes.c_int
+    L.kvq_attend_decode_noalloc.argtypes = [Shape, I32, P, View, View, View, View, P, P, P, I32, P, ctypes.c_float,
+                                            P, P]
     L.kvq_attend_decode_workspace.restype = ctypes.c_int
     L.kvq_attend_decode_workspace.argtypes = [Shape, I32, ctypes.POINTER(I64)]
     L.kvq_item_plan.restype = ctypes.c_int
@@ -405,12 +408,14 @@ def attend_decode_workspace_bytes(L: int, T: int, H: int, D: int, q_per_kv: int)
 
 
 def attend_decode(q, k_codes, k_scales, v_codes, v_scales, lam_k, lam_v, signs, group: int,
-                  softmax_scale=None, lengths=None, out=None, workspace=None, stream=None):
+                  softmax_scale=None, lengths=None, out=None, workspace=None, stream=None, noalloc=False):
     """One decode step of attention over int4 caches.  q [L, H*R, D] fp16
     (R query heads per KV head), caches [L, T, H, D/2] u8 and [L, T, H, D/G]
     fp16 as written by quantize, lam_k / lam_v [L, H, D] fp32, lengths [L]
     int32 or None -> fp16 [L, H*R, D].  The workspace (a uint8 tensor) is
-    allocated here when not given."""
+    allocated here when not given.  noalloc: call kvq_attend_decode_noalloc,
+    which keeps the partial states in the library's static device scratch
+    (out must then be given to allocate nothing at all)."""
     torch = _torch()
     for t, dt, name in ((q, torch.float16, "q"), (k_codes, torch.uint8, "k_codes"),
                         (k_scales, torch.float16, "k_scales"), (v_codes, torch.uint8, "v_codes"),
@@ -436,11 +441,19 @@ def attend_decode(q, k_codes, k_scales, v_codes, v_scales, lam_k, lam_v, signs, 
         if tuple(lengths.shape) != (L,) or not lengths.is_contiguous():
             raise ValueError("lengths must be a contiguous int32 [layers] tensor")
         pl = ctypes.c_void_p(lengths.data_ptr())
+    scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        _check(lib().kvq_attend_decode_noalloc(Shape(L, T, H, D), int(R), ctypes.c_void_p(q.data_ptr()),
+                                               _view(k_codes), _view(k_scales), _view(v_codes), _view(v_scales),
+                                               pk, pv, ps, int(group), pl, scale, ctypes.c_void_p(out.data_ptr()),
+                                               _stream(stream)))
+        return out
     need = attend_decode_workspace_bytes(L, T, H, D, R)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _need(workspace, torch.uint8, "workspace")
-    scale = (1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
     _check(lib().kvq_attend_decode(Shape(L, T, H, D), int(R), ctypes.c_void_p(q.data_ptr()), _view(k_codes),
                                    _view(k_scales), _view(v_codes), _view(v_scales), pk, pv, ps, int(group), pl,
                                    scale, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
@@ -387,6 +388,42 @@ kvq_status km_check(const kvq_shape& s, int32_t K, int32_t sub)
     return KVQ_OK;
 }
 
+// Static scratch of kvq_attend_decode_noalloc: the split partial states of
+// decode attention, for callers that cannot allocate.  Every GPU the library
+// runs on holds its own copy until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, once per device (with that device current), and only
+// that address is ever handed to a kernel.  Calls on one device share the
+// array, so calls that overlap on one device race; its contents on entry do
+// not matter (every partial a call reads, it has written).
+constexpr int64_t kAttnScratchBytes = 64ll << 20;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+kvq_status scratch_pointer(void** ptr)
+{
+    int dev = 0;
+    KVQ_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        KVQ_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+        if (!p) return fail(KVQ_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -587,13 +624,19 @@ kvq_status kvq_attend_decode_workspace(kvq_shape shape, int32_t q_per_kv, int64_
     return KVQ_OK;
 }
 
-kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f16, kvq_view k_codes_u8,
-                             kvq_view k_scales_f16, kvq_view v_codes_u8, kvq_view v_scales_f16,
-                             const float* lambda_k, const float* lambda_v, const int8_t* signs, int32_t group,
-                             const int32_t* lengths, float softmax_scale, void* out_f16, void* workspace,
-                             int64_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Everything kvq_attend_decode does.  workspace == nullptr with
+// use_scratch: the partial states go to this device's static scratch array
+// (kvq_attend_decode_noalloc), whose size is checked against the need first.
+kvq_status attend_any(kvq_shape shape, int32_t q_per_kv, const void* q_f16, kvq_view k_codes_u8,
+                      kvq_view k_scales_f16, kvq_view v_codes_u8, kvq_view v_scales_f16, const float* lambda_k,
+                      const float* lambda_v, const int8_t* signs, int32_t group, const int32_t* lengths,
+                      float softmax_scale, void* out_f16, void* workspace, int64_t workspace_bytes, void* stream,
+                      bool use_scratch)
 {
-    g_err[0] = 0;
     KVQ_TRY(attn_check(shape, q_per_kv));
     KVQ_TRY(check_group(group, shape.head_dim));
     if (shape.layers == 0 || shape.heads == 0) return KVQ_OK;
@@ -611,10 +654,13 @@ kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f1
         KVQ_TRY(check_view("v_scales_f16", v_scales_f16, 2, D / group, 2, shape));
     }
     const int64_t need = attn_workspace_bytes(shape, q_per_kv);
-    if (!workspace) return fail(KVQ_ERR_NULL, "workspace is NULL (%lld bytes needed)", (long long)need);
-    if (!aligned(workspace, 16)) return fail(KVQ_ERR_ALIGN, "workspace must be 16-byte aligned");
-    if (workspace_bytes < need)
-        return fail(KVQ_ERR_SHAPE, "workspace_bytes=%lld; %lld needed", (long long)workspace_bytes, (long long)need);
+    if (!use_scratch) {
+        if (!workspace) return fail(KVQ_ERR_NULL, "workspace is NULL (%lld bytes needed)", (long long)need);
+        if (!aligned(workspace, 16)) return fail(KVQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(KVQ_ERR_SHAPE, "workspace_bytes=%lld; %lld needed", (long long)workspace_bytes,
+                        (long long)need);
+    }
     kvq::AttnArgs a;
     a.L = (int32_t)shape.layers;
     a.T = (int32_t)shape.tokens;
@@ -647,6 +693,17 @@ kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f1
         a.parts = p.parts;
         a.xcd_map = ((int64_t)a.L * a.S) % 8 == 0;
     }
+    if (use_scratch) {
+        // the partial states of the kernel this call runs (at most the
+        // workspace query's bound, which covers either kernel)
+        const int64_t used = shape.layers * shape.heads * (int64_t)q_per_kv * a.parts * (D + 4) * (int64_t)sizeof(float);
+        if (used > kAttnScratchBytes)
+            return fail(KVQ_ERR_SHAPE,
+                        "this call needs %lld bytes of partial states; the static scratch holds %lld "
+                        "(call kvq_attend_decode with a workspace, or split the call)",
+                        (long long)used, (long long)kAttnScratchBytes);
+        KVQ_TRY(scratch_pointer(&workspace));
+    }
     a.q = static_cast<const _Float16*>(q_f16);
     a.out = static_cast<_Float16*>(out_f16);
     a.kc = t4(k_codes_u8);
@@ -660,6 +717,33 @@ kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f1
     a.qscale = softmax_scale * 1.4426950408889634f;
     a.ws = static_cast<float*>(workspace);
     return hip_status(kvq::launch_attend_decode(a, static_cast<hipStream_t>(stream)), "kvq_attend_decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_attend_decode(kvq_shape shape, int32_t q_per_kv, const void* q_f16, kvq_view k_codes_u8,
+                             kvq_view k_scales_f16, kvq_view v_codes_u8, kvq_view v_scales_f16,
+                             const float* lambda_k, const float* lambda_v, const int8_t* signs, int32_t group,
+                             const int32_t* lengths, float softmax_scale, void* out_f16, void* workspace,
+                             int64_t workspace_bytes, void* stream)
+{
+    g_err[0] = 0;
+    return attend_any(shape, q_per_kv, q_f16, k_codes_u8, k_scales_f16, v_codes_u8, v_scales_f16, lambda_k,
+                      lambda_v, signs, group, lengths, softmax_scale, out_f16, workspace, workspace_bytes, stream,
+                      false);
+}
+
+kvq_status kvq_attend_decode_noalloc(kvq_shape shape, int32_t q_per_kv, const void* q_f16, kvq_view k_codes_u8,
+                                     kvq_view k_scales_f16, kvq_view v_codes_u8, kvq_view v_scales_f16,
+                                     const float* lambda_k, const float* lambda_v, const int8_t* signs,
+                                     int32_t group, const int32_t* lengths, float softmax_scale, void* out_f16,
+                                     void* stream)
+{
+    g_err[0] = 0;
+    return attend_any(shape, q_per_kv, q_f16, k_codes_u8, k_scales_f16, v_codes_u8, v_scales_f16, lambda_k,
+                      lambda_v, signs, group, lengths, softmax_scale, out_f16, nullptr, 0, stream, true);
 }
 
 const char* kvq_status_string(kvq_status st)

@@ -33,7 +33,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "kvq_quantize", "kvq_dequantize", "kvq_vq_encode", "kvq_vq_decode",
-        "kvq_attend_decode", "kvq_attend_decode_workspace", "kvq_quantize_int8", "kvq_dequantize_int8",
+        "kvq_attend_decode", "kvq_attend_decode_workspace", "kvq_attend_decode_noalloc", "kvq_quantize_int8", "kvq_dequantize_int8",
         "kvq_quantize_mxfp4", "kvq_dequantize_mxfp4", "kvq_vq_encode_u8", "kvq_vq_decode_u8",
         "kvq_kmeans_step", "kvq_kmeans_step_workspace",
         "kvq_quantize_srft", "kvq_dequantize_srft", "kvq_item_plan",
@@ -263,6 +263,34 @@ def test_attend_validation(lib):
     assert att(lib, ws=A + 4) == ALIGN
     st, need = ws_bytes(lib, shape(), 4)
     assert att(lib, ws_bytes_=need - 1) == SHAPE
+
+
+def att_noalloc(lib, sh=None, R=4, qp=A, out=A, lk=A, lv=A, sg=A, group=32, scale=0.088):
+    sh = sh or shape()
+    D = sh.head_dim
+    kc = view(row=D // 2, L=sh.layers, T=sh.tokens, H=sh.heads)
+    ks = view(row=D // group, L=sh.layers, T=sh.tokens, H=sh.heads)
+    return lib.kvq_attend_decode_noalloc(sh, R, ctypes.c_void_p(qp), kc, ks, kc, ks, ctypes.c_void_p(lk),
+                                         ctypes.c_void_p(lv), ctypes.c_void_p(sg), group, None,
+                                         ctypes.c_float(scale), ctypes.c_void_p(out), None)
+
+
+def test_attend_noalloc_validation(lib):
+    """The allocation-free entry point validates like kvq_attend_decode and
+    refuses, before touching the device, a call whose partial states exceed
+    its 64 MiB static scratch (head_dim 64 runs the vector-ALU kernel, whose
+    partial count is the workspace query's)."""
+    assert att_noalloc(lib, sh=shape(0, 5, 3)) == OK
+    assert att_noalloc(lib, R=0) == SHAPE
+    assert att_noalloc(lib, qp=0) == NULL
+    assert att_noalloc(lib, qp=A + 8) == ALIGN
+    assert att_noalloc(lib, group=24) == UNSUP
+    assert att_noalloc(lib, scale=float("nan")) == SHAPE
+    big = shape(288, 32768, 8, 64)
+    st, need = ws_bytes(lib, big, 4)
+    assert st == OK and need > 64 << 20
+    assert att_noalloc(lib, sh=big, group=16) == SHAPE
+    assert b"static scratch" in lib.kvq_last_error()
 
 
 def test_int8_validation(lib):
