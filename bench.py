@@ -34,8 +34,10 @@ METRIC = "fused rotate+int4 quantize GB/s (% of HBM peak) and ns/vector at D=128
 HBM_PEAK_GBPS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_quantize_d128_g32_qwen3-8b.json")
+# the quantize kernel and its launch configuration (items per wavefront)
 KERNEL_SOURCES = ["kv_cache_quantization_quantize_amd/csrc/kvq_int4.hip",
-                  "kv_cache_quantization_quantize_amd/csrc/kvq_device.h"]
+                  "kv_cache_quantization_quantize_amd/csrc/kvq_device.h",
+                  "kv_cache_quantization_quantize_amd/csrc/kvq_api.cpp"]
 
 
 def bytes_per_vector(D: int, G: int) -> int:
@@ -211,6 +213,59 @@ def copy_ceiling(torch, nbytes: int, reps: int = 5):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def stream_ceilings(torch, dev, read_bytes: int = 16 << 30, reps: int = 3):
+    """Practical HBM bandwidth of this machine for the read/write mixes of the
+    quantizer's kernels, from the hand-written streaming kernels of
+    libkvq_stream.so: read only, 80/20 (the quantizer's 256 B in / 72 B out
+    is 78/22), 20/80 (the dequantizer's) and 1:1 copy, each with plain and
+    nontemporal loads and stores and one or eight units per wavefront.
+    GB/s = (bytes read + written) / kernel time (HIP events on the launching
+    stream), best of `reps`; the best variant of each mix is its ceiling."""
+    import ctypes
+    from kv_cache_quantization_quantize_amd import build as kbuild
+    lib = ctypes.CDLL(kbuild.STREAM_OUT)
+    lib.kvq_stream_run.restype = ctypes.c_int
+    lib.kvq_stream_run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    src = torch.empty(read_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(read_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    src.fill_(1)
+    stream = torch.cuda.current_stream()
+    # (name, mode, chunks read, chunks written per lane and unit)
+    mixes = (("read_only", 0, 4, 0), ("read80_write20", 1, 4, 1), ("read20_write80", 2, 1, 4),
+             ("copy", 3, 1, 1))
+    res = {}
+    for name, mode, rd, wr in mixes:
+        unit_bytes = 1024 * max(rd, wr)
+        n_units = read_bytes // unit_bytes
+        moved = n_units * 1024 * (rd + wr)
+        variants = {}
+        for nt in (0, 1):
+            for upw in (1, 8):
+                def run():
+                    st = lib.kvq_stream_run(mode, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                            n_units, upw, nt, ctypes.c_void_p(sink.data_ptr()),
+                                            ctypes.c_void_p(stream.cuda_stream))
+                    if st:
+                        raise RuntimeError("kvq_stream_run: hip error %d" % st)
+                run()
+                ms = []
+                for _ in range(reps):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    run()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    ms.append(a.elapsed_time(b))
+                variants["%s_upw%d" % ("nt" if nt else "plain", upw)] = round(moved / (min(ms) * 1e-3) / 1e9, 1)
+        best = max(variants, key=variants.get)
+        res[name] = {"GB_per_s": variants[best], "best": best, "variants": variants, "bytes_moved": moved}
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,7 +278,9 @@ def main():
     ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--no-srft", action="store_true")
-    ap.add_argument("--no-small", action="store_true", help="skip the Qwen2.5 / Gemma cache timings")
+    ap.add_argument("--no-small", action="store_true", help="skip the tiny / Qwen2.5 / Gemma cache timings")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-bandwidth ceilings")
+    ap.add_argument("--no-d256", action="store_true", help="skip the HBM-scale head_dim-256 cache")
     ap.add_argument("--attend-seqs", type=int, default=8,
                     help="sequences the int4 cache's token axis is split into for the decode-attention leg")
     ap.add_argument("--cpu-tokens", type=int, default=192, help="tokens per (layer, head) in the CPU sample")
@@ -352,10 +409,17 @@ def main():
     if not args.no_attend:
         attend = bench_attend(torch, kvq, codes, scales, lamK, lamV, signs, (L, T, H, D, G), args)
 
-    try:
-        copy_gbps = round(copy_ceiling(torch, args.copy_bytes), 1)
-    except RuntimeError:
-        copy_gbps = None
+    ceil = None
+    if not args.no_ceiling:
+        ceil = stream_ceilings(torch, dev)
+        for name, mix in (("quantize", "read80_write20"), ("dequantize", "read20_write80")):
+            kern[name]["frac_of_practical_ceiling"] = round(kern[name]["GB_per_s"] / ceil[mix]["GB_per_s"], 4)
+            kern[name]["practical_ceiling_mix"] = mix
+        roofline["frac_of_practical_ceiling"] = kern["quantize"]["frac_of_practical_ceiling"]
+
+    d256 = None
+    if not args.no_d256:
+        d256 = bench_d256(torch, kvq, synth, dev, args, ceil)
 
     vq = None
     if not args.no_vq:
@@ -381,7 +445,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kern,
-        "copy_ceiling_GB_per_s": copy_gbps,
+        "practical_ceiling": ceil,
+        "d256": d256,
         "vq": vq,
         "attend": attend,
         "int8": int8,
@@ -394,19 +459,38 @@ def main():
 
 
 def bench_small(torch, kvq, synth, dev, args):
-    """The pages' smaller caches: quantize + dequantize of Qwen2.5-1.5B- and
-    Gemma-3-1B-shaped K/V caches, warm (the tensors fit in the 256 MB
-    Infinity Cache) and after a 1 GB scrub, plus the Gemma decode append (one
-    token per layer, K and V) as a latency."""
+    """The pages' smaller caches: quantize + dequantize of the tiny key cache
+    (a launch latency), the Qwen2.5-1.5B-shaped K/V caches and the
+    Gemma-3-1B-shaped K/V caches at 256-, 1024- and 4096-token prefixes.
+    Each is timed warm (10 launches back to back, averaged: the tensors fit
+    in the 256 MB Infinity Cache, so this is not an HBM figure) and after a
+    1 GB scrub (inputs come from HBM; median of 10 single launches).  Every leg reports
+    microseconds, algorithmic GB/s, its fraction of the 8 TB/s HBM peak,
+    vectors/s and ns/vector.  Plus, on the 4096-token Gemma cache, the
+    decode append (one token per layer, K and V) and a decode-attention
+    call."""
     stream = torch.cuda.current_stream()
     scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     res = {}
 
     def timed(fn, reps, do_scrub):
+        """Median kernel time of fn.  Scrubbed: one launch per timed interval,
+        behind the scrub (which keeps the GPU busy while the events and the
+        launch are queued).  Warm: `reps` launches back to back between two
+        events, so that no host launch gap of an idle GPU is timed; the
+        interval is divided by the launch count."""
+        if not do_scrub:
+            fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
         ms = []
         for _ in range(reps):
-            if do_scrub:
-                scrub.zero_()
+            scrub.zero_()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             fn()
@@ -416,14 +500,22 @@ def bench_small(torch, kvq, synth, dev, args):
         ms.sort()
         return ms[len(ms) // 2]
 
-    for name, T in (("qwen2.5-1.5b", None), ("gemma-3-1b", 4096)):
+    def leg(ms, nvec, byt):
+        gbps = byt / (ms * 1e-3) / 1e9
+        return {"us": round(ms * 1e3, 2), "GB_per_s": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                "vectors_per_s": round(nvec / (ms * 1e-3), 1), "ns_per_vector": round(ms * 1e6 / nvec, 4)}
+
+    for name, T in (("tiny", None), ("qwen2.5-1.5b", None), ("gemma-3-1b", 256), ("gemma-3-1b", 1024),
+                    ("gemma-3-1b", 4096)):
         cfg = synth.config(name, T=T) if T else synth.config(name)
         inp = synth.make_inputs(cfg, dev)
         L, T, H, D, G = cfg.L, cfg.T, cfg.H, cfg.D, cfg.G
         nvec = L * T * H
         byt = nvec * bytes_per_vector(D, G)
-        r = {"shape": [L, T, H, D], "group": G}
+        r = {"shape": [L, T, H, D], "group": G, "vectors_per_tensor": nvec, "algorithmic_bytes_per_launch": byt}
         for t in ("K", "V"):
+            if t not in inp:
+                continue
             x, lam = inp[t], inp["lam_" + t]
             codes, scales = kvq.quantize(x, lam, inp["signs"], G, stream=stream)
             out = torch.empty_like(x)
@@ -432,10 +524,10 @@ def bench_small(torch, kvq, synth, dev, args):
                             10, mode == "scrubbed")
                 dms = timed(lambda: kvq.dequantize(codes, scales, lam, inp["signs"], G, out=out, stream=stream),
                             10, mode == "scrubbed")
-                r["%s_%s" % (t, mode)] = {"quantize_us": round(qms * 1e3, 2), "dequantize_us": round(dms * 1e3, 2),
-                                          "quantize_GB_per_s": round(byt / (qms * 1e-3) / 1e9, 1),
-                                          "dequantize_GB_per_s": round(byt / (dms * 1e-3) / 1e9, 1)}
-        if name == "gemma-3-1b":
+                r["%s_%s" % (t, mode)] = {
+                    "residency": "infinity cache (10 launches back to back)" if mode == "warm" else "hbm (after a 1 GB scrub)",
+                    "quantize": leg(qms, nvec, byt), "dequantize": leg(dms, nvec, byt)}
+        if name == "gemma-3-1b" and T == 4096:
             # decode append: layer by layer, K then V, one token into slot T - 1
             caches = {t: kvq.quantize(inp[t], inp["lam_" + t], inp["signs"], G, stream=stream) for t in ("K", "V")}
             tok = {t: inp[t][:, T - 1:T].contiguous() for t in ("K", "V")}
@@ -524,10 +616,57 @@ def bench_small(torch, kvq, synth, dev, args):
                                      "GB_per_s": round(abytes / (ams * 1e-3) / 1e9, 1),
                                      "note": "one call over all layers; small, so launch and tail bound"}
             del ws, ao
-        res[name] = r
+        res[name if name != "gemma-3-1b" else "%s_T%d" % (name, T)] = r
         del inp
         torch.cuda.empty_cache()
     del scrub
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_d256(torch, kvq, synth, dev, args, ceil):
+    """The head_dim-256 / group-64 kernels at HBM scale: a Gemma-3-1B-shaped
+    cache [26 layers, 262,144 tokens (64 sequences x 4,096), 1 KV head, 256],
+    K and V (3.49 GB each, far beyond the Infinity Cache), quantize then
+    dequantize, HIP events per launch."""
+    cfg = synth.config("gemma-3-1b", T=64 * 4096)
+    inp = synth.make_inputs(cfg, dev)
+    L, T, H, D, G = cfg.L, cfg.T, cfg.H, cfg.D, cfg.G
+    stream = torch.cuda.current_stream()
+    nvec = L * T * H
+    bpv = bytes_per_vector(D, G)
+    codes = torch.empty((L, T, H, D // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((L, T, H, D // G), dtype=torch.float16, device=dev)
+    out = torch.empty((L, T, H, D), dtype=torch.float16, device=dev)
+    ev = {"quantize": [], "dequantize": []}
+    for rep in range(1 + max(3, min(args.steps, 10))):
+        for t in ("K", "V"):
+            x, lam = inp[t], inp["lam_" + t]
+            for name, fn in (("quantize", lambda: kvq.quantize(x, lam, inp["signs"], G, codes=codes, scales=scales,
+                                                                stream=stream)),
+                             ("dequantize", lambda: kvq.dequantize(codes, scales, lam, inp["signs"], G, out=out,
+                                                                    stream=stream))):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                if rep:
+                    ev[name].append((a, b))
+    torch.cuda.synchronize()
+    res = {"workload": "gemma-3-1b-shaped cache at HBM scale [%d, %d, %d, %d] (64 sequences x 4096 tokens), "
+                       "group %d, K and V" % (L, T, H, D, G), "bytes_per_vector": bpv, "vectors_per_launch": nvec}
+    for name, pairs in ev.items():
+        ms = [a.elapsed_time(b) for a, b in pairs]
+        avg = sum(ms) / len(ms)
+        gbps = nvec * bpv / (avg * 1e-3) / 1e9
+        r = {"launches": len(ms), "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "GB_per_s": round(gbps, 1),
+             "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "ns_per_vector": round(avg * 1e6 / nvec, 5),
+             "vectors_per_s": round(nvec / (avg * 1e-3), 1)}
+        if ceil:
+            mix = "read80_write20" if name == "quantize" else "read20_write80"
+            r["frac_of_practical_ceiling"] = round(gbps / ceil[mix]["GB_per_s"], 4)
+        res[name] = r
+    del inp, codes, scales, out
     torch.cuda.empty_cache()
     return res
 

@@ -341,17 +341,18 @@ kvq_status kvq_attend_decode_noalloc(kvq_shape shape, int32_t q_per_kv, const vo
                                      const int8_t* signs, int32_t group, const int32_t* lengths,
                                      float softmax_scale, void* out_f16, void* stream);
 
-/* Work decomposition of the quantize and dequantize kernels of every format
- * (int4, int8, MXFP4, SRFT) for a shape; host arithmetic only, no HIP call.
- * An item is 16 head vectors: 16/heads consecutive tokens of one layer (all
- * heads) when heads divides 16 (*token_major = 1), else 16 consecutive
- * tokens of one (layer, head) (*token_major = 0).  Each wavefront runs
- * *items_per_wave consecutive items of the *n_items; the last one may run
- * fewer, and an item past the last token is partial.  Writes zeros for an
- * empty shape.  Errors as for kvq_quantize's shape checks, KVQ_ERR_NULL for
- * a NULL output pointer. */
-kvq_status kvq_item_plan(kvq_shape shape, int32_t* token_major, int64_t* n_items,
-                         int32_t* items_per_wave);
+/* Work decomposition of the quantize (inverse = 0) or dequantize
+ * (inverse = 1) kernels for a shape, for the Walsh-Hadamard formats (int4,
+ * int8, MXFP4; fourier = 0) or SRFT (fourier = 1); host arithmetic only, no
+ * HIP call.  An item is 16 head vectors: 16/heads consecutive tokens of one
+ * layer (all heads) when heads divides 16 (*token_major = 1), else 16
+ * consecutive tokens of one (layer, head) (*token_major = 0).  Each
+ * wavefront runs *items_per_wave consecutive items of the *n_items; the last
+ * one may run fewer, and an item past the last token is partial.  Writes
+ * zeros for an empty shape.  Errors as for kvq_quantize's shape checks,
+ * KVQ_ERR_NULL for a NULL output pointer. */
+kvq_status kvq_item_plan(kvq_shape shape, int32_t inverse, int32_t fourier, int32_t* token_major,
+                         int64_t* n_items, int32_t* items_per_wave);
 
 /* Static, human-readable name of a status code. */
 const char* kvq_status_string(kvq_status status);

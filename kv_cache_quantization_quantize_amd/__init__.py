@@ -99,7 +99,7 @@ def lib():
     L.kvq_attend_decode_workspace.restype = ctypes.c_int
     L.kvq_attend_decode_workspace.argtypes = [Shape, I32, ctypes.POINTER(I64)]
     L.kvq_item_plan.restype = ctypes.c_int
-    L.kvq_item_plan.argtypes = [Shape, ctypes.POINTER(I32), ctypes.POINTER(I64), ctypes.POINTER(I32)]
+    L.kvq_item_plan.argtypes = [Shape, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I64), ctypes.POINTER(I32)]
     L.kvq_status_string.restype = ctypes.c_char_p
     L.kvq_status_string.argtypes = [ctypes.c_int]
     L.kvq_last_error.restype = ctypes.c_char_p
@@ -462,9 +462,11 @@ def attend_decode(q, k_codes, k_scales, v_codes, v_scales, lam_k, lam_v, signs, 
 
 
 # ------------------------------------------------------ work decomposition
-def item_plan(L: int, T: int, H: int, D: int):
-    """(token_major, n_items, items_per_wave) of the quantize / dequantize
-    kernels for a [L, T, H, D] tensor (host arithmetic only)."""
+def item_plan(L: int, T: int, H: int, D: int, inverse: bool = False, fourier: bool = False):
+    """(token_major, n_items, items_per_wave) of the quantize (or, with
+    inverse, dequantize) kernels of the Walsh-Hadamard formats (or, with
+    fourier, SRFT) for a [L, T, H, D] tensor (host arithmetic only)."""
     tm, n, ipw = ctypes.c_int32(0), ctypes.c_int64(0), ctypes.c_int32(0)
-    _check(lib().kvq_item_plan(Shape(L, T, H, D), ctypes.byref(tm), ctypes.byref(n), ctypes.byref(ipw)))
+    _check(lib().kvq_item_plan(Shape(L, T, H, D), int(bool(inverse)), int(bool(fourier)), ctypes.byref(tm),
+                               ctypes.byref(n), ctypes.byref(ipw)))
     return bool(tm.value), int(n.value), int(ipw.value)

@@ -1,4 +1,5 @@
-"""Build libkvq.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
+"""Build libkvq.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc,
+and libkvq_stream.so (the benchmark's streaming-bandwidth kernels).
 
     python -m kv_cache_quantization_quantize_amd.build
 
@@ -20,6 +21,9 @@ OUT = os.path.join(HERE, "libkvq.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["kvq_int4.hip", "kvq_vq.hip", "kvq_attend.hip", "kvq_kmeans.hip", "kvq_api.cpp"]
+# practical-bandwidth kernels of the benchmark, in a library of their own
+STREAM_SOURCES = ["kvq_stream.hip"]
+STREAM_OUT = os.path.join(HERE, "libkvq_stream.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -65,21 +69,27 @@ def _compile(src: str, incremental: bool = False) -> str:
     return obj
 
 
-def build(verbose: bool = False, incremental: bool = False) -> str:
-    """Compile every source (incremental: only those whose object is older
-    than the source or a header) and link libkvq.so."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda src: _compile(src, incremental), SOURCES))
-    tmp = OUT + ".tmp%d" % os.getpid()
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("link of libkvq.so failed")
-    os.replace(tmp, OUT)
+        raise RuntimeError("link of %s failed" % os.path.basename(out))
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (incremental: only those whose object is older
+    than the source or a header), link libkvq.so, and link the benchmark's
+    streaming-bandwidth kernels into libkvq_stream.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(STREAM_SOURCES))) as ex:
+        objs = list(ex.map(lambda src: _compile(src, incremental), SOURCES + STREAM_SOURCES))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], STREAM_OUT)
     if verbose:
-        print("built", OUT)
+        print("built", OUT, "and", STREAM_OUT)
     return OUT
 
 

@@ -88,21 +88,38 @@ kvq_status check_params(const float* lambda, const int8_t* signs)
 
 kvq::Tensor4 t4(const kvq_view& v) { return kvq::Tensor4{v.data, v.stride_layer, v.stride_token, v.stride_head}; }
 
-// Consecutive items per wavefront: long runs keep lambda in registers; short
-// runs give small workloads enough wavefronts.
-int32_t items_per_wave(int64_t n_items)
+// Consecutive items per wavefront: about 2048 wavefronts (half of what the
+// 256 CUs hold at once) for small launches, so that every wavefront runs
+// several items and overlaps the next item's loads with the current item's
+// work; for large launches at most `cap` per wavefront.  Measured on MI355X
+// (19 GB Qwen3-8B-shaped tensors, head_dim 128): the Walsh-Hadamard
+// quantizers are fastest with runs of 2 (4.96 -> 4.55 ms against 16; short
+// runs keep more loads in flight across the chip, and their per-wavefront
+// set-up is a few multiplies), while the dequantizers and the SRFT kernels,
+// whose set-up (reciprocal multipliers, twiddles) costs more, are fastest
+// with 16 (2 costs 47% more); the head_dim-256 quantizer, which does not
+// prefetch, with 8.  The Qwen2.5-1.5B-shaped K cache dequantize went from
+// 38.6 to 28.4 us against one item per wavefront.
+int32_t items_per_wave(int64_t n_items, int64_t cap = 16)
 {
-    int64_t ipw = n_items / 16384;
+    int64_t ipw = (n_items + 2047) / 2048;
     if (ipw < 1) ipw = 1;
-    if (ipw > 64) ipw = 64;
+    if (ipw > cap) ipw = cap;
     return (int32_t)ipw;
+}
+
+// Run cap of the quantize / dequantize kernels (see items_per_wave).
+int64_t int4_run_cap(int64_t D, bool inverse, bool fourier)
+{
+    if (inverse || fourier) return 16;
+    return D <= 128 ? 2 : 8;
 }
 
 // Work items of the 4-lanes-per-vector kernels: token-major (16 consecutive
 // (token, head) vectors of a layer) when the head count divides 16, else
 // head-major (16 consecutive tokens of one (layer, head)).
 void set_items(const kvq_shape& s, int32_t& token_major, int32_t& h_shift, int32_t& items_per_group,
-               int32_t& tok_per_item, int32_t& ipw, int64_t& n_items)
+               int32_t& tok_per_item, int32_t& ipw, int64_t& n_items, int64_t cap = 16)
 {
     token_major = (kvq::kTokensPerTile % s.heads) == 0;
     h_shift = 0;
@@ -116,7 +133,7 @@ void set_items(const kvq_shape& s, int32_t& token_major, int32_t& h_shift, int32
         items_per_group = (int32_t)((s.tokens + kvq::kTokensPerTile - 1) / kvq::kTokensPerTile);
         n_items = s.layers * s.heads * (int64_t)items_per_group;
     }
-    ipw = items_per_wave(n_items);
+    ipw = items_per_wave(n_items, cap);
 }
 
 // Compute units of the current device (cached per device).
@@ -173,7 +190,8 @@ kvq_status int4_common(const kvq_shape& shape, const kvq_view& x, const float* l
     a.scales = t4(scales);
     a.lambda = lambda;
     a.signs = signs;
-    set_items(shape, a.token_major, a.h_shift, a.items_per_group, a.tok_per_item, a.items_per_wave, a.n_items);
+    set_items(shape, a.token_major, a.h_shift, a.items_per_group, a.tok_per_item, a.items_per_wave, a.n_items,
+              int4_run_cap(D, x_is_output, fourier));
     return KVQ_OK;
 }
 
@@ -598,7 +616,8 @@ kvq_status kvq_kmeans_step(kvq_shape shape, kvq_view x_f16, const float* lambda,
     return hip_status(kvq::launch_kmeans_update(a, static_cast<hipStream_t>(stream)), "kvq_kmeans_step launch");
 }
 
-kvq_status kvq_item_plan(kvq_shape shape, int32_t* token_major, int64_t* n_items, int32_t* items_per_wave)
+kvq_status kvq_item_plan(kvq_shape shape, int32_t inverse, int32_t fourier, int32_t* token_major,
+                         int64_t* n_items, int32_t* items_per_wave)
 {
     g_err[0] = 0;
     if (!token_major || !n_items || !items_per_wave)
@@ -609,7 +628,8 @@ kvq_status kvq_item_plan(kvq_shape shape, int32_t* token_major, int64_t* n_items
     KVQ_TRY(check_shape(shape));
     if (empty(shape)) return KVQ_OK;
     int32_t h_shift, items_per_group, tok_per_item;
-    set_items(shape, *token_major, h_shift, items_per_group, tok_per_item, *items_per_wave, *n_items);
+    set_items(shape, *token_major, h_shift, items_per_group, tok_per_item, *items_per_wave, *n_items,
+              int4_run_cap(shape.head_dim, inverse != 0, fourier != 0));
     return KVQ_OK;
 }
 

@@ -322,20 +322,28 @@ def test_mxfp4_validation(lib):
 
 def test_item_plan(lib):
     """The work decomposition the multi-item parity tests rely on: several
-    items per wavefront, a partial last item, runs that cross a lambda key."""
+    items per wavefront, a partial last item, runs that cross a lambda key;
+    runs of at most 2 for the head_dim-128 Walsh-Hadamard quantizers, 8 for
+    the head_dim-256 ones, 16 for the dequantizers and SRFT."""
     # token-major: 16 / H tokens of all heads per item
-    assert kvq.item_plan(5, 80001, 2, 128) == (True, 5 * 10001, 3)
-    assert kvq.item_plan(4, 65540, 2, 128) == (True, 4 * 8193, 2)
-    assert kvq.item_plan(3, 200003, 1, 256) == (True, 3 * 12501, 2)
+    assert kvq.item_plan(5, 80001, 2, 128) == (True, 5 * 10001, 2)
+    assert kvq.item_plan(5, 80001, 2, 128, inverse=True) == (True, 5 * 10001, 16)
+    assert kvq.item_plan(5, 80001, 2, 128, fourier=True) == (True, 5 * 10001, 16)
+    assert kvq.item_plan(3, 200003, 1, 256) == (True, 3 * 12501, 8)
+    assert kvq.item_plan(3, 200003, 1, 256, inverse=True, fourier=True) == (True, 3 * 12501, 16)
     # head-major: 16 tokens of one (layer, head) per item
     assert kvq.item_plan(3, 65541, 3, 128) == (False, 9 * 4097, 2)
-    assert kvq.item_plan(2, 87400, 3, 256) == (False, 6 * 5463, 2)
-    # small launches run one item per wavefront; long ones at most 64
+    assert kvq.item_plan(2, 87400, 3, 256, inverse=True) == (False, 6 * 5463, 16)
+    # about 2048 wavefronts for small launches
     assert kvq.item_plan(1, 64, 2, 128) == (True, 8, 1)
-    assert kvq.item_plan(28, 4096, 2, 128)[2] == 1
-    assert kvq.item_plan(36, 262144, 8, 128) == (True, 36 * 131072, 64)
+    assert kvq.item_plan(1, 16 * 2048, 1, 128, inverse=True) == (True, 2048, 1)
+    assert kvq.item_plan(1, 16 * 2049, 1, 128, inverse=True) == (True, 2049, 2)
+    assert kvq.item_plan(28, 4096, 2, 128, inverse=True) == (True, 28 * 512, 7)
+    assert kvq.item_plan(28, 4096, 2, 128) == (True, 28 * 512, 2)
+    assert kvq.item_plan(36, 262144, 8, 128) == (True, 36 * 131072, 2)
+    assert kvq.item_plan(36, 262144, 8, 128, inverse=True) == (True, 36 * 131072, 16)
     assert kvq.item_plan(0, 5, 3, 128) == (False, 0, 0)
     with pytest.raises(kvq.KvqError):
         kvq.item_plan(1, 5, 3, 96)
     tm, n, ipw = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
-    assert lib.kvq_item_plan(shape(), None, ctypes.byref(n), ctypes.byref(ipw)) == NULL
+    assert lib.kvq_item_plan(shape(), 0, 0, None, ctypes.byref(n), ctypes.byref(ipw)) == NULL

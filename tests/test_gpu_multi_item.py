@@ -10,9 +10,10 @@ Each case is checked two ways, through the C ABI via the binding:
   * against the fp64 oracle (contract in tests/parity.py) on every vector of
     every wavefront that holds a key boundary, the first and last
     wavefronts, and a seeded sample elsewhere;
-  * on every vector, bit for bit, against one call per layer, which runs one
-    item per wavefront (the decomposition every other parity test covers)
-    and computes each vector with the same arithmetic.
+  * on every vector, bit for bit, against calls over chunks of one layer's
+    tokens small enough (at most 2048 items) to run one item per wavefront
+    (the decomposition most other parity tests cover), which compute each
+    vector with the same arithmetic.
 Outputs are written into views of token-padded, sentinel-filled buffers, and
 the padding must come back untouched."""
 import math
@@ -63,8 +64,8 @@ def _fmt(name, G):
     raise KeyError(name)
 
 
-def _geometry(L, T, H, D):
-    tm, n_items, ipw = kvq.item_plan(L, T, H, D)
+def _geometry(L, T, H, D, inverse, fourier):
+    tm, n_items, ipw = kvq.item_plan(L, T, H, D, inverse=inverse, fourier=fourier)
     tpi = 16 // H if tm else 16
     ipg = math.ceil(T / tpi)                   # items per lambda key
     assert n_items == (L if tm else L * H) * ipg
@@ -80,26 +81,29 @@ def _item_rows(item, tm, tpi, ipg, T, H):
     return [(l, t, h) for t in range(t0, min(t0 + 16, T))]
 
 
-def boundary_rows(L, T, H, D, seed, n_sample=1024):
+def boundary_rows(L, T, H, D, seed, fourier=False, n_sample=1024):
     """Every vector of the wavefronts that hold a key boundary, of the first
-    and the last wavefront, plus a seeded sample; and the facts the shape was
-    chosen for."""
-    tm, n_items, ipw, tpi, ipg = _geometry(L, T, H, D)
-    n_waves = math.ceil(n_items / ipw)
-    waves = {0, n_waves - 1}
-    straddling = 0
-    for b in range(ipg, n_items, ipg):         # first item of each key after the first
-        w0, w1 = (b - 1) // ipw, b // ipw
-        waves.update((w0, w1))
-        straddling += w0 == w1
-    out = []
-    for w in sorted(waves):
-        for item in range(w * ipw, min((w + 1) * ipw, n_items)):
-            out.extend(_item_rows(item, tm, tpi, ipg, T, H))
+    and the last wavefront, in the quantize and in the dequantize plan (their
+    runs differ), plus a seeded sample; and, per plan, the facts the shape
+    was chosen for."""
+    out, facts = [], {}
+    for inverse in (False, True):
+        tm, n_items, ipw, tpi, ipg = _geometry(L, T, H, D, inverse, fourier)
+        n_waves = math.ceil(n_items / ipw)
+        waves = {0, n_waves - 1}
+        straddling = 0
+        for b in range(ipg, n_items, ipg):         # first item of each key after the first
+            w0, w1 = (b - 1) // ipw, b // ipw
+            waves.update((w0, w1))
+            straddling += w0 == w1
+        for w in sorted(waves):
+            for item in range(w * ipw, min((w + 1) * ipw, n_items)):
+                out.extend(_item_rows(item, tm, tpi, ipg, T, H))
+        facts["dequantize" if inverse else "quantize"] = {
+            "token_major": tm, "items_per_wave": ipw, "straddling_waves": straddling,
+            "partial_last_item": T % tpi != 0, "ragged_last_wave": n_items % ipw != 0}
     smp = synth.sample_rows(L, T, H, n_sample, seed).numpy()
     idx = np.unique(np.concatenate([np.array(out, dtype=np.int64), smp]), axis=0)
-    facts = {"token_major": tm, "items_per_wave": ipw, "straddling_waves": straddling,
-             "partial_last_item": T % tpi != 0, "ragged_last_wave": n_items % ipw != 0}
     return idx, facts
 
 
@@ -118,16 +122,20 @@ def test_multi_item_wavefronts(fmt, L, T, H, D, G):
     dev = device()
     quant, dequant, check, cdiv, sgrp, sdt, cdt = _fmt(fmt, G)
     seed = L * 7919 + T + H * 31 + D + G
-    log("multi-item %s shape=%s G=%d plan=%s" % (fmt, (L, T, H, D), G, kvq.item_plan(L, T, H, D)))
+    log("multi-item %s shape=%s G=%d" % (fmt, (L, T, H, D), G))
     x = synth.draw(L, T, H, D, synth.Dist("normal", lognormal_channels=True), seed, seed + 1, dev)
     g = torch.Generator(device="cpu").manual_seed(seed + 2)
     lam = torch.exp(0.3 * torch.randn((L, H, D), generator=g)).to(torch.float32).to(dev)
     s = (torch.randint(0, 2, (D,), generator=g) * 2 - 1).to(torch.int8).to(dev)
 
-    idx, facts = boundary_rows(L, T, H, D, seed + 3)
-    assert facts["items_per_wave"] > 1 and facts["straddling_waves"] > 0 and facts["partial_last_item"], facts
-    for l in range(L):
-        assert kvq.item_plan(1, T, H, D)[2] == 1          # the per-layer reference runs one item per wave
+    idx, facts = boundary_rows(L, T, H, D, seed + 3, fourier=fmt == "srft")
+    for f in facts.values():
+        assert f["items_per_wave"] > 1 and f["straddling_waves"] > 0 and f["partial_last_item"], facts
+    assert any(f["ragged_last_wave"] for f in facts.values()), facts
+    tm = facts["quantize"]["token_major"]
+    chunk = 2048 * (16 // H) if tm else 16 * (2048 // H)      # tokens per one-item-per-wave call
+    for inverse in (False, True):
+        assert kvq.item_plan(1, chunk, H, D, inverse=inverse, fourier=fmt == "srft")[2] == 1
 
     sfill = 0x7BFF if sdt == torch.float16 else 0xA5
     cbuf, codes = _padded(L, T, H, D // cdiv, cdt, 0x5A, dev)
@@ -146,18 +154,23 @@ def test_multi_item_wavefronts(fmt, L, T, H, D, G):
                 rows(out, idx))
     log("multi-item %s %s: %d rows %s; %s" % (fmt, (L, T, H, D, G), len(idx), facts, parity.summary(rep)))
 
-    # every vector against per-layer calls (one item per wavefront)
+    # every vector against token-chunked calls of one layer (one item per wavefront)
+    c1 = torch.empty((1, chunk) + tuple(codes.shape[2:]), dtype=codes.dtype, device=dev)
+    s1 = torch.empty((1, chunk) + tuple(scales.shape[2:]), dtype=scales.dtype, device=dev)
+    o1 = torch.empty((1, chunk, H, D), dtype=torch.float16, device=dev)
     for l in range(L):
-        c1 = torch.empty_like(codes[l:l + 1])
-        s1 = torch.empty_like(scales[l:l + 1])
-        o1 = torch.empty_like(out[l:l + 1])
-        quant(x[l:l + 1], lam[l:l + 1].contiguous(), s, c1, s1)
-        dequant(c1, s1, lam[l:l + 1].contiguous(), s, o1)
-        torch.cuda.synchronize()
-        for a, b, what in ((codes[l:l + 1], c1, "codes"), (scales[l:l + 1], s1, "scales"),
-                           (out[l:l + 1], o1, "dequantized")):
-            av = a.contiguous().view(torch.uint8)
-            bv = b.contiguous().view(torch.uint8)
-            if not torch.equal(av, bv):
-                bad = (av != bv).nonzero()[:5].tolist()
-                raise AssertionError("%s of layer %d differ from the one-item-per-wave run at %s" % (what, l, bad))
+        lam1 = lam[l:l + 1].contiguous()
+        for t0 in range(0, T, chunk):
+            n = min(chunk, T - t0)
+            quant(x[l:l + 1, t0:t0 + n], lam1, s, c1[:, :n], s1[:, :n])
+            dequant(c1[:, :n], s1[:, :n], lam1, s, o1[:, :n])
+            torch.cuda.synchronize()
+            for a, b, what in ((codes[l:l + 1, t0:t0 + n], c1[:, :n], "codes"),
+                               (scales[l:l + 1, t0:t0 + n], s1[:, :n], "scales"),
+                               (out[l:l + 1, t0:t0 + n], o1[:, :n], "dequantized")):
+                av = a.contiguous().view(torch.uint8)
+                bv = b.contiguous().view(torch.uint8)
+                if not torch.equal(av, bv):
+                    bad = (av != bv).nonzero()[:5].tolist()
+                    raise AssertionError("%s of layer %d, tokens %d.. differ from the one-item-per-wave run at %s"
+                                         % (what, l, t0, bad))
