@@ -27,10 +27,19 @@
 //
 // The codebook (<= 4096 centroids at a time, 64 KB) and its norms live in
 // LDS; a block of WAVES wavefronts shares it, each wavefront rotating 16 keys
-// of one (layer, head) and sweeping the codebook for GPR groups of 32
-// sub-vectors per pass.  Contraction work per key: D/8 x K x 8 MACs; the MFMAs
-// execute 2x that for the hi/lo split plus one half-size norm MFMA per tile
-// and GPR groups (2.25x in all for GPR = 4).
+// of one (layer, head) and sweeping the codebook for GPR (up to 8) groups of
+// 32 sub-vectors per pass.  Contraction work per key: D/8 x K x 8 MACs; the
+// MFMAs execute 2x that for the hi/lo split plus one half-size norm MFMA per
+// tile and GPR groups (2.125x for GPR = 8; in matrix-core time the norm MFMA
+// costs as much as a full one, 2.25x).
+//
+// What bounds the sweep (measured on MI355X with a timing probe of the
+// loop): a 32x32x16 f16 MFMA issues every 32 cycles, and the 32x32x8 norm
+// MFMA takes as long; v_max3_f32 takes about 8 cycles per wavefront, and
+// every score passes through one (16 scores per lane, group and tile: 7 max3
+// and 2 max), so with two wavefronts per SIMD the maxima cost about as much
+// SIMD time as the nine MFMAs of a tile.  The kernel therefore runs near the
+// balance of the two units rather than at the matrix cores' peak.
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -50,7 +59,7 @@ struct VqCfg {
     static constexpr int NJ = D / 32;              // 16-byte chunks per lane
     static constexpr int N = D / 4;                // coordinates per lane
     static constexpr int NGRP = D / 16;            // groups of 32 sub-vectors per 16 keys
-    static constexpr int GPR = NGRP < 4 ? NGRP : 4;   // groups per codebook sweep
+    static constexpr int GPR = NGRP < 8 ? NGRP : 8;   // groups per codebook sweep
     static constexpr int ROUNDS = NGRP / GPR;
     static constexpr int WAVES = (D == 256) ? 4 : 8;  // wavefronts per block (LDS budget)
 };
@@ -65,6 +74,15 @@ struct VqDecLds {
 __device__ __forceinline__ h8_t as_h8(uint4 u) { return __builtin_bit_cast(h8_t, u); }
 __device__ __forceinline__ h4_t as_h4(uint2 u) { return __builtin_bit_cast(h4_t, u); }
 
+
+// LDS slot of centroid k of a codebook chunk: rows are permuted within their
+// 32-centroid tile by the tile index, k ^ ((k / 32) % 16).  The sweep reads a
+// whole tile (one centroid per lane) and stays conflict-free; the re-score
+// gathers the same row of different best tiles across lanes, which without
+// the permutation all fall into the same four LDS banks (a 16-byte centroid
+// per row, 32 rows per tile): measured on MI355X, 77% of the encoder's LDS
+// cycles were bank conflicts.
+__device__ __forceinline__ int cb_slot(int k) { return k ^ ((k >> 5) & 15); }
 
 // Swizzled position of 16-byte sub-vector chunk s of key v in a staging row.
 template <int NS>
@@ -90,7 +108,6 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
     // and leaves four candidates (1.45 -> 0.96 ms for 2.4 M keys; sub-blocks
     // of 8 or 2 scores, or single scores, were slower).
     constexpr int NSUB = IDX8 ? 4 : 1, SUBW = 16 / NSUB;
-    constexpr int EPI_OPS = NSUB == 1 ? 10 : 20;           // VALU operations per group and tile
     __shared__ uint4 cb_lds[CHUNK];                    // centroid k: 8 fp16
     __shared__ uint32_t nrm_lds[CHUNK];                // packed (n_hi, n_lo)
     __shared__ uint4 stage[WAVES][2][16 * NS];         // [wave][hi/lo][key, sub-vector]
@@ -217,8 +234,8 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
                         }
                         const _Float16 nh = (_Float16)n;
                         const _Float16 nl = (_Float16)(n - (float)nh);
-                        cb_lds[k] = cv;
-                        nrm_lds[k] = __builtin_bit_cast(uint32_t, half2_t{nh, nl});
+                        cb_lds[cb_slot(k)] = cv;
+                        nrm_lds[cb_slot(k)] = __builtin_bit_cast(uint32_t, half2_t{nh, nl});
                     }
                     __syncthreads();
                     cur_cb = nchunks > 1 ? -1 : cbkey;
@@ -226,124 +243,144 @@ __global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs 
 
                 // ---- sweep the chunk: 32 centroids per MFMA tile -------------------
                 // The norm tile -(n_hi + n_lo)/2 is one MFMA per tile, shared by all
-                // groups as their accumulator input.  Software pipeline: tile t+1's
-                // MFMAs are issued (and tile t+2's operands read from LDS) before
-                // tile t's epilogue runs, so the matrix core and the VALU overlap.
+                // GPR groups as their accumulator input.  One accumulator per group:
+                // group g's epilogue of tile t-1 runs right before its MFMA of tile t
+                // (which overwrites the accumulator), GPR MFMAs after the one that
+                // produced it, so the matrix core runs tile t while the VALU takes
+                // the maxima of tile t-1.  (A second set of accumulators, with half
+                // the groups per sweep, ran 4% slower and needed 64 more VGPRs.)
                 const int ntiles = (kc + 31) / 32;
                 int best_tile[GPR];
 #pragma unroll
                 for (int gg = 0; gg < GPR; gg++) best_tile[gg] = -1;
-                const uint4* cb_col = cb_lds + col;
-                const uint32_t* nrm_col = nrm_lds + col;
                 auto read_a = [&](int tl, h8_t& aop, h4_t& a2) {
-                    const int base = tl * 32;
-                    aop = as_h8(cb_col[base]);
-                    a2 = as_h4(make_uint2(nrm_col[base], 0u));
+                    const int slot = cb_slot(tl * 32 + col);       // centroid tl * 32 + col
+                    aop = as_h8(cb_lds[slot]);
+                    a2 = as_h4(make_uint2(nrm_lds[slot], 0u));
                 };
-                auto issue = [&](const h8_t& aop, const h4_t& a2, f32x16_t (&acc)[GPR]) {
+                auto norm_tile = [&](const h4_t& a2) {
                     const f32x16_t zero = {};
-                    const f32x16_t nt = __builtin_amdgcn_mfma_f32_32x32x8f16(a2, b2, zero, 0, 0, 0);
-#pragma unroll
-                    for (int gg = 0; gg < GPR; gg++)
-                        acc[gg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop[gg], nt, 0, 0, 0);
+                    return __builtin_amdgcn_mfma_f32_32x32x8f16(a2, b2, zero, 0, 0, 0);
                 };
-                auto epilogue = [&](const f32x16_t (&acc)[GPR], int tl) {
+                // Maximum of group gg's 16 tile scores (a max3 tree) against the
+                // best so far, and the tile index where the best grew (strict >, so
+                // the earliest tile keeps a tie; with one-byte indices, per quarter
+                // of the tile's 16 scores).  The tree's temporary, unlike a chain
+                // through the running best, lets the running maxima keep their
+                // registers (a chain made the compiler rotate them: eight moves per
+                // tile).
+                auto epilogue = [&](const f32x16_t& acc, int gg, int tl) {
+                    if constexpr (NSUB == 1) {
+                        float mx = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
 #pragma unroll
-                    for (int gg = 0; gg < GPR; gg++) {
-                        if constexpr (NSUB == 1) {
-                            float mx = fmaxf(fmaxf(acc[gg][0], acc[gg][1]), acc[gg][2]);
+                        for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
+                        mx = fmaxf(mx, acc[15]);
+                        best_tile[gg] = mx > best_val[gg] ? tl : best_tile[gg];
+                        best_val[gg] = fmaxf(mx, best_val[gg]);
+                    } else {
 #pragma unroll
-                            for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[gg][r]), acc[gg][r + 1]);
-                            mx = fmaxf(mx, acc[gg][15]);
-                            if (mx > best_val[gg]) {
-                                best_val[gg] = mx;
-                                best_tile[gg] = tl;
-                            }
-                        } else {
+                        for (int sb = 0; sb < NSUB; sb++) {
+                            float nb = fmaxf(best_val[gg], acc[SUBW * sb]);
 #pragma unroll
-                            for (int sb = 0; sb < NSUB; sb++) {
-                                float mx = acc[gg][SUBW * sb];
-#pragma unroll
-                                for (int r = 1; r < SUBW; r++) mx = fmaxf(mx, acc[gg][SUBW * sb + r]);
-                                if (mx > best_val[gg]) {
-                                    best_val[gg] = mx;
-                                    best_tile[gg] = tl * NSUB + sb;
-                                }
-                            }
+                            for (int r = 1; r < SUBW; r++) nb = fmaxf(nb, acc[SUBW * sb + r]);
+                            best_tile[gg] = nb > best_val[gg] ? tl * NSUB + sb : best_tile[gg];
+                            best_val[gg] = nb;
                         }
                     }
                 };
-                // Interleave one tile's MFMAs with the previous tile's epilogue (one
-                // group's max tree between consecutive MFMAs; the first gap also
-                // covers the norm MFMA's latency before the dependent mains).
-                auto interleave = [&]() {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // norm MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // operand reads
-                    __builtin_amdgcn_sched_group_barrier(0x002, EPI_OPS, 0);
-#pragma unroll
-                    for (int gg = 0; gg < GPR; gg++) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, EPI_OPS, 0);
-                    }
-                };
-                f32x16_t acc0[GPR], acc1[GPR];
+                f32x16_t acc[GPR], nt0, nt1;
                 h8_t a_op;
                 h4_t a_n2;
                 read_a(0, a_op, a_n2);
-                issue(a_op, a_n2, acc0);
+                nt0 = norm_tile(a_n2);
+#pragma unroll
+                for (int gg = 0; gg < GPR; gg++)
+                    acc[gg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op, bop[gg], nt0, 0, 0, 0);
                 read_a(min(1, ntiles - 1), a_op, a_n2);
-                for (int tl = 0; tl < ntiles; tl += 2) {
-                    // tile tl+1 may not exist: its MFMAs then run on a repeated tile
-                    // and their result is never read
-                    issue(a_op, a_n2, acc1);
-                    read_a(min(tl + 2, ntiles - 1), a_op, a_n2);
-                    epilogue(acc0, tl);
-                    interleave();
-                    if (tl + 1 >= ntiles) break;
-                    issue(a_op, a_n2, acc0);
-                    read_a(min(tl + 3, ntiles - 1), a_op, a_n2);
-                    epilogue(acc1, tl + 1);
-                    interleave();
+                // tile tl: the maxima of tile tl - 1, then tile tl's MFMAs; the norm
+                // tiles alternate between two registers sets (unrolled by two)
+                auto step = [&](int tl, f32x16_t& nt) {
+                    nt = norm_tile(a_n2);
+#pragma unroll
+                    for (int gg = 0; gg < GPR; gg++) {
+                        epilogue(acc[gg], gg, tl - 1);
+                        acc[gg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op, bop[gg], nt, 0, 0, 0);
+                    }
+                    read_a(min(tl + 1, ntiles - 1), a_op, a_n2);
+                    // norm MFMA, then each group's maxima right before its MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+                    for (int gg = 0; gg < GPR; gg++) {
+                        __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+                };
+                int tl = 1;
+                for (; tl + 1 < ntiles; tl += 2) {
+                    step(tl, nt1);
+                    step(tl + 1, nt0);
                 }
+                if (tl < ntiles) step(tl, nt1);
+#pragma unroll
+                for (int gg = 0; gg < GPR; gg++) epilogue(acc[gg], gg, ntiles - 1);
 
                 // ---- lanes whose best moved into this chunk find its position -------
+                // The GPR groups' candidates are scored together, one candidate row
+                // of every group at a time, so that their LDS reads are in flight
+                // together (scored one group after another, the dependent read ->
+                // score chains left this phase latency-bound: a fifth of the
+                // kernel's time).  Lanes whose best did not move into this chunk
+                // (best_tile < 0) score tile 0 and discard the result.
+                {
+                    float y[GPR][8], bs[GPR];
+                    int bt[GPR], r0[GPR], bk[GPR];
 #pragma unroll
-                for (int gg = 0; gg < GPR; gg++) {
-                    if (best_tile[gg] >= 0) {
+                    for (int gg = 0; gg < GPR; gg++) {
                         const int sv = 32 * (rd * GPR + gg) + col;
                         const int ss = stage_slot<NS>(sv / NS, sv % NS);
                         const uint4 yh = stage[wid][0][ss], yl = stage[wid][1][ss];
                         const uint32_t hwv[4] = {yh.x, yh.y, yh.z, yh.w}, lwv[4] = {yl.x, yl.y, yl.z, yl.w};
-                        float y[8];
 #pragma unroll
                         for (int e = 0; e < 4; e++) {
-                            y[2 * e] = lo_half(hwv[e]) + lo_half(lwv[e]);
-                            y[2 * e + 1] = hi_half(hwv[e]) + hi_half(lwv[e]);
+                            y[gg][2 * e] = lo_half(hwv[e]) + lo_half(lwv[e]);
+                            y[gg][2 * e + 1] = hi_half(hwv[e]) + hi_half(lwv[e]);
                         }
-                        float bs = -__builtin_inff();
-                        int bk = 0;
-                        const int bt = best_tile[gg] / NSUB, r0 = SUBW * (best_tile[gg] % NSUB);
+                        const int b = max(best_tile[gg], 0);
+                        bt[gg] = b / NSUB;
+                        r0[gg] = SUBW * (b % NSUB);
+                        bs[gg] = -__builtin_inff();
+                        bk[gg] = 0;
+                    }
 #pragma unroll
-                        for (int rr = 0; rr < SUBW; rr++) {
-                            const int r = r0 + rr;
-                            const int row = 8 * (r / 4) + 4 * half + (r % 4);
-                            const int k = bt * 32 + row;
-                            const uint4 cv = cb_lds[k];
-                            const uint32_t nw = nrm_lds[k];
-                            const uint32_t w[4] = {cv.x, cv.y, cv.z, cv.w};
-                            float sc = -0.5f * (lo_half(nw) + hi_half(nw));
+                    for (int rr = 0; rr < SUBW; rr++) {
+                        uint4 cv[GPR];
+                        uint32_t nw[GPR];
+                        int kk[GPR];
+#pragma unroll
+                        for (int gg = 0; gg < GPR; gg++) {
+                            const int r = r0[gg] + rr;
+                            kk[gg] = bt[gg] * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                            cv[gg] = cb_lds[cb_slot(kk[gg])];
+                            nw[gg] = nrm_lds[cb_slot(kk[gg])];
+                        }
+#pragma unroll
+                        for (int gg = 0; gg < GPR; gg++) {
+                            const uint32_t w[4] = {cv[gg].x, cv[gg].y, cv[gg].z, cv[gg].w};
+                            float sc = -0.5f * (lo_half(nw[gg]) + hi_half(nw[gg]));
 #pragma unroll
                             for (int e = 0; e < 4; e++) {
-                                sc = fmaf(lo_half(w[e]), y[2 * e], sc);
-                                sc = fmaf(hi_half(w[e]), y[2 * e + 1], sc);
+                                sc = fmaf(lo_half(w[e]), y[gg][2 * e], sc);
+                                sc = fmaf(hi_half(w[e]), y[gg][2 * e + 1], sc);
                             }
-                            if (sc > bs) {
-                                bs = sc;
-                                bk = k;
+                            if (sc > bs[gg]) {
+                                bs[gg] = sc;
+                                bk[gg] = kk[gg];
                             }
                         }
-                        best_idx[gg] = min(kbase + bk, a.K - 1);     // a padded row is centroid K - 1
                     }
+#pragma unroll
+                    for (int gg = 0; gg < GPR; gg++)
+                        if (best_tile[gg] >= 0) best_idx[gg] = min(kbase + bk[gg], a.K - 1);  // a padded row is centroid K - 1
                 }
             }
 
