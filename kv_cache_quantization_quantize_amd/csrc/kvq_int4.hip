@@ -253,20 +253,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
         uint16_t sv[NSV];
     };
 
+    // In a partial item the lanes past the last token load the last token's
+    // vector: every vector is computed on its own quad and theirs are never
+    // stored, so the loads stay unconditional (masked loads cost the
+    // register zeroing on every item).
     auto load = [&](int item, uint4(&buf)[NJ]) {
         const Item it = decode_item<TM>(item, a);
-        const _Float16* p = xg + outer_offset(a.x, it) + x_lane;
-        if (it.full) {
+        int64_t off = outer_offset(a.x, it) + x_lane;
+        if (!it.full) off += (int64_t)(min(lm.tok, a.T - 1 - it.t0) - lm.tok) * a.x.st;
+        const _Float16* p = xg + off;
 #pragma unroll
-            for (int j = 0; j < NJ; j++) buf[j] = *reinterpret_cast<const uint4*>(p + j * 32);
-        } else {
-#pragma unroll
-            for (int j = 0; j < NJ; j++) buf[j] = make_uint4(0, 0, 0, 0);
-            if (it.t0 + lm.tok < a.T) {
-#pragma unroll
-                for (int j = 0; j < NJ; j++) buf[j] = *reinterpret_cast<const uint4*>(p + j * 32);
-            }
-        }
+        for (int j = 0; j < NJ; j++) buf[j] = *reinterpret_cast<const uint4*>(p + j * 32);
     };
 
     // Code bytes are transposed within each quad through a wave-private LDS
@@ -513,10 +510,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
         uint4 o[NJ];
     };
 
+    // Lanes past the last token of a partial item load the last token's
+    // codes and scales (their outputs are never stored), so the loads stay
+    // unconditional.
     auto load = [&](int item, Raw& raw) {
         const Item it = decode_item<TM>(item, a);
-        const uint8_t* cp = cg + outer_offset(a.codes, it) + c_lane;
-        const uint16_t* sp = sg + outer_offset(a.scales, it) + s_lane;
+        int64_t coff = outer_offset(a.codes, it) + c_lane, soff = outer_offset(a.scales, it) + s_lane;
+        if (!it.full) {
+            const int dt = min(lm.tok, a.T - 1 - it.t0) - lm.tok;
+            coff += (int64_t)dt * a.codes.st;
+            soff += (int64_t)dt * a.scales.st;
+        }
+        const uint8_t* cp = cg + coff;
+        const uint16_t* sp = sg + soff;
         auto ld = [&]() {
             if constexpr (BITS == 4) {
 #pragma unroll
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
                 }
             }
             if constexpr (MX) {
-                const uint8_t* sp8 = reinterpret_cast<const uint8_t*>(sg) + outer_offset(a.scales, it) + s_lane;
+                const uint8_t* sp8 = reinterpret_cast<const uint8_t*>(sg) + soff;
 #pragma unroll
                 for (int g = 0; g < NG; g++) raw.sw[g] = sp8[g];
             } else if constexpr (NG == 1) {
@@ -543,15 +549,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
                 for (int i = 0; i < NW; i++) raw.sw[i] = reinterpret_cast<const u32_a2*>(sp)[i];
             }
         };
-        if (it.full) {
-            ld();
-        } else {
-#pragma unroll
-            for (int j = 0; j < NJ * WPJ; j++) raw.w[j] = 0u;      // code 0
-#pragma unroll
-            for (int i = 0; i < (MX ? NG : NW); i++) raw.sw[i] = 0;
-            if (it.t0 + lm.tok < a.T) ld();
-        }
+        ld();
     };
 
     // The item's 16 output vectors (16 * 2D bytes) are staged through a
