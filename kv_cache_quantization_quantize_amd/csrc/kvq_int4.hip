@@ -160,8 +160,9 @@ struct QuantShape {
 // the item's one register buffer as soon as the first stage has consumed it
 // (a second buffer, with the loop unrolled by two, took 12 to 41 more VGPRs:
 // a wave per SIMD less for the quantizers and the SRFT dequantizer).
-// Without it (head_dim 256) each item's loads are issued right before its
-// first stage, and only the stores are deferred.
+// Without it (the head_dim-256 dequantizers and SRFT quantizer, where a
+// prefetch buffer would cost a wave per SIMD) each item's loads are issued
+// right before its first stage, and only the stores are deferred.
 template <typename Buf, typename Out, int N, bool PREFETCH, typename Load, typename First, typename Store,
           typename Finish>
 __device__ __forceinline__ void run_pipeline(int begin, int end, Load&& load, First&& first_stage,
@@ -457,7 +458,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
         }
     };
 
-    run_pipeline<uint4[NJ], Out, N, (D <= 128)>(begin, end, load, first_stage, store, finish);
+    // the head_dim-256 quantizers prefetch too (two waves per SIMD either
+    // way), except SRFT, which would drop to one
+    run_pipeline<uint4[NJ], Out, N, (D <= 128 || !FT)>(begin, end, load, first_stage, store, finish);
 }
 
 // ---------------------------------------------------------------------------
