@@ -351,7 +351,7 @@ kvq_status vq_decode_any(kvq_shape shape, kvq_view idx, const void* codebook_f16
     if (empty(shape)) return KVQ_OK;
     a.dec_rows_per_range = 0;
     a.dec_range_groups = 0;
-    if (n_centroids <= kvq::kVqChunk) {
+    if (n_centroids <= kvq::kVqChunk && shape.tokens >= kvq::kTokensPerTile) {
         // codebook in LDS: one block per CU.  The (layer, 16-token tile) rows
         // are cut into ranges; each range is decoded by H blocks, one per
         // head, placed on the same XCD so that the heads' indices of a token,

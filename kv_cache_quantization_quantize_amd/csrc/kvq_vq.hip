@@ -617,10 +617,18 @@ __global__ __launch_bounds__(64 * VqDecLds<D>::WAVES) void vq_decode_lds_kernel(
         if (begin >= end) continue;
 
         const uint8_t* ig_lh = ig + ((int64_t)l * a.idx.sl + (int64_t)h * a.idx.sh) * ISZ;
-        // the quad's index row; tokens past the end read the last token's
+        // Per-lane parts of the index and output addresses, fixed for the
+        // segment.  The host sends only T >= 16 here, and an item's first
+        // token is clamped to T - 16: the last item of a (layer, head) ends at
+        // its last token and recomputes (rewrites with the same bytes) the
+        // tokens it shares with the item before it, so no load or store is
+        // ever masked or clamped per lane.
+        const int64_t idx_lane = (int64_t)slot * a.idx.st * ISZ;
+        const int64_t out_lane = (int64_t)(lane / CV) * a.x.st + row_c * 8;     // + k * VPK rows
+        auto first_token = [&](int item) { return min(item * kTokensPerTile, a.T - kTokensPerTile); };
+        // the quad's index row
         auto load_idx = [&](int item, uint4 (&W)[NIW]) {
-            const int t = min(item * kTokensPerTile + slot, a.T - 1);
-            const uint8_t* ip = ig_lh + (int64_t)t * a.idx.st * ISZ;
+            const uint8_t* ip = ig_lh + (int64_t)first_token(item) * a.idx.st * ISZ + idx_lane;
             if constexpr (IB >= 16) {
 #pragma unroll
                 for (int i = 0; i < NIW; i++) W[i] = *reinterpret_cast<const uint4_a4*>(ip + 16 * i);
@@ -678,15 +686,12 @@ __global__ __launch_bounds__(64 * VqDecLds<D>::WAVES) void vq_decode_lds_kernel(
                 o.w = pack_half2(v[j * 8 + 6] * m[j * 8 + 6], v[j * 8 + 7] * m[j * 8 + 7]);
                 my_out[slot * CV + ((4 * j + q) ^ ((4 * slot) % CV))] = o;
             }
-            // rows of tokens past the end repeat the last token's row (same bytes)
-            const int t0 = item * kTokensPerTile;
-            _Float16* ob = og_lh + (int64_t)t0 * a.x.st;
-            const int last = a.T - 1 - t0;
+            _Float16* ob = og_lh + (int64_t)first_token(item) * a.x.st;
 #pragma unroll
             for (int k = 0; k < NJ; k++) {
                 const int vv = k * VPK + lane / CV;
                 const uint4 rowv = my_out[vv * CV + (row_c ^ ((4 * vv) % CV))];
-                *reinterpret_cast<uint4*>(ob + (int64_t)min(vv, last) * a.x.st + row_c * 8) = rowv;
+                *reinterpret_cast<uint4*>(ob + out_lane + (int64_t)(k * VPK) * a.x.st) = rowv;
             }
         };
 

@@ -161,6 +161,9 @@ def test_decode_clamps_out_of_range_indices():
     (4096, 1, 45, 1, 256),
     (5000, 2, 333, 2, 128),     # codebook above one LDS chunk: gathers from global memory, token-major
     (5000, 2, 50, 3, 256),      # ... head-major
+    (4096, 3, 7, 2, 128),       # fewer than 16 tokens: the global-gather decoder at any codebook size
+    (256, 2, 15, 3, 64),
+    (4096, 2, 17, 2, 128),      # one full 16-token item, and a last item shifted back to end at token 16
 ])
 def test_decode_random_indices(K, L, T, H, D):
     """Decode of indices drawn uniformly (not produced by the encoder), so
