@@ -34,6 +34,15 @@ METRIC = "fused rotate+int4 quantize GB/s (% of HBM peak) and ns/vector at D=128
 HBM_PEAK_GBPS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_quantize_d128_g32_qwen3-8b.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_vq_encode_vecinfer.json")
+# the VQ encoder and its launch configuration
+VQ_SOURCES = ["kv_cache_quantization_quantize_amd/csrc/kvq_vq.hip",
+              "kv_cache_quantization_quantize_amd/csrc/kvq_device.h",
+              "kv_cache_quantization_quantize_amd/csrc/kvq_api.cpp"]
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU
+N_XCD, N_CU, SIMD_PER_CU = 8, 256, 4
 # the quantize kernel and its launch configuration (items per wavefront)
 KERNEL_SOURCES = ["kv_cache_quantization_quantize_amd/csrc/kvq_int4.hip",
                   "kv_cache_quantization_quantize_amd/csrc/kvq_device.h",
@@ -46,12 +55,69 @@ def bytes_per_vector(D: int, G: int) -> int:
     return 2 * D + D // 2 + 2 * (D // G)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def ingest_mfma(csv_path, out_path=None):
+    """Turn a rocprofv3 `--pmc <MFMA_COUNTERS>` run of `bench.py --parts vq`
+    into per-kernel utilisation figures and write MFMA_FILE.
+
+    rocprofv3 sums each counter over its dimensions (XCDs, shader engines,
+    SIMDs), so: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8
+    XCDs x 1024 SIMDs) (the MfmaUtil definition with the per-XCD maximum
+    taken as the per-XCD mean); VALU busy = SQ_ACTIVE_INST_VALU / (256 CUs x
+    GRBM_GUI_ACTIVE / 8) (VALUBusy); executed fp16 MFMA flop =
+    SQ_INSTS_VALU_MFMA_MOPS_F16 x 512; clock = GRBM_GUI_ACTIVE / 8 over the
+    dispatch's duration."""
+    import csv
+    vals, dur = {}, {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            if not name.startswith("kvq::"):
+                continue
+            vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            dur.setdefault(name, {})[r["Dispatch_Id"]] = d
+    out = {"source_hash": kernel_source_hash(VQ_SOURCES), "counters": MFMA_COUNTERS,
+           "workload": "vecinfer-shaped keys [36, 8192, 8, 128], 4096-centroid fp16 codebooks per head "
+                       "(u16 indices); values with 256-centroid codebooks (u8 indices)", "kernels": {}}
+    for name, c in vals.items():
+        if not all(k in c for k in MFMA_COUNTERS):
+            continue
+        m = {k: sum(v) / len(v) for k, v in c.items()}
+        cyc = m["GRBM_GUI_ACTIVE"] / N_XCD
+        secs = sum(dur[name].values()) / len(dur[name])
+        k = {"dispatches": len(c["GRBM_GUI_ACTIVE"]), "avg_s": secs,
+             "clock_GHz": round(cyc / secs / 1e9, 3) if secs > 0 else None,
+             "mfma_busy": round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_CU * SIMD_PER_CU), 4),
+             "valu_busy": round(m["SQ_ACTIVE_INST_VALU"] / (cyc * N_CU), 4),
+             "mfma_instructions": int(m["SQ_INSTS_MFMA"]), "valu_instructions": int(m["SQ_INSTS_VALU"]),
+             "executed_fp16_mfma_flop": m["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512}
+        if secs > 0:
+            k["executed_fp16_TFLOP_per_s"] = round(k["executed_fp16_mfma_flop"] / secs / 1e12, 2)
+        out["kernels"][name] = k
+    with open(out_path or MFMA_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
+def load_mfma(path=None):
+    """The committed MFMA counter summary, or None if absent or taken on
+    different sources."""
+    try:
+        with open(path or MFMA_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash(VQ_SOURCES):
+        return None
+    return t
 
 
 def load_traffic(per_launch_alg_bytes):
@@ -288,11 +354,20 @@ def main():
     ap.add_argument("--parts", default="int4,vq",
                     help="comma list of what to run: int4 (the timed step), vq, copy (the plain-copy "
                          "reference of --copy-bytes, used to scale memory counters)")
+    ap.add_argument("--ingest-mfma", metavar="PMC_CSV",
+                    help="no GPU work: turn the counter_collection.csv of a `rocprofv3 --pmc %s` run of "
+                         "`bench.py --parts vq` into the MFMA summary under profiles/ and exit" % " ".join(MFMA_COUNTERS))
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and a "
                          "WRITE_SIZE rocprofv3 run of this benchmark into the traffic summary under "
                          "profiles/ and exit")
     args = ap.parse_args()
+
+    if args.ingest_mfma:
+        t = ingest_mfma(args.ingest_mfma)
+        print(json.dumps({k: {kk: v[kk] for kk in ("mfma_busy", "valu_busy", "clock_GHz")}
+                          for k, v in t["kernels"].items()}))
+        return
 
     if args.ingest_counters:
         t = ingest_counters(args.ingest_counters[0], args.ingest_counters[1], args.copy_bytes)
@@ -408,6 +483,11 @@ def main():
     attend = None
     if not args.no_attend:
         attend = bench_attend(torch, kvq, codes, scales, lamK, lamV, signs, (L, T, H, D, G), args)
+
+    if "copy" in parts:
+        # the plain-copy reference of --copy-bytes that scales the memory
+        # counters (not reported)
+        copy_ceiling(torch, args.copy_bytes)
 
     ceil = None
     if not args.no_ceiling:
@@ -856,6 +936,13 @@ def bench_vq(torch, kvq, synth, dev, args):
         res[name] = r
     res["workload"] = ("vecinfer-shaped keys and values [36, 8192, 8, 128]; key codebooks [8, 4096, 8] fp16, "
                        "value codebooks [8, 256, 8] fp16, sub_dim 8")
+    mf = load_mfma()
+    for name, kern in (("encode", "kvq::vq_encode_kernel<128, false>"), ("value_encode_u8", "kvq::vq_encode_kernel<128, true>")):
+        k = (mf or {}).get("kernels", {}).get(kern)
+        if k and name in res:
+            res[name]["counters"] = {"source": os.path.relpath(MFMA_FILE, ROOT), "mfma_busy": k["mfma_busy"],
+                                     "valu_busy": k["valu_busy"], "clock_GHz": k["clock_GHz"],
+                                     "executed_fp16_TFLOP_per_s": k.get("executed_fp16_TFLOP_per_s")}
     return res
 
 

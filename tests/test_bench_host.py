@@ -85,3 +85,35 @@ def test_ingest_scales_by_the_copy_reference(tmp_path, monkeypatch):
     _counter_csv(wp, "WRITE_SIZE", write[2:])
     with pytest.raises(SystemExit):
         bench.ingest_counters(str(fp), str(wp), copy_bytes)
+
+
+def test_ingest_mfma_derives_busy_fractions(tmp_path, monkeypatch):
+    """MFMA and VALU busy fractions from summed counters: per-XCD cycles are
+    GRBM_GUI_ACTIVE / 8, MFMA busy is over 1024 SIMDs, VALU busy over 256 CUs;
+    the summary is used only for the sources it was taken on."""
+    path = tmp_path / "mfma.json"
+    monkeypatch.setattr(bench, "MFMA_FILE", str(path))
+    enc = "void kvq::vq_encode_kernel<128, false>(kvq::VqArgs)"
+    cyc = 1_000_000                      # per XCD
+    counters = {"GRBM_GUI_ACTIVE": 8 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.4 * cyc * 1024,
+                "SQ_ACTIVE_INST_VALU": 0.65 * cyc * 256, "SQ_INSTS_VALU": 123.0, "SQ_INSTS_MFMA": 45.0,
+                "SQ_INSTS_VALU_MFMA_MOPS_F16": 1000.0, "SQ_BUSY_CYCLES": 1.0}
+    p = tmp_path / "pmc.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                    "End_Timestamp"])
+        for d in range(2):
+            for k, v in counters.items():
+                w.writerow([d, enc, k, v, 1000, 1000 + 500_000])            # 0.5 ms per dispatch
+            w.writerow([d, "__amd_rocclr_copyBuffer", "GRBM_GUI_ACTIVE", 5, 0, 1])
+    out = bench.ingest_mfma(str(p))
+    k = out["kernels"]["kvq::vq_encode_kernel<128, false>"]
+    assert k["dispatches"] == 2
+    assert k["mfma_busy"] == pytest.approx(0.4) and k["valu_busy"] == pytest.approx(0.65)
+    assert k["clock_GHz"] == pytest.approx(2.0)
+    assert k["executed_fp16_mfma_flop"] == 512000.0
+    assert list(out["kernels"]) == ["kvq::vq_encode_kernel<128, false>"]
+    assert bench.load_mfma()["kernels"] == out["kernels"]
+    path.write_text(json.dumps(dict(out, source_hash="0" * 16)))
+    assert bench.load_mfma() is None
