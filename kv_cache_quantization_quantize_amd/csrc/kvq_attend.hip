@@ -372,13 +372,19 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attend_partial_kernel(AttnArg
 // that share cache lines read them together.  A wavefront takes 32 tokens
 // per step and writes one partial.
 //
-// Codes enter both contractions as fp16 72 + c: one v_and_or_b32 puts two
-// offset-binary nibbles (c + 8) into the mantissas of 64.0 (bits 4-7 of each
-// half), and the constant part is removed from the results: 72 times the
-// group sum of the query from each score, 72 times the running sum of the
-// weight operand from each value row.  The biased operands are exact in fp16
-// and the constant is small next to the codes, so the results stay fp32
-// accurate.
+// Codes enter both contractions as biased fp16 values, two per dword from one
+// v_bitop3_b32 that masks two nibbles and, in the same operation, turns them
+// to offset binary (c + 8) and ors in an fp16 exponent: nibbles in bits 0-3 of
+// each half become the low mantissa bits of 1024.0 (value 1032 + c), nibbles
+// in bits 4-7 those of 64.0 (value 72 + c).  Even coordinates take the first
+// form and odd ones the second, so a dword of eight codes costs one shift and
+// four v_bitop3_b32.  The constant parts are removed from the results: from
+// each score through the accumulator's initial value, minus the bias-weighted
+// group sum of the query; from each value row through a running sum of its
+// weight operand (one more MFMA against a tile of ones), subtracted every
+// eight steps so that the accumulators never carry more than eight steps of
+// the large bias.  The biased operands are exact in fp16, so the results stay
+// fp32 accurate.
 //
 // Scores.  Rows are 16 tokens; columns are (group g, query r) = 4r + g; the
 // k-slice of lane row-slice sl is group sl, so B column (g, r) is the rotated
@@ -410,23 +416,74 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPermK[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 
-// fp16 of 64 + n for two offset-binary nibbles n held in bits 4-7 and 20-23:
-// one v_and_or_b32 (magic = 0x54005400, fp16 64 in both halves, in a VGPR).
-__device__ __forceinline__ uint32_t nib2_b64(uint32_t x, uint32_t magic)
+// fp16 operand words of the code nibbles (see above).  f(a, b, c) = (a & b) ^ c
+// is truth table 0x6A of v_bitop3_b32; the xor flips the nibble's top bit
+// (two's complement -> offset binary) and sets the exponent bits, which the
+// mask has cleared.
+constexpr uint32_t kMaskLo = 0x000F000Fu;     // nibbles in bits 0-3 of each half
+constexpr uint32_t kMaskHi = 0x00F000F0u;     // nibbles in bits 4-7 of each half
+constexpr uint32_t kXorLo = 0x64086408u;      // fp16 1024 | 8: value 1032 + c
+constexpr uint32_t kXorHi = 0x54805480u;      // fp16 64 | 8 << 4: value 72 + c
+constexpr float kBiasLo = 1032.0f, kBiasHi = 72.0f;
+
+__device__ __forceinline__ uint32_t nib2(uint32_t x, uint32_t mask, uint32_t k)
 {
-    uint32_t b;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(b) : "v"(x), "s"(0x00F000F0u), "v"(magic));
-    return b;
+    return __builtin_amdgcn_bitop3_b32(x, mask, k, (unsigned char)0x6A);
 }
 
-// Eight two's-complement codes c of a dword as fp16 72 + c (nibble e =
-// element e), in the order (0,4,1,5,2,6,3,7).
-__device__ __forceinline__ h8_t codes8_b72(uint32_t w, uint32_t magic)
+// Eight two's-complement codes of a dword (nibble e = element e) in the order
+// (0,4,1,5,2,6,3,7): even elements as 1032 + c, odd ones as 72 + c.
+__device__ __forceinline__ h8_t codes8(uint32_t w, uint32_t klo, uint32_t khi)
 {
-    const uint32_t x = w ^ 0x88888888u;
-    const uint4 o = make_uint4(nib2_b64(x << 4, magic), nib2_b64(x, magic), nib2_b64(x >> 4, magic),
-                               nib2_b64(x >> 8, magic));
+    const uint32_t y = w >> 8;
+    const uint4 o = make_uint4(nib2(w, kMaskLo, klo), nib2(w, kMaskHi, khi), nib2(y, kMaskLo, klo),
+                               nib2(y, kMaskHi, khi));
     return __builtin_bit_cast(h8_t, o);
+}
+
+// max(a, b) without the quieting copies the compiler adds to fmaxf for
+// operands it cannot prove canonical (lane moves); scores are never NaN.
+__device__ __forceinline__ float vmax(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 with the gfx950 lane swaps:
+// v_permlane16_swap_b32 (x, y) returns rows (x0, y0, x2, y2) and (x1, y1, x3,
+// y3), so with y = x the larger of the two is the pair max across l ^ 16;
+// v_permlane32_swap_b32 does the same across halves.  The optimizer must not
+// see that both operands are one value (it would take the two results as
+// equal and drop the max).
+__device__ __forceinline__ float vmax_xor16_32(float m)
+{
+    uint32_t a = __builtin_bit_cast(uint32_t, m), b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    m = vmax(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+    a = __builtin_bit_cast(uint32_t, m);
+    b = a;
+    asm volatile("" : "+v"(b));
+    const auto t = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return vmax(__builtin_bit_cast(float, (uint32_t)t[0]), __builtin_bit_cast(float, (uint32_t)t[1]));
+}
+
+// max(v, v of lane l ^ 1) and max(v, v of lane l ^ 2): a DPP max; the s_nop
+// covers the wait states a DPP read needs after a VALU write of its source.
+__device__ __forceinline__ float vmax_xor1(float v)
+{
+    float r;
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "=v"(r) : "v"(v));
+    return r;
+}
+__device__ __forceinline__ float vmax_xor2(float v)
+{
+    float r;
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "=v"(r) : "v"(v));
+    return r;
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b)
@@ -564,16 +621,27 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     __syncthreads();     // the zero block is shared by the block's wavefronts
     const uint4* bqp = bq_on ? &bqL[wid][0][0][j16] : &bqZero[0][0][j16];
 
-    // The codes enter the MFMAs as 72 + c: the score column (g, r) carries
-    // 72 times the sum of query r over group g, removed before scaling.
+    // The codes enter the MFMAs biased (1032 + c at even coordinates, 72 + c
+    // at odd ones): the score column (g, r) starts from minus the bias-weighted
+    // sum of query r over group g, taken over the same fp16 hi + lo halves the
+    // MFMAs multiply (their sum is exact in fp32).
     float kb;
     {
         const int r = j16 >> 2, g = j16 & 3;
         float sq = 0.0f;
 #pragma unroll 8
-        for (int c = 0; c < G; c++) sq += ldexpf(qt[wid][r][G * g + c], -qe);
-        kb = 72.0f * sq;
+        for (int c = 0; c < G; c++) {
+            const float v = ldexpf(qt[wid][r][G * g + c], -qe);
+            const _Float16 hv = (_Float16)v;
+            const float q2 = (float)hv + (float)(_Float16)(v - (float)hv);
+            sq = fmaf(q2, (c & 1) ? kBiasHi : kBiasLo, sq);
+        }
+        kb = sq;
     }
+    // head_dim 128 starts the score accumulators at -kb; head_dim 256, short
+    // of registers, starts them at zero and subtracts kb in the softmax
+    const f4_t kinit = NVD == 1 ? f4_t{-kb, -kb, -kb, -kb} : f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const float kb_late = NVD == 1 ? 0.0f : kb;
 
     // wave-private exchange tiles
     __shared__ _Float16 ksT[W][4][STEP], vsT[W][4][STEP];
@@ -664,29 +732,40 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
         }
     };
 
-    uint32_t magic = 0x54005400u;      // fp16 64 in both halves, kept in a VGPR
-    asm volatile("" : "+v"(magic));
+    uint32_t klo = kXorLo, khi = kXorHi;      // kept in VGPRs (v_bitop3_b32 takes one scalar)
+    asm volatile("" : "+v"(klo), "+v"(khi));
     float m_run = -__builtin_inff();   // running max of query j16 & 3 (log2 domain)
     float l_run = 0.0f;                // this lane's share of the weight sum
-    float vb = 0.0f;                   // sum of the lane's value-operand entries
     f4_t acc[NVD][8];
+    f4_t wsum = f4_t{0.0f, 0.0f, 0.0f, 0.0f};   // rows' weight-operand sums since the last bias removal
 #pragma unroll
     for (int hv = 0; hv < NVD; hv++)
 #pragma unroll
         for (int mt = 0; mt < 8; mt++) acc[hv][mt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // value sums minus their code biases (tile mt holds coordinates of parity mt)
+    auto remove_bias = [&]() {
+#pragma unroll
+        for (int hv = 0; hv < NVD; hv++)
+#pragma unroll
+            for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    acc[hv][mt][v] = fmaf((mt & 1) ? -kBiasHi : -kBiasLo, wsum[v], acc[hv][mt][v]);
+        wsum = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    };
 
     // per-group partial scores of a step's 2 x 16 tokens
     auto scores = [&](const KBuf& b, f4_t (&c)[2]) {
 #pragma unroll
         for (int tau = 0; tau < 2; tau++) {
-            c[tau] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            c[tau] = kinit;
 #pragma unroll
             for (int kq = 0; kq < KW; kq++) {
                 const uint32_t kw[4] = {b.k[tau][kq].x, b.k[tau][kq].y, b.k[tau][kq].z, b.k[tau][kq].w};
 #pragma unroll
                 for (int d = 0; d < 4; d++) {
                     const int m = 4 * kq + d;
-                    const h8_t am = codes8_b72(kw[d], magic);
+                    const h8_t am = codes8(kw[d], klo, khi);
                     const h8_t bh = __builtin_bit_cast(h8_t, bqp[m * 16]);
                     const h8_t bl = __builtin_bit_cast(h8_t, bqp[(NM + m) * 16]);
                     c[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, bh, c[tau], 0, 0, 0);
@@ -695,8 +774,23 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
             }
         }
     };
-    // softmax and value accumulation of a step, from its partial scores
-    auto finish = [&](int step, const VBuf& b, const f4_t (&c)[2]) {
+
+    // The value operand of a step: A row (g', r') = (j16 >> 2, j16 & 3) holds
+    // p * vscale of query r', group g' over tokens 8 sl + (0,4,1,5,...), as
+    // fp16 hi and lo halves.
+    struct PBuf {
+        h8_t hi, lo;
+    };
+    const int gS = j16 & 3, rS = j16 >> 2;     // score column: group, query
+    const int gV = j16 >> 2, rV = j16 & 3;     // value-operand row: group, query
+    const bool h1 = (gS & 1) != 0, h2 = (gS & 2) != 0;
+    // Softmax of a step from its partial scores, without branches: moves the
+    // reference max when needed (l_run is rescaled here; the factor of each
+    // query goes to aL for the accumulators, which the caller rescales when
+    // the returned flag is set) and builds the step's value operand.  Tokens
+    // at or past the wave's end, including every token of a step past the
+    // last one, get weight 0 and leave the state unchanged.
+    auto softmax = [&](int step, const VBuf& b, const f4_t (&c)[2], PBuf& pb) -> bool {
         const int tb = wb + step * STEP;
         // scale tiles, transposed to [group][token]
         {
@@ -711,138 +805,216 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
         // four lanes of a quad (columns 4r + g): a reduce-scatter leaves lane
         // g with the score of token 4 sl + g, so each lane carries on with
         // one score per 16 tokens.
-        const int gS = j16 & 3, rS = j16 >> 2;     // score column: group, query
-        const int g = j16 >> 2, r = j16 & 3;       // value-operand row: group, query
-        const bool h1 = (gS & 1) != 0, h2 = (gS & 2) != 0;
         float sc[2];
-        float smax = -__builtin_inff();
 #pragma unroll
         for (int tau = 0; tau < 2; tau++) {
             const uint2 kq = *reinterpret_cast<const uint2*>(&ksT[wid][gS][16 * tau + 4 * sl]);
-            const float kv[4] = {lo_half(kq.x), hi_half(kq.x), lo_half(kq.y), hi_half(kq.y)};
+            const h2_t k01 = __builtin_bit_cast(h2_t, kq.x), k23 = __builtin_bit_cast(h2_t, kq.y);
             float x[4];
-#pragma unroll
-            for (int v = 0; v < 4; v++) x[v] = (c[tau][v] - kb) * kv[v];
+            x[0] = fmaf(c[tau][0] - kb_late, (float)k01.x, 0.0f);
+            x[1] = fmaf(c[tau][1] - kb_late, (float)k01.y, 0.0f);
+            x[2] = fmaf(c[tau][2] - kb_late, (float)k23.x, 0.0f);
+            x[3] = fmaf(c[tau][3] - kb_late, (float)k23.y, 0.0f);
             // keep tokens 2 (g >> 1) + {0, 1}, add the partner's (lane g ^ 2)
             const float y0 = (h2 ? x[2] : x[0]) + dpp_mov<kDppXor2>(h2 ? x[0] : x[2]);
             const float y1 = (h2 ? x[3] : x[1]) + dpp_mov<kDppXor2>(h2 ? x[1] : x[3]);
             // keep token g, add lane g ^ 1's
-            const float sv = (h1 ? y1 : y0) + dpp_mov<kDppXor1>(h1 ? y0 : y1);
-            const bool valid = tb + 16 * tau + 4 * sl + gS < we;
-            sc[tau] = valid ? sv * sfac : -__builtin_inff();
-            smax = fmaxf(smax, sc[tau]);
+            const float sv = ((h1 ? y1 : y0) + dpp_mov<kDppXor1>(h1 ? y0 : y1)) * sfac;
+            sc[tau] = tb + 16 * tau + 4 * sl + gS < we ? sv : -__builtin_inff();
         }
-        smax = fmaxf(smax, dpp_mov<kDppXor1>(smax));
-        smax = fmaxf(smax, dpp_mov<kDppXor2>(smax));
-        smax = fmaxf(smax, __shfl_xor(smax, 16));
-        smax = fmaxf(smax, __shfl_xor(smax, 32));
+        float smax = vmax(sc[0], sc[1]);
+        smax = vmax_xor1(smax);
+        smax = vmax_xor2(smax);
+        smax = vmax_xor16_32(smax);
         // The weights are taken relative to a reference max that moves only
         // when a score exceeds it by more than 2^8 (weights stay below 256),
         // so the accumulators are rescaled a few times per wave rather than
         // every step.  The value operand p * vscale must stay finite in fp16:
-        // in a step with a value scale of 128 or more the reference moves to
-        // the step's max, so that p <= 1.
-        const uint32_t vsb = b.vs & 0x7fff7fffu;
-        const bool big = __builtin_amdgcn_ballot_w64((vsb & 0xffffu) >= 0x5800u || (vsb >> 16) >= 0x5800u) != 0;
-        if (__builtin_amdgcn_ballot_w64(smax > m_run + (big ? 0.0f : 8.0f))) {
-            const float m_new = fmaxf(m_run, smax);
-            const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-            if (gS == 0 && sl == 0) aL[wid][rS] = alpha;
-            __builtin_amdgcn_wave_barrier();
-            vb *= aL[wid][r];
-            // result rows 4 sl + v are queries v
-            const float4 al = *reinterpret_cast<const float4*>(&aL[wid][0]);
-            const float av[4] = {al.x, al.y, al.z, al.w};
-#pragma unroll
-            for (int hv = 0; hv < NVD; hv++)
-#pragma unroll
-                for (int mt = 0; mt < 8; mt++)
-#pragma unroll
-                    for (int v = 0; v < 4; v++) acc[hv][mt][v] *= av[v];
-        }
+        // in a step with a value scale of 128 (0x5800) or more the reference
+        // moves to the step's max, so that p <= 1.  Adding 0x2800 to each
+        // magnitude half carries into its bit 15 exactly when it is >= 0x5800.
+        const bool big = __builtin_amdgcn_ballot_w64((((b.vs & 0x7fff7fffu) + 0x28002800u) & 0x80008000u) != 0) != 0;
+        const bool moved = __builtin_amdgcn_ballot_w64(smax > m_run + (big ? 0.0f : 8.0f)) != 0;
+        const float m_new = moved ? fmaxf(m_run, smax) : m_run;
+        const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        aL[wid][rS] = alpha;    // the 16 lanes of a query store the same value
+        // m_run is finite here for a step in range (every such step has a
+        // token in range for each query), so a masked score gives
+        // exp2(-inf) = 0; a step past the end leaves m_run as it was
 #pragma unroll
         for (int tau = 0; tau < 2; tau++) {
-            const float pv = (sc[tau] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(sc[tau] - m_run);
+            const float pv = __builtin_amdgcn_exp2f(sc[tau] - m_run);
             l_run += pv;
             pL[wid][rS][16 * tau + 4 * sl + gS] = pv;
         }
         __builtin_amdgcn_wave_barrier();
-        // value operands: A row (g', r') = (j16 >> 2, j16 & 3), tokens 8 sl + (0,4,1,5,...)
-        h8_t ap_hi, ap_lo;
         {
-            const float4 p0 = *reinterpret_cast<const float4*>(&pL[wid][r][8 * sl]);
-            const float4 p1 = *reinterpret_cast<const float4*>(&pL[wid][r][8 * sl + 4]);
-            const uint4 vq = *reinterpret_cast<const uint4*>(&vsT[wid][g][8 * sl]);
+            const float4 p0 = *reinterpret_cast<const float4*>(&pL[wid][rV][8 * sl]);
+            const float4 p1 = *reinterpret_cast<const float4*>(&pL[wid][rV][8 * sl + 4]);
+            const uint4 vq = *reinterpret_cast<const uint4*>(&vsT[wid][gV][8 * sl]);
             const float pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-            const float vv[8] = {lo_half(vq.x), hi_half(vq.x), lo_half(vq.y), hi_half(vq.y),
-                                 lo_half(vq.z), hi_half(vq.z), lo_half(vq.w), hi_half(vq.w)};
-            uint32_t hw[4], lw[4];
+            const h2_t v2[4] = {__builtin_bit_cast(h2_t, vq.x), __builtin_bit_cast(h2_t, vq.y),
+                                __builtin_bit_cast(h2_t, vq.z), __builtin_bit_cast(h2_t, vq.w)};
+            const _Float16 vv[8] = {v2[0].x, v2[0].y, v2[1].x, v2[1].y, v2[2].x, v2[2].y, v2[3].x, v2[3].y};
+            h2_t hw[4], lw[4];
 #pragma unroll
             for (int k = 0; k < 4; k++) {
-                const float x0 = pp[k] * vv[k], x1 = pp[k + 4] * vv[k + 4];
-                vb += x0 + x1;
-                const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-                hw[k] = __builtin_bit_cast(uint32_t, h2_t{h0, h1});
-                lw[k] = pack_h2(x0 - (float)h0, x1 - (float)h1);
+                // fp16 hi and lo halves of p * vscale (tokens k and k + 4)
+                const _Float16 e0 = (_Float16)fmaf(pp[k], (float)vv[k], 0.0f);
+                const _Float16 e1 = (_Float16)fmaf(pp[k + 4], (float)vv[k + 4], 0.0f);
+                hw[k] = h2_t{e0, e1};
+                lw[k] = h2_t{(_Float16)fmaf(pp[k], (float)vv[k], -(float)e0),
+                             (_Float16)fmaf(pp[k + 4], (float)vv[k + 4], -(float)e1)};
             }
-            ap_hi = __builtin_bit_cast(h8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-            ap_lo = __builtin_bit_cast(h8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+            pb.hi = __builtin_bit_cast(h8_t, hw);
+            pb.lo = __builtin_bit_cast(h8_t, lw);
         }
-        // value B operands: tile 2q' / 2q'+1 from byte q' of the 8 tokens' dwords
-#pragma unroll
-        for (int hv = 0; hv < NVD; hv++) {
-            uint32_t vx[8];
-#pragma unroll
-            for (int tp = 0; tp < 8; tp++) vx[tp] = b.v[hv][tp] ^ 0x88888888u;      // offset binary
-#pragma unroll
-            for (int qb = 0; qb < 4; qb++) {
-                const uint32_t sel = (uint32_t)qb | (0x0cu << 8) | ((uint32_t)(4 + qb) << 16) | (0x0cu << 24);
-                uint32_t lo[4], hi[4];
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const uint32_t w = __builtin_amdgcn_perm(vx[k + 4], vx[k], sel);
-                    lo[k] = nib2_b64(w << 4, magic);
-                    hi[k] = nib2_b64(w, magic);
-                }
-                const h8_t bl = __builtin_bit_cast(h8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
-                const h8_t bh = __builtin_bit_cast(h8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-                f4_t& a0 = acc[hv][2 * qb];
-                f4_t& a1 = acc[hv][2 * qb + 1];
-                a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_hi, bl, a0, 0, 0, 0);
-                a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_lo, bl, a0, 0, 0, 0);
-                a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_hi, bh, a1, 0, 0, 0);
-                a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap_lo, bh, a1, 0, 0, 0);
-            }
-        }
+        return moved;
+    };
+    // the accumulators follow a moved reference: row 4 sl + v is query v
+    auto rescale = [&]() {
         __builtin_amdgcn_wave_barrier();
+        const float4 al = *reinterpret_cast<const float4*>(&aL[wid][0]);
+        const float av[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+        for (int v = 0; v < 4; v++) wsum[v] *= av[v];
+#pragma unroll
+        for (int hv = 0; hv < NVD; hv++)
+#pragma unroll
+            for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc[hv][mt][v] *= av[v];
+    };
+    // value B operands of tile (hv, 2 q' / 2 q' + 1) from byte q' of the 8
+    // tokens' dwords of part hv
+    auto value_operands = [&](const VBuf& b, int hv, h8_t (&bv)[8]) {
+#pragma unroll
+        for (int qb = 0; qb < 4; qb++) {
+            const uint32_t sel = (uint32_t)qb | (0x0cu << 8) | ((uint32_t)(4 + qb) << 16) | (0x0cu << 24);
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const uint32_t w = __builtin_amdgcn_perm(b.v[hv][k + 4], b.v[hv][k], sel);
+                lo[k] = nib2(w, kMaskLo, klo);
+                hi[k] = nib2(w, kMaskHi, khi);
+            }
+            bv[2 * qb] = __builtin_bit_cast(h8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+            bv[2 * qb + 1] = __builtin_bit_cast(h8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+        }
+    };
+    auto accumulate = [&](const PBuf& pb, int hv, const h8_t (&bv)[8]) {
+        if (hv == 0) {
+            const h8_t ones = __builtin_bit_cast(h8_t, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
+            wsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(pb.hi, ones, wsum, 0, 0, 0);
+            wsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(pb.lo, ones, wsum, 0, 0, 0);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++) {
+            acc[hv][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pb.hi, bv[mt], acc[hv][mt], 0, 0, 0);
+            acc[hv][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pb.lo, bv[mt], acc[hv][mt], 0, 0, 0);
+        }
     };
 
-    // Software pipeline: while step st is finished, the score MFMAs of step
-    // st + 1 run on the matrix cores, and the key codes of step st + 2 and
-    // the values and scales of step st + 1 are in flight (the key buffer is
-    // refilled as soon as its codes have become MFMA operands).  Steps past
-    // the last one repeat it (in range; their results are never used).
     if (nsteps > 0) {
-        KBuf K;
-        VBuf V0, V1;
-        f4_t c0[2], c1[2];
-        load_k(0, K);
-        load_v(0, V0);
-        scores(K, c0);
-        load_k(min(1, nsteps - 1), K);
-        for (int st = 0;; st += 2) {
-            load_v(min(st + 1, nsteps - 1), V1);
-            scores(K, c1);
-            load_k(min(st + 2, nsteps - 1), K);
-            finish(st, V0, c0);
-            if (st + 1 >= nsteps) break;
-            load_v(min(st + 2, nsteps - 1), V0);
+        if constexpr (NVD == 1) {
+            // Software pipeline over two steps: one iteration converts step
+            // st's value codes and issues its value MFMAs while the softmax of
+            // step st + 1 runs on the VALU and the score MFMAs of step st + 2
+            // run; the values of step st + 2 and the keys of step st + 3 are
+            // in flight.  The accumulators take step st + 1's rescale after
+            // step st's values.  Steps past the last one repeat its data (in
+            // range) and are masked by the softmax.
+            KBuf Ka, Kb;
+            VBuf Va, Vb;
+            f4_t ca[2], cb[2];
+            PBuf Pa, Pb;
+            const int last = nsteps - 1;
+            load_k(0, Ka);
+            load_v(0, Va);
+            load_k(min(1, last), Kb);
+            load_v(min(1, last), Vb);
+            scores(Ka, ca);
+            load_k(min(2, last), Ka);
+            scores(Kb, cb);
+            softmax(0, Va, ca, Pa);     // the accumulators are still zero
+            for (int st = 0;; st += 2) {
+                h8_t bv[8];
+                value_operands(Va, 0, bv);
+                load_v(min(st + 2, last), Va);
+                load_k(min(st + 3, last), Kb);
+                scores(Ka, ca);
+                bool moved = softmax(st + 1, Vb, cb, Pb);
+                accumulate(Pa, 0, bv);
+                if ((st & 7) == 7) remove_bias();
+                if (st + 1 >= nsteps) break;
+                if (moved) rescale();
+                value_operands(Vb, 0, bv);
+                load_v(min(st + 3, last), Vb);
+                load_k(min(st + 4, last), Ka);
+                scores(Kb, cb);
+                moved = softmax(st + 2, Va, ca, Pa);
+                accumulate(Pb, 0, bv);
+                if (((st + 1) & 7) == 7) remove_bias();
+                if (st + 2 >= nsteps) break;
+                if (moved) rescale();
+            }
+        } else {
+            // head_dim 256: the values of step st + 1 and keys of step st + 2
+            // are in flight and the score MFMAs of step st + 1 run while step
+            // st is finished (the registers hold no more)
+            KBuf K;
+            VBuf V0, V1;
+            f4_t c0[2], c1[2];
+            PBuf P;
+            auto finish = [&](int step, const VBuf& b, const f4_t (&c)[2]) {
+                if (softmax(step, b, c, P)) rescale();
+                h8_t ones = __builtin_bit_cast(h8_t, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
+                asm volatile("" : "+v"(ones));
+                wsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(P.hi, ones, wsum, 0, 0, 0);
+                wsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(P.lo, ones, wsum, 0, 0, 0);
+                // each pair of value tiles is built right before its MFMAs
+#pragma unroll
+                for (int hv = 0; hv < NVD; hv++) {
+#pragma unroll
+                    for (int qb = 0; qb < 4; qb++) {
+                        const uint32_t sel = (uint32_t)qb | (0x0cu << 8) | ((uint32_t)(4 + qb) << 16) | (0x0cu << 24);
+                        uint32_t lo[4], hi[4];
+#pragma unroll
+                        for (int k = 0; k < 4; k++) {
+                            const uint32_t w = __builtin_amdgcn_perm(b.v[hv][k + 4], b.v[hv][k], sel);
+                            lo[k] = nib2(w, kMaskLo, klo);
+                            hi[k] = nib2(w, kMaskHi, khi);
+                        }
+                        const h8_t bl = __builtin_bit_cast(h8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+                        const h8_t bh = __builtin_bit_cast(h8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                        f4_t& a0 = acc[hv][2 * qb];
+                        f4_t& a1 = acc[hv][2 * qb + 1];
+                        a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(P.hi, bl, a0, 0, 0, 0);
+                        a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(P.lo, bl, a0, 0, 0, 0);
+                        a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(P.hi, bh, a1, 0, 0, 0);
+                        a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(P.lo, bh, a1, 0, 0, 0);
+                    }
+                }
+                if ((step & 7) == 7) remove_bias();
+            };
+            load_k(0, K);
+            load_v(0, V0);
             scores(K, c0);
-            load_k(min(st + 3, nsteps - 1), K);
-            finish(st + 1, V1, c1);
-            if (st + 2 >= nsteps) break;
+            load_k(min(1, nsteps - 1), K);
+            for (int st = 0;; st += 2) {
+                load_v(min(st + 1, nsteps - 1), V1);
+                scores(K, c1);
+                load_k(min(st + 2, nsteps - 1), K);
+                finish(st, V0, c0);
+                if (st + 1 >= nsteps) break;
+                load_v(min(st + 2, nsteps - 1), V0);
+                scores(K, c0);
+                load_k(min(st + 3, nsteps - 1), K);
+                finish(st + 1, V1, c1);
+                if (st + 2 >= nsteps) break;
+            }
         }
     }
 
@@ -862,18 +1034,9 @@ __global__ __launch_bounds__(64 * kAttnMfmaWaves) void attend_partial_mfma_kerne
     }
     // result rows 4 sl + v = (group sl, query v); column j16 of tile (hv, mt)
     // is coordinate 128 hv + 8 j16 + mt, of group (128 hv + 8 j16) / G.
-    // Value codes entered as 72 + c: remove 72 times row (g, v)'s operand sum.
-    vb += __shfl_xor(vb, 16);
-    vb += __shfl_xor(vb, 32);
-    float vbias[RP];
-#pragma unroll
-    for (int v = 0; v < RP; v++) vbias[v] = 72.0f * __shfl(vb, 4 * sl + v);
+    remove_bias();
 #pragma unroll
     for (int hv = 0; hv < NVD; hv++) {
-#pragma unroll
-        for (int mt = 0; mt < 8; mt++)
-#pragma unroll
-            for (int v = 0; v < RP; v++) acc[hv][mt][v] -= vbias[v];
         if (sl == (128 * hv + 8 * j16) / G) {
 #pragma unroll
             for (int v = 0; v < RP; v++) {
