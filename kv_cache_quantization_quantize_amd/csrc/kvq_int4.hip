@@ -160,9 +160,10 @@ struct QuantShape {
 // the item's one register buffer as soon as the first stage has consumed it
 // (a second buffer, with the loop unrolled by two, took 12 to 41 more VGPRs:
 // a wave per SIMD less for the quantizers and the SRFT dequantizer).
-// Without it (the head_dim-256 dequantizers and SRFT quantizer, where a
-// prefetch buffer would cost a wave per SIMD) each item's loads are issued
-// right before its first stage, and only the stores are deferred.
+// Without it (the token-major head_dim-256 dequantizers and the head_dim-256
+// SRFT kernels, where a prefetch buffer would pass 256 VGPRs and cost a wave
+// per SIMD) each item's loads are issued right before its first stage, and
+// only the stores are deferred.
 template <typename Buf, typename Out, int N, bool PREFETCH, typename Load, typename First, typename Store,
           typename Finish>
 __device__ __forceinline__ void run_pipeline(int begin, int end, Load&& load, First&& first_stage,
@@ -696,7 +697,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void dequantize_kernel(Int4Arg
         }
     };
 
-    run_pipeline<Raw, Out, N, (D <= 128)>(begin, end, load, first_stage, store, finish);
+    run_pipeline<Raw, Out, N, (D <= 128 || (!TM && !FT))>(begin, end, load, first_stage, store, finish);
 }
 
 // ---------------------------------------------------------------------------

@@ -329,15 +329,18 @@ def test_item_plan(lib):
     assert kvq.item_plan(5, 80001, 2, 128) == (True, 5 * 10001, 2)
     assert kvq.item_plan(5, 80001, 2, 128, inverse=True) == (True, 5 * 10001, 16)
     assert kvq.item_plan(5, 80001, 2, 128, fourier=True) == (True, 5 * 10001, 16)
-    assert kvq.item_plan(3, 200003, 1, 256) == (True, 3 * 12501, 8)
-    assert kvq.item_plan(3, 200003, 1, 256, inverse=True, fourier=True) == (True, 3 * 12501, 16)
-    # head-major: 16 tokens of one (layer, head) per item
+    assert kvq.item_plan(2, 90001, 2, 256) == (True, 2 * 11251, 8)
+    assert kvq.item_plan(2, 90001, 2, 256, inverse=True) == (True, 2 * 11251, 11)
+    # head-major: 16 tokens of one (layer, head) per item; with one head the
+    # same items as token-major, taken head-major
     assert kvq.item_plan(3, 65541, 3, 128) == (False, 9 * 4097, 2)
     assert kvq.item_plan(2, 87400, 3, 256, inverse=True) == (False, 6 * 5463, 16)
+    assert kvq.item_plan(3, 200003, 1, 256) == (False, 3 * 12501, 8)
+    assert kvq.item_plan(3, 200003, 1, 256, inverse=True, fourier=True) == (False, 3 * 12501, 16)
     # about 2048 wavefronts for small launches
     assert kvq.item_plan(1, 64, 2, 128) == (True, 8, 1)
-    assert kvq.item_plan(1, 16 * 2048, 1, 128, inverse=True) == (True, 2048, 1)
-    assert kvq.item_plan(1, 16 * 2049, 1, 128, inverse=True) == (True, 2049, 2)
+    assert kvq.item_plan(1, 16 * 2048, 1, 128, inverse=True) == (False, 2048, 1)
+    assert kvq.item_plan(1, 16 * 2049, 1, 128, inverse=True) == (False, 2049, 2)
     assert kvq.item_plan(28, 4096, 2, 128, inverse=True) == (True, 28 * 512, 7)
     assert kvq.item_plan(28, 4096, 2, 128) == (True, 28 * 512, 2)
     assert kvq.item_plan(36, 262144, 8, 128) == (True, 36 * 131072, 2)

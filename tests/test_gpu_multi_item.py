@@ -3,8 +3,9 @@ int8, MXFP4, SRFT) at shapes where each wavefront runs several consecutive
 work items, so that the paths a one-item wavefront never takes are covered:
 a run that crosses a lambda key (a layer for token-major items, a (layer,
 head) for head-major ones) and reloads the multipliers mid-run, the
-prefetch of the next item (head_dim <= 128) and the deferred stores of the
-head_dim-256 loop, a partial last item, and a ragged last wavefront.
+prefetch of the next item and the deferred stores of the loops without it
+(token-major head_dim 256 dequantize, head_dim-256 SRFT), a partial last
+item, and a ragged last wavefront.
 
 Each case is checked two ways, through the C ABI via the binding:
   * against the fp64 oracle (contract in tests/parity.py) on every vector of
@@ -37,8 +38,9 @@ PAD = 8                       # sentinel token rows after each layer's outputs
 SHAPES = [
     (5, 80001, 2, 128, 32),   # token-major, 3 items per wavefront, ragged last wavefront
     (3, 65541, 3, 128, 16),   # head-major, 2 per wavefront, ragged last wavefront
-    (3, 200003, 1, 256, 64),  # head_dim 256 (no prefetch), ragged last wavefront
+    (3, 200003, 1, 256, 64),  # head_dim 256, one head (head-major items), ragged last wavefront
     (2, 87400, 3, 256, 32),   # head-major head_dim 256
+    (2, 90001, 2, 256, 64),   # token-major head_dim 256 (dequantize without prefetch)
     (2, 70001, 4, 64, 8),     # head_dim 64, 4 tokens per item
 ]
 
