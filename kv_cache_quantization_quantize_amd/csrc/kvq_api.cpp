@@ -233,7 +233,7 @@ kvq_status vq_common(const kvq_shape& shape, const kvq_view& x, const float* lam
     set_items(shape, a.token_major, a.h_shift, a.items_per_group, a.tok_per_item, a.items_per_wave, a.n_items);
     a.dec_waves_per_group = (a.items_per_group + a.items_per_wave - 1) / a.items_per_wave;
     a.dec_n_waves = (a.n_items / a.items_per_group) * a.dec_waves_per_group;
-    const int64_t tpu = 16 * kvq::vq_encode_waves((int)D);
+    const int64_t tpu = 16 * kvq::vq_encode_waves((int)D, idx8);
     a.enc_units_per_lh = (int32_t)((shape.tokens + tpu - 1) / tpu);
     a.enc_n_units = shape.layers * shape.heads * (int64_t)a.enc_units_per_lh;
     a.enc_units_per_block = 1;
@@ -337,9 +337,10 @@ kvq_status vq_encode_any(kvq_shape shape, kvq_view x_f16, const float* lambda, c
     KVQ_TRY(vq_common(shape, x_f16, lambda, signs, codebook_f16, codebook_layer_stride, n_centroids, sub_dim,
                       idx, a, false, idx8));
     if (empty(shape)) return KVQ_OK;
-    // one block per CU holds the 144 KB of LDS; four blocks' worth of units
-    // per CU balance the tail
-    const int64_t blocks = std::min<int64_t>(a.enc_n_units, 4 * (int64_t)device_cus());
+    // one block per CU holds the 144 KB of LDS (three four-wavefront blocks
+    // per CU for one-byte indices); four rounds of resident blocks' worth of
+    // units per CU balance the tail
+    const int64_t blocks = std::min<int64_t>(a.enc_n_units, (idx8 ? 12 : 4) * (int64_t)device_cus());
     a.enc_units_per_block = (int32_t)((a.enc_n_units + blocks - 1) / blocks);
     return hip_status(kvq::launch_vq_encode(a, static_cast<hipStream_t>(stream)), "kvq_vq_encode launch");
 }

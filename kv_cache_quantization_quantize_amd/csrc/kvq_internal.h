@@ -117,7 +117,7 @@ struct KmArgs {
 constexpr int kKmMaxCentroids = 4096;   // LDS: 36 bytes per centroid
 
 // Wavefronts per VQ-encode block for a head dim (each stages 16 keys).
-int vq_encode_waves(int D);
+int vq_encode_waves(int D, bool idx8);
 
 // Launchers: enqueue on `stream`, return the launch status.  Arguments have
 // been validated by the caller.

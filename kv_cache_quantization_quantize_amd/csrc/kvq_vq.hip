@@ -53,15 +53,27 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-template <int D>
+// Encoder shape.  Each wavefront issues a VALU instruction only every 5-6
+// clocks, while the SIMD executes one in about two, so VALU-bound work runs
+// faster with more wavefronts per SIMD.  The 4096-centroid encoder is bound
+// by the matrix pipe during its sweep and keeps eight groups per sweep at two
+// wavefronts per SIMD (four groups at three measured slower); the one-byte
+// encoder (256 centroids, a short sweep and a longer maxima epilogue per
+// tile) is VALU-bound and sweeps four groups at a time in four-wavefront
+// blocks, which fit three wavefronts per SIMD (164 VGPRs): 0.917 -> 0.799 ms
+// for 2.4 M value vectors on MI355X (two groups at four wavefronts per SIMD
+// measured the same).
+template <int D, bool IDX8 = false>
 struct VqCfg {
     static constexpr int NS = D / 8;               // sub-vectors per key
     static constexpr int NJ = D / 32;              // 16-byte chunks per lane
     static constexpr int N = D / 4;                // coordinates per lane
     static constexpr int NGRP = D / 16;            // groups of 32 sub-vectors per 16 keys
-    static constexpr int GPR = NGRP < 8 ? NGRP : 8;   // groups per codebook sweep
+    static constexpr int GMAX = IDX8 ? 4 : 8;
+    static constexpr int GPR = NGRP < GMAX ? NGRP : GMAX;   // groups per codebook sweep
     static constexpr int ROUNDS = NGRP / GPR;
-    static constexpr int WAVES = (D == 256) ? 4 : 8;  // wavefronts per block (LDS budget)
+    static constexpr int WAVES = (D == 256 || IDX8) ? 4 : 8;  // wavefronts per block (LDS budget)
+    static constexpr int MINW = IDX8 ? 3 : 1;      // waves per SIMD the registers must allow
 };
 
 // Wavefronts per block of the LDS-codebook decoder (one block per CU:
@@ -92,10 +104,10 @@ __device__ __forceinline__ int stage_slot(int v, int s) { return v * NS + (s ^ (
 
 // IDX8: one-byte indices (codebooks of at most 256 centroids), else u16.
 template <int D, bool IDX8>
-__global__ __launch_bounds__(64 * VqCfg<D>::WAVES) void vq_encode_kernel(VqArgs a)
+__global__ __launch_bounds__((64 * VqCfg<D, IDX8>::WAVES), (VqCfg<D, IDX8>::MINW)) void vq_encode_kernel(VqArgs a)
 {
     typedef typename std::conditional<IDX8, uint8_t, uint16_t>::type idx_t;
-    using C = VqCfg<D>;
+    using C = VqCfg<D, IDX8>;
     constexpr int NS = C::NS, NJ = C::NJ, N = C::N, GPR = C::GPR, ROUNDS = C::ROUNDS, WAVES = C::WAVES;
 
     // one-byte indices imply at most 256 centroids: a small codebook area
@@ -723,8 +735,8 @@ template <int D>
 hipError_t launch_enc(const VqArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)((a.enc_n_units + a.enc_units_per_block - 1) / a.enc_units_per_block));
-    if (a.idx8) hipLaunchKernelGGL((vq_encode_kernel<D, true>), grid, dim3(64 * VqCfg<D>::WAVES), 0, s, a);
-    else hipLaunchKernelGGL((vq_encode_kernel<D, false>), grid, dim3(64 * VqCfg<D>::WAVES), 0, s, a);
+    if (a.idx8) hipLaunchKernelGGL((vq_encode_kernel<D, true>), grid, dim3(64 * VqCfg<D, true>::WAVES), 0, s, a);
+    else hipLaunchKernelGGL((vq_encode_kernel<D, false>), grid, dim3(64 * VqCfg<D, false>::WAVES), 0, s, a);
     return hipGetLastError();
 }
 
@@ -746,7 +758,11 @@ hipError_t launch_dec(const VqArgs& a, hipStream_t s)
 
 }  // namespace
 
-int vq_encode_waves(int D) { return D == 256 ? VqCfg<256>::WAVES : VqCfg<128>::WAVES; }
+int vq_encode_waves(int D, bool idx8)
+{
+    if (idx8) return D == 256 ? VqCfg<256, true>::WAVES : VqCfg<128, true>::WAVES;
+    return D == 256 ? VqCfg<256>::WAVES : VqCfg<128>::WAVES;
+}
 
 hipError_t launch_vq_encode(const VqArgs& a, hipStream_t s)
 {
