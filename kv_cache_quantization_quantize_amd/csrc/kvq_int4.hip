@@ -141,6 +141,19 @@ __device__ __forceinline__ uint16_t pick_scale(const uint16_t (&s)[NG], int g)
 
 }  // namespace
 
+// Quantizer outputs (codes and scales) are stored with the nontemporal hint:
+// they are not read again by the launch, and keeping them out of the caches'
+// normal replacement leaves more room for the input stream.  Measured on
+// MI355X: Qwen3-8B-shaped int4 quantize 4.59 -> 4.38 ms, MXFP4 4.47 -> 4.27,
+// int8 5.37 -> 5.35, Gemma-shaped head_dim 256 0.882 -> 0.837 ms.  The same
+// hint on the loads (4.56 -> 4.67 ms) or on the dequantizers' fp16 stores
+// made them slower.
+__device__ __forceinline__ void store_nt(void* p, uint4 v)
+{
+    typedef uint32_t u4nt __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u4nt{v.x, v.y, v.z, v.w}, reinterpret_cast<u4nt*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Quantize
 // ---------------------------------------------------------------------------
@@ -306,28 +319,28 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
             // lanes with q + 4k >= NCH (int4, head_dim 64 only) read a valid slot and do not store
             const int c = q + 4 * k;
             const uint4 chunk = *reinterpret_cast<const uint4*>(&my_codes[chunk_pos(slot, c % NCH)]);
-            if (ok && c < NCH) *reinterpret_cast<uint4*>(cp + 64 * k) = chunk;
+            if (ok && c < NCH) store_nt(cp + 64 * k, chunk);
         }
         if (ok) {
             if constexpr (MX) {
                 uint8_t* sp8 = sg8 + outer_offset(a.scales, it) + s_lane;
 #pragma unroll
                 for (int k = 0; k < NSV; k++)
-                    if (4 * k + q < NG) sp8[4 * k + q] = (uint8_t)o.sv[k];
+                    if (4 * k + q < NG) __builtin_nontemporal_store((uint8_t)o.sv[k], sp8 + 4 * k + q);
             } else if constexpr (G >= 32) {
                 // lane q writes groups q, q+4, ...
 #pragma unroll
                 for (int k = 0; k < NSV; k++)
-                    if (4 * k + q < NG) sp[4 * k + q] = o.sv[k];
+                    if (4 * k + q < NG) __builtin_nontemporal_store(o.sv[k], sp + 4 * k + q);
             } else if constexpr (G == 16) {
                 // lanes q and q^1 share group 2j + (q >> 1); the even lane writes
                 if ((q & 1) == 0) {
 #pragma unroll
-                    for (int j = 0; j < NJ; j++) sp[2 * j + (q >> 1)] = o.sv[j];
+                    for (int j = 0; j < NJ; j++) __builtin_nontemporal_store(o.sv[j], sp + 2 * j + (q >> 1));
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < NJ; j++) sp[4 * j + q] = o.sv[j];
+                for (int j = 0; j < NJ; j++) __builtin_nontemporal_store(o.sv[j], sp + 4 * j + q);
             }
         }
     };
