@@ -345,8 +345,9 @@ kvq_status kvq_attend_decode_noalloc(kvq_shape shape, int32_t q_per_kv, const vo
  * (inverse = 1) kernels for a shape, for the Walsh-Hadamard formats (int4,
  * int8, MXFP4; fourier = 0) or SRFT (fourier = 1); host arithmetic only, no
  * HIP call.  An item is 16 head vectors: 16/heads consecutive tokens of one
- * layer (all heads) when heads divides 16 (*token_major = 1), else 16
- * consecutive tokens of one (layer, head) (*token_major = 0).  Each
+ * layer (all heads) when heads is above 1 and divides 16 (*token_major =
+ * 1), else 16 consecutive tokens of one (layer, head) (*token_major = 0;
+ * with one head the two orders give the same items).  Each
  * wavefront runs *items_per_wave consecutive items of the *n_items; the last
  * one may run fewer, and an item past the last token is partial.  Writes
  * zeros for an empty shape.  Errors as for kvq_quantize's shape checks,
