@@ -96,6 +96,23 @@ def test_decode_random_indices_and_clamp(D):
     assert rep["bad"] == 0
 
 
+@pytest.mark.parametrize("D", [128, 256])
+def test_multi_unit_blocks_ragged(D):
+    """Encoder blocks that run several 64-token units, across (layer, head)
+    boundaries, with a ragged last unit per (layer, head): [4, 6500, 8, D]
+    gives 102 units per (layer, head) (the last one 36 tokens) and more units
+    than the launch has blocks.  Checked on every vector of the first and
+    last unit of every (layer, head) and a seeded sample elsewhere."""
+    L, T, H = 4, 6500, 8
+    x, lam, s, cb = rand_case(L, T, H, D, 256, seed=611 + D)
+    idx, out = run8(x, lam, s, cb)
+    edge = [(l, t, h) for l in range(L) for h in range(H)
+            for t in list(range(0, 64)) + list(range(6400, T))]
+    smp = synth.sample_rows(L, T, H, 1024, 612 + D).numpy()
+    sel = np.unique(np.concatenate([np.array(edge, dtype=np.int64), smp]), axis=0)
+    check(x, lam, s, cb, idx, out, sel, "u8 multi-unit D=%d" % D)
+
+
 def test_vecinfer_values_full_size_sampled():
     """The VecInfer-shaped value cache at full size ([36, 8192, 8, 128],
     per-head 256-centroid fp16 codebooks, one-byte indices), in the
