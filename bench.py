@@ -280,7 +280,7 @@ def copy_ceiling(torch, nbytes: int, reps: int = 5):
 
 
 def stream_ceilings(torch, dev, read_bytes: int = 16 << 30, reps: int = 3):
-    """Practical HBM bandwidth of this machine for the read/write mixes of the
+    """Practical HBM bandwidth of this GPU for the read/write mixes of the
     quantizer's kernels, from the hand-written streaming kernels of
     libkvq_stream.so: read only, 80/20 (the quantizer's 256 B in / 72 B out
     is 78/22), 20/80 (the dequantizer's) and 1:1 copy, each with plain and

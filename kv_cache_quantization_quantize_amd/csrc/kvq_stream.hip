@@ -1,5 +1,5 @@
 // kvq_stream.hip -- streaming kernels that measure the practical HBM
-// bandwidth of the box for the read/write mixes of the quantizer's kernels
+// bandwidth of the GPU for the read/write mixes of the quantizer's kernels
 // (libkvq_stream.so, loaded only by the benchmark).
 //
 // A work unit is RD 16-byte chunks read and WR 16-byte chunks written: a
