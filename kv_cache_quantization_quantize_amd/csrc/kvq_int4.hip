@@ -154,6 +154,17 @@ __device__ __forceinline__ void store_nt(void* p, uint4 v)
     __builtin_nontemporal_store(u4nt{v.x, v.y, v.z, v.w}, reinterpret_cast<u4nt*>(p));
 }
 
+// A scale store takes the hint only when an item's scales fill whole
+// 128-byte lines (at least 8 bytes of scales per vector, 16 vectors per
+// item); smaller rows are left to the cache to merge: MXFP4 at head_dim 128
+// (4 bytes per vector) 4.31 -> 4.23 ms with plain scale stores.
+template <bool NT, typename T>
+__device__ __forceinline__ void store_scale(T* p, T v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 // ---------------------------------------------------------------------------
 // Quantize
 // ---------------------------------------------------------------------------
@@ -232,6 +243,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
     constexpr int NJ = S::NJ, N = S::N, NG = S::NG, LG = S::LG, CH_PER_G = S::CH_PER_G;
     // scale values a lane stores per vector
     constexpr int NSV = (G >= 32) ? (NG + 3) / 4 : NJ;
+    constexpr bool SNT = (MX ? NG : 2 * NG) >= 8;     // scale bytes per vector fill lines
 
     const int lane = threadIdx.x & 63;
     const int q = lane & 3;
@@ -348,21 +360,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_kernel(Int4Args 
                 uint8_t* sp8 = sg8 + outer_offset(a.scales, it) + s_lane;
 #pragma unroll
                 for (int k = 0; k < NSV; k++)
-                    if (4 * k + q < NG) __builtin_nontemporal_store((uint8_t)o.sv[k], sp8 + 4 * k + q);
+                    if (4 * k + q < NG) store_scale<SNT>(sp8 + 4 * k + q, (uint8_t)o.sv[k]);
             } else if constexpr (G >= 32) {
                 // lane q writes groups q, q+4, ...
 #pragma unroll
                 for (int k = 0; k < NSV; k++)
-                    if (4 * k + q < NG) __builtin_nontemporal_store(o.sv[k], sp + 4 * k + q);
+                    if (4 * k + q < NG) store_scale<SNT>(sp + 4 * k + q, o.sv[k]);
             } else if constexpr (G == 16) {
                 // lanes q and q^1 share group 2j + (q >> 1); the even lane writes
                 if ((q & 1) == 0) {
 #pragma unroll
-                    for (int j = 0; j < NJ; j++) __builtin_nontemporal_store(o.sv[j], sp + 2 * j + (q >> 1));
+                    for (int j = 0; j < NJ; j++) store_scale<SNT>(sp + 2 * j + (q >> 1), o.sv[j]);
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < NJ; j++) __builtin_nontemporal_store(o.sv[j], sp + 4 * j + q);
+                for (int j = 0; j < NJ; j++) store_scale<SNT>(sp + 4 * j + q, o.sv[j]);
             }
         }
     };
