@@ -63,6 +63,14 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
+def spread(ms):
+    """Median, minimum and maximum of a list of launch times (ms)."""
+    srt = sorted(ms)
+    n = len(srt)
+    med = srt[n // 2] if n % 2 else 0.5 * (srt[n // 2 - 1] + srt[n // 2])
+    return {"median_ms": round(med, 4), "min_ms": round(srt[0], 4), "max_ms": round(srt[-1], 4)}
+
+
 def ingest_mfma(csv_path, out_path=None):
     """Turn a rocprofv3 `--pmc <MFMA_COUNTERS>` run of `bench.py --parts vq`
     into per-kernel utilisation figures and write MFMA_FILE.
@@ -452,8 +460,7 @@ def main():
         ms = [a.elapsed_time(b) for (k, a, b) in ev if k == name]
         avg = sum(ms) / len(ms)
         gbps = nvec * bpv / (avg * 1e-3) / 1e9
-        kern[name] = {"launches": len(ms), "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4),
-                      "max_ms": round(max(ms), 4), "GB_per_s": round(gbps, 1),
+        kern[name] = {"launches": len(ms), "avg_ms": round(avg, 4), **spread(ms), "GB_per_s": round(gbps, 1),
                       "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                       "ns_per_vector": round(avg * 1e6 / nvec, 5),
                       "vectors_per_s": round(nvec / (avg * 1e-3), 1)}
@@ -739,7 +746,7 @@ def bench_d256(torch, kvq, synth, dev, args, ceil):
         ms = [a.elapsed_time(b) for a, b in pairs]
         avg = sum(ms) / len(ms)
         gbps = nvec * bpv / (avg * 1e-3) / 1e9
-        r = {"launches": len(ms), "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "GB_per_s": round(gbps, 1),
+        r = {"launches": len(ms), "avg_ms": round(avg, 4), **spread(ms), "GB_per_s": round(gbps, 1),
              "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "ns_per_vector": round(avg * 1e6 / nvec, 5),
              "vectors_per_s": round(nvec / (avg * 1e-3), 1)}
         if ceil:
@@ -799,7 +806,7 @@ def bench_variant(torch, kvq, K, lamK, signs, dims, args, kind):
         ms = [a.elapsed_time(b) for a, b in pairs]
         avg = sum(ms) / len(ms)
         gbps = nvec * bpv / (avg * 1e-3) / 1e9
-        res[name] = {"avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "GB_per_s": round(gbps, 1),
+        res[name] = {"avg_ms": round(avg, 4), **spread(ms), "GB_per_s": round(gbps, 1),
                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                      "ns_per_vector": round(avg * 1e6 / nvec, 5)}
     del codes, scales, out
@@ -849,7 +856,7 @@ def bench_attend(torch, kvq, codes, scales, lamK, lamV, signs, dims, args):
     gbps = byt / (avg * 1e-3) / 1e9
     return {"workload": "qwen3-8b-shaped decode step: %d layers x %d sequences x %d tokens, %d KV heads, "
                         "%d query heads per KV head, head_dim %d, group %d" % (L, B, Tq, H, R, D, G),
-            "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "GB_per_s": round(gbps, 1),
+            "avg_ms": round(avg, 4), **spread(ms), "GB_per_s": round(gbps, 1),
             "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_call": byt,
             "ns_per_token_head": round(avg * 1e6 / (Lo * Tq * H), 5),
             "workspace_bytes": int(ws.numel())}
@@ -905,7 +912,7 @@ def bench_vq(torch, kvq, synth, dev, args):
             torch.cuda.synchronize()
             ms.append(a.elapsed_time(b))
         avg = sum(ms) / len(ms)
-        r = {"avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "ns_per_key": round(avg * 1e6 / nkeys, 4)}
+        r = {"avg_ms": round(avg, 4), **spread(ms), "ns_per_key": round(avg * 1e6 / nkeys, 4)}
         if name in ("encode", "kmeans_step"):
             flop = nkeys * (D // sub) * cfg.n_centroids * sub * 2
             tf = flop / (avg * 1e-3) / 1e12

@@ -1,7 +1,7 @@
 """Host-side logic of bench.py, on the CPU: the one-GPU guard, the gate that
 keeps a counter-derived traffic figure only while the kernel sources match
-the ones it was taken on, and the scaling of FETCH_SIZE / WRITE_SIZE
-counters by the plain-copy reference."""
+the ones it was taken on, the scaling of FETCH_SIZE / WRITE_SIZE counters
+by the plain-copy reference, and the launch-time spread."""
 import csv
 import json
 import os
@@ -23,6 +23,13 @@ def test_bytes_per_vector():
     assert bench.bytes_per_vector(128, 32) == 256 + 64 + 8
     assert bench.bytes_per_vector(256, 64) == 512 + 128 + 8
     assert bench.bytes_per_vector(64, 8) == 128 + 32 + 16
+
+
+def test_launch_time_spread():
+    # median of an odd and an even count, with the extremes
+    assert bench.spread([3.0, 1.0, 2.0]) == {"median_ms": 2.0, "min_ms": 1.0, "max_ms": 3.0}
+    assert bench.spread([4.0, 1.0, 3.0, 2.0]) == {"median_ms": 2.5, "min_ms": 1.0, "max_ms": 4.0}
+    assert bench.spread([0.12345]) == {"median_ms": 0.1235, "min_ms": 0.1235, "max_ms": 0.1235}
 
 
 @pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})])
