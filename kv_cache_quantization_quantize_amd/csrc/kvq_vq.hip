@@ -36,9 +36,9 @@
 // What bounds the sweep (measured on MI355X with a timing probe of the
 // loop): a 32x32x16 f16 MFMA issues every 32 cycles, and the 32x32x8 norm
 // MFMA takes as long; v_max3_f32 takes about 8 cycles per wavefront, and
-// every score passes through one (16 scores per lane, group and tile: 7 max3
-// and 2 max), so with two wavefronts per SIMD the maxima cost about as much
-// SIMD time as the nine MFMAs of a tile.  The kernel therefore runs near the
+// every score passes through one (16 scores per lane, group and tile, and the
+// running best: 8 max3), so with two wavefronts per SIMD the maxima cost
+// about as much SIMD time as the nine MFMAs of a tile.  The kernel therefore runs near the
 // balance of the two units rather than at the matrix cores' peak.
 #include <type_traits>
 
@@ -122,6 +122,7 @@ __global__ __launch_bounds__((64 * VqCfg<D, IDX8>::WAVES), (VqCfg<D, IDX8>::MINW
     constexpr int NSUB = IDX8 ? 4 : 1, SUBW = 16 / NSUB;
     __shared__ uint4 cb_lds[CHUNK];                    // centroid k: 8 fp16
     __shared__ uint32_t nrm_lds[CHUNK];                // packed (n_hi, n_lo)
+    __shared__ float hn_lds[CHUNK];                    // -(n_hi + n_lo) / 2, for the re-score
     __shared__ uint4 stage[WAVES][2][16 * NS];         // [wave][hi/lo][key, sub-vector]
 
     const int lane = threadIdx.x & 63;
@@ -248,6 +249,7 @@ __global__ __launch_bounds__((64 * VqCfg<D, IDX8>::WAVES), (VqCfg<D, IDX8>::MINW
                         const _Float16 nl = (_Float16)(n - (float)nh);
                         cb_lds[cb_slot(k)] = cv;
                         nrm_lds[cb_slot(k)] = __builtin_bit_cast(uint32_t, half2_t{nh, nl});
+                        hn_lds[cb_slot(k)] = -0.5f * ((float)nh + (float)nl);
                     }
                     __syncthreads();
                     cur_cb = nchunks > 1 ? -1 : cbkey;
@@ -281,25 +283,34 @@ __global__ __launch_bounds__((64 * VqCfg<D, IDX8>::WAVES), (VqCfg<D, IDX8>::MINW
                 // through the running best, lets the running maxima keep their
                 // registers (a chain made the compiler rotate them: eight moves per
                 // tile).
-                auto epilogue = [&](const f32x16_t& acc, int gg, int tl) {
+                // The running best goes into the tree (16 scores and it: eight max3),
+                // read from bin and written to bout; with the full-tile tracking the
+                // two arrays alternate from tile to tile, so no register is copied to
+                // keep the running best in place (eight max3 and a compare and select
+                // per group and tile); the sub-block tracking, shorter on registers,
+                // updates one array in place.
+                auto epilogue = [&](const f32x16_t& acc, int gg, int tl, const float (&bin)[GPR], float (&bout)[GPR]) {
                     if constexpr (NSUB == 1) {
-                        float mx = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+                        float mx = fmaxf(fmaxf(bin[gg], acc[0]), acc[1]);
 #pragma unroll
-                        for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
-                        mx = fmaxf(mx, acc[15]);
-                        best_tile[gg] = mx > best_val[gg] ? tl : best_tile[gg];
-                        best_val[gg] = fmaxf(mx, best_val[gg]);
+                        for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
+                        best_tile[gg] = mx > bin[gg] ? tl : best_tile[gg];
+                        bout[gg] = mx;
                     } else {
+                        float b = bin[gg];
 #pragma unroll
                         for (int sb = 0; sb < NSUB; sb++) {
-                            float nb = fmaxf(best_val[gg], acc[SUBW * sb]);
+                            float nb = fmaxf(b, acc[SUBW * sb]);
 #pragma unroll
                             for (int r = 1; r < SUBW; r++) nb = fmaxf(nb, acc[SUBW * sb + r]);
-                            best_tile[gg] = nb > best_val[gg] ? tl * NSUB + sb : best_tile[gg];
-                            best_val[gg] = nb;
+                            best_tile[gg] = nb > b ? tl * NSUB + sb : best_tile[gg];
+                            b = nb;
                         }
+                        bout[gg] = b;
                     }
                 };
+                constexpr int EPI_VALU = NSUB == 1 ? 10 : 11;   // VALU operations per group's epilogue
+                float best_alt[GPR];
                 f32x16_t acc[GPR], nt0, nt1;
                 h8_t a_op;
                 h4_t a_n2;
@@ -311,11 +322,11 @@ __global__ __launch_bounds__((64 * VqCfg<D, IDX8>::WAVES), (VqCfg<D, IDX8>::MINW
                 read_a(min(1, ntiles - 1), a_op, a_n2);
                 // tile tl: the maxima of tile tl - 1, then tile tl's MFMAs; the norm
                 // tiles alternate between two registers sets (unrolled by two)
-                auto step = [&](int tl, f32x16_t& nt) {
+                auto step = [&](int tl, f32x16_t& nt, const float (&bin)[GPR], float (&bout)[GPR]) {
                     nt = norm_tile(a_n2);
 #pragma unroll
                     for (int gg = 0; gg < GPR; gg++) {
-                        epilogue(acc[gg], gg, tl - 1);
+                        epilogue(acc[gg], gg, tl - 1, bin, bout);
                         acc[gg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op, bop[gg], nt, 0, 0, 0);
                     }
                     read_a(min(tl + 1, ntiles - 1), a_op, a_n2);
@@ -323,18 +334,30 @@ __global__ __launch_bounds__((64 * VqCfg<D, IDX8>::WAVES), (VqCfg<D, IDX8>::MINW
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
                     for (int gg = 0; gg < GPR; gg++) {
-                        __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, EPI_VALU, 0);
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     }
                 };
-                int tl = 1;
-                for (; tl + 1 < ntiles; tl += 2) {
-                    step(tl, nt1);
-                    step(tl + 1, nt0);
-                }
-                if (tl < ntiles) step(tl, nt1);
+                // tile pairs take the running best from best_val to nxt and back
+                auto sweep = [&](float (&nxt)[GPR]) {
+                    int tl = 1;
+                    for (; tl + 1 < ntiles; tl += 2) {
+                        step(tl, nt1, best_val, nxt);
+                        step(tl + 1, nt0, nxt, best_val);
+                    }
+                    if (tl < ntiles) {
+                        step(tl, nt1, best_val, nxt);
 #pragma unroll
-                for (int gg = 0; gg < GPR; gg++) epilogue(acc[gg], gg, ntiles - 1);
+                        for (int gg = 0; gg < GPR; gg++) epilogue(acc[gg], gg, ntiles - 1, nxt, best_val);
+                    } else {
+#pragma unroll
+                        for (int gg = 0; gg < GPR; gg++) epilogue(acc[gg], gg, ntiles - 1, best_val, nxt);
+#pragma unroll
+                        for (int gg = 0; gg < GPR; gg++) best_val[gg] = nxt[gg];
+                    }
+                };
+                if constexpr (NSUB == 1) sweep(best_alt);
+                else sweep(best_val);
 
                 // ---- lanes whose best moved into this chunk find its position -------
                 // The GPR groups' candidates are scored together, one candidate row
@@ -366,26 +389,30 @@ __global__ __launch_bounds__((64 * VqCfg<D, IDX8>::WAVES), (VqCfg<D, IDX8>::MINW
 #pragma unroll
                     for (int rr = 0; rr < SUBW; rr++) {
                         uint4 cv[GPR];
-                        uint32_t nw[GPR];
+                        float sc[GPR];
                         int kk[GPR];
 #pragma unroll
                         for (int gg = 0; gg < GPR; gg++) {
                             const int r = r0[gg] + rr;
                             kk[gg] = bt[gg] * 32 + 8 * (r / 4) + 4 * half + (r % 4);
                             cv[gg] = cb_lds[cb_slot(kk[gg])];
-                            nw[gg] = nrm_lds[cb_slot(kk[gg])];
+                            sc[gg] = hn_lds[cb_slot(kk[gg])];
+                        }
+                        // the groups' dot products step by step, so that their
+                        // dependent fma chains interleave
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+#pragma unroll
+                            for (int gg = 0; gg < GPR; gg++) {
+                                const uint32_t w = e == 0 ? cv[gg].x : e == 1 ? cv[gg].y : e == 2 ? cv[gg].z : cv[gg].w;
+                                sc[gg] = fmaf(lo_half(w), y[gg][2 * e], sc[gg]);
+                                sc[gg] = fmaf(hi_half(w), y[gg][2 * e + 1], sc[gg]);
+                            }
                         }
 #pragma unroll
                         for (int gg = 0; gg < GPR; gg++) {
-                            const uint32_t w[4] = {cv[gg].x, cv[gg].y, cv[gg].z, cv[gg].w};
-                            float sc = -0.5f * (lo_half(nw[gg]) + hi_half(nw[gg]));
-#pragma unroll
-                            for (int e = 0; e < 4; e++) {
-                                sc = fmaf(lo_half(w[e]), y[gg][2 * e], sc);
-                                sc = fmaf(hi_half(w[e]), y[gg][2 * e + 1], sc);
-                            }
-                            if (sc > bs[gg]) {
-                                bs[gg] = sc;
+                            if (sc[gg] > bs[gg]) {
+                                bs[gg] = sc[gg];
                                 bk[gg] = kk[gg];
                             }
                         }
