@@ -342,12 +342,61 @@ __device__ __forceinline__ void unpack_twiddle(int q, float scale, float& cw, fl
     sw = fmaf(cs, lc, cc * ls);
 }
 
+// The forward transform's twiddles as a table row in LDS: the FFT twiddles
+// of Tw (l0, l1, j), then the Hermitian unpacking's (cos, sin) pair of every
+// register.  A wavefront keeps one row per quad lane q, and the quantizer
+// reads its row back per item instead of holding 50 values in registers
+// across items: that takes the head_dim-128 SRFT quantizer from 201 to 153
+// VGPRs, three wavefronts per SIMD instead of two.  (At head_dim 256 it
+// would go from 326 to 232 VGPRs, two wavefronts instead of one, but
+// measured 2.5% slower; that quantizer keeps its twiddles in registers.)
+template <int D>
+struct TwRow {
+    using T = Tw<D, -1>;
+    static constexpr int L0 = 0, L1 = 2, J = 5, U = 5 + T::NJT, N = U + D / 8;
+};
+
+template <int D>
+__device__ __forceinline__ void write_twiddle_row(float2* row, int q)
+{
+    using R = TwRow<D>;
+    const Tw<D, -1> t = make_twiddles<D, -1>(q);
+#pragma unroll
+    for (int k = 0; k < 2; k++) row[R::L0 + k] = make_float2(t.l0r[k], t.l0i[k]);
+#pragma unroll
+    for (int k = 0; k < 3; k++) row[R::L1 + k] = make_float2(t.l1r[k], t.l1i[k]);
+#pragma unroll
+    for (int k = 0; k < Tw<D, -1>::NJT; k++) row[R::J + k] = make_float2(t.jr[k], t.ji[k]);
+    static_for<0, D / 8>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        float cw, sw;
+        unpack_twiddle<D, i>(q, 1.0f, cw, sw);
+        row[R::U + i] = make_float2(cw, sw);
+    });
+}
+
+template <int D>
+__device__ __forceinline__ Tw<D, -1> read_twiddles(const float2* row)
+{
+    using R = TwRow<D>;
+    Tw<D, -1> t;
+#pragma unroll
+    for (int k = 0; k < 2; k++) { const float2 w = row[R::L0 + k]; t.l0r[k] = w.x; t.l0i[k] = w.y; }
+#pragma unroll
+    for (int k = 0; k < 3; k++) { const float2 w = row[R::L1 + k]; t.l1r[k] = w.x; t.l1i[k] = w.y; }
+#pragma unroll
+    for (int k = 0; k < Tw<D, -1>::NJT; k++) { const float2 w = row[R::J + k]; t.jr[k] = w.x; t.ji[k] = w.y; }
+    return t;
+}
+
 // Forward SRFT of the quad's vector, in place on v (natural layout, values
 // already multiplied by s * lambda / sqrt(D), and by 1/sqrt2, which the
 // unpacking's weights would otherwise apply): afterwards v holds y times
-// sigma(q).  row: the quad's LDS row of N float2.
-template <int D>
-__device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, const Tw<D, -1>& tw)
+// sigma(q).  row: the quad's LDS row of N float2; tw: the FFT twiddles;
+// utw(integral_constant i): the unpacking's (cos, sin) pair of register i.
+template <int D, typename UnpackTw>
+__device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, const Tw<D, -1>& tw,
+                                        UnpackTw&& utw)
 {
     constexpr int P = D / 8;
     float c[D / 4];
@@ -364,8 +413,8 @@ __device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, c
     constexpr float sqrt2 = 1.41421356237309504880f;
     static_for<0, P>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
-        float cw, sw;
-        unpack_twiddle<D, i>(q, 1.0f, cw, sw);
+        const float2 u = utw(ii);
+        const float cw = u.x, sw = u.y;
         const float a = c[i], b = c[P + i], cc = pc[i], d = pc[P + i];
         float s1, d1, s2, d2;
         if constexpr (i % 4 == 0) {
@@ -386,6 +435,25 @@ __device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, c
         v[8 * (i / 4) + 2 * (i % 4)] = y0;
         v[8 * (i / 4) + 2 * (i % 4) + 1] = y1;
     });
+}
+
+// forward with every twiddle held in registers (tw built once per kernel)
+template <int D>
+__device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, const Tw<D, -1>& tw)
+{
+    forward<D>(v, row, q, tw, [&](auto ii) {
+        float cw, sw;
+        unpack_twiddle<D, decltype(ii)::value>(q, 1.0f, cw, sw);
+        return make_float2(cw, sw);
+    });
+}
+
+// forward with the twiddles read from the lane's LDS row (TwRow)
+template <int D>
+__device__ __forceinline__ void forward(float (&v)[D / 4], float2* row, int q, const float2* twrow)
+{
+    forward<D>(v, row, q, read_twiddles<D>(twrow),
+               [&](auto ii) { return twrow[TwRow<D>::U + decltype(ii)::value]; });
 }
 
 // Inverse SRFT of the quad's vector, in place on v (natural layout, true
